@@ -1,0 +1,192 @@
+/*
+ * locks.h — C ABI of liblocks.so, the MI355X (gfx950) LOCKS decode path.
+ *
+ * Sources cited below:
+ *   (A) blog post "LOCKS: per-page SVD cuts KV-cache reads 10x at 1M context"
+ *       (sections "How LOCKS works", "Code", "Results", "Caveats");
+ *   (B) technical summary "LOCKS – 효율적인 롱 컨텍스트 디코딩을 위한 페이지 로컬
+ *       압축 키 요약" on gist.science, paper 2607.24555 (section 2 "방법론",
+ *       mechanisms 1-4).
+ *
+ * What the library computes (one decode step, one query token per sequence):
+ *   1. score every 16-token KV page from its compressed key summary alone
+ *      (A "How LOCKS works", page-score equation; B mechanism 2);
+ *   2. turn the per-head scores into one key per (sequence, KV head) by
+ *      averaging each head's normalised mass share over the GQA group
+ *      (B mechanism 3);
+ *   3. keep the k = budget/16 pages with the largest key (A "Code", top-k);
+ *   4. run exact softmax attention over the kept pages only, renormalised
+ *      over the kept tokens (A "Code", sparse attention).
+ * The summary build (A "How LOCKS works", summary list; B mechanism 1) is a
+ * separate, off-critical-path call.
+ *
+ * Conventions for every entry point:
+ *  - All array arguments are DEVICE pointers owned by the caller; the library
+ *    never allocates, frees, copies host<->device or synchronises inside a
+ *    call. Work is enqueued on `stream` and is asynchronous; results are
+ *    valid once the stream reaches that point.
+ *  - Arguments are checked on the host before anything is enqueued. A failed
+ *    check returns a negative locks_status and enqueues nothing;
+ *    locks_last_error() then describes it. Nothing is thrown across the ABI.
+ *  - Identical inputs give bitwise-identical outputs (no float atomics).
+ *  - Supported shape: head_dim 128, page_size 16, rank 8,
+ *    1 <= n_q_heads/n_kv_heads <= 16 (n_q_heads % n_kv_heads == 0).
+ *    Other values return LOCKS_ERR_UNSUPPORTED.
+ *  - Page table: page_table[b*max_pages_per_seq + j] is the physical block
+ *    that holds logical page j of sequence b. Sequence b has
+ *    n_b = min(seq_lens[b] / 16, max_pages_per_seq) full pages; tokens after
+ *    the last full page are ignored (summaries exist only for full pages,
+ *    A "How LOCKS works"). A block id outside [0, num_blocks) marks an absent
+ *    page: it is never read, never scored and never selected.
+ *  - Query head h uses KV head h / G, G = n_q_heads / n_kv_heads.
+ *
+ * Layouts (row-major, C order):
+ *   k_cache, v_cache  bf16  [num_blocks][n_kv_heads][16][128]
+ *   summaries         u8    [num_blocks][n_kv_heads][LOCKS_SUMMARY_STRIDE]
+ *   q                 f32   [batch][n_q_heads][128]
+ *   out               f32   [batch][n_q_heads][128]
+ *   selected          i32   [batch][n_kv_heads][budget/16]
+ *   page_scores       f32   [batch][n_q_heads][max_pages_per_seq]
+ *
+ * Summary record (one per physical block and KV head, A "How LOCKS works",
+ * B mechanism 1; every scale is an fp16 per-page absmax scale):
+ *   bytes [  0, 512)  V codes, k-major: for k in 0..7, 16 little-endian u32
+ *                     words w = 0..15; byte b (0..3) of word w holds
+ *                     V[8w+b][k] in its low nibble and V[8w+4+b][k] in its
+ *                     high nibble, 4-bit two's complement, range -7..7.
+ *   bytes [512, 640)  mu codes, int8[128], range -127..127.
+ *   bytes [640, 768)  C codes, int8[16][8] (token-major), range -127..127.
+ *   bytes [768, 776)  fp16 scales {s_mu, s_V, s_C, 0}.
+ *   bytes [776, 832)  zero padding (keeps each record 64-byte aligned).
+ *   Dequantised: mu = s_mu*mu_code, V = s_V*V_code, C = s_C*C_code.
+ */
+#ifndef LOCKS_H
+#define LOCKS_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LOCKS_HEAD_DIM 128
+#define LOCKS_PAGE_SIZE 16
+#define LOCKS_RANK 8
+#define LOCKS_SUMMARY_STRIDE 832
+#define LOCKS_SUMMARY_PAYLOAD 776
+#define LOCKS_MAX_GROUP 16
+
+typedef struct locks_dims {
+  int32_t batch;             /* B, sequences (one query token each) */
+  int32_t n_q_heads;         /* Hq */
+  int32_t n_kv_heads;        /* Hkv; G = Hq / Hkv query heads share a KV head */
+  int32_t head_dim;          /* must be 128 */
+  int32_t page_size;         /* must be 16 */
+  int32_t rank;              /* must be 8 */
+  int32_t max_pages_per_seq; /* row length of page_table */
+  int32_t num_blocks;        /* physical blocks in k_cache / v_cache / summaries */
+} locks_dims;
+
+typedef enum locks_status {
+  LOCKS_OK = 0,
+  LOCKS_ERR_INVALID_ARG = -1, /* NULL/misaligned pointer, bad size or budget */
+  LOCKS_ERR_UNSUPPORTED = -2, /* shape outside the supported set */
+  LOCKS_ERR_WORKSPACE = -3,   /* workspace smaller than locks_workspace_bytes */
+  LOCKS_ERR_HIP = -4          /* a launch failed; see locks_last_error() */
+} locks_status;
+
+/* Bytes per summary record (LOCKS_SUMMARY_STRIDE). */
+size_t locks_summary_record_bytes(void);
+
+/* Message for the last failed call on this thread ("" if none). The pointer
+ * stays valid until the next call on the same thread. */
+const char* locks_last_error(void);
+
+/* Workspace bytes that locks_decode_step (and its three phases) and
+ * locks_dense_attention need for these dims and budget. Pure host call.
+ * budget_tokens must be a positive multiple of 16 (A "Code": the page count
+ * is the token budget divided by the page size); pass 16 when sizing for
+ * locks_dense_attention alone. */
+locks_status locks_workspace_bytes(const locks_dims* dims, int32_t budget_tokens,
+                                   size_t* out_bytes);
+
+/* Builds the summary record of every full page of every sequence (A "How LOCKS
+ * works": centroid, rank-8 basis of the centred keys, per-token coefficients;
+ * B mechanism 1: eigendecomposition of the page's small Gram matrix, int4
+ * basis, int8 centroid and coefficients). For each (b, j < n_b, kv head) it
+ * reads the 16x128 key tile of block page_table[b][j] and writes that block's
+ * record. Records of blocks no sequence references are left untouched; a block
+ * referenced twice is written twice with identical bytes.
+ * k_cache: bf16 keys; summaries: 16-byte aligned output. */
+locks_status locks_build_summaries(const locks_dims* dims, const void* k_cache,
+                                   const int32_t* page_table, const int32_t* seq_lens,
+                                   void* summaries, hipStream_t stream);
+
+/* One LOCKS decode step = locks_score_pages + locks_select_pages +
+ * locks_sparse_attention on the same workspace.
+ *  q            f32 queries, one token per sequence.
+ *  summaries    records written by locks_build_summaries (or any records in
+ *               the documented format).
+ *  budget_tokens  positive multiple of 16; k = budget_tokens / 16 pages are
+ *               kept per (sequence, KV head).
+ *  out          f32 attention output; heads of a sequence with n_b == 0 get 0.
+ *  selected     kept logical page ids per (sequence, KV head) in ascending
+ *               order; when fewer than k pages exist, the tail is -1.
+ *  page_scores  optional (NULL = not written): per-head page score s_hat
+ *               (A page-score equation); entries j >= n_b are not written.
+ *  workspace    >= locks_workspace_bytes(dims, budget_tokens) bytes of device
+ *               memory, 256-byte aligned, ZERO-FILLED before its first use;
+ *               every call leaves it reusable. Calls sharing a workspace must
+ *               be stream-ordered. */
+locks_status locks_decode_step(const locks_dims* dims, const float* q, const void* summaries,
+                               const void* k_cache, const void* v_cache,
+                               const int32_t* page_table, const int32_t* seq_lens,
+                               int32_t budget_tokens, float* out, int32_t* selected,
+                               float* page_scores, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
+/* Phase 1 of the step: per-head page scores s_hat[b][h][j] (A "How LOCKS
+ * works", page-score equation; B mechanism 2) computed from the summaries
+ * only — no key or value byte is read — plus the per-head partial
+ * log-sum-exp terms the group combine needs. Results stay in the workspace
+ * (and in page_scores when it is not NULL). */
+locks_status locks_score_pages(const locks_dims* dims, const float* q, const void* summaries,
+                               const int32_t* page_table, const int32_t* seq_lens,
+                               int32_t budget_tokens, float* page_scores, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream);
+
+/* Phase 2: group combine (B mechanism 3: every head's mass share averaged over
+ * the GQA group) and top-k (A "Code": top-k by score, ids sorted ascending).
+ * Ties between equal keys go to the lower page id. Must follow
+ * locks_score_pages on the same workspace, budget and page_scores argument. */
+locks_status locks_select_pages(const locks_dims* dims, const int32_t* page_table,
+                                const int32_t* seq_lens, int32_t budget_tokens,
+                                int32_t* selected, const float* page_scores, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream);
+
+/* Phase 3: exact attention over the selected pages only (A "Code": attention
+ * over the gathered tokens of the kept pages, softmax scale 1/sqrt(128)).
+ * `selected` may come from locks_select_pages or from the caller: entries < 0
+ * or >= n_b are skipped; ids should be distinct. */
+locks_status locks_sparse_attention(const locks_dims* dims, const float* q,
+                                    const void* k_cache, const void* v_cache,
+                                    const int32_t* page_table, const int32_t* seq_lens,
+                                    int32_t budget_tokens, const int32_t* selected, float* out,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Dense decode attention over every full page (A "Code": the full-KV
+ * comparison; A "Results": the dense baseline the speed-ups are quoted
+ * against). Same layouts and workspace rules as locks_decode_step; size the
+ * workspace with budget_tokens = 16. */
+locks_status locks_dense_attention(const locks_dims* dims, const float* q, const void* k_cache,
+                                   const void* v_cache, const int32_t* page_table,
+                                   const int32_t* seq_lens, float* out, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LOCKS_H */

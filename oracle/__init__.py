@@ -1,0 +1,276 @@
+"""fp64 CPU oracle of the LOCKS decode path — TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s CPU-baseline leg
+import this package. It wraps ``locks_oracle.c`` (plain C, double precision)
+with ctypes and numpy arrays; it never touches the GPU library, and the GPU
+library never touches it.
+
+Sources, cited by title and section:
+  (A) "LOCKS: per-page SVD cuts KV-cache reads 10x at 1M context" — "How LOCKS
+      works" (summary contents, page-score equation), "Code" (build, scoring,
+      top-k and attention steps).
+  (B) "LOCKS – 효율적인 롱 컨텍스트 디코딩을 위한 페이지 로컬 압축 키 요약"
+      (gist.science, paper 2607.24555) — section 2, mechanisms 1-3.
+
+Parity pins for every function are in ``tests/test_oracle_pins.py`` and
+``tests/test_oracle_units.py``. The QUANTISED scores and selections have no pin
+other than their pieces (the quantiser, the pack format and the unquantised
+score each are pinned; their composition is not): "parity unpinned" for the
+quantised end-to-end numbers.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "locks_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liblocks_oracle.so")
+
+PAGE = 16
+DIM = 128
+RANK = 8
+RECORD_BYTES = 832
+
+
+def build(force: bool = True) -> str:
+    """Compile locks_oracle.c with gcc (-O2, OpenMP). Returns the .so path."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=gnu11", "-Wall",
+               "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build(force=True)
+        L = ctypes.CDLL(_LIB_PATH)
+        P = ctypes.c_void_p
+        I = ctypes.c_int
+        L.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
+        L.oracle_bf16_to_double.restype = ctypes.c_double
+        L.oracle_f16_to_double.argtypes = [ctypes.c_uint16]
+        L.oracle_f16_to_double.restype = ctypes.c_double
+        L.oracle_double_to_f16.argtypes = [ctypes.c_double]
+        L.oracle_double_to_f16.restype = ctypes.c_uint16
+        L.oracle_jacobi_eigh.argtypes = [I, P, P, P]
+        L.oracle_jacobi_eigh.restype = I
+        L.oracle_page_summary_f64.argtypes = [P, I, P, P, P, P]
+        L.oracle_page_summary_f64.restype = None
+        L.oracle_build_record.argtypes = [P, P, P, P, P, P]
+        L.oracle_build_record.restype = None
+        L.oracle_unpack_record.argtypes = [P, P, P, P]
+        L.oracle_unpack_record.restype = None
+        L.oracle_build_summaries.argtypes = [I, I, I, I, P, P, P, P]
+        L.oracle_build_summaries.restype = None
+        L.oracle_page_score_f64.argtypes = [P, P, P, P, I]
+        L.oracle_page_score_f64.restype = ctypes.c_double
+        L.oracle_exact_page_lse.argtypes = [P, P]
+        L.oracle_exact_page_lse.restype = ctypes.c_double
+        L.oracle_scores.argtypes = [I, I, I, I, I, P, P, P, P, P]
+        L.oracle_scores.restype = None
+        L.oracle_group_keys.argtypes = [I, I, I, I, P, P]
+        L.oracle_group_keys.restype = None
+        L.oracle_select.argtypes = [I, I, I, P, I, P]
+        L.oracle_select.restype = None
+        L.oracle_attention.argtypes = [I, I, I, I, I, P, P, P, P, P, P, I, P]
+        L.oracle_attention.restype = None
+        L.oracle_decode_step.argtypes = [I, I, I, I, I, P, P, P, P, P, P, I, P, P, P, P]
+        L.oracle_decode_step.restype = None
+        L.oracle_num_threads.argtypes = []
+        L.oracle_num_threads.restype = I
+        _lib = L
+    return _lib
+
+
+def _ptr(a: np.ndarray | None):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"], "oracle arrays must be C-contiguous"
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _as(a, dtype) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def num_threads() -> int:
+    return int(lib().oracle_num_threads())
+
+
+# ---------------------------------------------------------------- formats
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16/int16) -> float64, exactly."""
+    b = np.asarray(bits).astype(np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def f16_bits_to_f64(h: int) -> float:
+    return float(lib().oracle_f16_to_double(int(h) & 0xFFFF))
+
+
+def f64_to_f16_bits(x: float) -> int:
+    return int(lib().oracle_double_to_f16(float(x)))
+
+
+# ---------------------------------------------------------------- build
+
+def jacobi_eigh(a: np.ndarray):
+    """Cyclic Jacobi on a symmetric matrix: (eigenvalues, eigenvectors as columns, sweeps)."""
+    a = _as(a, np.float64).copy()
+    n = a.shape[0]
+    w = np.zeros(n)
+    u = np.zeros((n, n))
+    sweeps = lib().oracle_jacobi_eigh(n, _ptr(a), _ptr(w), _ptr(u))
+    return w, u, sweeps
+
+
+def page_summary_f64(keys: np.ndarray, rank: int = RANK):
+    """Unquantised rank-r summary of one page (keys: 16x128 float64).
+
+    Returns mu[128], V[128, r], C[16, r], lam[16] (descending)."""
+    keys = _as(keys, np.float64)
+    assert keys.shape == (PAGE, DIM) and 1 <= rank <= 15
+    mu = np.zeros(DIM)
+    V = np.zeros((DIM, rank))
+    C = np.zeros((PAGE, rank))
+    lam = np.zeros(PAGE)
+    lib().oracle_page_summary_f64(_ptr(keys), rank, _ptr(mu), _ptr(V), _ptr(C), _ptr(lam))
+    return mu, V, C, lam
+
+
+def build_record(keys_bf16: np.ndarray):
+    """Quantised 832-byte record of one page from its 16x128 bf16 bits.
+
+    Returns (record uint8[832], lam[16], mu, V, C unquantised)."""
+    kb = _as(keys_bf16, np.uint16)
+    assert kb.shape == (PAGE, DIM)
+    rec = np.zeros(RECORD_BYTES, dtype=np.uint8)
+    lam = np.zeros(PAGE)
+    mu = np.zeros(DIM)
+    V = np.zeros((DIM, RANK))
+    C = np.zeros((PAGE, RANK))
+    lib().oracle_build_record(_ptr(kb), _ptr(rec), _ptr(lam), _ptr(mu), _ptr(V), _ptr(C))
+    return rec, lam, mu, V, C
+
+
+def unpack_record(rec: np.ndarray):
+    """Dequantised (mu[128], V[128, 8], C[16, 8]) of one record."""
+    rec = _as(rec, np.uint8)
+    assert rec.shape == (RECORD_BYTES,)
+    mu = np.zeros(DIM)
+    V = np.zeros((DIM, RANK))
+    C = np.zeros((PAGE, RANK))
+    lib().oracle_unpack_record(_ptr(rec), _ptr(mu), _ptr(V), _ptr(C))
+    return mu, V, C
+
+
+def build_summaries(k_cache_bits: np.ndarray, page_table: np.ndarray, seq_lens: np.ndarray,
+                    summaries: np.ndarray | None = None) -> np.ndarray:
+    """Records for every full page. k_cache_bits: uint16 [num_blocks, Hkv, 16, 128]."""
+    kc = _as(k_cache_bits, np.uint16)
+    nb, hkv = kc.shape[0], kc.shape[1]
+    pt = _as(page_table, np.int32)
+    sl = _as(seq_lens, np.int32)
+    if summaries is None:
+        summaries = np.zeros((nb, hkv, RECORD_BYTES), dtype=np.uint8)
+    lib().oracle_build_summaries(pt.shape[0], hkv, pt.shape[1], nb, _ptr(kc), _ptr(pt),
+                                 _ptr(sl), _ptr(summaries))
+    return summaries
+
+
+# ---------------------------------------------------------------- decode
+
+def page_score_f64(q: np.ndarray, mu: np.ndarray, V: np.ndarray, C: np.ndarray) -> float:
+    """s_hat for one head and one page from (unquantised or dequantised) summaries."""
+    q = _as(q, np.float64)
+    V = _as(V, np.float64)
+    C = _as(C, np.float64)
+    r = V.shape[1]
+    assert V.shape == (DIM, r) and C.shape == (PAGE, r)
+    return float(lib().oracle_page_score_f64(_ptr(q), _ptr(_as(mu, np.float64)), _ptr(V),
+                                             _ptr(C), r))
+
+
+def exact_page_lse(q: np.ndarray, keys: np.ndarray) -> float:
+    """log sum_i exp(q.k_i / sqrt(128)) over a page's real keys."""
+    return float(lib().oracle_exact_page_lse(_ptr(_as(q, np.float64)),
+                                             _ptr(_as(keys, np.float64))))
+
+
+def scores(q, summaries, page_table, seq_lens, num_kv_heads: int) -> np.ndarray:
+    """s_hat[b, h, j] (float64; -inf for absent pages and j >= n_b)."""
+    q = _as(q, np.float32)
+    B, Hq, _ = q.shape
+    pt = _as(page_table, np.int32)
+    sm = _as(summaries, np.uint8)
+    out = np.zeros((B, Hq, pt.shape[1]))
+    lib().oracle_scores(B, Hq, num_kv_heads, pt.shape[1], sm.shape[0], _ptr(q), _ptr(sm),
+                        _ptr(pt), _ptr(_as(seq_lens, np.int32)), _ptr(out))
+    return out
+
+
+def group_keys(scores_: np.ndarray, num_kv_heads: int) -> np.ndarray:
+    s = _as(scores_, np.float64)
+    B, Hq, N = s.shape
+    out = np.zeros((B, num_kv_heads, N))
+    lib().oracle_group_keys(B, Hq, num_kv_heads, N, _ptr(s), _ptr(out))
+    return out
+
+
+def select(keys: np.ndarray, k: int) -> np.ndarray:
+    kk = _as(keys, np.float64)
+    B, Hkv, N = kk.shape
+    out = np.zeros((B, Hkv, k), dtype=np.int32)
+    lib().oracle_select(B, Hkv, N, _ptr(kk), k, _ptr(out))
+    return out
+
+
+def attention(q, k_cache_bits, v_cache_bits, page_table, seq_lens, selected=None) -> np.ndarray:
+    """Attention over the listed pages (selected[b, kvh, :]) or, with None, every full page."""
+    q = _as(q, np.float32)
+    B, Hq, _ = q.shape
+    kc = _as(k_cache_bits, np.uint16)
+    vc = _as(v_cache_bits, np.uint16)
+    pt = _as(page_table, np.int32)
+    hkv = kc.shape[1]
+    sel = None if selected is None else _as(selected, np.int32)
+    k = 0 if sel is None else sel.shape[2]
+    out = np.zeros((B, Hq, DIM))
+    lib().oracle_attention(B, Hq, hkv, pt.shape[1], kc.shape[0], _ptr(q), _ptr(kc), _ptr(vc),
+                           _ptr(pt), _ptr(_as(seq_lens, np.int32)), _ptr(sel), k, _ptr(out))
+    return out
+
+
+def decode_step(q, summaries, k_cache_bits, v_cache_bits, page_table, seq_lens,
+                budget_tokens: int):
+    """Whole step: returns (out[B,Hq,128], selected[B,Hkv,k], scores, keys)."""
+    q = _as(q, np.float32)
+    B, Hq, _ = q.shape
+    kc = _as(k_cache_bits, np.uint16)
+    vc = _as(v_cache_bits, np.uint16)
+    pt = _as(page_table, np.int32)
+    sm = _as(summaries, np.uint8)
+    hkv = kc.shape[1]
+    N = pt.shape[1]
+    k = budget_tokens // PAGE
+    out = np.zeros((B, Hq, DIM))
+    sel = np.zeros((B, hkv, k), dtype=np.int32)
+    sc = np.zeros((B, Hq, N))
+    ky = np.zeros((B, hkv, N))
+    lib().oracle_decode_step(B, Hq, hkv, N, kc.shape[0], _ptr(q), _ptr(sm), _ptr(kc), _ptr(vc),
+                             _ptr(pt), _ptr(_as(seq_lens, np.int32)), budget_tokens, _ptr(out),
+                             _ptr(sel), _ptr(sc), _ptr(ky))
+    return out, sel, sc, ky

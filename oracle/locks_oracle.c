@@ -1,0 +1,558 @@
+/*
+ * locks_oracle.c — plain, slow fp64 CPU oracle of the LOCKS decode path.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing in the product (the HIP library and its
+ * Python binding) includes, links, loads or calls this file; only the tests,
+ * the smoke check and the benchmark's CPU-baseline leg do. It shares no code,
+ * header, table or constant with the GPU path: the record format below is
+ * re-derived here from its documented definition.
+ *
+ * Sources (cited by title and section):
+ *   (A) "LOCKS: per-page SVD cuts KV-cache reads 10x at 1M context" — sections
+ *       "How LOCKS works" (summary contents, page-score equation), "Code"
+ *       (build loop, scoring loop, top-k, attention), "Caveats".
+ *   (B) "LOCKS – 효율적인 롱 컨텍스트 디코딩을 위한 페이지 로컬 압축 키 요약"
+ *       (gist.science, paper 2607.24555) — section 2, mechanism 1 (page-local
+ *       eigendecomposition, int4 basis, int8 coefficients and centroid, r = 8,
+ *       page size 16), mechanism 2 (reconstructed in-page logits and their
+ *       log-sum-exp), mechanism 3 (GQA group-shared selection).
+ *
+ * All arithmetic is double precision on the exact input bits (bf16 keys and
+ * values, fp32 queries). Each step is written in the order the pages give it;
+ * the only library routines are libm's exp/log/sqrt/rint and qsort.
+ * OpenMP only spreads independent (page, head) or (sequence, KV head) units
+ * over threads; it changes no arithmetic.
+ *
+ * Readings of points the pages leave open (each is listed in the design
+ * notes): one fp16 absmax scale per tensor per page; symmetric ranges +-127
+ * (int8) and +-7 (int4), round half to even; coefficients taken from the
+ * unquantised basis; Jacobi on the 16x16 Gram of the centred keys; group key =
+ * log of the group-mean normalised mass share; top-k ties to the lower page
+ * id; ids output ascending.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define OD 128        /* head dimension */
+#define OP 16         /* tokens per page */
+#define OR 8          /* rank of the shipped summary */
+#define OSTRIDE 832   /* bytes per summary record */
+#define OV_OFF 0      /* V codes */
+#define OMU_OFF 512   /* centroid codes */
+#define OC_OFF 640    /* coefficient codes */
+#define OS_OFF 768    /* fp16 scales */
+
+/* ------------------------------------------------------------------ */
+/* Number formats                                                       */
+/* ------------------------------------------------------------------ */
+
+/* bf16 is the top half of an IEEE binary32. */
+double oracle_bf16_to_double(uint16_t b) {
+  uint32_t u = ((uint32_t)b) << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+/* IEEE binary16 (1 sign, 5 exponent bits with bias 15, 10 fraction bits). */
+double oracle_f16_to_double(uint16_t h) {
+  int sign = (h >> 15) & 1;
+  int e = (h >> 10) & 0x1f;
+  int m = h & 0x3ff;
+  double v;
+  if (e == 0)
+    v = ldexp((double)m, -24); /* subnormal: m * 2^-24 */
+  else if (e == 31)
+    v = m ? NAN : INFINITY;
+  else
+    v = ldexp((double)(1024 + m), e - 25); /* (1 + m/1024) * 2^(e-15) */
+  return sign ? -v : v;
+}
+
+/* Round a double to the nearest binary16, ties to even; returns the bits. */
+uint16_t oracle_double_to_f16(double x) {
+  uint16_t sign = 0;
+  if (x < 0 || (x == 0 && signbit(x))) { sign = 0x8000; x = -x; }
+  if (isnan(x)) return 0x7e00;
+  if (x == 0) return sign;
+  /* 65520 = largest finite (65504) plus half its spacing: ties go to even = inf */
+  if (x >= 65520.0) return sign | 0x7c00;
+  int e2;
+  frexp(x, &e2);                  /* x = f * 2^e2, f in [0.5, 1) -> binade 2^(e2-1) */
+  int e = e2 - 1;                 /* x in [2^e, 2^(e+1)) */
+  double quantum = (e < -14) ? ldexp(1.0, -24) : ldexp(1.0, e - 10);
+  double n = rint(x / quantum);   /* exact division by a power of two; ties to even */
+  double v = n * quantum;
+  if (v >= 65520.0) return sign | 0x7c00;
+  if (v < ldexp(1.0, -14)) {      /* subnormal (or rounded up to the smallest normal) */
+    uint32_t m = (uint32_t)rint(v / ldexp(1.0, -24));
+    return sign | (uint16_t)m;    /* m == 1024 encodes 2^-14 correctly */
+  }
+  int ev;
+  frexp(v, &ev);
+  ev -= 1;
+  uint32_t frac = (uint32_t)rint((v / ldexp(1.0, ev) - 1.0) * 1024.0);
+  return sign | (uint16_t)(((ev + 15) << 10) | frac);
+}
+
+/* Symmetric absmax quantiser: scale = fp16(absmax / qmax) (ties to even),
+ * code = clamp(round_half_even(x / scale), -qmax, qmax); a zero scale gives
+ * zero codes. Writes the scale's fp16 bits. */
+static void quantize_block(const double* x, int n, int qmax, int* codes, uint16_t* scale_bits) {
+  double amax = 0;
+  for (int i = 0; i < n; i++) amax = fmax(amax, fabs(x[i]));
+  uint16_t sb = oracle_double_to_f16(amax / (double)qmax);
+  double s = oracle_f16_to_double(sb);
+  *scale_bits = sb;
+  for (int i = 0; i < n; i++) {
+    if (s == 0 || isinf(s)) { codes[i] = 0; continue; }
+    double c = rint(x[i] / s);
+    if (c > qmax) c = qmax;
+    if (c < -qmax) c = -qmax;
+    codes[i] = (int)c;
+  }
+}
+
+/* ------------------------------------------------------------------ */
+/* Symmetric eigendecomposition: cyclic Jacobi (Golub & Van Loan,       */
+/* "Matrix Computations", section 8.5, cyclic-by-row Jacobi).           */
+/* ------------------------------------------------------------------ */
+
+/* a: n*n symmetric (destroyed); w: eigenvalues; u: n*n, column k is the
+ * eigenvector of w[k]. Returns the number of sweeps used. */
+int oracle_jacobi_eigh(int n, double* a, double* w, double* u) {
+  for (int i = 0; i < n; i++)
+    for (int j = 0; j < n; j++) u[i * n + j] = (i == j) ? 1.0 : 0.0;
+  int sweep;
+  for (sweep = 0; sweep < 100; sweep++) {
+    double off = 0, tot = 0;
+    for (int i = 0; i < n; i++)
+      for (int j = 0; j < n; j++) {
+        double v = a[i * n + j] * a[i * n + j];
+        tot += v;
+        if (i != j) off += v;
+      }
+    if (off == 0 || sqrt(off) <= 1e-15 * sqrt(tot)) break;
+    for (int p = 0; p < n - 1; p++)
+      for (int q = p + 1; q < n; q++) {
+        double apq = a[p * n + q];
+        if (apq == 0) continue;
+        /* symmetric Schur 2x2: choose the rotation that zeroes a[p][q] */
+        double tau = (a[q * n + q] - a[p * n + p]) / (2.0 * apq);
+        double t = (tau >= 0 ? 1.0 : -1.0) / (fabs(tau) + sqrt(1.0 + tau * tau));
+        double c = 1.0 / sqrt(1.0 + t * t), s = t * c;
+        /* A <- J^T A J, J = identity except J[p][p]=J[q][q]=c, J[p][q]=s, J[q][p]=-s */
+        for (int k = 0; k < n; k++) {
+          double akp = a[k * n + p], akq = a[k * n + q];
+          a[k * n + p] = c * akp - s * akq;
+          a[k * n + q] = s * akp + c * akq;
+        }
+        for (int k = 0; k < n; k++) {
+          double apk = a[p * n + k], aqk = a[q * n + k];
+          a[p * n + k] = c * apk - s * aqk;
+          a[q * n + k] = s * apk + c * aqk;
+        }
+        for (int k = 0; k < n; k++) {
+          double ukp = u[k * n + p], ukq = u[k * n + q];
+          u[k * n + p] = c * ukp - s * ukq;
+          u[k * n + q] = s * ukp + c * ukq;
+        }
+      }
+  }
+  for (int i = 0; i < n; i++) w[i] = a[i * n + i];
+  return sweep;
+}
+
+/* ------------------------------------------------------------------ */
+/* Summary build (A "How LOCKS works" + A "Code" build loop;            */
+/* B mechanism 1)                                                       */
+/* ------------------------------------------------------------------ */
+
+/* Unquantised rank-r summary of one 16x128 key tile.
+ * keys: 16*128 doubles. Outputs mu[128], V[128*r] (column k = basis vector k),
+ * C[16*r] (row i = coefficients of token i), lam[16] eigenvalues of the
+ * centred Gram, descending. r in 1..15. */
+void oracle_page_summary_f64(const double* keys, int r, double* mu, double* V, double* C,
+                             double* lam) {
+  double D[OP * OD], G[OP * OP], w[OP], U[OP * OP];
+  /* centroid: mean key over the page's 16 tokens */
+  for (int d = 0; d < OD; d++) {
+    double s = 0;
+    for (int i = 0; i < OP; i++) s += keys[i * OD + d];
+    mu[d] = s / OP;
+  }
+  /* centred deviations */
+  for (int i = 0; i < OP; i++)
+    for (int d = 0; d < OD; d++) D[i * OD + d] = keys[i * OD + d] - mu[d];
+  /* the page's small Gram matrix D D^T (16x16) */
+  for (int i = 0; i < OP; i++)
+    for (int j = 0; j < OP; j++) {
+      double s = 0;
+      for (int d = 0; d < OD; d++) s += D[i * OD + d] * D[j * OD + d];
+      G[i * OP + j] = s;
+    }
+  oracle_jacobi_eigh(OP, G, w, U);
+  /* order eigenpairs by eigenvalue, descending; equal values keep index order */
+  int ord[OP];
+  for (int i = 0; i < OP; i++) ord[i] = i;
+  for (int i = 1; i < OP; i++) { /* insertion sort: stable */
+    int x = ord[i], j = i - 1;
+    while (j >= 0 && w[ord[j]] < w[x]) { ord[j + 1] = ord[j]; j--; }
+    ord[j + 1] = x;
+  }
+  for (int k = 0; k < OP; k++) lam[k] = w[ord[k]];
+  /* basis: right singular vectors of D, V[:,k] = D^T u_k / sqrt(lambda_k);
+   * directions with (numerically) zero energy give a zero column: energy at
+   * most 1e-12 of the leading direction's, or at most 1e-24 of the keys' own
+   * energy (the level of double rounding in the centring) */
+  double energy = 0;
+  for (int i = 0; i < OP * OD; i++) energy += keys[i] * keys[i];
+  for (int k = 0; k < r; k++) {
+    double l = lam[k];
+    int keep = (lam[0] > 0) && (l > 1e-12 * lam[0]) && (l > 1e-24 * energy);
+    for (int d = 0; d < OD; d++) {
+      double s = 0;
+      if (keep)
+        for (int i = 0; i < OP; i++) s += D[i * OD + d] * U[i * OP + ord[k]];
+      V[d * r + k] = keep ? s / sqrt(l) : 0.0;
+    }
+  }
+  /* sign convention: the largest-magnitude entry of each basis vector is
+   * positive (lowest d on ties) */
+  for (int k = 0; k < r; k++) {
+    int dm = 0;
+    for (int d = 1; d < OD; d++)
+      if (fabs(V[d * r + k]) > fabs(V[dm * r + k])) dm = d;
+    if (V[dm * r + k] < 0)
+      for (int d = 0; d < OD; d++) V[d * r + k] = -V[d * r + k];
+  }
+  /* coefficients: the deviations projected on the basis, C = D V */
+  for (int i = 0; i < OP; i++)
+    for (int k = 0; k < r; k++) {
+      double s = 0;
+      for (int d = 0; d < OD; d++) s += D[i * OD + d] * V[d * r + k];
+      C[i * r + k] = s;
+    }
+}
+
+/* Pack codes into the 832-byte record (format documented in the C ABI). */
+static void pack_record(const int* mu_c, const int* v_c /* [128][8] */, const int* c_c /* [16][8] */,
+                        const uint16_t* scales /* 3 */, uint8_t* rec) {
+  memset(rec, 0, OSTRIDE);
+  for (int k = 0; k < OR; k++)
+    for (int w = 0; w < 16; w++)
+      for (int b = 0; b < 4; b++) {
+        int lo = v_c[(8 * w + b) * OR + k] & 0xf;
+        int hi = v_c[(8 * w + 4 + b) * OR + k] & 0xf;
+        rec[OV_OFF + k * 64 + w * 4 + b] = (uint8_t)(lo | (hi << 4));
+      }
+  for (int d = 0; d < OD; d++) rec[OMU_OFF + d] = (uint8_t)(int8_t)mu_c[d];
+  for (int i = 0; i < OP * OR; i++) rec[OC_OFF + i] = (uint8_t)(int8_t)c_c[i];
+  for (int s = 0; s < 3; s++) {
+    rec[OS_OFF + 2 * s] = (uint8_t)(scales[s] & 0xff);
+    rec[OS_OFF + 2 * s + 1] = (uint8_t)(scales[s] >> 8);
+  }
+}
+
+/* Quantised record of one page from its bf16 key tile (16*128 bf16 bits).
+ * Optional diagnostics: lam[16] eigenvalues; mu/V/C unquantised (may be NULL). */
+void oracle_build_record(const uint16_t* keys_bf16, uint8_t* rec, double* lam_out,
+                         double* mu_out, double* v_out, double* c_out) {
+  double keys[OP * OD], mu[OD], V[OD * OR], C[OP * OR], lam[OP];
+  for (int i = 0; i < OP * OD; i++) keys[i] = oracle_bf16_to_double(keys_bf16[i]);
+  oracle_page_summary_f64(keys, OR, mu, V, C, lam);
+  int mu_c[OD], v_c[OD * OR], c_c[OP * OR];
+  uint16_t sc[3];
+  quantize_block(mu, OD, 127, mu_c, &sc[0]);
+  quantize_block(V, OD * OR, 7, v_c, &sc[1]);
+  quantize_block(C, OP * OR, 127, c_c, &sc[2]);
+  pack_record(mu_c, v_c, c_c, sc, rec);
+  if (lam_out) memcpy(lam_out, lam, sizeof lam);
+  if (mu_out) memcpy(mu_out, mu, sizeof mu);
+  if (v_out) memcpy(v_out, V, sizeof V);
+  if (c_out) memcpy(c_out, C, sizeof C);
+}
+
+/* Decode a record back to doubles: mu[128], V[128*8], C[16*8]. */
+void oracle_unpack_record(const uint8_t* rec, double* mu, double* V, double* C) {
+  double s_mu = oracle_f16_to_double((uint16_t)(rec[OS_OFF] | (rec[OS_OFF + 1] << 8)));
+  double s_v = oracle_f16_to_double((uint16_t)(rec[OS_OFF + 2] | (rec[OS_OFF + 3] << 8)));
+  double s_c = oracle_f16_to_double((uint16_t)(rec[OS_OFF + 4] | (rec[OS_OFF + 5] << 8)));
+  for (int k = 0; k < OR; k++)
+    for (int w = 0; w < 16; w++)
+      for (int b = 0; b < 4; b++) {
+        uint8_t byte = rec[OV_OFF + k * 64 + w * 4 + b];
+        int lo = byte & 0xf, hi = byte >> 4;
+        if (lo >= 8) lo -= 16; /* 4-bit two's complement */
+        if (hi >= 8) hi -= 16;
+        V[(8 * w + b) * OR + k] = s_v * lo;
+        V[(8 * w + 4 + b) * OR + k] = s_v * hi;
+      }
+  for (int d = 0; d < OD; d++) mu[d] = s_mu * (int8_t)rec[OMU_OFF + d];
+  for (int i = 0; i < OP * OR; i++) C[i] = s_c * (int8_t)rec[OC_OFF + i];
+}
+
+/* Summaries of every full page of every sequence; records of unreferenced
+ * blocks are left untouched. */
+void oracle_build_summaries(int B, int Hkv, int max_pages, int num_blocks,
+                            const uint16_t* k_cache, const int32_t* page_table,
+                            const int32_t* seq_lens, uint8_t* summaries) {
+  for (int b = 0; b < B; b++) {
+    int n = seq_lens[b] / OP;
+    if (n > max_pages) n = max_pages;
+    if (n < 0) n = 0;
+#pragma omp parallel for schedule(dynamic, 64)
+    for (int u = 0; u < n * Hkv; u++) {
+      int j = u / Hkv, kvh = u % Hkv;
+      int blk = page_table[(size_t)b * max_pages + j];
+      if (blk < 0 || blk >= num_blocks) continue;
+      const uint16_t* tile = k_cache + ((size_t)blk * Hkv + kvh) * OP * OD;
+      oracle_build_record(tile, summaries + ((size_t)blk * Hkv + kvh) * OSTRIDE, 0, 0, 0, 0);
+    }
+  }
+}
+
+/* ------------------------------------------------------------------ */
+/* Page score (A "How LOCKS works" page-score equation; A "Code"        */
+/* scoring loop; B mechanism 2)                                         */
+/* ------------------------------------------------------------------ */
+
+/* s_hat(q) = log sum_{i in page} exp((q.mu + (V^T q).c_i) / sqrt(d)).
+ * V is [128][r] (column k = basis vector k), C is [16][r]. */
+double oracle_page_score_f64(const double* q, const double* mu, const double* V,
+                             const double* C, int r) {
+  const double scale = 1.0 / sqrt((double)OD);
+  double global_t = 0;
+  for (int d = 0; d < OD; d++) global_t += q[d] * mu[d];
+  global_t *= scale;
+  double p[16];
+  for (int k = 0; k < r; k++) {
+    double s = 0;
+    for (int d = 0; d < OD; d++) s += V[d * r + k] * q[d];
+    p[k] = s;
+  }
+  double t[OP], m = -INFINITY;
+  for (int i = 0; i < OP; i++) {
+    double local = 0;
+    for (int k = 0; k < r; k++) local += C[i * r + k] * p[k];
+    t[i] = global_t + local * scale;
+    if (t[i] > m) m = t[i];
+  }
+  double s = 0;
+  for (int i = 0; i < OP; i++) s += exp(t[i] - m);
+  return m + log(s);
+}
+
+/* The exact per-page log-sum-exp of q.k/sqrt(d) over the page's real keys
+ * (the selector that reads every key, B section 3 experiments). */
+double oracle_exact_page_lse(const double* q, const double* keys) {
+  const double scale = 1.0 / sqrt((double)OD);
+  double t[OP], m = -INFINITY;
+  for (int i = 0; i < OP; i++) {
+    double s = 0;
+    for (int d = 0; d < OD; d++) s += q[d] * keys[i * OD + d];
+    t[i] = s * scale;
+    if (t[i] > m) m = t[i];
+  }
+  double s = 0;
+  for (int i = 0; i < OP; i++) s += exp(t[i] - m);
+  return m + log(s);
+}
+
+static int valid_pages(const int32_t* seq_lens, int b, int max_pages) {
+  int n = seq_lens[b] / OP;
+  if (n > max_pages) n = max_pages;
+  return n < 0 ? 0 : n;
+}
+
+/* Scores of every (sequence, query head, page) from packed summaries.
+ * scores: [B][Hq][max_pages]; pages j >= n_b and absent pages get -inf. */
+void oracle_scores(int B, int Hq, int Hkv, int max_pages, int num_blocks, const float* q,
+                   const uint8_t* summaries, const int32_t* page_table, const int32_t* seq_lens,
+                   double* scores) {
+  int G = Hq / Hkv;
+  for (int b = 0; b < B; b++) {
+    int n = valid_pages(seq_lens, b, max_pages);
+#pragma omp parallel for schedule(dynamic, 64)
+    for (int u = 0; u < max_pages * Hkv; u++) {
+      int j = u / Hkv, kvh = u % Hkv;
+      int blk = (j < n) ? page_table[(size_t)b * max_pages + j] : -1;
+      double mu[OD], V[OD * OR], C[OP * OR];
+      int present = blk >= 0 && blk < num_blocks;
+      if (present) oracle_unpack_record(summaries + ((size_t)blk * Hkv + kvh) * OSTRIDE, mu, V, C);
+      for (int g = 0; g < G; g++) {
+        int h = kvh * G + g;
+        double qd[OD];
+        for (int d = 0; d < OD; d++) qd[d] = q[((size_t)b * Hq + h) * OD + d];
+        scores[((size_t)b * Hq + h) * max_pages + j] =
+            present ? oracle_page_score_f64(qd, mu, V, C, OR) : -INFINITY;
+      }
+    }
+  }
+}
+
+/* ------------------------------------------------------------------ */
+/* Group-shared selection (B mechanism 3) and top-k (A "Code")          */
+/* ------------------------------------------------------------------ */
+
+/* key[b][kvh][j] = log( (1/G) sum_g exp(s_hat[g][j] - L_g) ), with
+ * L_g = log sum_j exp(s_hat[g][j]) over the sequence's pages: the log of the
+ * group-mean normalised mass share. Absent pages keep -inf. */
+void oracle_group_keys(int B, int Hq, int Hkv, int max_pages, const double* scores,
+                       double* keys) {
+  int G = Hq / Hkv;
+  for (int b = 0; b < B; b++)
+    for (int kvh = 0; kvh < Hkv; kvh++) {
+      double L[64];
+      for (int g = 0; g < G; g++) {
+        const double* s = scores + ((size_t)b * Hq + kvh * G + g) * max_pages;
+        double m = -INFINITY;
+        for (int j = 0; j < max_pages; j++) m = fmax(m, s[j]);
+        double acc = 0;
+        if (m > -INFINITY)
+          for (int j = 0; j < max_pages; j++) acc += exp(s[j] - m);
+        L[g] = (m > -INFINITY) ? m + log(acc) : -INFINITY;
+      }
+      for (int j = 0; j < max_pages; j++) {
+        double e[64], m = -INFINITY;
+        for (int g = 0; g < G; g++) {
+          double sj = scores[((size_t)b * Hq + kvh * G + g) * max_pages + j];
+          e[g] = (sj > -INFINITY) ? sj - L[g] : -INFINITY;
+          m = fmax(m, e[g]);
+        }
+        double acc = 0;
+        if (m > -INFINITY)
+          for (int g = 0; g < G; g++) acc += exp(e[g] - m);
+        keys[((size_t)b * Hkv + kvh) * max_pages + j] =
+            (m > -INFINITY) ? m + log(acc) - log((double)G) : -INFINITY;
+      }
+    }
+}
+
+typedef struct { double key; int id; } keyed;
+static int cmp_keyed(const void* x, const void* y) {
+  const keyed* a = (const keyed*)x;
+  const keyed* b = (const keyed*)y;
+  if (a->key > b->key) return -1; /* larger key first */
+  if (a->key < b->key) return 1;
+  return (a->id > b->id) - (a->id < b->id); /* then lower page id */
+}
+static int cmp_int(const void* x, const void* y) {
+  int a = *(const int*)x, b = *(const int*)y;
+  return (a > b) - (a < b);
+}
+
+/* selected[b][kvh][0..k): the k largest keys (ties to the lower id), sorted
+ * ascending; -inf keys are never selected; unused slots are -1. */
+void oracle_select(int B, int Hkv, int max_pages, const double* keys, int k, int32_t* selected) {
+  keyed* buf = (keyed*)malloc(sizeof(keyed) * (size_t)(max_pages > 0 ? max_pages : 1));
+  int* ids = (int*)malloc(sizeof(int) * (size_t)(k > 0 ? k : 1));
+  for (int b = 0; b < B; b++)
+    for (int kvh = 0; kvh < Hkv; kvh++) {
+      const double* kk = keys + ((size_t)b * Hkv + kvh) * max_pages;
+      int n = 0;
+      for (int j = 0; j < max_pages; j++)
+        if (kk[j] > -INFINITY) { buf[n].key = kk[j]; buf[n].id = j; n++; }
+      qsort(buf, (size_t)n, sizeof(keyed), cmp_keyed);
+      int m = n < k ? n : k;
+      for (int i = 0; i < m; i++) ids[i] = buf[i].id;
+      qsort(ids, (size_t)m, sizeof(int), cmp_int);
+      int32_t* out = selected + ((size_t)b * Hkv + kvh) * k;
+      for (int i = 0; i < k; i++) out[i] = (i < m) ? ids[i] : -1;
+    }
+  free(buf);
+  free(ids);
+}
+
+/* ------------------------------------------------------------------ */
+/* Attention (A "Code": exact attention over the gathered tokens of the */
+/* kept pages; with every page kept it is the dense full-KV attention)  */
+/* ------------------------------------------------------------------ */
+
+/* out[b][h][128] = softmax_t(q_h . k_t / sqrt(128)) v_t over the tokens of the
+ * pages listed in sel[b][kvh][0..k) (entries < 0 or >= n_b skipped). With
+ * sel == NULL every full page of the sequence is used (dense attention).
+ * Heads with no token get 0. */
+void oracle_attention(int B, int Hq, int Hkv, int max_pages, int num_blocks, const float* q,
+                      const uint16_t* k_cache, const uint16_t* v_cache,
+                      const int32_t* page_table, const int32_t* seq_lens, const int32_t* sel,
+                      int k, double* out) {
+  int G = Hq / Hkv;
+  const double scale = 1.0 / sqrt((double)OD);
+  for (int b = 0; b < B; b++) {
+    int n = valid_pages(seq_lens, b, max_pages);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int h = 0; h < Hq; h++) {
+      int kvh = h / G;
+      int npg = sel ? k : n;
+      double qd[OD];
+      for (int d = 0; d < OD; d++) qd[d] = q[((size_t)b * Hq + h) * OD + d];
+      /* pass 1: the maximum logit */
+      double m = -INFINITY;
+      for (int s = 0; s < npg; s++) {
+        int j = sel ? sel[((size_t)b * Hkv + kvh) * k + s] : s;
+        if (j < 0 || j >= n) continue;
+        int blk = page_table[(size_t)b * max_pages + j];
+        if (blk < 0 || blk >= num_blocks) continue;
+        const uint16_t* kt = k_cache + ((size_t)blk * Hkv + kvh) * OP * OD;
+        for (int i = 0; i < OP; i++) {
+          double l = 0;
+          for (int d = 0; d < OD; d++) l += qd[d] * oracle_bf16_to_double(kt[i * OD + d]);
+          m = fmax(m, l * scale);
+        }
+      }
+      double o[OD], den = 0;
+      for (int d = 0; d < OD; d++) o[d] = 0;
+      if (m > -INFINITY) {
+        /* pass 2: softmax weights and the weighted sum of values */
+        for (int s = 0; s < npg; s++) {
+          int j = sel ? sel[((size_t)b * Hkv + kvh) * k + s] : s;
+          if (j < 0 || j >= n) continue;
+          int blk = page_table[(size_t)b * max_pages + j];
+          if (blk < 0 || blk >= num_blocks) continue;
+          const uint16_t* kt = k_cache + ((size_t)blk * Hkv + kvh) * OP * OD;
+          const uint16_t* vt = v_cache + ((size_t)blk * Hkv + kvh) * OP * OD;
+          for (int i = 0; i < OP; i++) {
+            double l = 0;
+            for (int d = 0; d < OD; d++) l += qd[d] * oracle_bf16_to_double(kt[i * OD + d]);
+            double w = exp(l * scale - m);
+            den += w;
+            for (int d = 0; d < OD; d++) o[d] += w * oracle_bf16_to_double(vt[i * OD + d]);
+          }
+        }
+      }
+      for (int d = 0; d < OD; d++)
+        out[((size_t)b * Hq + h) * OD + d] = (den > 0) ? o[d] / den : 0.0;
+    }
+  }
+}
+
+/* The whole decode step on packed summaries: scores -> group keys -> top-k ->
+ * attention over the kept pages. Any of scores_out / keys_out may be NULL. */
+void oracle_decode_step(int B, int Hq, int Hkv, int max_pages, int num_blocks, const float* q,
+                        const uint8_t* summaries, const uint16_t* k_cache,
+                        const uint16_t* v_cache, const int32_t* page_table,
+                        const int32_t* seq_lens, int budget_tokens, double* out,
+                        int32_t* selected, double* scores_out, double* keys_out) {
+  int k = budget_tokens / OP;
+  size_t ns = (size_t)B * Hq * max_pages, nk = (size_t)B * Hkv * max_pages;
+  double* scores = scores_out ? scores_out : (double*)malloc(sizeof(double) * (ns ? ns : 1));
+  double* keys = keys_out ? keys_out : (double*)malloc(sizeof(double) * (nk ? nk : 1));
+  oracle_scores(B, Hq, Hkv, max_pages, num_blocks, q, summaries, page_table, seq_lens, scores);
+  oracle_group_keys(B, Hq, Hkv, max_pages, scores, keys);
+  oracle_select(B, Hkv, max_pages, keys, k, selected);
+  oracle_attention(B, Hq, Hkv, max_pages, num_blocks, q, k_cache, v_cache, page_table, seq_lens,
+                   selected, k, out);
+  if (!scores_out) free(scores);
+  if (!keys_out) free(keys);
+}
+
+/* Threads the OpenMP loops above use (1 when built without OpenMP). */
+#ifdef _OPENMP
+#include <omp.h>
+int oracle_num_threads(void) { return omp_get_max_threads(); }
+#else
+int oracle_num_threads(void) { return 1; }
+#endif

@@ -1,0 +1,381 @@
+"""Pins of the fp64 oracle against things other than itself.
+
+Each test ties an oracle function to a closed form, a library routine
+(LAPACK via numpy, torch's SDPA, scipy's logsumexp on real keys), an invariant
+the mathematics fixes, or a brute force on tiny inputs. Sources:
+(A) "LOCKS: per-page SVD cuts KV-cache reads 10x at 1M context", sections
+"How LOCKS works" and "Code"; (B) the gist.science technical summary of paper
+2607.24555, section 2 mechanisms 1-3 and section 3 (theory).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+from scipy.special import logsumexp
+
+PAGE, DIM = 16, 128
+
+
+def rng(seed):
+    return np.random.default_rng(seed)
+
+
+def exact_lse(q, keys):
+    """Library form of the exact per-page log-sum-exp of q.k/sqrt(d)."""
+    return float(logsumexp(keys @ q / math.sqrt(DIM)))
+
+
+def planted_page(r, rank, noise=0.0, scale=1.0):
+    mu = r.standard_normal(DIM) * scale
+    basis, _ = np.linalg.qr(r.standard_normal((DIM, rank)))
+    coef = r.standard_normal((PAGE, rank)) / np.arange(1, rank + 1)
+    return mu + coef @ basis.T + noise * r.standard_normal((PAGE, DIM))
+
+
+# ------------------------------------------------------------ number formats
+
+def test_bf16_decode_matches_torch(orc):
+    bits = np.arange(0, 65536, dtype=np.uint32).astype(np.uint16)
+    finite = ((bits >> 7) & 0xFF) != 0xFF
+    ours = np.array([orc.lib().oracle_bf16_to_double(int(b)) for b in bits[finite][::7]])
+    ref = torch.from_numpy(bits[finite][::7].view(np.int16)).view(torch.bfloat16).double().numpy()
+    assert np.array_equal(ours, ref)
+
+
+def test_f16_decode_all_patterns_match_numpy(orc):
+    bits = np.arange(0, 65536, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    ours = np.array([orc.f16_bits_to_f64(int(b)) for b in bits])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], ref[~nan])
+
+
+def test_f16_encode_round_half_even_matches_numpy(orc):
+    r = rng(1)
+    xs = np.concatenate([
+        r.standard_normal(4000) * 10.0 ** r.integers(-9, 5, 4000),
+        np.array([0.0, 65504.0, 65519.99, 65520.0, 2.0 ** -24, 2.0 ** -25, 3 * 2.0 ** -26,
+                  2.0 ** -14, 2.0 ** -14 - 2.0 ** -25, 1 + 2.0 ** -11, 1 + 3 * 2.0 ** -11]),
+    ])
+    for x in xs:
+        for s in (1.0, -1.0):
+            got = orc.f64_to_f16_bits(s * x)
+            with np.errstate(over="ignore"):
+                want = int(np.array([s * x]).astype(np.float16).view(np.uint16)[0])
+            assert got == want, (s * x, hex(got), hex(want))
+
+
+# ------------------------------------------------------------ eigensolver
+
+@pytest.mark.parametrize("seed", range(6))
+def test_jacobi_matches_lapack(orc, seed):
+    r = rng(seed)
+    d = r.standard_normal((PAGE, DIM)) * r.uniform(0.1, 3)
+    a = d @ d.T
+    w, u, sweeps = orc.jacobi_eigh(a)
+    ref = np.linalg.eigvalsh(a)
+    assert np.allclose(np.sort(w), ref, rtol=1e-11, atol=1e-11 * ref.max())
+    assert np.allclose(u.T @ u, np.eye(PAGE), atol=1e-12)
+    assert np.allclose(a @ u, u * w, atol=1e-10 * ref.max())
+    assert sweeps < 30
+
+
+def test_jacobi_diagonal_and_degenerate(orc):
+    w, u, sweeps = orc.jacobi_eigh(np.diag(np.arange(16.0)))
+    assert sweeps == 0 and np.array_equal(w, np.arange(16.0))
+    w, u, _ = orc.jacobi_eigh(np.ones((16, 16)))  # rank one: eigenvalues {16, 0 x15}
+    assert np.allclose(np.sort(w), [0.0] * 15 + [16.0], atol=1e-12)
+
+
+# ------------------------------------------------------------ summary build
+
+@pytest.mark.parametrize("seed", range(4))
+def test_rank15_reconstruction_makes_scores_exact(orc, seed):
+    """Centred 16-token deviations have rank <= 15, so an unquantised rank-15
+    summary reproduces every key and the page score equals the exact LSE
+    (A page-score equation; the centring makes the 16th direction null)."""
+    r = rng(100 + seed)
+    keys = r.standard_normal((PAGE, DIM)) * 1.5 + r.standard_normal(DIM)
+    mu, V, C, lam = orc.page_summary_f64(keys, rank=15)
+    assert np.allclose(mu[None, :] + C @ V.T, keys, atol=1e-11)
+    for t in range(5):
+        q = r.standard_normal(DIM) * (1 + t)
+        assert abs(orc.page_score_f64(q, mu, V, C) - exact_lse(q, keys)) < 1e-11
+
+
+def test_planted_rank8_page_scores_exact_at_rank8(orc):
+    r = rng(7)
+    for _ in range(5):
+        keys = planted_page(r, 8)
+        mu, V, C, lam = orc.page_summary_f64(keys, rank=8)
+        assert np.abs(lam[8:]).max() < 1e-13 * lam[0]  # null up to fp64 rounding
+        q = r.standard_normal(DIM)
+        assert abs(orc.page_score_f64(q, mu, V, C) - exact_lse(q, keys)) < 1e-11
+
+
+@pytest.mark.parametrize("rank", [1, 2, 4, 8, 12])
+def test_eckart_young_tail_energy(orc, rank):
+    """The page-local basis is residual-optimal: ||D - C V^T||_F^2 equals the
+    sum of the discarded squared singular values of D (B section 3, theory;
+    Eckart-Young), checked against LAPACK's SVD."""
+    r = rng(rank)
+    keys = planted_page(r, 10, noise=0.1)
+    mu, V, C, lam = orc.page_summary_f64(keys, rank=rank)
+    D = keys - keys.mean(0)
+    sv = np.linalg.svd(D, compute_uv=False)
+    assert np.allclose(mu, keys.mean(0), atol=1e-14)
+    assert np.allclose(lam, np.concatenate([sv ** 2, np.zeros(PAGE - len(sv))]), atol=1e-10)
+    resid = np.sum((D - C @ V.T) ** 2)
+    assert abs(resid - np.sum(sv[rank:] ** 2)) < 1e-9 * np.sum(sv ** 2)
+    assert np.allclose(V.T @ V, np.eye(rank), atol=1e-12)     # orthonormal basis
+    assert np.allclose(C, D @ V, atol=1e-12)                 # coefficients = projections
+    for k in range(rank):                                     # sign convention
+        dm = int(np.argmax(np.abs(V[:, k])))
+        assert V[dm, k] > 0
+
+
+def test_constant_page_has_zero_basis_and_closed_form_score(orc):
+    r = rng(3)
+    row = r.standard_normal(DIM)
+    keys = np.tile(row, (PAGE, 1))
+    mu, V, C, lam = orc.page_summary_f64(keys, rank=8)
+    assert np.all(V == 0) and np.all(C == 0) and np.allclose(lam, 0)
+    q = r.standard_normal(DIM)
+    # all 16 logits equal: LSE = logit + ln 16
+    assert abs(orc.page_score_f64(q, mu, V, C) - (q @ row / math.sqrt(DIM) + math.log(16))) < 1e-12
+
+
+# ------------------------------------------------------------ quantised record
+
+def bf16_round(x):
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16), t.double().numpy()
+
+
+def test_record_quantiser_bounds_and_pack_roundtrip(orc):
+    r = rng(11)
+    for _ in range(20):
+        bits, keys = bf16_round(planted_page(r, 8, noise=0.05, scale=r.uniform(0.1, 4)))
+        rec, lam, mu, V, C = orc.build_record(bits)
+        mu_h, V_h, C_h = orc.unpack_record(rec)
+        scales = [orc.f16_bits_to_f64(int(rec[768 + 2 * i]) | (int(rec[769 + 2 * i]) << 8))
+                  for i in range(3)]
+        for x, xh, s, qmax in ((mu, mu_h, scales[0], 127), (V, V_h, scales[1], 7),
+                               (C, C_h, scales[2], 127)):
+            amax = np.abs(x).max()
+            # scale is the fp16 rounding of absmax/qmax (numpy's float16 as the library check)
+            assert s == float(np.float16(amax / qmax))
+            codes = xh / s
+            assert np.array_equal(codes, np.round(codes))       # integer codes
+            assert np.abs(codes).max() == qmax                    # absmax maps to +-qmax
+            assert np.all(np.abs(x - xh) <= s / 2 * (1 + 1e-12))  # half-step error bound
+        assert np.all(rec[776:] == 0) and rec[774] == 0 and rec[775] == 0
+
+
+def test_record_format_matches_documented_layout(orc):
+    """Byte-level check of the documented record layout with a record built
+    here independently (numpy bit packing), decoded by the oracle."""
+    r = rng(5)
+    vc = r.integers(-7, 8, size=(DIM, 8))
+    mc = r.integers(-127, 128, size=DIM)
+    cc = r.integers(-127, 128, size=(PAGE, 8))
+    s = np.array([0.03125, 0.25, 0.0078125], dtype=np.float16)
+    rec = np.zeros(832, dtype=np.uint8)
+    nib = (vc & 0xF).astype(np.uint8)                  # [d][k] two's complement nibbles
+    for k in range(8):
+        col = nib[:, k].reshape(16, 2, 4)              # [word][half][byte]
+        rec[k * 64:(k + 1) * 64] = (col[:, 0, :] | (col[:, 1, :] << 4)).reshape(-1)
+    rec[512:640] = mc.astype(np.int8).view(np.uint8)
+    rec[640:768] = cc.reshape(-1).astype(np.int8).view(np.uint8)
+    rec[768:774] = s.view(np.uint8)
+    mu, V, C = orc.unpack_record(rec)
+    assert np.array_equal(mu, mc * float(s[0]))
+    assert np.array_equal(V, vc * float(s[1]))
+    assert np.array_equal(C, cc * float(s[2]))
+
+
+def test_summary_payload_is_about_ten_percent(orc):
+    """(A "How LOCKS works"; B mechanism 1): the summary is about 10% of the
+    page's KV bytes. Payload 776 B vs 16 tokens x 128 x bf16 x (K+V)."""
+    payload = 128 * 8 // 2 + 128 + 16 * 8 + 6
+    assert payload == 774
+    assert 0.09 < (payload + 2) / (PAGE * DIM * 2 * 2) < 0.105
+    assert 832 / (PAGE * DIM * 2 * 2) < 0.11
+
+
+# ------------------------------------------------------------ group keys + top-k
+
+def test_group_keys_are_log_mean_shares(orc):
+    r = rng(21)
+    B, Hkv, G, N = 2, 3, 4, 37
+    s = r.standard_normal((B, Hkv * G, N)) * 3
+    keys = orc.group_keys(s, Hkv)
+    # shares of each head sum to one, so the group-mean share sums to one too
+    assert np.allclose(np.exp(keys).sum(-1), 1.0, atol=1e-12)
+    # per-head constant offsets cancel (normalisation by each head's total)
+    s2 = s + r.standard_normal((B, Hkv * G, 1)) * 5
+    assert np.allclose(orc.group_keys(s2, Hkv), keys, atol=1e-12)
+    # permuting heads inside a group changes nothing
+    perm = np.concatenate([kv * G + r.permutation(G) for kv in range(Hkv)])
+    assert np.allclose(orc.group_keys(s[:, perm], Hkv), keys, atol=1e-12)
+    # a group of identical heads reduces to a single head (G = 1 case)
+    same = np.repeat(s[:, ::G][:, :, None, :], G, axis=2).reshape(B, Hkv * G, N)
+    assert np.allclose(orc.group_keys(same, Hkv), orc.group_keys(s[:, ::G], Hkv), atol=1e-12)
+    # G = 1: the key is the score minus a per-row constant -> same order as the score
+    k1 = orc.group_keys(s[:, :Hkv], Hkv)
+    d = k1 - s[:, :Hkv]
+    assert np.allclose(d, d[..., :1], atol=1e-12)
+
+
+def test_group_keys_average_shares_not_scores(orc):
+    """Two heads, two pages: head 0 puts almost all mass on page 0, head 1
+    splits evenly. Mean share: page 0 = (1 + .5)/2 = .75."""
+    s = np.log(np.array([[[1 - 1e-9, 1e-9], [0.5, 0.5]]]))
+    keys = orc.group_keys(s, 1)
+    assert np.allclose(np.exp(keys[0, 0]), [0.75 - 5e-10, 0.25 + 5e-10], atol=1e-12)
+
+
+def test_select_matches_stable_full_sort(orc):
+    r = rng(31)
+    for trial in range(30):
+        N = int(r.integers(1, 60))
+        k = int(r.integers(1, 70))
+        keys = np.round(r.standard_normal((2, 3, N)), 1)     # many exact ties
+        keys[r.random(keys.shape) < 0.1] = -np.inf            # absent pages
+        sel = orc.select(keys, k)
+        for b in range(2):
+            for h in range(3):
+                kk = keys[b, h]
+                order = np.lexsort((np.arange(N), -kk))        # key desc, then id asc
+                order = [j for j in order if np.isfinite(kk[j])][:k]
+                want = sorted(order) + [-1] * (k - len(order))
+                assert list(sel[b, h]) == want
+
+
+# ------------------------------------------------------------ attention
+
+def sdpa_ref(q, keys, vals):
+    """torch SDPA in float64 on the CPU (library routine)."""
+    out = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None, None, None, :], torch.from_numpy(keys)[None, None],
+        torch.from_numpy(vals)[None, None])
+    return out[0, 0, 0].numpy()
+
+
+def small_cache(r, B, Hkv, N, extra=3):
+    nb = B * N + extra
+    kb, kd = bf16_round(r.standard_normal((nb, Hkv, PAGE, DIM)))
+    vb, vd = bf16_round(r.standard_normal((nb, Hkv, PAGE, DIM)))
+    pt = r.permutation(nb)[: B * N].reshape(B, N).astype(np.int32)
+    return kb, kd, vb, vd, pt
+
+
+def test_dense_attention_matches_sdpa(orc):
+    r = rng(41)
+    B, Hq, Hkv, N = 2, 4, 2, 5
+    kb, kd, vb, vd, pt = small_cache(r, B, Hkv, N)
+    q = r.standard_normal((B, Hq, DIM)).astype(np.float32)
+    lens = np.array([N * PAGE, 3 * PAGE + 7], dtype=np.int32)  # second: ragged tail ignored
+    out = orc.attention(q, kb, vb, pt, lens)
+    G = Hq // Hkv
+    for b in range(B):
+        n = lens[b] // PAGE
+        for h in range(Hq):
+            blks = pt[b, :n]
+            keys = kd[blks, h // G].reshape(-1, DIM)
+            vals = vd[blks, h // G].reshape(-1, DIM)
+            assert np.allclose(out[b, h], sdpa_ref(q[b, h].astype(np.float64), keys, vals),
+                               atol=1e-12)
+
+
+def test_sparse_attention_matches_sdpa_on_gathered_tokens(orc):
+    r = rng(43)
+    B, Hq, Hkv, N, k = 1, 2, 1, 9, 4
+    kb, kd, vb, vd, pt = small_cache(r, B, Hkv, N)
+    q = r.standard_normal((B, Hq, DIM)).astype(np.float32)
+    lens = np.array([N * PAGE], dtype=np.int32)
+    sel = np.array([[[1, 4, 7, -1]]], dtype=np.int32)
+    out = orc.attention(q, kb, vb, pt, lens, sel)
+    blks = pt[0, [1, 4, 7]]
+    for h in range(Hq):
+        ref = sdpa_ref(q[0, h].astype(np.float64), kd[blks, 0].reshape(-1, DIM),
+                       vd[blks, 0].reshape(-1, DIM))
+        assert np.allclose(out[0, h], ref, atol=1e-12)
+    empty = orc.attention(q, kb, vb, pt, lens, np.full((1, 1, 4), -1, dtype=np.int32))
+    assert np.all(empty == 0)
+
+
+# ------------------------------------------------------------ whole step
+
+def oracle_inputs(r, B, Hq, Hkv, N, structured=True):
+    nb = B * N + 2
+    keys = np.stack([np.stack([planted_page(r, 8, noise=0.05) if structured
+                               else r.standard_normal((PAGE, DIM))
+                               for _ in range(Hkv)]) for _ in range(nb)])
+    kb, kd = bf16_round(keys)
+    vb, vd = bf16_round(r.standard_normal((nb, Hkv, PAGE, DIM)))
+    pt = r.permutation(nb)[: B * N].reshape(B, N).astype(np.int32)
+    q = r.standard_normal((B, Hq, DIM)).astype(np.float32)
+    return kb, kd, vb, vd, pt, q
+
+
+def test_full_budget_reproduces_dense_attention(orc):
+    """budget = whole sequence -> every page kept -> exactly dense attention
+    (A "Code": the sparse output against the full-KV output)."""
+    r = rng(51)
+    B, Hq, Hkv, N = 2, 8, 2, 6
+    kb, kd, vb, vd, pt, q = oracle_inputs(r, B, Hq, Hkv, N)
+    lens = np.full(B, N * PAGE, dtype=np.int32)
+    summ = orc.build_summaries(kb, pt, lens)
+    out, sel, sc, ky = orc.decode_step(q, summ, kb, vb, pt, lens, N * PAGE)
+    assert np.array_equal(sel, np.tile(np.arange(N, dtype=np.int32), (B, Hkv, 1)))
+    dense = orc.attention(q, kb, vb, pt, lens)
+    assert np.allclose(out, dense, atol=1e-13)
+
+
+def test_scores_from_records_match_unpacked_formula_and_selection_order(orc):
+    r = rng(61)
+    B, Hq, Hkv, N = 1, 4, 2, 20
+    kb, kd, vb, vd, pt, q = oracle_inputs(r, B, Hq, Hkv, N)
+    lens = np.array([N * PAGE - 5], dtype=np.int32)      # last page partial -> ignored
+    summ = orc.build_summaries(kb, pt, lens)
+    out, sel, sc, ky = orc.decode_step(q, summ, kb, vb, pt, lens, 5 * PAGE)
+    n = N - 1
+    assert np.all(np.isneginf(sc[..., n:])) and np.all(np.isfinite(sc[..., :n]))
+    G = Hq // Hkv
+    for h in range(Hq):
+        for j in range(n):
+            mu, V, C = orc.unpack_record(summ[pt[0, j], h // G])
+            assert sc[0, h, j] == orc.page_score_f64(q[0, h].astype(np.float64), mu, V, C)
+    for kvh in range(Hkv):
+        order = np.lexsort((np.arange(n), -ky[0, kvh, :n]))[:5]
+        assert list(sel[0, kvh]) == sorted(order)
+
+
+@pytest.mark.parametrize("rank", [2, 4, 8])
+def test_theorem1_mass_retention_bound(orc, rank):
+    """(A "How LOCKS works", Theorem 1; B section 3 retention guarantees.)
+    Reading: eta = max over tokens of |q.(k - k_hat)|/sqrt(d) for the
+    unquantised rank-r reconstruction k_hat. Each page score is then within eta
+    of the exact page LSE, so the exact mass of the pages chosen by the
+    estimated score is at least e^(-4 eta) (indeed e^(-2 eta)) times the exact
+    mass of the best k pages."""
+    r = rng(70 + rank)
+    N, k = 64, 8
+    pages = [planted_page(r, 10, noise=0.05) for _ in range(N)]
+    q = r.standard_normal(DIM)
+    est, exact, eta = [], [], 0.0
+    for keys in pages:
+        mu, V, C, lam = orc.page_summary_f64(keys, rank=rank)
+        est.append(orc.page_score_f64(q, mu, V, C))
+        exact.append(exact_lse(q, keys))
+        khat = mu[None, :] + C @ V.T
+        eta = max(eta, float(np.max(np.abs((keys - khat) @ q)) / math.sqrt(DIM)))
+    est, exact = np.array(est), np.array(exact)
+    chosen = orc.select(est[None, None, :], k)[0, 0]
+    best = np.argsort(-exact)[:k]
+    mass = lambda idx: np.exp(exact[idx]).sum()
+    assert mass(chosen) >= math.exp(-2 * eta) * mass(best) * (1 - 1e-12)
+    assert mass(chosen) >= math.exp(-4 * eta) * mass(best)
