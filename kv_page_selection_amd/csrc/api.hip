@@ -1,0 +1,311 @@
+// api.hip — the C ABI of liblocks.so: argument checks, workspace layout and
+// the launch sequence of each entry point. See include/locks.h for the
+// contract of every call.
+#include <stdint.h>
+#include <string.h>
+
+#include <string>
+
+#include "device_common.h"
+#include "internal.h"
+#include "locks.h"
+
+namespace locks {
+
+namespace {
+
+size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+bool ws_layout(const locks_dims& d, int k, WsLayout* L, const char** why) {
+  const long long B = d.batch, Hq = d.n_q_heads, Hkv = d.n_kv_heads, N = d.max_pages_per_seq;
+  L->k = k;
+  L->n_score_wg = (int)((N + kScorePagesPerWG - 1) / kScorePagesPerWG);
+  // select chunks: about 512 workgroups overall, and the union of the chunk
+  // winners of one (sequence, KV head) must fit one ranking workgroup
+  long long M = 256;
+  while (M < kSelectMaxElems && B * Hkv * ((N + M - 1) / M) > 512) M *= 2;
+  for (;;) {
+    const long long nch = (N + M - 1) / M;
+    const long long slots = k < M ? k : M;
+    if (nch <= 1024 && nch * slots <= kSelectMaxElems) break;
+    if (M >= kSelectMaxElems) {
+      *why = "budget/16 pages times the chunk count exceeds the ranking capacity (8192 candidates)";
+      return false;
+    }
+    M *= 2;
+  }
+  L->sel_chunk = (int)M;
+  L->n_sel_chunks = (int)((N + M - 1) / M);
+  L->cand_slots = (int)(k < M ? k : M);
+  L->n_att_split = (k + kSparsePagesPerSplit - 1) / kSparsePagesPerSplit;
+  L->n_dense_split = (int)((N + kDensePagesPerSplit - 1) / kDensePagesPerSplit);
+  // regions that do not depend on the budget come first, so a workspace sized
+  // for one budget keeps its counters and dense partials at the same offsets
+  // for every call
+  size_t off = 0;
+  L->counters = off;   off = align_up(off + (size_t)(3 * B * Hkv) * 4);
+  L->dense_part = off; off = align_up(off + (size_t)(B * Hq) * L->n_dense_split * kPartialFloats * 4);
+  L->score_part = off; off = align_up(off + (size_t)(B * Hq * L->n_score_wg) * 2 * 4);
+  L->scores = off;     off = align_up(off + (size_t)(B * Hq * N) * 4);
+  L->cand = off;       off = align_up(off + (size_t)(B * Hkv * L->n_sel_chunks) * L->cand_slots * 8);
+  L->cand_count = off; off = align_up(off + (size_t)(B * Hkv * L->n_sel_chunks) * 4);
+  L->att_part = off;   off = align_up(off + (size_t)(B * Hq) * L->n_att_split * kPartialFloats * 4);
+  L->total = off;
+  return true;
+}
+
+DevPtrs ws_ptrs(const locks_dims& d, const WsLayout& L, void* ws, float* page_scores) {
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  DevPtrs P;
+  P.ws = w;
+  P.scores = page_scores ? page_scores : reinterpret_cast<float*>(w + L.scores);
+  P.score_part = reinterpret_cast<float*>(w + L.score_part);
+  P.cand = reinterpret_cast<unsigned long long*>(w + L.cand);
+  P.cand_count = reinterpret_cast<int32_t*>(w + L.cand_count);
+  P.att_part = reinterpret_cast<float*>(w + L.att_part);
+  P.dense_part = reinterpret_cast<float*>(w + L.dense_part);
+  uint32_t* c = reinterpret_cast<uint32_t*>(w + L.counters);
+  const size_t n = (size_t)d.batch * d.n_kv_heads;
+  P.cnt_select = c;
+  P.cnt_attend = c + n;
+  P.cnt_dense = c + 2 * n;
+  return P;
+}
+
+}  // namespace locks
+
+using namespace locks;
+
+namespace {
+
+thread_local std::string g_err;
+
+locks_status fail(locks_status s, const std::string& msg) {
+  g_err = msg;
+  return s;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+locks_status check_dims(const locks_dims* d) {
+  if (!d) return fail(LOCKS_ERR_INVALID_ARG, "dims is NULL");
+  if (d->batch < 1 || d->n_q_heads < 1 || d->n_kv_heads < 1 || d->max_pages_per_seq < 1 ||
+      d->num_blocks < 1)
+    return fail(LOCKS_ERR_INVALID_ARG, "batch, head counts, max_pages_per_seq and num_blocks must be >= 1");
+  if (d->head_dim != kDim || d->page_size != kPage || d->rank != kRank)
+    return fail(LOCKS_ERR_UNSUPPORTED, "only head_dim 128, page_size 16, rank 8 are supported");
+  if (d->n_q_heads % d->n_kv_heads != 0)
+    return fail(LOCKS_ERR_INVALID_ARG, "n_q_heads must be a multiple of n_kv_heads");
+  const int G = d->n_q_heads / d->n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16)
+    return fail(LOCKS_ERR_UNSUPPORTED, "GQA group size must be 1, 2, 4, 8 or 16");
+  if (d->max_pages_per_seq > (1 << 23))
+    return fail(LOCKS_ERR_UNSUPPORTED, "max_pages_per_seq above 2^23");
+  if ((long long)d->batch * d->n_kv_heads > 65535 || d->batch > 65535)
+    return fail(LOCKS_ERR_UNSUPPORTED, "batch * n_kv_heads above 65535");
+  return LOCKS_OK;
+}
+
+locks_status check_budget(int32_t budget) {
+  if (budget < kPage || budget % kPage != 0)
+    return fail(LOCKS_ERR_INVALID_ARG, "budget_tokens must be a positive multiple of 16");
+  return LOCKS_OK;
+}
+
+locks_status layout(const locks_dims* d, int32_t budget, WsLayout* L) {
+  const char* why = nullptr;
+  if (!ws_layout(*d, budget / kPage, L, &why)) return fail(LOCKS_ERR_UNSUPPORTED, why);
+  return LOCKS_OK;
+}
+
+locks_status check_ws(const WsLayout& L, const void* ws, size_t bytes) {
+  if (!ws) return fail(LOCKS_ERR_INVALID_ARG, "workspace is NULL");
+  if (!aligned(ws, 256)) return fail(LOCKS_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  if (bytes < L.total)
+    return fail(LOCKS_ERR_WORKSPACE, "workspace too small: need " + std::to_string(L.total) +
+                                         " bytes, got " + std::to_string(bytes));
+  return LOCKS_OK;
+}
+
+locks_status need(const void* p, size_t align, const char* name) {
+  if (!p) return fail(LOCKS_ERR_INVALID_ARG, std::string(name) + " is NULL");
+  if (!aligned(p, align))
+    return fail(LOCKS_ERR_INVALID_ARG, std::string(name) + " must be " + std::to_string(align) +
+                                           "-byte aligned");
+  return LOCKS_OK;
+}
+
+locks_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess)
+    return fail(LOCKS_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+  return LOCKS_OK;
+}
+
+#define LOCKS_TRY(x)                  \
+  do {                                \
+    const locks_status st_ = (x);     \
+    if (st_ != LOCKS_OK) return st_;  \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+size_t locks_summary_record_bytes(void) { return kStride; }
+
+const char* locks_last_error(void) { return g_err.c_str(); }
+
+locks_status locks_workspace_bytes(const locks_dims* dims, int32_t budget_tokens, size_t* out_bytes) {
+  g_err.clear();
+  LOCKS_TRY(check_dims(dims));
+  LOCKS_TRY(check_budget(budget_tokens));
+  if (!out_bytes) return fail(LOCKS_ERR_INVALID_ARG, "out_bytes is NULL");
+  WsLayout L;
+  LOCKS_TRY(layout(dims, budget_tokens, &L));
+  *out_bytes = L.total;
+  return LOCKS_OK;
+}
+
+locks_status locks_build_summaries(const locks_dims* dims, const void* k_cache,
+                                   const int32_t* page_table, const int32_t* seq_lens,
+                                   void* summaries, hipStream_t stream) {
+  g_err.clear();
+  LOCKS_TRY(check_dims(dims));
+  LOCKS_TRY(need(k_cache, 16, "k_cache"));
+  LOCKS_TRY(need(page_table, 4, "page_table"));
+  LOCKS_TRY(need(seq_lens, 4, "seq_lens"));
+  LOCKS_TRY(need(summaries, 16, "summaries"));
+  (void)hipGetLastError();
+  return hip_status(launch_build(*dims, static_cast<const uint16_t*>(k_cache), page_table, seq_lens,
+                                 static_cast<uint8_t*>(summaries), stream),
+                    "summary build launch");
+}
+
+locks_status locks_score_pages(const locks_dims* dims, const float* q, const void* summaries,
+                               const int32_t* page_table, const int32_t* seq_lens,
+                               int32_t budget_tokens, float* page_scores, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+  g_err.clear();
+  LOCKS_TRY(check_dims(dims));
+  LOCKS_TRY(check_budget(budget_tokens));
+  LOCKS_TRY(need(q, 4, "q"));
+  LOCKS_TRY(need(summaries, 16, "summaries"));
+  LOCKS_TRY(need(page_table, 4, "page_table"));
+  LOCKS_TRY(need(seq_lens, 4, "seq_lens"));
+  if (page_scores) LOCKS_TRY(need(page_scores, 4, "page_scores"));
+  WsLayout L;
+  LOCKS_TRY(layout(dims, budget_tokens, &L));
+  LOCKS_TRY(check_ws(L, workspace, workspace_bytes));
+  const DevPtrs P = ws_ptrs(*dims, L, workspace, page_scores);
+  (void)hipGetLastError();
+  return hip_status(launch_score(*dims, L, P, q, static_cast<const uint8_t*>(summaries), page_table,
+                                 seq_lens, stream),
+                    "score launch");
+}
+
+locks_status locks_select_pages(const locks_dims* dims, const int32_t* page_table,
+                                const int32_t* seq_lens, int32_t budget_tokens, int32_t* selected,
+                                const float* page_scores, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
+  g_err.clear();
+  LOCKS_TRY(check_dims(dims));
+  LOCKS_TRY(check_budget(budget_tokens));
+  LOCKS_TRY(need(page_table, 4, "page_table"));
+  LOCKS_TRY(need(seq_lens, 4, "seq_lens"));
+  LOCKS_TRY(need(selected, 4, "selected"));
+  if (page_scores) LOCKS_TRY(need(page_scores, 4, "page_scores"));
+  WsLayout L;
+  LOCKS_TRY(layout(dims, budget_tokens, &L));
+  LOCKS_TRY(check_ws(L, workspace, workspace_bytes));
+  const DevPtrs P = ws_ptrs(*dims, L, workspace, const_cast<float*>(page_scores));
+  (void)hipGetLastError();
+  return hip_status(launch_select(*dims, L, P, page_table, seq_lens, selected, stream),
+                    "select launch");
+}
+
+locks_status locks_sparse_attention(const locks_dims* dims, const float* q, const void* k_cache,
+                                    const void* v_cache, const int32_t* page_table,
+                                    const int32_t* seq_lens, int32_t budget_tokens,
+                                    const int32_t* selected, float* out, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream) {
+  g_err.clear();
+  LOCKS_TRY(check_dims(dims));
+  LOCKS_TRY(check_budget(budget_tokens));
+  LOCKS_TRY(need(q, 4, "q"));
+  LOCKS_TRY(need(k_cache, 16, "k_cache"));
+  LOCKS_TRY(need(v_cache, 16, "v_cache"));
+  LOCKS_TRY(need(page_table, 4, "page_table"));
+  LOCKS_TRY(need(seq_lens, 4, "seq_lens"));
+  LOCKS_TRY(need(selected, 4, "selected"));
+  LOCKS_TRY(need(out, 4, "out"));
+  WsLayout L;
+  LOCKS_TRY(layout(dims, budget_tokens, &L));
+  LOCKS_TRY(check_ws(L, workspace, workspace_bytes));
+  const DevPtrs P = ws_ptrs(*dims, L, workspace, nullptr);
+  (void)hipGetLastError();
+  return hip_status(launch_attend(*dims, L, P, q, static_cast<const uint16_t*>(k_cache),
+                                  static_cast<const uint16_t*>(v_cache), page_table, seq_lens,
+                                  selected, out, false, stream),
+                    "sparse attention launch");
+}
+
+locks_status locks_decode_step(const locks_dims* dims, const float* q, const void* summaries,
+                               const void* k_cache, const void* v_cache,
+                               const int32_t* page_table, const int32_t* seq_lens,
+                               int32_t budget_tokens, float* out, int32_t* selected,
+                               float* page_scores, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+  g_err.clear();
+  LOCKS_TRY(check_dims(dims));
+  LOCKS_TRY(check_budget(budget_tokens));
+  LOCKS_TRY(need(q, 4, "q"));
+  LOCKS_TRY(need(summaries, 16, "summaries"));
+  LOCKS_TRY(need(k_cache, 16, "k_cache"));
+  LOCKS_TRY(need(v_cache, 16, "v_cache"));
+  LOCKS_TRY(need(page_table, 4, "page_table"));
+  LOCKS_TRY(need(seq_lens, 4, "seq_lens"));
+  LOCKS_TRY(need(out, 4, "out"));
+  LOCKS_TRY(need(selected, 4, "selected"));
+  if (page_scores) LOCKS_TRY(need(page_scores, 4, "page_scores"));
+  WsLayout L;
+  LOCKS_TRY(layout(dims, budget_tokens, &L));
+  LOCKS_TRY(check_ws(L, workspace, workspace_bytes));
+  const DevPtrs P = ws_ptrs(*dims, L, workspace, page_scores);
+  (void)hipGetLastError();
+  LOCKS_TRY(hip_status(launch_score(*dims, L, P, q, static_cast<const uint8_t*>(summaries),
+                                    page_table, seq_lens, stream),
+                       "score launch"));
+  LOCKS_TRY(hip_status(launch_select(*dims, L, P, page_table, seq_lens, selected, stream),
+                       "select launch"));
+  return hip_status(launch_attend(*dims, L, P, q, static_cast<const uint16_t*>(k_cache),
+                                  static_cast<const uint16_t*>(v_cache), page_table, seq_lens,
+                                  selected, out, false, stream),
+                    "sparse attention launch");
+}
+
+locks_status locks_dense_attention(const locks_dims* dims, const float* q, const void* k_cache,
+                                   const void* v_cache, const int32_t* page_table,
+                                   const int32_t* seq_lens, float* out, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream) {
+  g_err.clear();
+  LOCKS_TRY(check_dims(dims));
+  LOCKS_TRY(need(q, 4, "q"));
+  LOCKS_TRY(need(k_cache, 16, "k_cache"));
+  LOCKS_TRY(need(v_cache, 16, "v_cache"));
+  LOCKS_TRY(need(page_table, 4, "page_table"));
+  LOCKS_TRY(need(seq_lens, 4, "seq_lens"));
+  LOCKS_TRY(need(out, 4, "out"));
+  WsLayout L;
+  LOCKS_TRY(layout(dims, kPage, &L));
+  LOCKS_TRY(check_ws(L, workspace, workspace_bytes));
+  const DevPtrs P = ws_ptrs(*dims, L, workspace, nullptr);
+  (void)hipGetLastError();
+  return hip_status(launch_attend(*dims, L, P, q, static_cast<const uint16_t*>(k_cache),
+                                  static_cast<const uint16_t*>(v_cache), page_table, seq_lens,
+                                  nullptr, out, true, stream),
+                    "dense attention launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,66 @@
+// internal.h — host-side pieces shared by the library's translation units:
+// workspace layout and the kernel launchers behind the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "locks.h"
+
+namespace locks {
+
+constexpr int kScorePagesPerWG = 256;   // 4 waves x 4 tiles x 16 pages
+constexpr int kSelectMaxElems = 8192;   // candidates one select WG ranks (32 per thread)
+constexpr int kSparsePagesPerSplit = 4; // one page per wave
+constexpr int kDensePagesPerSplit = 256;
+constexpr int kPartialFloats = 130;     // (m, l, o[128]) per head and split
+
+// Byte offsets of the regions of the caller's workspace (each 256-aligned).
+struct WsLayout {
+  size_t scores = 0;       // f32 [B][Hq][N]   page scores when the caller passes none
+  size_t score_part = 0;   // f32 [B][Hq][n_score_wg][2]  (max, sum) in log2 units
+  size_t cand = 0;         // u64 [B][Hkv][n_sel_chunks][cand_slots = min(k, chunk)]
+  size_t cand_count = 0;   // i32 [B][Hkv][n_sel_chunks]
+  size_t att_part = 0;     // f32 [B][Hq][n_att_split][130]
+  size_t dense_part = 0;   // f32 [B][Hq][n_dense_split][130]
+  size_t counters = 0;     // u32 [3][B][Hkv]  select / sparse attention / dense
+  size_t total = 0;
+  int k = 0;
+  int n_score_wg = 0;
+  int sel_chunk = 0, n_sel_chunks = 0, cand_slots = 0;
+  int n_att_split = 0, n_dense_split = 0;
+};
+
+// Returns false (and sets *why) when the dims/budget exceed the kernels' limits.
+bool ws_layout(const locks_dims& d, int k, WsLayout* L, const char** why);
+
+struct DevPtrs {
+  uint8_t* ws;
+  float* scores;
+  float* score_part;
+  unsigned long long* cand;
+  int32_t* cand_count;
+  float* att_part;
+  float* dense_part;
+  uint32_t* cnt_select;
+  uint32_t* cnt_attend;
+  uint32_t* cnt_dense;
+};
+DevPtrs ws_ptrs(const locks_dims& d, const WsLayout& L, void* ws, float* page_scores);
+
+// Kernel launchers (enqueue only; return hipGetLastError()).
+hipError_t launch_score(const locks_dims& d, const WsLayout& L, const DevPtrs& P, const float* q,
+                        const uint8_t* summ, const int32_t* page_table, const int32_t* seq_lens,
+                        hipStream_t s);
+hipError_t launch_select(const locks_dims& d, const WsLayout& L, const DevPtrs& P,
+                         const int32_t* page_table, const int32_t* seq_lens, int32_t* selected,
+                         hipStream_t s);
+hipError_t launch_attend(const locks_dims& d, const WsLayout& L, const DevPtrs& P, const float* q,
+                         const uint16_t* kc, const uint16_t* vc, const int32_t* page_table,
+                         const int32_t* seq_lens, const int32_t* selected, float* out,
+                         bool dense, hipStream_t s);
+hipError_t launch_build(const locks_dims& d, const uint16_t* kc, const int32_t* page_table,
+                        const int32_t* seq_lens, uint8_t* summ, hipStream_t s);
+
+}  // namespace locks

@@ -1,0 +1,122 @@
+"""Helpers shared by the GPU parity tests: run the HIP path and the fp64 oracle
+on the same bits and compare them to the bars the decode path is held to:
+  page scores within 1e-3 absolute; selected page sets identical except pages
+  whose oracle key lies within 1e-4 of the k-th key; attention output within
+  2e-2 max-abs with cosine >= 0.999, against the oracle run on the GPU's set.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import oracle
+import workloads
+
+SCORE_TOL = 1e-3
+TIE_TOL = 1e-4
+OUT_TOL = 2e-2
+COS_MIN = 0.999
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def host(w: workloads.Workload):
+    return (w.q.cpu().numpy(), w.page_table.cpu().numpy(), w.seq_lens.cpu().numpy())
+
+
+def compact_cache(w: workloads.Workload, sel: np.ndarray):
+    """Host bits of only the blocks the selection touches, with a page table
+    remapped onto them (unlisted pages become absent). Keeps full-size parity
+    cheap: the oracle reads the same bytes the GPU read."""
+    pt = w.page_table.cpu().numpy()
+    B, Hkv, k = sel.shape
+    blocks = set()
+    for b in range(B):
+        ids = sel[b].reshape(-1)
+        ids = ids[(ids >= 0) & (ids < pt.shape[1])]
+        blocks.update(pt[b, np.unique(ids)].tolist())
+    blocks = sorted(b for b in blocks if 0 <= b < w.num_blocks)
+    remap = -np.ones(w.num_blocks, dtype=np.int64)
+    remap[blocks] = np.arange(len(blocks))
+    idx = torch.tensor(blocks if blocks else [0], dtype=torch.long, device=w.k_cache.device)
+    kb = workloads.bf16_bits(w.k_cache.index_select(0, idx))
+    vb = workloads.bf16_bits(w.v_cache.index_select(0, idx))
+    new_pt = np.where(pt >= 0, remap[np.clip(pt, 0, w.num_blocks - 1)], -1).astype(np.int32)
+    return kb, vb, new_pt
+
+
+def selection_ok(g_sel: np.ndarray, o_sel: np.ndarray, o_keys: np.ndarray, k: int,
+                 n_valid: np.ndarray):
+    """Checks the GPU selection against the oracle's; returns #near-tie swaps."""
+    B, Hkv, _ = g_sel.shape
+    swaps = 0
+    for b in range(B):
+        for h in range(Hkv):
+            g = g_sel[b, h]
+            m = int(min(k, n_valid[b, h]))
+            assert np.all(g[m:] == -1), "unused slots must be -1"
+            gv = g[:m]
+            assert np.all(np.diff(gv) > 0), "selected ids must be strictly ascending"
+            keys = o_keys[b, h]
+            assert np.all(np.isfinite(keys[gv])), "selected an absent page"
+            if m == 0:
+                continue
+            kth = np.sort(keys[np.isfinite(keys)])[::-1][m - 1]
+            diff = set(gv.tolist()) ^ set(o_sel[b, h, :m].tolist())
+            for j in diff:
+                assert abs(keys[j] - kth) <= TIE_TOL, (
+                    f"(b={b}, kvh={h}) page {j} key {keys[j]:.6f} vs k-th {kth:.6f}")
+            swaps += len(diff) // 2
+    return swaps
+
+
+def out_ok(g: np.ndarray, ref: np.ndarray):
+    g = g.astype(np.float64)
+    err = float(np.abs(g - ref).max()) if g.size else 0.0
+    num = float((g * ref).sum())
+    den = float(np.sqrt((g * g).sum() * (ref * ref).sum()))
+    cos = num / den if den > 0 else 1.0
+    assert err <= OUT_TOL, f"output max-abs error {err}"
+    assert cos >= COS_MIN, f"output cosine {cos}"
+    return err, cos
+
+
+def decode_and_check(w: workloads.Workload, summ: torch.Tensor, budget: int | None = None,
+                     full_oracle_attention: bool = True):
+    """GPU decode step vs the oracle on the same packed summaries."""
+    import kv_page_selection_amd as locks
+    budget = budget or w.budget
+    k = budget // 16
+    dev = w.q.device
+    scores = torch.full((w.batch, w.n_q_heads, w.max_pages), float("nan"), device=dev)
+    out, sel = locks.decode_step(w.q, summ, w.k_cache, w.v_cache, w.page_table, w.seq_lens,
+                                 budget, page_scores=scores)
+    torch.cuda.synchronize()
+    q, pt, sl = host(w)
+    sm = summ.cpu().numpy()
+    o_sc = oracle.scores(q, sm, pt, sl, w.n_kv_heads)
+    valid = np.isfinite(o_sc)
+    g_sc = scores.cpu().numpy()
+    s_err = float(np.abs(g_sc[valid] - o_sc[valid]).max()) if valid.any() else 0.0
+    assert s_err <= SCORE_TOL, f"page score error {s_err}"
+    o_keys = oracle.group_keys(o_sc, w.n_kv_heads)
+    o_sel = oracle.select(o_keys, k)
+    g_sel = sel.cpu().numpy()
+    n_valid = np.isfinite(o_keys).sum(-1)
+    swaps = selection_ok(g_sel, o_sel, o_keys, k, n_valid)
+    if full_oracle_attention:
+        kb, vb = workloads.bf16_bits(w.k_cache), workloads.bf16_bits(w.v_cache)
+        ref = oracle.attention(q, kb, vb, pt, sl, g_sel)
+    else:
+        kb, vb, cpt = compact_cache(w, g_sel)
+        ref = oracle.attention(q, kb, vb, cpt, sl, g_sel)
+    err, cos = out_ok(out.cpu().numpy(), ref)
+    say(f"  {w.recipe} budget={budget}: score err {s_err:.2e}, near-tie swaps {swaps}, "
+        f"out max-abs {err:.2e}, cos {cos:.7f}")
+    return dict(score_err=s_err, swaps=swaps, out_err=err, cos=cos, out=out, sel=sel,
+                scores=scores, o_keys=o_keys)

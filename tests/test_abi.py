@@ -1,0 +1,100 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry point
+include/locks.h declares, and rejects bad arguments on the host before
+anything is enqueued."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "locks.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    import kv_page_selection_amd as m
+    if not os.path.exists(m.LIB_PATH):
+        from kv_page_selection_amd import _build
+        _build.build()
+    return m
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(locks_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    syms = declared_symbols()
+    for name in ("locks_build_summaries", "locks_decode_step", "locks_score_pages",
+                 "locks_select_pages", "locks_sparse_attention", "locks_dense_attention",
+                 "locks_workspace_bytes", "locks_summary_record_bytes", "locks_last_error"):
+        assert name in syms
+
+
+def test_library_exports_every_declared_symbol(L):
+    lib = L.lib()
+    missing = [s for s in declared_symbols() if not hasattr(lib, s)]
+    assert not missing, f"not exported: {missing}"
+
+
+def dims(L, **kw):
+    d = dict(batch=1, n_q_heads=32, n_kv_heads=8, head_dim=128, page_size=16, rank=8,
+             max_pages_per_seq=65536, num_blocks=65536)
+    d.update(kw)
+    return L.Dims(*[d[k] for k, _ in L.Dims._fields_])
+
+
+def test_record_size(L):
+    assert L.summary_record_bytes() == 832
+
+
+def test_workspace_sizing_and_validation(L):
+    n = L.workspace_bytes(dims(L), 2048)
+    assert n > 32 * 65536 * 4  # holds at least the per-head page scores
+    assert L.workspace_bytes(dims(L), 512) < n
+    with pytest.raises(L.LocksError) as e:
+        L.workspace_bytes(dims(L), 2040)  # not a multiple of 16
+    assert e.value.status == L.ERR_INVALID_ARG
+    for bad in (dict(head_dim=64), dict(page_size=32), dict(rank=4), dict(n_q_heads=24)):
+        with pytest.raises(L.LocksError) as e:
+            L.workspace_bytes(dims(L, **bad), 512)
+        assert e.value.status == L.ERR_UNSUPPORTED, bad
+    with pytest.raises(L.LocksError) as e:
+        L.workspace_bytes(dims(L, n_q_heads=30), 512)
+    assert e.value.status == L.ERR_INVALID_ARG
+    with pytest.raises(L.LocksError) as e:
+        L.workspace_bytes(dims(L, batch=0), 512)
+    assert e.value.status == L.ERR_INVALID_ARG
+
+
+def test_entry_points_reject_null_and_small_workspace_on_host(L):
+    lib = L.lib()
+    d = dims(L)
+    P = ctypes.c_void_p
+    fake = P(1 << 20)  # aligned, never dereferenced: validation fails first
+    st = lib.locks_decode_step(ctypes.byref(d), None, fake, fake, fake, fake, fake, 2048, fake,
+                               fake, None, fake, 16, None)
+    assert st == L.ERR_INVALID_ARG and b"q is NULL" in lib.locks_last_error()
+    st = lib.locks_decode_step(ctypes.byref(d), fake, fake, fake, fake, fake, fake, 2048, fake,
+                               fake, None, fake, 16, None)
+    assert st == L.ERR_WORKSPACE and b"too small" in lib.locks_last_error()
+    st = lib.locks_decode_step(ctypes.byref(d), fake, P((1 << 20) + 4), fake, fake, fake, fake,
+                               2048, fake, fake, None, fake, 1 << 40, None)
+    assert st == L.ERR_INVALID_ARG and b"aligned" in lib.locks_last_error()
+    st = lib.locks_build_summaries(ctypes.byref(d), None, fake, fake, fake, None)
+    assert st == L.ERR_INVALID_ARG
+    st = lib.locks_dense_attention(None, fake, fake, fake, fake, fake, fake, fake, 1 << 40, None)
+    assert st == L.ERR_INVALID_ARG and b"dims is NULL" in lib.locks_last_error()
+
+
+def test_binding_refuses_cpu_tensors(L):
+    import torch
+    q = torch.zeros(1, 4, 128)
+    kc = torch.zeros(8, 1, 16, 128, dtype=torch.bfloat16)
+    pt = torch.zeros(1, 8, dtype=torch.int32)
+    sl = torch.zeros(1, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        L.dense_attention(q, kc, kc, pt, sl)

@@ -1,0 +1,202 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the
+same seeded inputs, for the five workloads at reduced and at full size, plus
+edge cases. Bars: page scores <= 1e-3 abs; selected sets identical except keys
+within 1e-4 of the k-th; output <= 2e-2 max-abs, cosine >= 0.999."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from parity import COS_MIN, decode_and_check, host, out_ok, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def locks():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import kv_page_selection_amd as m
+    m.lib()
+    return m
+
+
+DEV = "cuda"
+
+# reduced sizes: several score tiles, several select chunks, ragged tails
+SMALL = [
+    dict(config=1),                                             # the full 4K workload
+    dict(config=2, ctx=16 * 1000 + 7 * 16),                     # 1007 pages: ragged vs 256-page tiles
+    dict(config=3, ctx=16 * 1500, batch=3),                     # carrier pages, batch
+    dict(config=4, ctx=16 * 2048, budget=512),
+    dict(config=4, ctx=16 * 2048, budget=2048),
+    dict(config=5, ctx=16 * 3000, budget=512),                  # G = 16
+    dict(config=2, ctx=16 * 640, n_kv_heads=16, n_q_heads=32),  # G = 2
+    dict(config=2, ctx=16 * 640, n_kv_heads=4, n_q_heads=32),   # G = 8
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
+def test_decode_parity_on_gpu_built_summaries(locks, case):
+    say(f"decode parity {case}")
+    w = workloads.make(device=DEV, **case)
+    summ = locks.build_summaries(w.k_cache, w.page_table, w.seq_lens)
+    r = decode_and_check(w, summ)
+    if w.carrier is not None:  # report retention of the planted carrier page
+        sel = r["sel"].cpu().numpy()
+        kept = [[int(w.carrier[b]) in set(sel[b, h].tolist()) for h in range(w.n_kv_heads)]
+                for b in range(w.batch)]
+        say(f"  carrier retention {np.mean(kept):.3f}")
+
+
+def test_decode_parity_on_oracle_built_summaries(locks):
+    """Summaries packed by the oracle, decoded by the GPU: the record format is
+    read the same way on both sides."""
+    w = workloads.make(2, device=DEV, ctx=16 * 700, seed=11)
+    q, pt, sl = host(w)
+    summ = oracle.build_summaries(workloads.bf16_bits(w.k_cache), pt, sl)
+    decode_and_check(w, torch.from_numpy(summ).to(DEV))
+
+
+def test_edge_cases(locks):
+    """Empty sequence, partial last page, absent pages (block -1), budget >= pages."""
+    w = workloads.make(2, device=DEV, ctx=16 * 300, batch=4, budget=512,
+                       seq_lens=[0, 16 * 300, 16 * 37 + 9, 16 * 20], seed=5)
+    pt = w.page_table.clone()
+    pt[1, 5] = -1
+    pt[1, 200] = w.num_blocks + 3   # out of range: absent
+    w.page_table = pt
+    summ = locks.build_summaries(w.k_cache, w.page_table, w.seq_lens)
+    r = decode_and_check(w, summ)
+    sel = r["sel"].cpu().numpy()
+    assert np.all(sel[0] == -1)                      # empty sequence selects nothing
+    assert np.all(r["out"][0].cpu().numpy() == 0)    # and attends to nothing
+    assert list(sel[3, 0, :20]) == list(range(20)) and np.all(sel[3, :, 20:] == -1)
+    assert 5 not in sel[1] and 200 not in sel[1]
+
+
+def test_sparse_attention_on_given_selection(locks):
+    w = workloads.make(4, device=DEV, ctx=16 * 1024, seed=3)
+    q, pt, sl = host(w)
+    rng = np.random.default_rng(0)
+    k = w.k_pages
+    sel = np.stack([np.stack([np.sort(rng.choice(w.max_pages, k, replace=False))
+                              for _ in range(w.n_kv_heads)])]).astype(np.int32)
+    sel[0, 0, -5:] = -1  # unused slots
+    out = torch.empty_like(w.q)
+    dims = locks.make_dims(w.q, w.k_cache, w.page_table)
+    ws = locks.new_workspace(dims, w.budget, DEV)
+    locks.sparse_attention(w.q, w.k_cache, w.v_cache, w.page_table, w.seq_lens, w.budget,
+                           torch.from_numpy(sel).to(DEV), out, ws)
+    torch.cuda.synchronize()
+    ref = oracle.attention(q, workloads.bf16_bits(w.k_cache), workloads.bf16_bits(w.v_cache),
+                           pt, sl, sel)
+    err, cos = out_ok(out.cpu().numpy(), ref)
+    say(f"  sparse attention on a given set: max-abs {err:.2e} cos {cos:.7f}")
+    assert err < 1e-4  # same set, fp32 accumulation vs fp64
+
+
+@pytest.mark.parametrize("config,ctx", [(1, 4096), (2, 16 * 1500), (5, 16 * 2000)])
+def test_dense_attention_parity(locks, config, ctx):
+    w = workloads.make(config, device=DEV, ctx=ctx, seed=21)
+    out = locks.dense_attention(w.q, w.k_cache, w.v_cache, w.page_table, w.seq_lens)
+    torch.cuda.synchronize()
+    q, pt, sl = host(w)
+    ref = oracle.attention(q, workloads.bf16_bits(w.k_cache), workloads.bf16_bits(w.v_cache),
+                           pt, sl)
+    err, cos = out_ok(out.cpu().numpy(), ref)
+    say(f"  dense config {config} ctx {ctx}: max-abs {err:.2e} cos {cos:.7f}")
+    assert err < 1e-4
+
+
+def test_full_budget_equals_dense(locks):
+    w = workloads.make(2, device=DEV, ctx=16 * 512, seed=8)
+    summ = locks.build_summaries(w.k_cache, w.page_table, w.seq_lens)
+    out, sel = locks.decode_step(w.q, summ, w.k_cache, w.v_cache, w.page_table, w.seq_lens,
+                                 16 * 512)
+    dense = locks.dense_attention(w.q, w.k_cache, w.v_cache, w.page_table, w.seq_lens)
+    torch.cuda.synchronize()
+    assert torch.equal(sel.cpu(), torch.arange(512, dtype=torch.int32).expand(1, 8, 512))
+    assert float((out - dense).abs().max()) < 1e-5
+
+
+def test_deterministic_and_workspace_reuse(locks):
+    """Bitwise-identical repeats; one workspace reused across budgets and the
+    dense call (counters are left at zero by every call)."""
+    w = workloads.make(4, device=DEV, ctx=16 * 2048, seed=4)
+    summ = locks.build_summaries(w.k_cache, w.page_table, w.seq_lens)
+    dims = locks.make_dims(w.q, w.k_cache, w.page_table)
+    ws = locks.new_workspace(dims, 2048, DEV)
+    outs = []
+    for budget in (2048, 512, 2048):
+        o, s = locks.decode_step(w.q, summ, w.k_cache, w.v_cache, w.page_table, w.seq_lens,
+                                 budget, workspace=ws)
+        d = locks.dense_attention(w.q, w.k_cache, w.v_cache, w.page_table, w.seq_lens,
+                                  workspace=ws)
+        outs.append((o.clone(), s.clone(), d.clone()))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][0], outs[2][0]) and torch.equal(outs[0][1], outs[2][1])
+    assert torch.equal(outs[0][2], outs[1][2])
+    o512, s512 = locks.decode_step(w.q, summ, w.k_cache, w.v_cache, w.page_table, w.seq_lens, 512)
+    assert torch.equal(o512, outs[1][0]) and torch.equal(s512, outs[1][1])
+
+
+def test_graph_replay_matches_eager(locks):
+    """The step captured in a HIP graph, replayed several times with eager work
+    in between, gives the eager result every time."""
+    w = workloads.make(4, device=DEV, ctx=16 * 2048, seed=6)
+    summ = locks.build_summaries(w.k_cache, w.page_table, w.seq_lens)
+    dims = locks.make_dims(w.q, w.k_cache, w.page_table)
+    ws = locks.new_workspace(dims, w.budget, DEV)
+    out = torch.empty_like(w.q)
+    sel = torch.empty(1, 8, w.k_pages, dtype=torch.int32, device=DEV)
+    ref_o, ref_s = locks.decode_step(w.q, summ, w.k_cache, w.v_cache, w.page_table, w.seq_lens,
+                                     w.budget)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):  # warm-up on the capture stream
+        locks.decode_step(w.q, summ, w.k_cache, w.v_cache, w.page_table, w.seq_lens, w.budget,
+                          out=out, selected=sel, workspace=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        locks.decode_step(w.q, summ, w.k_cache, w.v_cache, w.page_table, w.seq_lens, w.budget,
+                          out=out, selected=sel, workspace=ws)
+    for rep in range(4):
+        out.zero_()
+        sel.fill_(-7)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_o) and torch.equal(sel, ref_s), f"replay {rep}"
+        _ = (w.q * 2).sum().item()  # eager work between replays
+
+
+# ----------------------------------------------------------------- full size
+
+@pytest.mark.parametrize("config,budget", [(4, 2048), (4, 512), (5, 512)])
+def test_full_size_decode_parity(locks, config, budget):
+    """The full 1M-token workloads in the launch configuration the benchmark
+    times: every score and selection compared, output against the oracle on
+    the GPU's selected pages (only those K/V blocks are copied to the host)."""
+    say(f"full-size decode parity config {config} budget {budget}")
+    w = workloads.make(config, device=DEV, budget=budget)
+    summ = locks.build_summaries(w.k_cache, w.page_table, w.seq_lens)
+    decode_and_check(w, summ, full_oracle_attention=False)
+    del w, summ
+    torch.cuda.empty_cache()
+
+
+def test_full_size_batch8_carrier(locks):
+    say("full-size decode parity config 3 (256K x 8)")
+    w = workloads.make(3, device=DEV)
+    summ = locks.build_summaries(w.k_cache, w.page_table, w.seq_lens)
+    r = decode_and_check(w, summ, full_oracle_attention=False)
+    sel = r["sel"].cpu().numpy()
+    kept = np.mean([[int(w.carrier[b]) in set(sel[b, h].tolist()) for h in range(8)]
+                    for b in range(8)])
+    say(f"  carrier retention {kept:.3f}")
+    del w, summ
+    torch.cuda.empty_cache()
