@@ -29,9 +29,11 @@
  *    check returns a negative locks_status and enqueues nothing;
  *    locks_last_error() then describes it. Nothing is thrown across the ABI.
  *  - Identical inputs give bitwise-identical outputs (no float atomics).
- *  - Supported shape: head_dim 128, page_size 16, rank 8,
- *    1 <= n_q_heads/n_kv_heads <= 16 (n_q_heads % n_kv_heads == 0).
+ *  - Supported shape: head_dim 128, page_size 16, rank 8, and a GQA group
+ *    size G = n_q_heads / n_kv_heads in {1, 2, 4, 8, 16}; budget/16 <= 4096
+ *    pages; max_pages_per_seq <= 2^20; batch * n_kv_heads <= 65535.
  *    Other values return LOCKS_ERR_UNSUPPORTED.
+ *  - q must be finite.
  *  - Page table: page_table[b*max_pages_per_seq + j] is the physical block
  *    that holds logical page j of sequence b. Sequence b has
  *    n_b = min(seq_lens[b] / 16, max_pages_per_seq) full pages; tokens after
@@ -57,7 +59,7 @@
  *   bytes [512, 640)  mu codes, int8[128], range -127..127.
  *   bytes [640, 768)  C codes, int8[16][8] (token-major), range -127..127.
  *   bytes [768, 776)  fp16 scales {s_mu, s_V, s_C, 0}.
- *   bytes [776, 832)  zero padding (keeps each record 64-byte aligned).
+ *   bytes [776, 784)  zero padding (keeps every record 16-byte aligned).
  *   Dequantised: mu = s_mu*mu_code, V = s_V*V_code, C = s_C*C_code.
  */
 #ifndef LOCKS_H
@@ -74,7 +76,7 @@ extern "C" {
 #define LOCKS_HEAD_DIM 128
 #define LOCKS_PAGE_SIZE 16
 #define LOCKS_RANK 8
-#define LOCKS_SUMMARY_STRIDE 832
+#define LOCKS_SUMMARY_STRIDE 784
 #define LOCKS_SUMMARY_PAYLOAD 776
 #define LOCKS_MAX_GROUP 16
 
@@ -97,7 +99,7 @@ typedef enum locks_status {
   LOCKS_ERR_HIP = -4          /* a launch failed; see locks_last_error() */
 } locks_status;
 
-/* Bytes per summary record (LOCKS_SUMMARY_STRIDE). */
+/* Bytes per summary record (LOCKS_SUMMARY_STRIDE = 784; payload 776). */
 size_t locks_summary_record_bytes(void);
 
 /* Message for the last failed call on this thread ("" if none). The pointer
@@ -137,9 +139,8 @@ locks_status locks_build_summaries(const locks_dims* dims, const void* k_cache,
  *  page_scores  optional (NULL = not written): per-head page score s_hat
  *               (A page-score equation); entries j >= n_b are not written.
  *  workspace    >= locks_workspace_bytes(dims, budget_tokens) bytes of device
- *               memory, 256-byte aligned, ZERO-FILLED before its first use;
- *               every call leaves it reusable. Calls sharing a workspace must
- *               be stream-ordered. */
+ *               memory, 256-byte aligned; its contents need no initialisation.
+ *               Calls sharing a workspace must be stream-ordered. */
 locks_status locks_decode_step(const locks_dims* dims, const float* q, const void* summaries,
                                const void* k_cache, const void* v_cache,
                                const int32_t* page_table, const int32_t* seq_lens,

@@ -111,7 +111,7 @@ def workspace_bytes(dims: Dims, budget_tokens: int) -> int:
 
 
 def new_workspace(dims: Dims, budget_tokens: int, device) -> torch.Tensor:
-    """Zero-filled workspace (the counters inside must start at zero)."""
+    """A workspace of the size the C ABI asks for (zero-filled for tidiness)."""
     return torch.zeros(workspace_bytes(dims, budget_tokens), dtype=torch.uint8, device=device)
 
 
@@ -134,7 +134,7 @@ def _check_common(q, k_cache, page_table, seq_lens):
 
 def build_summaries(k_cache: torch.Tensor, page_table: torch.Tensor, seq_lens: torch.Tensor,
                     summaries: torch.Tensor | None = None, n_q_heads: int = 1) -> torch.Tensor:
-    """Summary records [num_blocks, Hkv, 832] (uint8) of every full page."""
+    """Summary records [num_blocks, Hkv, 784] (uint8) of every full page."""
     _check_common(None, k_cache, page_table, seq_lens)
     dims = make_dims(page_table.shape[0], k_cache, page_table, n_q_heads=k_cache.shape[1])
     if summaries is None:

@@ -21,35 +21,34 @@ size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 bool ws_layout(const locks_dims& d, int k, WsLayout* L, const char** why) {
   const long long B = d.batch, Hq = d.n_q_heads, Hkv = d.n_kv_heads, N = d.max_pages_per_seq;
   L->k = k;
-  L->n_score_wg = (int)((N + kScorePagesPerWG - 1) / kScorePagesPerWG);
-  // select chunks: about 512 workgroups overall, and the union of the chunk
-  // winners of one (sequence, KV head) must fit one ranking workgroup
+  L->n_score_wg = (int)((N + kScorePagesPerWave - 1) / kScorePagesPerWave);
+  // select chunks of up to 1024 pages; every page's sort key fits the chunk's slots
+  if (k > kSelectMaxK) {
+    *why = "budget/16 above 4096 pages";
+    return false;
+  }
   long long M = 256;
-  while (M < kSelectMaxElems && B * Hkv * ((N + M - 1) / M) > 512) M *= 2;
-  for (;;) {
-    const long long nch = (N + M - 1) / M;
-    const long long slots = k < M ? k : M;
-    if (nch <= 1024 && nch * slots <= kSelectMaxElems) break;
-    if (M >= kSelectMaxElems) {
-      *why = "budget/16 pages times the chunk count exceeds the ranking capacity (8192 candidates)";
-      return false;
-    }
-    M *= 2;
+  while (M < kSelectChunk && M < N) M *= 2;
+  if ((N + M - 1) / M > 1024) {
+    *why = "more than 1024 select chunks (max_pages_per_seq above 2^20)";
+    return false;
   }
   L->sel_chunk = (int)M;
   L->n_sel_chunks = (int)((N + M - 1) / M);
-  L->cand_slots = (int)(k < M ? k : M);
   L->n_att_split = (k + kSparsePagesPerSplit - 1) / kSparsePagesPerSplit;
-  L->n_dense_split = (int)((N + kDensePagesPerSplit - 1) / kDensePagesPerSplit);
-  // regions that do not depend on the budget come first, so a workspace sized
-  // for one budget keeps its counters and dense partials at the same offsets
-  // for every call
+  if (L->n_att_split > kMaxSplits) {
+    *why = "budget/16 above the sparse-attention split capacity";
+    return false;
+  }
+  long long dps = kDensePagesPerSplit;
+  while ((N + dps - 1) / dps > kMaxSplits) dps *= 2;
+  L->dense_pages_per_split = (int)dps;
+  L->n_dense_split = (int)((N + dps - 1) / dps);
   size_t off = 0;
-  L->counters = off;   off = align_up(off + (size_t)(3 * B * Hkv) * 4);
   L->dense_part = off; off = align_up(off + (size_t)(B * Hq) * L->n_dense_split * kPartialFloats * 4);
   L->score_part = off; off = align_up(off + (size_t)(B * Hq * L->n_score_wg) * 2 * 4);
   L->scores = off;     off = align_up(off + (size_t)(B * Hq * N) * 4);
-  L->cand = off;       off = align_up(off + (size_t)(B * Hkv * L->n_sel_chunks) * L->cand_slots * 8);
+  L->cand = off;       off = align_up(off + (size_t)(B * Hkv * L->n_sel_chunks) * L->sel_chunk * 8);
   L->cand_count = off; off = align_up(off + (size_t)(B * Hkv * L->n_sel_chunks) * 4);
   L->att_part = off;   off = align_up(off + (size_t)(B * Hq) * L->n_att_split * kPartialFloats * 4);
   L->total = off;
@@ -66,11 +65,7 @@ DevPtrs ws_ptrs(const locks_dims& d, const WsLayout& L, void* ws, float* page_sc
   P.cand_count = reinterpret_cast<int32_t*>(w + L.cand_count);
   P.att_part = reinterpret_cast<float*>(w + L.att_part);
   P.dense_part = reinterpret_cast<float*>(w + L.dense_part);
-  uint32_t* c = reinterpret_cast<uint32_t*>(w + L.counters);
-  const size_t n = (size_t)d.batch * d.n_kv_heads;
-  P.cnt_select = c;
-  P.cnt_attend = c + n;
-  P.cnt_dense = c + 2 * n;
+  (void)d;
   return P;
 }
 
@@ -103,6 +98,8 @@ locks_status check_dims(const locks_dims* d) {
     return fail(LOCKS_ERR_UNSUPPORTED, "GQA group size must be 1, 2, 4, 8 or 16");
   if (d->max_pages_per_seq > (1 << 23))
     return fail(LOCKS_ERR_UNSUPPORTED, "max_pages_per_seq above 2^23");
+  if (d->max_pages_per_seq > (1 << 20))
+    return fail(LOCKS_ERR_UNSUPPORTED, "max_pages_per_seq above 2^20");
   if ((long long)d->batch * d->n_kv_heads > 65535 || d->batch > 65535)
     return fail(LOCKS_ERR_UNSUPPORTED, "batch * n_kv_heads above 65535");
   return LOCKS_OK;

@@ -14,9 +14,9 @@
 //   online softmax in base 2 over the page's 16 tokens (16-lane shuffles);
 //   PV: lane owns d = 2*lane, 2*lane+1, reads one bf16 pair per token row
 //       (coalesced 256-byte rows) and takes each token's weight by readlane.
-// Waves merge in LDS into one (max, sum, o[128]) partial per head and split;
-// the last split of each (sequence, KV head) (device-scope counter) merges the
-// partials in fixed order and writes the output. No float atomics.
+// Waves merge in LDS into one (max, sum, o[128]) partial per head and split; a
+// second launch, one workgroup per (sequence, query head), merges the splits
+// in fixed order and writes the output. No float atomics.
 #include "device_common.h"
 #include "internal.h"
 
@@ -32,7 +32,6 @@ struct AttnArgs {
   const int32_t* seq_lens;
   const int32_t* sel;  // nullptr: dense (every full page)
   float* partials;
-  uint32_t* counters;
   float* out;
   int Hq, Hkv, N, num_blocks, k, pages_per_split, n_split;
 };
@@ -51,7 +50,6 @@ __global__ __launch_bounds__(256) void attend_kernel(AttnArgs a) {
   __shared__ __align__(16) float q_s[G][kDim];
   __shared__ float wm_s[4][G], wl_s[4][G];
   __shared__ float wo_s[4][G][kDim];
-  __shared__ int last_s;
 
   const float qscale = kLog2e * kInvSqrtD;  // logits in base-2 units
   for (int i = tid; i < G * kDim; i += 256)
@@ -161,35 +159,43 @@ __global__ __launch_bounds__(256) void attend_kernel(AttnArgs a) {
     ph[2 + d] = O;
     if (d == 0) { ph[0] = M; ph[1] = L; }
   }
+}
 
-  // ---- last split of this (sequence, KV head) writes the output
-  __threadfence();
+// Merge of the split partials of one (sequence, query head): 256 threads =
+// 128 output dims x 2 halves of the split list; fixed order, base-2 units.
+__global__ __launch_bounds__(256) void attend_merge_kernel(const float* partials, float* out,
+                                                           int Hq, int n_split) {
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x, d = tid & 127, half = tid >> 7;
+  __shared__ float red_s[4];
+  __shared__ float w_s[kMaxSplits];
+  __shared__ float l_s[2], o_s[2][kDim];
+  const float* ph = partials + ((size_t)b * Hq + h) * n_split * kPartialFloats;
+  float M = -INFINITY;
+  for (int sp = tid; sp < n_split; sp += 256) M = fmaxf(M, ph[(size_t)sp * kPartialFloats]);
+  M = wave_max(M);
+  if ((tid & 63) == 0) red_s[tid >> 6] = M;
   __syncthreads();
-  if (tid == 0) {
-    const uint32_t prev = atomicAdd(&a.counters[b * a.Hkv + kvh], 1u);
-    last_s = (prev == (uint32_t)(a.n_split - 1));
+  M = fmaxf(fmaxf(red_s[0], red_s[1]), fmaxf(red_s[2], red_s[3]));
+  for (int sp = tid; sp < n_split; sp += 256) {
+    const float ms = ph[(size_t)sp * kPartialFloats];
+    w_s[sp] = (M == -INFINITY) ? 0.f : exp2f(ms - M);
   }
   __syncthreads();
-  if (!last_s) return;
-  __threadfence();
-  const float* pbase = a.partials + ((size_t)b * a.Hq + (size_t)kvh * G) * a.n_split * kPartialFloats;
-  for (int i = tid; i < G * kDim; i += 256) {
-    const int h = i / kDim, d = i % kDim;
-    const float* ph = pbase + (size_t)h * a.n_split * kPartialFloats;
-    float M = -INFINITY;
-    for (int sp = 0; sp < a.n_split; ++sp) M = fmaxf(M, __builtin_nontemporal_load(&ph[sp * kPartialFloats]));
-    float L = 0.f, O = 0.f;
-    if (M != -INFINITY) {
-      for (int sp = 0; sp < a.n_split; ++sp) {
-        const float ms = __builtin_nontemporal_load(&ph[sp * kPartialFloats]);
-        const float f = exp2f(ms - M);
-        L += __builtin_nontemporal_load(&ph[sp * kPartialFloats + 1]) * f;
-        O += __builtin_nontemporal_load(&ph[sp * kPartialFloats + 2 + d]) * f;
-      }
-    }
-    a.out[((size_t)b * a.Hq + (size_t)kvh * G + h) * kDim + d] = (L > 0.f) ? O / L : 0.f;
+  const int s0 = half * ((n_split + 1) / 2), s1 = min(n_split, s0 + (n_split + 1) / 2);
+  float L = 0.f, O = 0.f;
+  for (int sp = s0; sp < s1; ++sp) {
+    const float wgt = w_s[sp];
+    L += ph[(size_t)sp * kPartialFloats + 1] * wgt;
+    O += ph[(size_t)sp * kPartialFloats + 2 + d] * wgt;
   }
-  if (tid == 0) a.counters[b * a.Hkv + kvh] = 0;
+  if (d == 0) l_s[half] = L;
+  o_s[half][d] = O;
+  __syncthreads();
+  if (half == 0) {
+    const float Lt = l_s[0] + l_s[1];
+    out[((size_t)b * Hq + h) * kDim + d] = (Lt > 0.f) ? (o_s[0][d] + o_s[1][d]) / Lt : 0.f;
+  }
 }
 
 template <int G>
@@ -204,17 +210,17 @@ hipError_t launch_g(const locks_dims& d, const WsLayout& L, const DevPtrs& P, co
   a.seq_lens = sl;
   a.sel = dense ? nullptr : sel;
   a.partials = dense ? P.dense_part : P.att_part;
-  a.counters = dense ? P.cnt_dense : P.cnt_attend;
   a.out = out;
   a.Hq = d.n_q_heads;
   a.Hkv = d.n_kv_heads;
   a.N = d.max_pages_per_seq;
   a.num_blocks = d.num_blocks;
   a.k = L.k;
-  a.pages_per_split = dense ? kDensePagesPerSplit : kSparsePagesPerSplit;
+  a.pages_per_split = dense ? L.dense_pages_per_split : kSparsePagesPerSplit;
   a.n_split = dense ? L.n_dense_split : L.n_att_split;
-  dim3 grid(a.n_split, d.n_kv_heads, d.batch);
-  hipLaunchKernelGGL(attend_kernel<G>, grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL(attend_kernel<G>, dim3(a.n_split, d.n_kv_heads, d.batch), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(attend_merge_kernel, dim3(d.n_q_heads, d.batch), dim3(256), 0, s, a.partials,
+                     out, d.n_q_heads, a.n_split);
   return hipGetLastError();
 }
 

@@ -275,7 +275,7 @@ __global__ __launch_bounds__(256) void build_kernel(BuildArgs a) {
   S.rec[kMuOff + 2 * lane + 1] = (uint8_t)(int8_t)quant(S.mu[2 * lane + 1], s_mu, 127);
 #pragma unroll
   for (int u = 0; u < 2; ++u) S.rec[kCOff + lane + 64 * u] = (uint8_t)(int8_t)quant(cval[u], s_c, 127);
-  if (lane < 16) {  // bytes [768, 832): scales then zero padding, as dwords
+  if (lane < (kStride - kSOff) / 4) {  // bytes [768, 784): scales then zero padding, as dwords
     uint32_t w = 0;
     if (lane == 0) w = f16_bits(s_mu) | (f16_bits(s_v) << 16);
     if (lane == 1) w = f16_bits(s_c);

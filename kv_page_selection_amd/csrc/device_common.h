@@ -10,7 +10,7 @@ namespace locks {
 constexpr int kDim = 128;        // head dimension
 constexpr int kPage = 16;        // tokens per page
 constexpr int kRank = 8;         // summary rank
-constexpr int kStride = 832;     // bytes per summary record
+constexpr int kStride = 784;     // bytes per summary record
 constexpr int kVOff = 0;         // V codes, k-major nibbles
 constexpr int kMuOff = 512;      // centroid codes, int8[128]
 constexpr int kCOff = 640;       // coefficient codes, int8[16][8]
@@ -56,6 +56,30 @@ __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
   return v;
+}
+
+// Raw hardware 2^x and log2(x) (v_exp_f32 / v_log_f32): results that would be
+// fp32 denormals flush to zero, which only drops terms below 2^-126 of a sum.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Butterfly partners across 32-lane halves and across 16-lane rows (gfx950
+// v_permlane32_swap / v_permlane16_swap): returns op(x, x of lane ^ 32 / ^ 16).
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor16_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor16_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // Merge of two (max, sum-of-exp2) pairs in base-2 log units; m = -inf means empty.

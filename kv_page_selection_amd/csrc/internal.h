@@ -10,26 +10,28 @@
 
 namespace locks {
 
-constexpr int kScorePagesPerWG = 256;   // 4 waves x 4 tiles x 16 pages
-constexpr int kSelectMaxElems = 8192;   // candidates one select WG ranks (32 per thread)
+constexpr int kScorePagesPerWave = 64;  // 4 tiles x 16 pages per wave and KV head
+constexpr int kSelectMaxElems = 8192;   // candidates ranked per merge round (32 per thread)
+constexpr int kSelectMaxK = 4096;       // budget/16 limit (the merge keeps up to k between rounds)
+constexpr int kSelectChunk = 1024;      // pages per chunk workgroup (4 per thread)
 constexpr int kSparsePagesPerSplit = 4; // one page per wave
-constexpr int kDensePagesPerSplit = 256;
+constexpr int kDensePagesPerSplit = 256; // at least; grows so that splits <= kMaxSplits
+constexpr int kMaxSplits = 2048;        // split partials one merge workgroup combines
 constexpr int kPartialFloats = 130;     // (m, l, o[128]) per head and split
 
 // Byte offsets of the regions of the caller's workspace (each 256-aligned).
 struct WsLayout {
   size_t scores = 0;       // f32 [B][Hq][N]   page scores when the caller passes none
-  size_t score_part = 0;   // f32 [B][Hq][n_score_wg][2]  (max, sum) in log2 units
-  size_t cand = 0;         // u64 [B][Hkv][n_sel_chunks][cand_slots = min(k, chunk)]
+  size_t score_part = 0;   // f32 [B][Hq][n_score_wg][2]  (max, sum) per 64-page range, base 2
+  size_t cand = 0;         // u64 [B][Hkv][n_sel_chunks][chunk] survivors of each chunk
   size_t cand_count = 0;   // i32 [B][Hkv][n_sel_chunks]
   size_t att_part = 0;     // f32 [B][Hq][n_att_split][130]
   size_t dense_part = 0;   // f32 [B][Hq][n_dense_split][130]
-  size_t counters = 0;     // u32 [3][B][Hkv]  select / sparse attention / dense
   size_t total = 0;
   int k = 0;
   int n_score_wg = 0;
-  int sel_chunk = 0, n_sel_chunks = 0, cand_slots = 0;
-  int n_att_split = 0, n_dense_split = 0;
+  int sel_chunk = 0, n_sel_chunks = 0;
+  int n_att_split = 0, n_dense_split = 0, dense_pages_per_split = 0;
 };
 
 // Returns false (and sets *why) when the dims/budget exceed the kernels' limits.
@@ -43,9 +45,6 @@ struct DevPtrs {
   int32_t* cand_count;
   float* att_part;
   float* dense_part;
-  uint32_t* cnt_select;
-  uint32_t* cnt_attend;
-  uint32_t* cnt_dense;
 };
 DevPtrs ws_ptrs(const locks_dims& d, const WsLayout& L, void* ws, float* page_scores);
 

@@ -4,19 +4,25 @@
 // group, computes the page score of the LOCKS blog post ("How LOCKS works",
 // page-score equation; technical summary, section 2 mechanism 2):
 //   s_hat = log sum_{i<16} exp((q.mu + (V^T q).c_i) / sqrt(128))
-// from the page's 832-byte summary record alone (no key or value is read).
+// from the page's summary record alone (no key or value is read).
 //
-// Mapping. One workgroup = 4 waves = 256 consecutive pages of one (b, KV head).
-// A wave handles 16 pages per tile. The two contractions with q, mu^T q and
-// V^T q, run on int8 MFMA (v_mfma_i32_16x16x64_i8): the A operand is the
-// record's codes exactly as stored (mu bytes as they are; V nibbles widened to
-// 16*code bytes with one shift and mask), the B operand is each query head as a
-// 22-bit fixed-point integer split into three signed int8 digits, so every
-// product and sum is exact in int32 and one fp32 rounding combines the digits.
-// Tile rows: 16 pages' mu rows in one MFMA tile; 2 pages x 8 basis vectors in
-// each of 8 V tiles. Columns: the G query heads. The in-page part (C p and the
-// 16-token log-sum-exp) runs on VALU from LDS, in base-2 units.
-// Each workgroup also leaves, per head, the (max, sum) of exp over its pages,
+// Mapping. A workgroup is 4 waves; wave w scores 64 consecutive pages (4 tiles
+// of 16) of one KV head, and the waves of a workgroup take consecutive KV
+// heads of the same pages, so the records of one physical block (adjacent in
+// memory) are fetched together.
+//
+// Stage 1, mu.q and V^T q, on v_mfma_i32_16x16x64_i8, exact: the row operand is
+// each query head as a 22-bit fixed-point integer in three signed int8 digits
+// (rows = 4 heads x 4 digit slots, the 4th slot zero), the column operand is
+// the record's codes as stored (mu bytes; V nibbles widened to 16*code with
+// one shift and mask). A lane then holds all three digit sums of one value,
+// which it combines in int32 and one fp32 rounding.
+// Stage 2, the in-page contraction C p (16 tokens x 8 x G heads), on
+// v_mfma_f32_16x16x{32,16}_f16: C codes are exact in f16 and p enters as an
+// f16 hi + lo pair (about 22 significant bits); 16/G pages are packed
+// block-diagonally along K so one pass fills the 16 output columns. The
+// 16-token log-sum-exp is one in-lane step and two cross-row swaps, in base 2.
+// Every wave also leaves, per head, the (max, sum) of exp over its 64 pages,
 // which the group combine needs for every head's total mass.
 #include "device_common.h"
 #include "internal.h"
@@ -25,6 +31,12 @@ namespace locks {
 
 namespace {
 
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+
+constexpr int kTiles = kScorePagesPerWave / 16;
+
 struct ScoreArgs {
   const float* q;
   const uint8_t* summ;
@@ -32,100 +44,136 @@ struct ScoreArgs {
   const int32_t* seq_lens;
   float* scores;
   float* partials;
-  uint32_t* reset;
-  int n_reset;
-  int Hq, Hkv, N, num_blocks, n_wg;
+  int Hq, Hkv, N, num_blocks, n_ranges;
 };
 
 __device__ __forceinline__ int nib_lo(uint32_t x) { return (int)((x << 4) & 0xF0F0F0F0u); }
 __device__ __forceinline__ int nib_hi(uint32_t x) { return (int)(x & 0xF0F0F0F0u); }
 
-// acc2*2^16 + acc1*2^8 + acc0, exact in int arithmetic up to the last fp32 rounding.
-__device__ __forceinline__ float digits_value(int a2, int a1, int a0) {
-  return (float)(a2 * 256 + a1) * 256.0f + (float)a0;
+// Four int8 codes -> four exact f16 values: bias to u = code + 128, place u in
+// the mantissa of 1024.0 (0x64uu), subtract 1152 with one packed f16 add.
+__device__ __forceinline__ h4 codes_to_h4(uint32_t x) {
+  const uint32_t u = x ^ 0x80808080u;
+  const h2 bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+  const h2 lo = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u)) + bias;
+  const h2 hi = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u)) + bias;
+  return h4{lo[0], lo[1], hi[0], hi[1]};
 }
 
 __device__ __forceinline__ v4i mfma_i8(v4i a, v4i b, v4i c) {
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
 
+// Per-wave LDS staging of one 16-page tile.
+template <int G>
+struct TileLds {
+  __align__(16) int8_t c[16][144];      // C codes per page (token-major), padded rows
+  __align__(16) _Float16 ph[16][G][8];  // p (scaled by 2^-22) high part, [page][head][k]
+  __align__(16) _Float16 pl[16][G][8];  // low part
+  __align__(16) _Float16 zero[8];       // masked B operand
+  float a[16][G + 1];                   // mu . q (exact integer), [page][head]; column G spare
+  float sc[16][4];                      // s_mu, s_V/16 * s_C, valid
+};
+
+// Per wave: the q digit planes are dead once the row operands are in
+// registers, so they share storage with the tile staging.
+template <int G>
+union WaveLds {
+  TileLds<G> t;
+  __align__(16) int8_t dig[3][G][kDim];
+};
+
+template <int G>
+struct ScoreLds {
+  WaveLds<G> w[4];
+  float esc[4][16];
+};
+
 template <int G>
 __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
-  constexpr int kPairs = 16 * G;  // (page, head) pairs of a tile
-  constexpr int kSlots = (kPairs + 63) / 64;
-  const int wg = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int RB = G < 4 ? 1 : G / 4;   // stage-1 row blocks (4 heads each)
+  constexpr int PG = 16 / G;              // pages per stage-2 pass
+  __shared__ ScoreLds<G> S;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = lane & 15, kg = lane >> 4;
+  const int b = blockIdx.z;
+  // waves -> (KV head, page range): up to 4 KV heads share the same pages
+  const int hw = a.Hkv < 4 ? a.Hkv : 4;
+  const int slots = 4 / hw;
+  const int kvh = blockIdx.y * hw + wave % hw;
+  const int range = blockIdx.x * slots + wave / hw;
+  if (wave / hw >= slots || kvh >= a.Hkv || range >= a.n_ranges) return;  // whole wave
   const int N = a.N;
   const int n_b = full_pages(a.seq_lens, b, N);
+  TileLds<G>& T = S.w[wave].t;
 
-  __shared__ float q_s[G * kDim];
-  __shared__ int qmax_s[G];
-  __shared__ __align__(16) int8_t dig_s[3][G][kDim];
-  __shared__ float esc_s[G];
-  __shared__ float pv_s[4][16][kRank][G];
-  __shared__ float a_s[4][16][G];
-  __shared__ __align__(16) uint8_t c_s[4][16][128];
-  __shared__ float sc_s[4][16][3];
-  __shared__ float red_s[4][G][2];
-
-  // Counters of the later phases start every step at zero.
-  if (wg == 0 && kvh == 0 && b == 0)
-    for (int i = tid; i < a.n_reset; i += 256) a.reset[i] = 0;
-
-  // ---- q of the group -> per-head exponent -> three int8 digit planes
-  if (tid < G) qmax_s[tid] = 0;
-  const float* qg = a.q + ((size_t)b * a.Hq + (size_t)kvh * G) * kDim;
-  for (int i = tid; i < G * kDim; i += 256) q_s[i] = qg[i];
-  __syncthreads();
-  for (int i = tid; i < G * kDim; i += 256)
-    atomicMax(&qmax_s[i / kDim], __float_as_int(fabsf(q_s[i])));
-  __syncthreads();
-  for (int i = tid; i < G * kDim; i += 256) {
-    const int h = i / kDim, d = i % kDim;
-    const float qm = __int_as_float(qmax_s[h]);
-    int e = 0;
-    if (qm > 0.f) {
-      int E;
-      frexpf(qm, &E);
-      e = 22 - E;  // max |q| * 2^e in [2^21, 2^22)
+  // ---- q of the group -> per-head exponent -> three int8 digit planes (wave-local)
+  {
+    const float* qg = a.q + ((size_t)b * a.Hq + (size_t)kvh * G) * kDim;
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float q0 = qg[h * kDim + lane], q1 = qg[h * kDim + 64 + lane];
+      const float qm = wave_max(fmaxf(fabsf(q0), fabsf(q1)));
+      int e = 0;
+      if (qm > 0.f) {
+        int E;
+        frexpf(qm, &E);
+        e = 22 - E;  // max |q| * 2^e in [2^21, 2^22)
+      }
+      const float qs[2] = {q0, q1};
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int qf = (int)rintf(ldexpf(qs[u], e));
+        const int d0 = ((qf + 128) & 255) - 128;
+        const int r1 = (qf - d0) / 256;
+        const int d1 = ((r1 + 128) & 255) - 128;
+        const int d2 = (r1 - d1) / 256;
+        S.w[wave].dig[0][h][lane + 64 * u] = (int8_t)d0;
+        S.w[wave].dig[1][h][lane + 64 * u] = (int8_t)d1;
+        S.w[wave].dig[2][h][lane + 64 * u] = (int8_t)d2;
+      }
+      if (lane == 0) S.esc[wave][h] = ldexpf(1.0f, -e) * (kLog2e * kInvSqrtD);
     }
-    const int qf = (int)rintf(ldexpf(q_s[i], e));
-    const int d0 = ((qf + 128) & 255) - 128;
-    const int r1 = (qf - d0) / 256;
-    const int d1 = ((r1 + 128) & 255) - 128;
-    const int d2 = (r1 - d1) / 256;
-    dig_s[0][h][d] = (int8_t)d0;
-    dig_s[1][h][d] = (int8_t)d1;
-    dig_s[2][h][d] = (int8_t)d2;
-    if (d == 0) esc_s[h] = ldexpf(1.0f, -e);
   }
-  __syncthreads();
-
-  // B operands: lane (column = head `row`, K group kg) holds d in [32kg+16m, +16).
-  v4i bop[2][3];
+  wave_lds_sync();
+  // row operands: lane (row = (head 4rb + row/4, digit row%4), K group kg), d in [32kg+16m, +16)
+  v4i aop[RB][2];
 #pragma unroll
-  for (int m = 0; m < 2; ++m)
+  for (int rb = 0; rb < RB; ++rb) {
+    const int h = 4 * rb + (row >> 2), dg = row & 3;
 #pragma unroll
-    for (int dg = 0; dg < 3; ++dg)
-      bop[m][dg] = (row < G) ? *reinterpret_cast<const v4i*>(&dig_s[dg][row < G ? row : 0][32 * kg + 16 * m])
-                             : v4i{0, 0, 0, 0};
+    for (int m = 0; m < 2; ++m)
+      aop[rb][m] = (h < G && dg < 3)
+                       ? *reinterpret_cast<const v4i*>(&S.w[wave].dig[dg < 3 ? dg : 0][h < G ? h : 0][32 * kg + 16 * m])
+                       : v4i{0, 0, 0, 0};
+  }
+  wave_lds_sync();  // digit planes consumed; the storage becomes tile staging
+  if (lane < 8) T.zero[lane] = (_Float16)0.0f;
 
-  float run_m = -INFINITY, run_s = 0.f;  // this lane's head, log2 units
+  // stage-2 output column col = (page pc of the pass, head hc)
+  const int pc = row / G, hc = row % G;
+  const float es = S.esc[wave][hc];
+  float run_m = -1e30f, run_s = 0.f;  // head hc, base 2; -1e30 = empty
 
-  for (int t = 0; t < 4; ++t) {
-    const int pbase = wg * kScorePagesPerWG + wave * 64 + t * 16;
-    const int j = pbase + row;
-    int blk = -1;
+  // page table of this wave's 64 pages, one entry per lane
+  const int p0 = range * kScorePagesPerWave;
+  int myblk = -1;
+  {
+    const int j = p0 + lane;
     if (j < n_b) {
-      blk = a.page_table[(size_t)b * N + j];
-      if (blk < 0 || blk >= a.num_blocks) blk = -1;
+      myblk = a.page_table[(size_t)b * N + j];
+      if (myblk < 0 || myblk >= a.num_blocks) myblk = -1;
     }
+  }
+
+  for (int t = 0; t < kTiles; ++t) {
+    const int pbase = p0 + t * 16;
+    const int blk = __shfl(myblk, t * 16 + row);  // page pbase + row
     // ---- loads: V rows (page 2vt + row/8, basis vector row%8), mu, C, scales
     uint4 vraw[8];
 #pragma unroll
     for (int vt = 0; vt < 8; ++vt) {
-      const int blk2 = __shfl(blk, 2 * vt + (row >> 3));
+      const int blk2 = __shfl(myblk, t * 16 + 2 * vt + (row >> 3));
       vraw[vt] = make_uint4(0, 0, 0, 0);
       if (blk2 >= 0)
         vraw[vt] = *reinterpret_cast<const uint4*>(
@@ -141,114 +189,115 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
       c1 = *reinterpret_cast<const uint4*>(rec + kCOff + kg * 32 + 16);
       if (kg == 0) scl = *reinterpret_cast<const uint2*>(rec + kSOff);
     }
-    *reinterpret_cast<uint4*>(&c_s[wave][row][kg * 32]) = c0;
-    *reinterpret_cast<uint4*>(&c_s[wave][row][kg * 32 + 16]) = c1;
+    *reinterpret_cast<uint4*>(&T.c[row][kg * 32]) = c0;
+    *reinterpret_cast<uint4*>(&T.c[row][kg * 32 + 16]) = c1;
     if (kg == 0) {
-      sc_s[wave][row][0] = f16bits_to_float(scl.x);
-      sc_s[wave][row][1] = f16bits_to_float(scl.x >> 16) * (1.0f / 16.0f) * f16bits_to_float(scl.y);
-      sc_s[wave][row][2] = (blk >= 0) ? 1.0f : 0.0f;
+      T.sc[row][0] = f16bits_to_float(scl.x);
+      T.sc[row][1] = f16bits_to_float(scl.x >> 16) * (1.0f / 16.0f) * f16bits_to_float(scl.y);
+      T.sc[row][2] = (blk >= 0) ? 1.0f : 0.0f;
     }
 
-    // ---- mu tile: rows = the 16 pages
+    // ---- stage 1: mu tile (columns = the 16 pages); lane (page row, kg) -> head 4rb + kg
     {
-      v4i acc[3] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
-      const v4i A0 = {(int)mu0.x, (int)mu0.y, (int)mu0.z, (int)mu0.w};
-      const v4i A1 = {(int)mu1.x, (int)mu1.y, (int)mu1.z, (int)mu1.w};
+      const v4i B0 = {(int)mu0.x, (int)mu0.y, (int)mu0.z, (int)mu0.w};
+      const v4i B1 = {(int)mu1.x, (int)mu1.y, (int)mu1.z, (int)mu1.w};
 #pragma unroll
-      for (int dg = 0; dg < 3; ++dg) {
-        acc[dg] = mfma_i8(A0, bop[0][dg], acc[dg]);
-        acc[dg] = mfma_i8(A1, bop[1][dg], acc[dg]);
-      }
-      if (row < G) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          a_s[wave][4 * kg + i][row < G ? row : 0] = digits_value(acc[2][i], acc[1][i], acc[0][i]);
+      for (int rb = 0; rb < RB; ++rb) {
+        v4i acc = mfma_i8(aop[rb][0], B0, v4i{0, 0, 0, 0});
+        acc = mfma_i8(aop[rb][1], B1, acc);
+        const int h = 4 * rb + kg;
+        T.a[row][h < G ? h : G] = (float)(acc[2] * 256 + acc[1]) * 256.0f + (float)acc[0];
       }
     }
-    // ---- V tiles: rows = (page 2vt + r/8, basis vector r%8)
+    // ---- stage 1: V tiles (columns = (page 2vt + row/8, basis vector row%8))
 #pragma unroll
     for (int vt = 0; vt < 8; ++vt) {
       const uint4 v = vraw[vt];
-      const v4i A0 = {nib_lo(v.x), nib_hi(v.x), nib_lo(v.y), nib_hi(v.y)};
-      const v4i A1 = {nib_lo(v.z), nib_hi(v.z), nib_lo(v.w), nib_hi(v.w)};
-      v4i acc[3] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
+      const v4i B0 = {nib_lo(v.x), nib_hi(v.x), nib_lo(v.y), nib_hi(v.y)};
+      const v4i B1 = {nib_lo(v.z), nib_hi(v.z), nib_lo(v.w), nib_hi(v.w)};
 #pragma unroll
-      for (int dg = 0; dg < 3; ++dg) {
-        acc[dg] = mfma_i8(A0, bop[0][dg], acc[dg]);
-        acc[dg] = mfma_i8(A1, bop[1][dg], acc[dg]);
-      }
-      if (row < G) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          pv_s[wave][2 * vt + (kg >> 1)][4 * (kg & 1) + i][row < G ? row : 0] =
-              digits_value(acc[2][i], acc[1][i], acc[0][i]);
-      }
-    }
-    wave_lds_sync();
-
-    // ---- in-page logits and their log-sum-exp; lane <-> (page, head) pairs
-#pragma unroll
-    for (int s = 0; s < kSlots; ++s) {
-      const int pi = lane + 64 * s;
-      if (pi < kPairs) {
-        const int p = pi / G, h = pi % G;
-        if (sc_s[wave][p][2] != 0.0f) {
-          const float es = esc_s[h] * (kLog2e * kInvSqrtD);
-          const float cs = sc_s[wave][p][1] * es;
-          float pk[kRank], psum = 0.f;
-#pragma unroll
-          for (int k = 0; k < kRank; ++k) {
-            pk[k] = pv_s[wave][p][k][h] * cs;
-            psum += pk[k];
-          }
-          // C codes are read as unsigned bytes (code + 128); the offset is removed once.
-          const float base = a_s[wave][p][h] * sc_s[wave][p][0] * es - 128.0f * psum;
-          float t2[kPage], m = -INFINITY;
-#pragma unroll
-          for (int i = 0; i < kPage; ++i) {
-            const uint2 cw = *reinterpret_cast<const uint2*>(&c_s[wave][p][i * 8]);
-            const uint32_t u0 = cw.x ^ 0x80808080u, u1 = cw.y ^ 0x80808080u;
-            float acc = base;
-            acc = fmaf((float)(u0 & 0xffu), pk[0], acc);
-            acc = fmaf((float)((u0 >> 8) & 0xffu), pk[1], acc);
-            acc = fmaf((float)((u0 >> 16) & 0xffu), pk[2], acc);
-            acc = fmaf((float)(u0 >> 24), pk[3], acc);
-            acc = fmaf((float)(u1 & 0xffu), pk[4], acc);
-            acc = fmaf((float)((u1 >> 8) & 0xffu), pk[5], acc);
-            acc = fmaf((float)((u1 >> 16) & 0xffu), pk[6], acc);
-            acc = fmaf((float)(u1 >> 24), pk[7], acc);
-            t2[i] = acc;
-            m = fmaxf(m, acc);
-          }
-          float ssum = 0.f;
-#pragma unroll
-          for (int i = 0; i < kPage; ++i) ssum += exp2f(t2[i] - m);
-          const float shat2 = m + log2f(ssum);
-          a.scores[((size_t)b * a.Hq + (size_t)kvh * G + h) * N + pbase + p] = shat2 * kLn2;
-          lse2_merge(run_m, run_s, shat2, 1.0f);
+      for (int rb = 0; rb < RB; ++rb) {
+        v4i acc = mfma_i8(aop[rb][0], B0, v4i{0, 0, 0, 0});
+        acc = mfma_i8(aop[rb][1], B1, acc);
+        const int h = 4 * rb + kg;
+        // exact integer (|.| < 2^37) -> fp32 -> scaled into f16 range, split hi + lo
+        const float x = ((float)(acc[2] * 256 + acc[1]) * 256.0f + (float)acc[0]) * 0x1p-22f;
+        const _Float16 xh = (_Float16)x;
+        const _Float16 xl = (_Float16)(x - (float)xh);
+        if (h < G) {
+          T.ph[2 * vt + (row >> 3)][h < G ? h : 0][row & 7] = xh;
+          T.pl[2 * vt + (row >> 3)][h < G ? h : 0][row & 7] = xl;
         }
       }
     }
     wave_lds_sync();
+
+    // ---- stage 2 + LSE, one pass per PG pages
+#pragma unroll
+    for (int gp = 0; gp < G; ++gp) {
+      v4f acc = {0.f, 0.f, 0.f, 0.f};
+      const int pp = gp * PG + pc;  // tile page of this lane's output column
+      if constexpr (PG >= 4) {
+        // K = 32 per MFMA = 4 page slots x 8 basis vectors; lane group kg = slot
+#pragma unroll
+        for (int ch = 0; ch < PG / 4; ++ch) {
+          const int slot = 4 * ch + kg;
+          const uint2 cw = *reinterpret_cast<const uint2*>(&T.c[gp * PG + slot][row * 8]);
+          const h4 c_lo = codes_to_h4(cw.x), c_hi = codes_to_h4(cw.y);
+          const h8 A = {c_lo[0], c_lo[1], c_lo[2], c_lo[3], c_hi[0], c_hi[1], c_hi[2], c_hi[3]};
+          const bool on = (pc == slot);
+          const h8 Bh = *reinterpret_cast<const h8*>(on ? &T.ph[pp][hc][0] : &T.zero[0]);
+          const h8 Bl = *reinterpret_cast<const h8*>(on ? &T.pl[pp][hc][0] : &T.zero[0]);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bh, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bl, acc, 0, 0, 0);
+        }
+      } else {
+        // K = 16 per MFMA = 2 page slots x 8; lane group kg = (slot kg/2, half kg%2)
+        const int slot = kg >> 1, half = kg & 1;
+        const int pg = gp * PG + (slot < PG ? slot : 0);
+        const uint32_t cw = *reinterpret_cast<const uint32_t*>(&T.c[pg][row * 8 + 4 * half]);
+        const h4 cv = codes_to_h4(cw);
+        const h4 A = (slot < PG) ? cv : h4{0, 0, 0, 0};
+        const bool on = (pc == slot);
+        const h4 Bh = *reinterpret_cast<const h4*>(on ? &T.ph[pp][hc][4 * half] : &T.zero[0]);
+        const h4 Bl = *reinterpret_cast<const h4*>(on ? &T.pl[pp][hc][4 * half] : &T.zero[0]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x16f16(A, Bh, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x16f16(A, Bl, acc, 0, 0, 0);
+      }
+      // lane (col = row, kg) holds tokens 4kg .. 4kg+3 of (page pp, head hc)
+      const float sa = T.sc[pp][0] * es, sv = T.sc[pp][1] * es * 0x1p22f;
+      const float base = T.a[pp][hc] * sa;
+      const float t0 = fmaf(acc[0], sv, base), t1 = fmaf(acc[1], sv, base);
+      const float t2 = fmaf(acc[2], sv, base), t3 = fmaf(acc[3], sv, base);
+      float mx = fmaxf(fmaxf(t0, t1), fmaxf(t2, t3));
+      mx = xor32_max(xor16_max(mx));
+      float ssum = fast_exp2(t0 - mx) + fast_exp2(t1 - mx) + fast_exp2(t2 - mx) + fast_exp2(t3 - mx);
+      ssum = xor32_sum(xor16_sum(ssum));
+      const float shat2 = mx + fast_log2(ssum);
+      const bool valid = T.sc[pp][2] != 0.0f;
+      if (kg == 0 && pbase + pp < n_b)  // absent pages are marked -inf
+        a.scores[((size_t)b * a.Hq + (size_t)kvh * G + hc) * N + pbase + pp] = valid ? shat2 * kLn2 : -INFINITY;
+      // running (max, sum) of this head, branch-free; absent pages add nothing
+      const float x = valid ? shat2 : -1e30f;
+      const float mn = fmaxf(run_m, x);
+      run_s = run_s * fast_exp2(run_m - mn) + fast_exp2(x - mn);
+      run_m = mn;
+    }
+    wave_lds_sync();
   }
 
-  // ---- per-head (max, sum) over this workgroup's pages
+  // ---- per-head (max, sum) over this wave's pages: lanes 0..15, head = lane % G
 #pragma unroll
-  for (int off = G; off < 64; off <<= 1) {
+  for (int off = G; off < 16; off <<= 1) {
     const float m2 = __shfl_xor(run_m, off), s2 = __shfl_xor(run_s, off);
-    lse2_merge(run_m, run_s, m2, s2);
+    const float mn = fmaxf(run_m, m2);
+    run_s = run_s * fast_exp2(run_m - mn) + s2 * fast_exp2(m2 - mn);
+    run_m = mn;
   }
   if (lane < G) {
-    red_s[wave][lane < G ? lane : 0][0] = run_m;
-    red_s[wave][lane < G ? lane : 0][1] = run_s;
-  }
-  __syncthreads();
-  if (tid < G) {
-    float m = red_s[0][tid][0], s = red_s[0][tid][1];
-    for (int w = 1; w < 4; ++w) lse2_merge(m, s, red_s[w][tid][0], red_s[w][tid][1]);
-    float* dst = a.partials + (((size_t)b * a.Hq + (size_t)kvh * G + tid) * a.n_wg + wg) * 2;
-    dst[0] = m;
-    dst[1] = s;
+    float* dst = a.partials + (((size_t)b * a.Hq + (size_t)kvh * G + lane) * a.n_ranges + range) * 2;
+    dst[0] = (run_s > 0.f) ? run_m : -INFINITY;
+    dst[1] = run_s;
   }
 }
 
@@ -262,14 +311,14 @@ hipError_t launch_g(const locks_dims& d, const WsLayout& L, const DevPtrs& P, co
   a.seq_lens = sl;
   a.scores = P.scores;
   a.partials = P.score_part;
-  a.reset = P.cnt_select;  // select and sparse-attention counters are adjacent
-  a.n_reset = 2 * d.batch * d.n_kv_heads;
   a.Hq = d.n_q_heads;
   a.Hkv = d.n_kv_heads;
   a.N = d.max_pages_per_seq;
   a.num_blocks = d.num_blocks;
-  a.n_wg = L.n_score_wg;
-  dim3 grid(L.n_score_wg, d.n_kv_heads, d.batch);
+  a.n_ranges = L.n_score_wg;
+  const int hw = d.n_kv_heads < 4 ? d.n_kv_heads : 4;
+  const int slots = 4 / hw;
+  dim3 grid((L.n_score_wg + slots - 1) / slots, (d.n_kv_heads + hw - 1) / hw, d.batch);
   hipLaunchKernelGGL(score_kernel<G>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }

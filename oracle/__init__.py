@@ -12,8 +12,7 @@ Sources, cited by title and section:
   (B) "LOCKS – 효율적인 롱 컨텍스트 디코딩을 위한 페이지 로컬 압축 키 요약"
       (gist.science, paper 2607.24555) — section 2, mechanisms 1-3.
 
-Parity pins for every function are in ``tests/test_oracle_pins.py`` and
-``tests/test_oracle_units.py``. The QUANTISED scores and selections have no pin
+Parity pins for every function are in ``tests/test_oracle_pins.py``. The QUANTISED scores and selections have no pin
 other than their pieces (the quantiser, the pack format and the unquantised
 score each are pinned; their composition is not): "parity unpinned" for the
 quantised end-to-end numbers.
@@ -33,7 +32,7 @@ _LIB_PATH = os.path.join(_HERE, "liblocks_oracle.so")
 PAGE = 16
 DIM = 128
 RANK = 8
-RECORD_BYTES = 832
+RECORD_BYTES = 784
 
 
 def build(force: bool = True) -> str:
@@ -152,9 +151,9 @@ def page_summary_f64(keys: np.ndarray, rank: int = RANK):
 
 
 def build_record(keys_bf16: np.ndarray):
-    """Quantised 832-byte record of one page from its 16x128 bf16 bits.
+    """Quantised 784-byte record of one page from its 16x128 bf16 bits.
 
-    Returns (record uint8[832], lam[16], mu, V, C unquantised)."""
+    Returns (record uint8[784], lam[16], mu, V, C unquantised)."""
     kb = _as(keys_bf16, np.uint16)
     assert kb.shape == (PAGE, DIM)
     rec = np.zeros(RECORD_BYTES, dtype=np.uint8)

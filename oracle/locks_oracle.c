@@ -38,7 +38,7 @@
 #define OD 128        /* head dimension */
 #define OP 16         /* tokens per page */
 #define OR 8          /* rank of the shipped summary */
-#define OSTRIDE 832   /* bytes per summary record */
+#define OSTRIDE 784   /* bytes per summary record */
 #define OV_OFF 0      /* V codes */
 #define OMU_OFF 512   /* centroid codes */
 #define OC_OFF 640    /* coefficient codes */
@@ -237,7 +237,7 @@ void oracle_page_summary_f64(const double* keys, int r, double* mu, double* V, d
     }
 }
 
-/* Pack codes into the 832-byte record (format documented in the C ABI). */
+/* Pack codes into the 784-byte record (format documented in the C ABI). */
 static void pack_record(const int* mu_c, const int* v_c /* [128][8] */, const int* c_c /* [16][8] */,
                         const uint16_t* scales /* 3 */, uint8_t* rec) {
   memset(rec, 0, OSTRIDE);

@@ -48,7 +48,7 @@ def dims(L, **kw):
 
 
 def test_record_size(L):
-    assert L.summary_record_bytes() == 832
+    assert L.summary_record_bytes() == 784
 
 
 def test_workspace_sizing_and_validation(L):

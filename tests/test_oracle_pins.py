@@ -182,7 +182,7 @@ def test_record_format_matches_documented_layout(orc):
     mc = r.integers(-127, 128, size=DIM)
     cc = r.integers(-127, 128, size=(PAGE, 8))
     s = np.array([0.03125, 0.25, 0.0078125], dtype=np.float16)
-    rec = np.zeros(832, dtype=np.uint8)
+    rec = np.zeros(784, dtype=np.uint8)
     nib = (vc & 0xF).astype(np.uint8)                  # [d][k] two's complement nibbles
     for k in range(8):
         col = nib[:, k].reshape(16, 2, 4)              # [word][half][byte]
@@ -202,7 +202,7 @@ def test_summary_payload_is_about_ten_percent(orc):
     payload = 128 * 8 // 2 + 128 + 16 * 8 + 6
     assert payload == 774
     assert 0.09 < (payload + 2) / (PAGE * DIM * 2 * 2) < 0.105
-    assert 832 / (PAGE * DIM * 2 * 2) < 0.11
+    assert 784 / (PAGE * DIM * 2 * 2) < 0.1
 
 
 # ------------------------------------------------------------ group keys + top-k
