@@ -22,6 +22,13 @@ bool ws_layout(const locks_dims& d, int k, WsLayout* L, const char** why) {
   const long long B = d.batch, Hq = d.n_q_heads, Hkv = d.n_kv_heads, N = d.max_pages_per_seq;
   L->k = k;
   L->n_score_wg = (int)((N + kScorePagesPerWave - 1) / kScorePagesPerWave);
+  {
+    const int G = d.n_q_heads / d.n_kv_heads;
+    int S = 1;
+    while ((long long)G * ((L->n_score_wg + S - 1) / S) > kBoundSlots) S *= 2;
+    L->bound_sup = S;
+    L->bound_n_sup = (L->n_score_wg + S - 1) / S;
+  }
   // select chunks of up to 1024 pages; every page's sort key fits the chunk's slots
   if (k > kSelectMaxK) {
     *why = "budget/16 above 4096 pages";
@@ -48,8 +55,12 @@ bool ws_layout(const locks_dims& d, int k, WsLayout* L, const char** why) {
   L->dense_part = off; off = align_up(off + (size_t)(B * Hq) * L->n_dense_split * kPartialFloats * 4);
   L->score_part = off; off = align_up(off + (size_t)(B * Hq * L->n_score_wg) * 2 * 4);
   L->scores = off;     off = align_up(off + (size_t)(B * Hq * N) * 4);
+  L->Lg = off;         off = align_up(off + (size_t)(B * Hq) * 4);
+  L->tlb = off;        off = align_up(off + (size_t)(B * Hkv) * 4);
   L->cand = off;       off = align_up(off + (size_t)(B * Hkv * L->n_sel_chunks) * L->sel_chunk * 8);
+  L->cand_blk = off;   off = align_up(off + (size_t)(B * Hkv * L->n_sel_chunks) * L->sel_chunk * 4);
   L->cand_count = off; off = align_up(off + (size_t)(B * Hkv * L->n_sel_chunks) * 4);
+  L->sel_blk = off;    off = align_up(off + (size_t)(B * Hkv) * k * 4);
   L->att_part = off;   off = align_up(off + (size_t)(B * Hq) * L->n_att_split * kPartialFloats * 4);
   L->total = off;
   return true;
@@ -61,8 +72,12 @@ DevPtrs ws_ptrs(const locks_dims& d, const WsLayout& L, void* ws, float* page_sc
   P.ws = w;
   P.scores = page_scores ? page_scores : reinterpret_cast<float*>(w + L.scores);
   P.score_part = reinterpret_cast<float*>(w + L.score_part);
+  P.Lg = reinterpret_cast<float*>(w + L.Lg);
+  P.tlb = reinterpret_cast<float*>(w + L.tlb);
   P.cand = reinterpret_cast<unsigned long long*>(w + L.cand);
+  P.cand_blk = reinterpret_cast<int32_t*>(w + L.cand_blk);
   P.cand_count = reinterpret_cast<int32_t*>(w + L.cand_count);
+  P.sel_blk = reinterpret_cast<int32_t*>(w + L.sel_blk);
   P.att_part = reinterpret_cast<float*>(w + L.att_part);
   P.dense_part = reinterpret_cast<float*>(w + L.dense_part);
   (void)d;
@@ -96,8 +111,6 @@ locks_status check_dims(const locks_dims* d) {
   const int G = d->n_q_heads / d->n_kv_heads;
   if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16)
     return fail(LOCKS_ERR_UNSUPPORTED, "GQA group size must be 1, 2, 4, 8 or 16");
-  if (d->max_pages_per_seq > (1 << 23))
-    return fail(LOCKS_ERR_UNSUPPORTED, "max_pages_per_seq above 2^23");
   if (d->max_pages_per_seq > (1 << 20))
     return fail(LOCKS_ERR_UNSUPPORTED, "max_pages_per_seq above 2^20");
   if ((long long)d->batch * d->n_kv_heads > 65535 || d->batch > 65535)
@@ -244,7 +257,7 @@ locks_status locks_sparse_attention(const locks_dims* dims, const float* q, cons
   (void)hipGetLastError();
   return hip_status(launch_attend(*dims, L, P, q, static_cast<const uint16_t*>(k_cache),
                                   static_cast<const uint16_t*>(v_cache), page_table, seq_lens,
-                                  selected, out, false, stream),
+                                  selected, nullptr, out, false, stream),
                     "sparse attention launch");
 }
 
@@ -278,7 +291,7 @@ locks_status locks_decode_step(const locks_dims* dims, const float* q, const voi
                        "select launch"));
   return hip_status(launch_attend(*dims, L, P, q, static_cast<const uint16_t*>(k_cache),
                                   static_cast<const uint16_t*>(v_cache), page_table, seq_lens,
-                                  selected, out, false, stream),
+                                  selected, P.sel_blk, out, false, stream),
                     "sparse attention launch");
 }
 
@@ -301,7 +314,7 @@ locks_status locks_dense_attention(const locks_dims* dims, const float* q, const
   (void)hipGetLastError();
   return hip_status(launch_attend(*dims, L, P, q, static_cast<const uint16_t*>(k_cache),
                                   static_cast<const uint16_t*>(v_cache), page_table, seq_lens,
-                                  nullptr, out, true, stream),
+                                  nullptr, nullptr, out, true, stream),
                     "dense attention launch");
 }
 

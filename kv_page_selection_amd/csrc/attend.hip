@@ -30,7 +30,8 @@ struct AttnArgs {
   const uint16_t* vc;
   const int32_t* page_table;
   const int32_t* seq_lens;
-  const int32_t* sel;  // nullptr: dense (every full page)
+  const int32_t* sel;      // nullptr: dense (every full page)
+  const int32_t* sel_blk;  // physical blocks of sel's pages (nullptr: look them up)
   float* partials;
   float* out;
   int Hq, Hkv, N, num_blocks, k, pages_per_split, n_split;
@@ -51,6 +52,21 @@ __global__ __launch_bounds__(256) void attend_kernel(AttnArgs a) {
   __shared__ float wm_s[4][G], wl_s[4][G];
   __shared__ float wo_s[4][G][kDim];
 
+  // physical block of list entry s (-1: skip): from the selection's block
+  // list, through the page table, or (dense) page s itself
+  auto page_block = [&](int s) -> int {
+    int blk;
+    if (a.sel_blk) {
+      blk = a.sel_blk[((size_t)b * a.Hkv + kvh) * a.k + s];
+    } else {
+      const int j = a.sel ? a.sel[((size_t)b * a.Hkv + kvh) * a.k + s] : s;
+      if (j < 0 || j >= n_b) return -1;
+      blk = a.page_table[(size_t)b * N + j];
+    }
+    return (blk >= 0 && blk < a.num_blocks) ? blk : -1;
+  };
+  int blk_next = (s0 + wave < s1) ? page_block(s0 + wave) : -1;  // in flight during q staging
+
   const float qscale = kLog2e * kInvSqrtD;  // logits in base-2 units
   for (int i = tid; i < G * kDim; i += 256)
     q_s[i / kDim][i % kDim] = a.q[((size_t)b * a.Hq + (size_t)kvh * G) * kDim + i] * qscale;
@@ -61,10 +77,9 @@ __global__ __launch_bounds__(256) void attend_kernel(AttnArgs a) {
   for (int h = 0; h < G; ++h) { m[h] = -INFINITY; l[h] = 0.f; o0[h] = 0.f; o1[h] = 0.f; }
 
   for (int s = s0 + wave; s < s1; s += 4) {
-    const int j = a.sel ? a.sel[((size_t)b * a.Hkv + kvh) * a.k + s] : s;
-    if (j < 0 || j >= n_b) continue;
-    const int blk = a.page_table[(size_t)b * N + j];
-    if (blk < 0 || blk >= a.num_blocks) continue;
+    const int blk = blk_next;
+    blk_next = (s + 4 < s1) ? page_block(s + 4) : -1;
+    if (blk < 0) continue;
     const size_t tile = ((size_t)blk * a.Hkv + kvh) * (kPage * kDim);
     const uint4* krow = reinterpret_cast<const uint4*>(a.kc + tile + tok * kDim + c * 32);
     uint4 kr[4];
@@ -162,46 +177,57 @@ __global__ __launch_bounds__(256) void attend_kernel(AttnArgs a) {
 }
 
 // Merge of the split partials of one (sequence, query head): 256 threads =
-// 128 output dims x 2 halves of the split list; fixed order, base-2 units.
+// 128 output dims x 2 halves of the split list. Each half folds its splits in
+// fixed order with an online rescale, 8 splits' loads in flight at a time;
+// then half 1 is folded into half 0. Base-2 units throughout.
 __global__ __launch_bounds__(256) void attend_merge_kernel(const float* partials, float* out,
                                                            int Hq, int n_split) {
   const int h = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x, d = tid & 127, half = tid >> 7;
-  __shared__ float red_s[4];
-  __shared__ float w_s[kMaxSplits];
-  __shared__ float l_s[2], o_s[2][kDim];
+  __shared__ float m_s, l_s, o_s[kDim];
   const float* ph = partials + ((size_t)b * Hq + h) * n_split * kPartialFloats;
-  float M = -INFINITY;
-  for (int sp = tid; sp < n_split; sp += 256) M = fmaxf(M, ph[(size_t)sp * kPartialFloats]);
-  M = wave_max(M);
-  if ((tid & 63) == 0) red_s[tid >> 6] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(red_s[0], red_s[1]), fmaxf(red_s[2], red_s[3]));
-  for (int sp = tid; sp < n_split; sp += 256) {
-    const float ms = ph[(size_t)sp * kPartialFloats];
-    w_s[sp] = (M == -INFINITY) ? 0.f : exp2f(ms - M);
+  const int per = (n_split + 1) / 2;
+  const int s0 = half * per, s1 = min(n_split, s0 + per);
+  float M = -1e30f, L = 0.f, O = 0.f;  // (-1e30, 0, 0) = empty
+  for (int sb = s0; sb < s1; sb += 8) {
+    float mv[8], lv[8], ov[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int sp = (sb + i < s1) ? sb + i : s0;
+      const float* p = ph + (size_t)sp * kPartialFloats;
+      mv[i] = p[0];
+      lv[i] = p[1];
+      ov[i] = p[2 + d];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float mi = (sb + i < s1) ? fmaxf(mv[i], -1e30f) : -1e30f;
+      const float mn = fmaxf(M, mi);
+      const float fa = fast_exp2(M - mn), fb = (sb + i < s1) ? fast_exp2(mi - mn) : 0.f;
+      L = L * fa + lv[i] * fb;
+      O = O * fa + ov[i] * fb;
+      M = mn;
+    }
   }
-  __syncthreads();
-  const int s0 = half * ((n_split + 1) / 2), s1 = min(n_split, s0 + (n_split + 1) / 2);
-  float L = 0.f, O = 0.f;
-  for (int sp = s0; sp < s1; ++sp) {
-    const float wgt = w_s[sp];
-    L += ph[(size_t)sp * kPartialFloats + 1] * wgt;
-    O += ph[(size_t)sp * kPartialFloats + 2 + d] * wgt;
+  if (half == 1) {
+    if (d == 0) { m_s = M; l_s = L; }
+    o_s[d] = O;
   }
-  if (d == 0) l_s[half] = L;
-  o_s[half][d] = O;
   __syncthreads();
   if (half == 0) {
-    const float Lt = l_s[0] + l_s[1];
-    out[((size_t)b * Hq + h) * kDim + d] = (Lt > 0.f) ? (o_s[0][d] + o_s[1][d]) / Lt : 0.f;
+    const float M1 = m_s, mn = fmaxf(M, M1);
+    const float fa = fast_exp2(M - mn), fb = fast_exp2(M1 - mn);
+    const float Lt = L * fa + l_s * fb;
+    const float Ot = O * fa + o_s[d] * fb;
+    out[((size_t)b * Hq + h) * kDim + d] = (Lt > 0.f) ? Ot / Lt : 0.f;
   }
 }
 
 template <int G>
 hipError_t launch_g(const locks_dims& d, const WsLayout& L, const DevPtrs& P, const float* q,
                     const uint16_t* kc, const uint16_t* vc, const int32_t* pt, const int32_t* sl,
-                    const int32_t* sel, float* out, bool dense, hipStream_t s) {
+                    const int32_t* sel, const int32_t* sel_blk, float* out, bool dense,
+                    hipStream_t s) {
   AttnArgs a;
   a.q = q;
   a.kc = kc;
@@ -209,6 +235,7 @@ hipError_t launch_g(const locks_dims& d, const WsLayout& L, const DevPtrs& P, co
   a.page_table = pt;
   a.seq_lens = sl;
   a.sel = dense ? nullptr : sel;
+  a.sel_blk = dense ? nullptr : sel_blk;
   a.partials = dense ? P.dense_part : P.att_part;
   a.out = out;
   a.Hq = d.n_q_heads;
@@ -228,14 +255,14 @@ hipError_t launch_g(const locks_dims& d, const WsLayout& L, const DevPtrs& P, co
 
 hipError_t launch_attend(const locks_dims& d, const WsLayout& L, const DevPtrs& P, const float* q,
                          const uint16_t* kc, const uint16_t* vc, const int32_t* pt,
-                         const int32_t* sl, const int32_t* sel, float* out, bool dense,
-                         hipStream_t s) {
+                         const int32_t* sl, const int32_t* sel, const int32_t* sel_blk,
+                         float* out, bool dense, hipStream_t s) {
   switch (d.n_q_heads / d.n_kv_heads) {
-    case 1: return launch_g<1>(d, L, P, q, kc, vc, pt, sl, sel, out, dense, s);
-    case 2: return launch_g<2>(d, L, P, q, kc, vc, pt, sl, sel, out, dense, s);
-    case 4: return launch_g<4>(d, L, P, q, kc, vc, pt, sl, sel, out, dense, s);
-    case 8: return launch_g<8>(d, L, P, q, kc, vc, pt, sl, sel, out, dense, s);
-    case 16: return launch_g<16>(d, L, P, q, kc, vc, pt, sl, sel, out, dense, s);
+    case 1: return launch_g<1>(d, L, P, q, kc, vc, pt, sl, sel, sel_blk, out, dense, s);
+    case 2: return launch_g<2>(d, L, P, q, kc, vc, pt, sl, sel, sel_blk, out, dense, s);
+    case 4: return launch_g<4>(d, L, P, q, kc, vc, pt, sl, sel, sel_blk, out, dense, s);
+    case 8: return launch_g<8>(d, L, P, q, kc, vc, pt, sl, sel, sel_blk, out, dense, s);
+    case 16: return launch_g<16>(d, L, P, q, kc, vc, pt, sl, sel, sel_blk, out, dense, s);
     default: return hipErrorInvalidValue;
   }
 }

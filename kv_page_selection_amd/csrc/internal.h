@@ -11,9 +11,10 @@
 namespace locks {
 
 constexpr int kScorePagesPerWave = 64;  // 4 tiles x 16 pages per wave and KV head
-constexpr int kSelectMaxElems = 8192;   // candidates ranked per merge round (32 per thread)
+constexpr int kSelectMaxElems = 8192;   // candidates ranked per merge round (8 per thread)
 constexpr int kSelectMaxK = 4096;       // budget/16 limit (the merge keeps up to k between rounds)
 constexpr int kSelectChunk = 1024;      // pages per chunk workgroup (4 per thread)
+constexpr int kBoundSlots = 16384;      // (head, super-range) maxima the bound pass holds in LDS
 constexpr int kSparsePagesPerSplit = 4; // one page per wave
 constexpr int kDensePagesPerSplit = 256; // at least; grows so that splits <= kMaxSplits
 constexpr int kMaxSplits = 2048;        // split partials one merge workgroup combines
@@ -23,13 +24,18 @@ constexpr int kPartialFloats = 130;     // (m, l, o[128]) per head and split
 struct WsLayout {
   size_t scores = 0;       // f32 [B][Hq][N]   page scores when the caller passes none
   size_t score_part = 0;   // f32 [B][Hq][n_score_wg][2]  (max, sum) per 64-page range, base 2
+  size_t Lg = 0;           // f32 [B][Hq]      total mass of each head, base 2
+  size_t tlb = 0;          // f32 [B][Hkv]     lower bound on the k-th largest key, base 2
   size_t cand = 0;         // u64 [B][Hkv][n_sel_chunks][chunk] survivors of each chunk
+  size_t cand_blk = 0;     // i32 [B][Hkv][n_sel_chunks][chunk] their physical blocks
   size_t cand_count = 0;   // i32 [B][Hkv][n_sel_chunks]
+  size_t sel_blk = 0;      // i32 [B][Hkv][k]  physical blocks of the selected pages
   size_t att_part = 0;     // f32 [B][Hq][n_att_split][130]
   size_t dense_part = 0;   // f32 [B][Hq][n_dense_split][130]
   size_t total = 0;
   int k = 0;
   int n_score_wg = 0;
+  int bound_sup = 0, bound_n_sup = 0;  // ranges per super-range, super-ranges per head
   int sel_chunk = 0, n_sel_chunks = 0;
   int n_att_split = 0, n_dense_split = 0, dense_pages_per_split = 0;
 };
@@ -41,8 +47,12 @@ struct DevPtrs {
   uint8_t* ws;
   float* scores;
   float* score_part;
+  float* Lg;
+  float* tlb;
   unsigned long long* cand;
+  int32_t* cand_blk;
   int32_t* cand_count;
+  int32_t* sel_blk;
   float* att_part;
   float* dense_part;
 };
@@ -57,8 +67,8 @@ hipError_t launch_select(const locks_dims& d, const WsLayout& L, const DevPtrs& 
                          hipStream_t s);
 hipError_t launch_attend(const locks_dims& d, const WsLayout& L, const DevPtrs& P, const float* q,
                          const uint16_t* kc, const uint16_t* vc, const int32_t* page_table,
-                         const int32_t* seq_lens, const int32_t* selected, float* out,
-                         bool dense, hipStream_t s);
+                         const int32_t* seq_lens, const int32_t* selected,
+                         const int32_t* selected_blocks, float* out, bool dense, hipStream_t s);
 hipError_t launch_build(const locks_dims& d, const uint16_t* kc, const int32_t* page_table,
                         const int32_t* seq_lens, uint8_t* summ, hipStream_t s);
 

@@ -50,6 +50,27 @@ def test_decode_parity_on_gpu_built_summaries(locks, case):
         say(f"  carrier retention {np.mean(kept):.3f}")
 
 
+# selection paths the reduced cases do not reach
+SELECT_PATHS = [
+    # 512 ranges of 64 pages but 1024 pages to keep: no pruning bound exists, so
+    # every one of the 32768 pages is a candidate and the merge runs several rounds
+    dict(config=4, ctx=16 * 32768, budget=16 * 1024),
+    # G = 16 with 2048 ranges: the 32768 (head, range) maxima exceed what the
+    # bound pass holds, so it pools ranges in pairs
+    dict(config=5, ctx=16 * 131072, budget=512, n_kv_heads=1, n_q_heads=16),
+]
+
+
+@pytest.mark.parametrize("case", SELECT_PATHS, ids=lambda c: "-".join(f"{k}{v}" for k, v in c.items()))
+def test_selection_paths(locks, case):
+    say(f"selection path {case}")
+    w = workloads.make(device=DEV, **case)
+    summ = locks.build_summaries(w.k_cache, w.page_table, w.seq_lens)
+    decode_and_check(w, summ, full_oracle_attention=False)
+    del w, summ
+    torch.cuda.empty_cache()
+
+
 def test_decode_parity_on_oracle_built_summaries(locks):
     """Summaries packed by the oracle, decoded by the GPU: the record format is
     read the same way on both sides."""
