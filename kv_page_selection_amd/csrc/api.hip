@@ -34,10 +34,10 @@ bool ws_layout(const locks_dims& d, int k, WsLayout* L, const char** why) {
     *why = "budget/16 above 4096 pages";
     return false;
   }
-  long long M = 256;
+  long long M = 1024;
   while (M < kSelectChunk && M < N) M *= 2;
   if ((N + M - 1) / M > 1024) {
-    *why = "more than 1024 select chunks (max_pages_per_seq above 2^20)";
+    *why = "more than 1024 select chunks (max_pages_per_seq above 2^22)";
     return false;
   }
   L->sel_chunk = (int)M;
@@ -55,8 +55,6 @@ bool ws_layout(const locks_dims& d, int k, WsLayout* L, const char** why) {
   L->dense_part = off; off = align_up(off + (size_t)(B * Hq) * L->n_dense_split * kPartialFloats * 4);
   L->score_part = off; off = align_up(off + (size_t)(B * Hq * L->n_score_wg) * 2 * 4);
   L->scores = off;     off = align_up(off + (size_t)(B * Hq * N) * 4);
-  L->Lg = off;         off = align_up(off + (size_t)(B * Hq) * 4);
-  L->tlb = off;        off = align_up(off + (size_t)(B * Hkv) * 4);
   L->cand = off;       off = align_up(off + (size_t)(B * Hkv * L->n_sel_chunks) * L->sel_chunk * 8);
   L->cand_blk = off;   off = align_up(off + (size_t)(B * Hkv * L->n_sel_chunks) * L->sel_chunk * 4);
   L->cand_count = off; off = align_up(off + (size_t)(B * Hkv * L->n_sel_chunks) * 4);
@@ -67,20 +65,18 @@ bool ws_layout(const locks_dims& d, int k, WsLayout* L, const char** why) {
 }
 
 DevPtrs ws_ptrs(const locks_dims& d, const WsLayout& L, void* ws, float* page_scores) {
+  (void)d;
   uint8_t* w = static_cast<uint8_t*>(ws);
   DevPtrs P;
   P.ws = w;
   P.scores = page_scores ? page_scores : reinterpret_cast<float*>(w + L.scores);
   P.score_part = reinterpret_cast<float*>(w + L.score_part);
-  P.Lg = reinterpret_cast<float*>(w + L.Lg);
-  P.tlb = reinterpret_cast<float*>(w + L.tlb);
   P.cand = reinterpret_cast<unsigned long long*>(w + L.cand);
   P.cand_blk = reinterpret_cast<int32_t*>(w + L.cand_blk);
   P.cand_count = reinterpret_cast<int32_t*>(w + L.cand_count);
   P.sel_blk = reinterpret_cast<int32_t*>(w + L.sel_blk);
   P.att_part = reinterpret_cast<float*>(w + L.att_part);
   P.dense_part = reinterpret_cast<float*>(w + L.dense_part);
-  (void)d;
   return P;
 }
 

@@ -10,8 +10,8 @@
 // wave handles one page at a time for all G heads of the group:
 //   QK: lane (token i = lane%16, d-chunk c = lane/16) reads 64 contiguous bytes
 //       of key row i and dots them with the LDS-resident query chunk; two
-//       cross-row shuffles finish each logit;
-//   online softmax in base 2 over the page's 16 tokens (16-lane shuffles);
+//       permlane swaps (lanes l^16, l^32) finish each logit;
+//   online softmax in base 2 over the page's 16 tokens (DPP row butterflies);
 //   PV: lane owns d = 2*lane, 2*lane+1, reads one bf16 pair per token row
 //       (coalesced 256-byte rows) and takes each token's weight by readlane.
 // Waves merge in LDS into one (max, sum, o[128]) partial per head and split; a
@@ -116,18 +116,13 @@ __global__ __launch_bounds__(256) void attend_kernel(AttnArgs a) {
     float pw[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      float x = lg[h];
-      x += __shfl_xor(x, 16);
-      x += __shfl_xor(x, 32);
-      float pm = x;
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) pm = fmaxf(pm, __shfl_xor(pm, o));
+      float x = xor16_sum(lg[h]);  // the four d-chunks of token `tok`
+      x = xor32_sum(x);
+      const float pm = row16_reduce(x, [](float u, float v) { return fmaxf(u, v); });
       const float mn = fmaxf(m[h], pm);
       const float alpha = exp2f(m[h] - mn);  // m = -inf -> 0
       const float p = exp2f(x - mn);
-      float ps = p;
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) ps += __shfl_xor(ps, o);
+      const float ps = row16_reduce(p, [](float u, float v) { return u + v; });
       l[h] = l[h] * alpha + ps;
       m[h] = mn;
       o0[h] *= alpha;

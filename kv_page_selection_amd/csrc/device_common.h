@@ -46,18 +46,6 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <typename T>
-__device__ __forceinline__ T wave_sum(T v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
-}
-
 // Raw hardware 2^x and log2(x) (v_exp_f32 / v_log_f32): results that would be
 // fp32 denormals flush to zero, which only drops terms below 2^-126 of a sum.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -80,6 +68,97 @@ __device__ __forceinline__ float xor16_max(float x) {
 __device__ __forceinline__ float xor16_sum(float x) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// ---- wave-level data movement without LDS round trips (gfx950 DPP and
+// permlane swaps; every helper expects all 64 lanes active).
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]: lane ^ 1
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]: lane ^ 2
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i within each 8-lane half row
+constexpr int kDppMirror = 0x140;     // lane i <-> 15-i within each 16-lane row
+constexpr int kDppShr1 = 0x111;       // row_shr:n, lanes n..15 of a row read lane i-n
+constexpr int kDppShr2 = 0x112;
+constexpr int kDppShr4 = 0x114;
+constexpr int kDppShr8 = 0x118;
+
+template <int kCtrl>
+__device__ __forceinline__ uint32_t dpp_mov(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kCtrl, 0xF, 0xF, false);
+}
+template <int kCtrl>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __uint_as_float(dpp_mov<kCtrl>(__float_as_uint(x)));
+}
+// row_shr with zero fill for lanes whose source lies outside the row
+template <int kCtrl>
+__device__ __forceinline__ uint32_t dpp_shr(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kCtrl, 0xF, 0xF, true);
+}
+
+// op over the 16 lanes of each row: a butterfly whose pairings are lane^1,
+// lane^2, then the 8-lane halves and the 16-lane row mirrored onto each other.
+// op must be commutative (every lane then gets bit-identical results).
+template <typename T, typename Op>
+__device__ __forceinline__ T row16_reduce(T x, Op op) {
+  x = op(x, dpp_mov<kDppXor1>(x));
+  x = op(x, dpp_mov<kDppXor2>(x));
+  x = op(x, dpp_mov<kDppHalfMirror>(x));
+  x = op(x, dpp_mov<kDppMirror>(x));
+  return x;
+}
+// op over lanes l and l^16 / l^32 (both operands in the same order in both lanes)
+template <typename Op>
+__device__ __forceinline__ uint32_t xor16_op(uint32_t x, Op op) {
+  const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  return op((uint32_t)r[0], (uint32_t)r[1]);
+}
+template <typename Op>
+__device__ __forceinline__ uint32_t xor32_op(uint32_t x, Op op) {
+  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return op((uint32_t)r[0], (uint32_t)r[1]);
+}
+
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t x) {
+  auto add = [](uint32_t a, uint32_t b) { return a + b; };
+  x = row16_reduce(x, add);
+  x = xor16_op(x, add);
+  return xor32_op(x, add);
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
+  auto mn = [](uint32_t a, uint32_t b) { return a < b ? a : b; };
+  x = row16_reduce(x, mn);
+  x = xor16_op(x, mn);
+  return xor32_op(x, mn);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  auto mx = [](uint32_t a, uint32_t b) { return a > b ? a : b; };
+  x = row16_reduce(x, mx);
+  x = xor16_op(x, mx);
+  return xor32_op(x, mx);
+}
+__device__ __forceinline__ float wave_max(float x) {
+  auto mx = [](float a, float b) { return fmaxf(a, b); };
+  x = row16_reduce(x, mx);
+  x = xor16_max(x);
+  return xor32_max(x);
+}
+__device__ __forceinline__ float wave_sum(float x) {
+  auto add = [](float a, float b) { return a + b; };
+  x = row16_reduce(x, add);
+  x = xor16_sum(x);
+  return xor32_sum(x);
+}
+
+// Inclusive prefix sum over the 64 lanes (lane order).
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+  x += dpp_shr<kDppShr1>(x);
+  x += dpp_shr<kDppShr2>(x);
+  x += dpp_shr<kDppShr4>(x);
+  x += dpp_shr<kDppShr8>(x);
+  const uint32_t t0 = __builtin_amdgcn_readlane(x, 15), t1 = __builtin_amdgcn_readlane(x, 31),
+                 t2 = __builtin_amdgcn_readlane(x, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  return x + (row >= 1 ? t0 : 0u) + (row >= 2 ? t1 : 0u) + (row >= 3 ? t2 : 0u);
 }
 
 // Merge of two (max, sum-of-exp2) pairs in base-2 log units; m = -inf means empty.

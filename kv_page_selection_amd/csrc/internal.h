@@ -13,7 +13,7 @@ namespace locks {
 constexpr int kScorePagesPerWave = 64;  // 4 tiles x 16 pages per wave and KV head
 constexpr int kSelectMaxElems = 8192;   // candidates ranked per merge round (8 per thread)
 constexpr int kSelectMaxK = 4096;       // budget/16 limit (the merge keeps up to k between rounds)
-constexpr int kSelectChunk = 1024;      // pages per chunk workgroup (4 per thread)
+constexpr int kSelectChunk = 4096;      // pages per select workgroup at most (4 per thread)
 constexpr int kBoundSlots = 16384;      // (head, super-range) maxima the bound pass holds in LDS
 constexpr int kSparsePagesPerSplit = 4; // one page per wave
 constexpr int kDensePagesPerSplit = 256; // at least; grows so that splits <= kMaxSplits
@@ -24,8 +24,6 @@ constexpr int kPartialFloats = 130;     // (m, l, o[128]) per head and split
 struct WsLayout {
   size_t scores = 0;       // f32 [B][Hq][N]   page scores when the caller passes none
   size_t score_part = 0;   // f32 [B][Hq][n_score_wg][2]  (max, sum) per 64-page range, base 2
-  size_t Lg = 0;           // f32 [B][Hq]      total mass of each head, base 2
-  size_t tlb = 0;          // f32 [B][Hkv]     lower bound on the k-th largest key, base 2
   size_t cand = 0;         // u64 [B][Hkv][n_sel_chunks][chunk] survivors of each chunk
   size_t cand_blk = 0;     // i32 [B][Hkv][n_sel_chunks][chunk] their physical blocks
   size_t cand_count = 0;   // i32 [B][Hkv][n_sel_chunks]
@@ -47,8 +45,6 @@ struct DevPtrs {
   uint8_t* ws;
   float* scores;
   float* score_part;
-  float* Lg;
-  float* tlb;
   unsigned long long* cand;
   int32_t* cand_blk;
   int32_t* cand_count;
