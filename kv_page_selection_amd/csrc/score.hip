@@ -73,6 +73,7 @@ struct TileLds {
   __align__(16) _Float16 zero[8];       // masked B operand
   float a[16][G + 1];                   // mu . q (exact integer), [page][head]; column G spare
   float sc[16][4];                      // s_mu, s_V/16 * s_C, valid
+  float out[G][16];                     // the tile's page scores, [head][page], natural log
 };
 
 // Per wave: the q digit planes are dead once the row operands are in
@@ -166,6 +167,9 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
     }
   }
 
+  float myscore[G];  // lane = page of this wave: its score for every head
+#pragma unroll
+  for (int h = 0; h < G; ++h) myscore[h] = 0.f;
   for (int t = 0; t < kTiles; ++t) {
     const int pbase = p0 + t * 16;
     const int blk = __shfl(myblk, t * 16 + row);  // page pbase + row
@@ -275,8 +279,7 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
       ssum = xor32_sum(xor16_sum(ssum));
       const float shat2 = mx + fast_log2(ssum);
       const bool valid = T.sc[pp][2] != 0.0f;
-      if (kg == 0 && pbase + pp < n_b)  // absent pages are marked -inf
-        a.scores[((size_t)b * a.Hq + (size_t)kvh * G + hc) * N + pbase + pp] = valid ? shat2 * kLn2 : -INFINITY;
+      if (kg == 0) T.out[hc][pp] = valid ? shat2 * kLn2 : -INFINITY;  // absent pages: -inf
       // running (max, sum) of this head, branch-free; absent pages add nothing
       const float x = valid ? shat2 : -1e30f;
       const float mn = fmaxf(run_m, x);
@@ -284,7 +287,21 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
       run_m = mn;
     }
     wave_lds_sync();
+    if ((lane >> 4) == t) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) myscore[h] = T.out[h][lane & 15];
+    }
+    wave_lds_sync();
   }
+
+  // ---- the wave's scores, written once after its last loads: a store in
+  // flight would hold up the wait for later loads (one in-order counter
+  // covers both); whole 256-byte rows per head coalesce, and streaming
+  // (non-temporal) stores keep them from sitting dirty in L2 until the end
+  // of the launch
+#pragma unroll
+  for (int h = 0; h < G; ++h)
+    if (p0 + lane < n_b) __builtin_nontemporal_store(myscore[h], &a.scores[((size_t)b * a.Hq + (size_t)kvh * G + h) * N + p0 + lane]);
 
   // ---- per-head (max, sum) over this wave's pages: lanes 0..15, head = lane % G
 #pragma unroll
