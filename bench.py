@@ -9,8 +9,16 @@ budget 2048 tokens (128 pages), structured per-page low-rank keys.
 Prints one JSON line: metric/value (achieved HBM GB/s on the step's
 algorithmic bytes), the decode-step time, pages scored per second, the dense
 flash-decode comparator on the same inputs, a roofline object for the
-dominant (scoring) kernel timed with HIP events on its own stream, and the
-fp64 CPU oracle timed on the host cores.
+dominant (scoring) kernel — its average launch time from HIP events around a
+captured graph of back-to-back launches on the stream they run on, and its
+HBM traffic from rocprofv3 counters when profiles/score_kernel_traffic.json
+matches the current kernel source and workload — and the fp64 CPU oracle
+timed on the host cores (about --cpu-seconds of repeated full steps).
+
+`--traffic-from FETCH_CSV WRITE_CSV BENCH_LOG` (no GPU) writes that traffic
+file from two `rocprofv3 --pmc FETCH_SIZE|WRITE_SIZE` runs of
+`bench.py --calibrate-copy`, scaling each counter by what it reads for the
+256 MiB device copy that flag adds.
 """
 from __future__ import annotations
 
@@ -51,6 +59,56 @@ def source_hash(paths):
     return h.hexdigest()
 
 
+COPY_BYTES = 256 << 20  # the known-size copy the HBM counters are scaled by
+
+
+def traffic_from(fetch_csv, write_csv, bench_log):
+    """Offline step (no GPU): per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the
+    scoring kernel from two rocprofv3 --pmc runs of `bench.py --calibrate-copy`,
+    each scaled by what the same counter reads for the 256 MiB device copy that
+    flag adds, written to profiles/score_kernel_traffic.json together with the
+    scoring sources' hash (a kernel change makes the numbers stale)."""
+    import csv
+
+    def per_dispatch(path):
+        score, copy = [], []
+        for r in csv.DictReader(open(path)):
+            name, v = r["Kernel_Name"], float(r["Counter_Value"])
+            if "score_kernel" in name:
+                score.append(v)
+            elif "copyBuffer" in name:
+                copy.append((int(r["Dispatch_Id"]), v))
+        if not score or len(copy) < 3:
+            raise SystemExit(f"{path}: no scoring-kernel or calibration-copy dispatches")
+        # the calibration copies are the run's last three device copies
+        last = sorted(v for _, v in sorted(copy)[-3:])
+        return sum(score) / len(score), last[1]
+
+    f_score, f_copy = per_dispatch(fetch_csv)
+    w_score, w_copy = per_dispatch(write_csv)
+    f_scale = (COPY_BYTES / 1024) / f_copy
+    w_scale = (COPY_BYTES / 1024) / w_copy
+    line = next(json.loads(l) for l in open(bench_log) if l.startswith("{"))
+    out = {
+        "kernel": "score_kernel",
+        "workload": line["config"]["workload"],
+        "kernel_source_sha256": source_hash(SCORE_SOURCES),
+        "fetch_kib_per_dispatch_raw": round(f_score, 1),
+        "write_kib_per_dispatch_raw": round(w_score, 1),
+        "copy_fetch_kib_raw": round(f_copy, 1),
+        "copy_write_kib_raw": round(w_copy, 1),
+        "fetch_scale": round(f_scale, 4),
+        "write_scale": round(w_scale, 4),
+        "hbm_bytes_per_launch": int(f_score * f_scale * 1024 + w_score * w_scale * 1024),
+        "algorithmic_bytes_per_launch": line["roofline"]["algorithmic_bytes_per_launch"],
+    }
+    os.makedirs(os.path.dirname(PROFILE_TRAFFIC), exist_ok=True)
+    with open(PROFILE_TRAFFIC, "w") as fh:
+        json.dump(out, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(out))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -61,8 +119,17 @@ def main():
     ap.add_argument("--replicas", type=int, default=0, help="0 = enough to exceed 1 GB per cycle")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
-    ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="host time the oracle baseline repeats the step for")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a 256 MiB device copy (reference for HBM counters)")
+    ap.add_argument("--traffic-from", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "BENCH_LOG"),
+                    help="offline: write profiles/score_kernel_traffic.json from rocprofv3 "
+                         "counter files and this script's output line, then exit")
     args = ap.parse_args()
+    if args.traffic_from:
+        traffic_from(*args.traffic_from)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the LOCKS path here "
               "is single-GPU. Run with --gpus 1.", file=sys.stderr)
@@ -137,26 +204,45 @@ def main():
     step_bytes = sb + ab
     gbs = step_bytes / (step_ms * 1e-3) / 1e9
 
-    # ---- per-phase kernel times with HIP events on the launch stream (eager launches)
-    stream = torch.cuda.current_stream()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    for i in range(args.warmup):
-        step(i % R)
-    for i in range(args.steps):
-        r = i % R
-        s_, kc_, vc_ = reps[r]
-        ev[i][0].record(stream)
+    # ---- per-phase kernel times: one graph per phase holding PHASE_REPS
+    # back-to-back launches (replicas rotating), replayed between two HIP
+    # events on the stream it runs on, so no host gap sits inside the interval
+    PHASE_REPS = 20
+
+    def phase_graph(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(PHASE_REPS):
+                fn(i % R)
+        return g
+
+    def score_fn(r):
+        s_, kc_, _ = reps[r]
         locks.score_pages(w.q, s_, kc_, w.page_table, w.seq_lens, w.budget, ws[r])
-        ev[i][1].record(stream)
-        locks.select_pages(w.q, kc_, w.page_table, w.seq_lens, w.budget, sels[r], ws[r])
-        ev[i][2].record(stream)
+
+    def select_fn(r):
+        locks.select_pages(w.q, reps[r][1], w.page_table, w.seq_lens, w.budget, sels[r], ws[r])
+
+    def attend_fn(r):
+        _, kc_, vc_ = reps[r]
         locks.sparse_attention(w.q, kc_, vc_, w.page_table, w.seq_lens, w.budget, sels[r],
                                outs[r], ws[r])
-        ev[i][3].record(stream)
-    torch.cuda.synchronize()
-    score_us = float(np.mean([e[0].elapsed_time(e[1]) for e in ev])) * 1e3
-    select_us = float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) * 1e3
-    attend_us = float(np.mean([e[2].elapsed_time(e[3]) for e in ev])) * 1e3
+
+    phase_us = {}
+    for name, fn in (("score", score_fn), ("select", select_fn), ("attend", attend_fn)):
+        g = phase_graph(fn)
+        g.replay()
+        torch.cuda.synchronize()
+        samples = []
+        for _ in range(max(1, args.steps // PHASE_REPS)):
+            ts.record()
+            g.replay()
+            te.record()
+            torch.cuda.synchronize()
+            samples.append(ts.elapsed_time(te) * 1e3 / PHASE_REPS)
+        phase_us[name] = float(np.median(samples))
+        del g
+    score_us, select_us, attend_us = phase_us["score"], phase_us["select"], phase_us["attend"]
     score_gbs = sb / (score_us * 1e-6) / 1e9
 
     traffic = None
@@ -201,19 +287,26 @@ def main():
         q, pt, sl = w.q.cpu().numpy(), w.page_table.cpu().numpy(), w.seq_lens.cpu().numpy()
         sm = summ.cpu().numpy()
         kb, vb = workloads.bf16_bits(w.k_cache), workloads.bf16_bits(w.v_cache)
+        # repeat the whole step for about args.cpu_seconds of host time
         times = []
-        for _ in range(args.cpu_reps):
+        while len(times) < 3 or (sum(times) < args.cpu_seconds and len(times) < 1000):
             c0 = time.perf_counter()
             oracle.decode_step(q, sm, kb, vb, pt, sl, w.budget)
             times.append(time.perf_counter() - c0)
-            if sum(times) > 30:
-                break
         cpu_s = float(np.median(times))
         cpu = {"value": round(step_bytes / cpu_s / 1e9, 4), "unit": "GB/s",
                "cores": oracle.num_threads(), "kind": "oracle",
                "sample": f"the full decode step of this workload ({w.recipe}), summaries prebuilt, "
                          f"median of {len(times)} run(s)",
                "step_s": round(cpu_s, 3)}
+
+    if args.calibrate_copy:
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     line = {
         "metric": METRIC,
