@@ -112,8 +112,8 @@ def traffic_from(fetch_csv, write_csv, bench_log):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=4)
     ap.add_argument("--budget", type=int, default=None)
     ap.add_argument("--replicas", type=int, default=0, help="0 = enough to exceed 1 GB per cycle")
@@ -147,6 +147,34 @@ def main():
     B, Hq, Hkv, N, k = w.batch, w.n_q_heads, w.n_kv_heads, w.max_pages, w.k_pages
     print(f"[bench] workload {w.recipe} generated in {time.time() - t0:.1f}s", file=sys.stderr,
           flush=True)
+
+    # ---- input fingerprint: SHA-256 over q, page table, seq_lens and per-block
+    # 64-bit sums of the K and V cache bits (hashing 8 GiB on the host would
+    # dominate the run)
+    def cache_digest(c):
+        return c.view(torch.int16).view(c.shape[0], -1).sum(dim=1, dtype=torch.int64).cpu().numpy().tobytes()
+
+    hsh = hashlib.sha256()
+    for t in (w.q, w.page_table, w.seq_lens):
+        hsh.update(t.cpu().numpy().tobytes())
+    hsh.update(cache_digest(w.k_cache))
+    hsh.update(cache_digest(w.v_cache))
+    input_sha = hsh.hexdigest()
+
+    # ---- device copy bandwidth on this machine (1 GiB read + 1 GiB written)
+    csrc = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+    cdst = torch.empty_like(csrc)
+    cdst.copy_(csrc)
+    torch.cuda.synchronize()
+    c0e, c1e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0e.record()
+    for _ in range(5):
+        cdst.copy_(csrc)
+    c1e.record()
+    torch.cuda.synchronize()
+    copy_gbs = 5 * 2 * csrc.numel() * 4 / (c0e.elapsed_time(c1e) * 1e-3) / 1e9
+    del csrc, cdst
+    props = torch.cuda.get_device_properties(dev)
 
     # ---- summary build (timed separately; off the decode critical path)
     summ = locks.build_summaries(w.k_cache, w.page_table, w.seq_lens)
@@ -294,8 +322,16 @@ def main():
             oracle.decode_step(q, sm, kb, vb, pt, sl, w.budget)
             times.append(time.perf_counter() - c0)
         cpu_s = float(np.median(times))
+        cpu_model = ""
+        try:
+            for ln in open("/proc/cpuinfo"):
+                if ln.startswith("model name"):
+                    cpu_model = ln.split(":", 1)[1].strip()
+                    break
+        except OSError:
+            pass
         cpu = {"value": round(step_bytes / cpu_s / 1e9, 4), "unit": "GB/s",
-               "cores": oracle.num_threads(), "kind": "oracle",
+               "cores": oracle.num_threads(), "kind": "oracle", "cpu_model": cpu_model,
                "sample": f"the full decode step of this workload ({w.recipe}), summaries prebuilt, "
                          f"median of {len(times)} run(s)",
                "step_s": round(cpu_s, 3)}
@@ -327,6 +363,9 @@ def main():
                    "algorithmic_bytes_per_step": step_bytes, "replicas": R,
                    "parallelism": "single GPU"},
         "hbm_fraction": round(gbs / HBM_PEAK_GBS, 4),
+        "input_sha256": input_sha,
+        "device": {"name": props.name, "cus": props.multi_processor_count,
+                   "copy_gbs": round(copy_gbs, 1)},
         "page_heads_scored_per_s": round(B * Hkv * N / (step_ms * 1e-3), 1),
         "phases_us": {"score": round(score_us, 2), "select": round(select_us, 2),
                       "attend": round(attend_us, 2)},

@@ -1,4 +1,4 @@
-// build.hip — summary build, one wave per (block, KV head) page (gfx950).
+// build.hip — summary build (gfx950): 4 pages per wave.
 //
 // Steps (blog post, "How LOCKS works" and "Code" build loop; technical summary,
 // section 2 mechanism 1): centroid mu = mean of the page's 16 keys; centred
@@ -7,13 +7,24 @@
 // coefficients C[:,k] = sqrt(lambda_k) u_k (= D V); fp16 absmax scales; codes
 // int8 (mu, C, +-127) and int4 (V, +-7), round half to even; pack the record.
 //
-// Mapping: lane (token i = lane%16, K group kg = lane/16) holds key row i,
-// d in [32kg, 32kg+32). The Gram is 32 chained v_mfma_f32_16x16x4_f32 with the
-// same register as A and B (lane (i, kg) holds D[i][32kg+s]; for a sum over d
-// only the pairing of A and B lanes matters, which is symmetric). The
-// eigensolver is cyclic Jacobi in parallel (round-robin) order: 15 rounds of 8
-// disjoint rotations per sweep, applied to LDS copies of the Gram and the
-// eigenvector matrix. Waves are independent (wave-scope LDS ordering only).
+// A wave builds 4 page records in three phases:
+//  1. per page, all 64 lanes: lane (token i = lane%16, group kg = lane/16)
+//     holds key row i, d in [32kg, 32kg+32); the centroid comes from 16-lane
+//     row sums, and the Gram is 32 chained v_mfma_f32_16x16x4_f32 with the
+//     same register as A and B (for a sum over d only the pairing of A and B
+//     lanes matters, which is symmetric).
+//  2. the 4 eigenproblems at once, 16 lanes each: lane i holds row i of the
+//     Gram and of the eigenvector matrix in registers, column-permuted by XOR
+//     (slot t = column i ^ t). Cyclic Jacobi with XOR pairings: round m of a
+//     sweep rotates the 8 pairs (i, i ^ m), m = 1..15, so every pair is
+//     rotated once per sweep. In this layout the diagonal is slot 0, the
+//     rotated element is slot m, the partner row is one ds_swizzle (XOR m)
+//     away and reads slot-permuted by XOR m, and the column rotation of slot
+//     t uses the angle of column i ^ t, published through a 16-entry LDS
+//     table: no register is indexed per lane.
+//  3. per page, all 64 lanes: lane owns d = 2*lane, 2*lane+1 of all 16 keys
+//     (reloaded, L2-resident), forms V, the sign rule, C, the scales and the
+//     codes, and writes the record.
 #include "device_common.h"
 #include "internal.h"
 
@@ -22,7 +33,11 @@ namespace locks {
 namespace {
 
 constexpr int kWaves = 4;
+constexpr int kPagesPerWave = 4;
 constexpr int kMaxSweeps = 12;
+// converged when the off-diagonal energy is below this fraction of the total
+// (off-diagonal norm ~1e-5 of the Frobenius norm; the codes keep 4-8 bits)
+constexpr float kOffTol = 1e-10f;
 
 struct BuildArgs {
   const uint16_t* kc;
@@ -30,17 +45,21 @@ struct BuildArgs {
   const int32_t* seq_lens;
   uint8_t* summ;
   int B, Hkv, N, num_blocks;
+  long long items;
 };
 
 struct WaveLds {
-  float D[kPage][kDim];
-  float A[kPage][kPage + 1];
-  float U[kPage][kPage + 1];
-  float mu[kDim];
-  int mate[kPage];
-  float cx[kPage], sx[kPage];
-  int perm[kPage];
-  float lam[kPage];
+  // Gram rows, slot-permuted (slot t = column i ^ t), until phase 2 has them in
+  // registers; then the eigenvectors, transposed: [column][row]
+  union {
+    float A[kPagesPerWave][kPage][kPage];
+    float UT[kPagesPerWave][kPage][kPage];
+  };
+  float2 rot[kPagesPerWave][kPage];      // this round's (cos, signed sin) per column
+  float lam[kPagesPerWave][kPage];       // eigenvalues, descending
+  int perm[kPagesPerWave][kPage];        // column of U holding the r-th eigenvector
+  float diag[kPagesPerWave][kPage];
+  float energy[kPagesPerWave];           // sum of squared deviations per page
   int8_t vq[kRank][kDim];
   __align__(16) uint8_t rec[kStride];
 };
@@ -57,248 +76,333 @@ __device__ __forceinline__ uint32_t f16_bits(float x) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x);
 }
 
-__global__ __launch_bounds__(256) void build_kernel(BuildArgs a) {
-  __shared__ WaveLds lds_all[kWaves];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  WaveLds& S = lds_all[wave];
-  const long long item = (long long)blockIdx.x * kWaves + wave;  // (b, j, kvh)
-  const int kvh = (int)(item % a.Hkv);
+// value of lane (lane ^ M) (M < 16: stays in the lane's 16-lane group)
+template <int M>
+__device__ __forceinline__ float swz(float x) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(x), (M << 10) | 0x1F));
+}
+
+// One Jacobi round: rotate the pairs (i, i ^ M) of every page of the wave.
+// J[p][p] = J[q][q] = c, J[p][q] = s, J[q][p] = -s (p < q); A <- J^T A J,
+// U <- U J; the rotated element becomes exactly zero. The angle table is read
+// per slot at column i ^ t: those 16 addresses are the same in every round
+// (a per-pair read would need different addresses in each of the 15
+// unrolled rounds, all kept live across the sweep loop).
+template <int M>
+__device__ __forceinline__ void jacobi_round(float (&a)[kPage], float (&u)[kPage], int i,
+                                             float2* rot) {
+  const bool lower = i < (i ^ M);
+  const float d_me = a[0], d_other = swz<M>(a[0]);
+  const float o_me = a[M], o_other = swz<M>(a[M]);
+  // both lanes of a pair take the same inputs, hence the same angle
+  const float app = lower ? d_me : d_other, aqq = lower ? d_other : d_me;
+  const float apq = lower ? o_me : o_other;
+  // hardware reciprocal / square root (about 1 ulp): any rotation keeps the
+  // matrix orthogonally similar, a slightly inexact angle only leaves a tiny
+  // residual for the next sweep
+  const float safe = (apq != 0.f) ? apq : 1.f;
+  const float tau = (aqq - app) * __builtin_amdgcn_rcpf(2.f * safe);
+  const float t = copysignf(1.0f, tau) *
+                  __builtin_amdgcn_rcpf(fabsf(tau) + __builtin_amdgcn_sqrtf(fmaf(tau, tau, 1.f)));
+  const float c = (apq != 0.f) ? __builtin_amdgcn_rsqf(fmaf(t, t, 1.f)) : 1.f;
+  const float s = (apq != 0.f) ? t * c : 0.f;
+  const float sg = lower ? -s : s;
+  // rows: row_i <- c row_i + sg row_partner; the partner's slot t ^ M is column i ^ t
+  float ar[kPage];
+#pragma unroll
+  for (int tt = 0; tt < kPage; ++tt) ar[tt] = fmaf(c, a[tt], sg * swz<M>(a[tt ^ M]));
+  rot[i] = make_float2(c, sg);
+  wave_lds_sync();
+  // columns: slot t is column x = i ^ t, rotated with column x ^ M (slot t ^ M);
+  // updated in place one slot pair at a time
+#pragma unroll
+  for (int tt = 0; tt < kPage; ++tt) {
+    if (tt < (tt ^ M)) {
+      const int t2 = tt ^ M;
+      const float2 r1 = rot[i ^ tt], r2 = rot[i ^ t2];
+      a[tt] = fmaf(r1.x, ar[tt], r1.y * ar[t2]);
+      a[t2] = fmaf(r2.x, ar[t2], r2.y * ar[tt]);
+      const float u1 = u[tt], u2 = u[t2];
+      u[tt] = fmaf(r1.x, u1, r1.y * u2);
+      u[t2] = fmaf(r2.x, u2, r2.y * u1);
+      // pin the update to this round (an empty asm consuming the value): nothing
+      // reads U until the end, and sinking the rotations would keep every
+      // round's angles live
+      asm volatile("" : "+v"(u[tt]), "+v"(u[t2]));
+    }
+  }
+  a[M] = 0.f;
+  wave_lds_sync();  // every lane has read this round's angles
+}
+
+__device__ __forceinline__ void jacobi_sweep(float (&a)[kPage], float (&u)[kPage], int i,
+                                             float2* rot) {
+  jacobi_round<1>(a, u, i, rot);
+  jacobi_round<2>(a, u, i, rot);
+  jacobi_round<3>(a, u, i, rot);
+  jacobi_round<4>(a, u, i, rot);
+  jacobi_round<5>(a, u, i, rot);
+  jacobi_round<6>(a, u, i, rot);
+  jacobi_round<7>(a, u, i, rot);
+  jacobi_round<8>(a, u, i, rot);
+  jacobi_round<9>(a, u, i, rot);
+  jacobi_round<10>(a, u, i, rot);
+  jacobi_round<11>(a, u, i, rot);
+  jacobi_round<12>(a, u, i, rot);
+  jacobi_round<13>(a, u, i, rot);
+  jacobi_round<14>(a, u, i, rot);
+  jacobi_round<15>(a, u, i, rot);
+}
+
+// (b, j, kvh) of work item `item`; blk < 0 when there is nothing to build
+__device__ __forceinline__ int item_block(const BuildArgs& a, long long item, int* kvh) {
+  *kvh = 0;
+  if (item >= a.items) return -1;
+  *kvh = (int)(item % a.Hkv);
   const long long bj = item / a.Hkv;
   const int j = (int)(bj % a.N);
   const int b = (int)(bj / a.N);
-  if (b >= a.B) return;
-  if (j >= full_pages(a.seq_lens, b, a.N)) return;
+  if (j >= full_pages(a.seq_lens, b, a.N)) return -1;
   const int blk = a.page_table[(size_t)b * a.N + j];
-  if (blk < 0 || blk >= a.num_blocks) return;
+  return (blk >= 0 && blk < a.num_blocks) ? blk : -1;
+}
 
+__global__ __launch_bounds__(64 * kWaves) void build_kernel(BuildArgs a) {
+  __shared__ WaveLds lds_all[kWaves];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  WaveLds& S = lds_all[wave];
+  const long long item0 = ((long long)blockIdx.x * kWaves + wave) * kPagesPerWave;
   const int ti = lane & 15, kg = lane >> 4;
-  // ---- keys: row ti, d in [32kg, 32kg+32)
-  float kf[32];
-  {
-    const uint4* src = reinterpret_cast<const uint4*>(
-        a.kc + ((size_t)blk * a.Hkv + kvh) * (kPage * kDim) + ti * kDim + kg * 32);
+
+  // ================================================ 1. centroid, deviations, Gram
+#pragma unroll 1
+  for (int pg = 0; pg < kPagesPerWave; ++pg) {
+    int kvh;
+    const int blk = item_block(a, item0 + pg, &kvh);
+    float kf[32];
+    if (blk >= 0) {
+      const uint4* src = reinterpret_cast<const uint4*>(
+          a.kc + ((size_t)blk * a.Hkv + kvh) * (kPage * kDim) + ti * kDim + kg * 32);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const uint4 w = src[u];
-      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+      for (int uu = 0; uu < 4; ++uu) {
+        const uint4 w = src[uu];
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        kf[u * 8 + 2 * e] = bf16lo(ws[e]);
-        kf[u * 8 + 2 * e + 1] = bf16hi(ws[e]);
+        for (int e = 0; e < 4; ++e) {
+          kf[uu * 8 + 2 * e] = bf16lo(ws[e]);
+          kf[uu * 8 + 2 * e + 1] = bf16hi(ws[e]);
+        }
       }
-    }
-  }
-  float energy = 0.f;
+    } else {
 #pragma unroll
-  for (int s = 0; s < 32; ++s) {
-    S.D[ti][kg * 32 + s] = kf[s];
-    energy = fmaf(kf[s], kf[s], energy);
+      for (int s = 0; s < 32; ++s) kf[s] = 0.f;
+    }
+    // centroid of d = 32kg + s: sum over the 16 token lanes of the group
+    float en = 0.f;
+#pragma unroll
+    for (int s = 0; s < 32; ++s) {
+      const float mu = row16_reduce(kf[s], [](float x, float y) { return x + y; }) * (1.0f / kPage);
+      kf[s] -= mu;
+      en = fmaf(kf[s], kf[s], en);
+    }
+    en = wave_sum(en);
+    if (lane == 0) S.energy[pg] = en;
+    v4f g = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 32; ++s) g = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[s], kf[s], g, 0, 0, 0);
+    // lane holds G[4kg + r][ti]; row i stores column ti at slot i ^ ti
+#pragma unroll
+    for (int r = 0; r < 4; ++r) S.A[pg][4 * kg + r][(4 * kg + r) ^ ti] = g[r];
   }
-  energy = wave_sum(energy);
   wave_lds_sync();
-  // ---- centroid (lane owns d = 2*lane, 2*lane+1)
+
+  // ================================================ 2. four eigenproblems, 16 lanes each
   {
-    float s0 = 0.f, s1 = 0.f;
+    const int pg = lane >> 4, i = lane & 15;
+    float a_[kPage], u_[kPage];
+#pragma unroll
+    for (int tt = 0; tt < kPage; ++tt) {
+      a_[tt] = S.A[pg][i][tt];
+      u_[tt] = (tt == 0) ? 1.0f : 0.0f;  // identity: U[i][i ^ t] = (t == 0)
+    }
+    for (int sweep = 0; sweep < kMaxSweeps; ++sweep) {
+      float off = 0.f, tot = a_[0] * a_[0];
+#pragma unroll
+      for (int tt = 1; tt < kPage; ++tt) off = fmaf(a_[tt], a_[tt], off);
+      tot += off;
+      const auto add = [](float x, float y) { return x + y; };
+      off = row16_reduce(off, add);
+      tot = row16_reduce(tot, add);
+      if (__ballot(off > kOffTol * tot) == 0) break;  // all 4 pages converged
+      jacobi_sweep(a_, u_, i, S.rot[pg]);
+    }
+    S.diag[pg][i] = a_[0];
+    // (storage shared with the Gram rows this wave read above: one wave's LDS
+    // operations complete in order, and the union keeps the compiler from
+    // reordering them)
+#pragma unroll
+    for (int tt = 0; tt < kPage; ++tt) S.UT[pg][i ^ tt][i] = u_[tt];
+    wave_lds_sync();
+    // eigenvalues in descending order, equal values keep index order
+    const float lx = a_[0];
+    int rank = 0;
+#pragma unroll
+    for (int y = 0; y < kPage; ++y) {
+      const float ly = S.diag[pg][y];
+      rank += (ly > lx) || (ly == lx && y < i);
+    }
+    S.perm[pg][rank] = i;
+    S.lam[pg][rank] = lx;
+  }
+  wave_lds_sync();
+
+  // ================================================ 3. basis, coefficients, codes, record
+#pragma unroll 1
+  for (int pg = 0; pg < kPagesPerWave; ++pg) {
+    int kvh;
+    const int blk = item_block(a, item0 + pg, &kvh);
+    if (blk < 0) continue;  // wave-uniform
+    // keys d = 2*lane, 2*lane+1 of all 16 tokens
+    const uint32_t* kw = reinterpret_cast<const uint32_t*>(
+        a.kc + ((size_t)blk * a.Hkv + kvh) * (kPage * kDim)) + lane;
+    float d0[kPage], d1[kPage];
+    float m0 = 0.f, m1 = 0.f;
 #pragma unroll
     for (int i = 0; i < kPage; ++i) {
-      s0 += S.D[i][2 * lane];
-      s1 += S.D[i][2 * lane + 1];
+      const uint32_t w = kw[i * (kDim / 2)];
+      d0[i] = bf16lo(w);
+      d1[i] = bf16hi(w);
+      m0 += d0[i];
+      m1 += d1[i];
     }
-    S.mu[2 * lane] = s0 * (1.0f / kPage);
-    S.mu[2 * lane + 1] = s1 * (1.0f / kPage);
-  }
-  wave_lds_sync();
-  // ---- deviations, in registers and in LDS
+    const float mu0 = m0 * (1.0f / kPage), mu1 = m1 * (1.0f / kPage);
 #pragma unroll
-  for (int s = 0; s < 32; ++s) {
-    kf[s] -= S.mu[kg * 32 + s];
-    S.D[ti][kg * 32 + s] = kf[s];
-  }
-  // ---- Gram = D D^T (16x16) on MFMA
-  v4f g = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int s = 0; s < 32; ++s) g = __builtin_amdgcn_mfma_f32_16x16x4f32(kf[s], kf[s], g, 0, 0, 0);
-  // lane (col ti, row group kg) holds G[4kg + r][ti]
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    S.A[4 * kg + r][ti] = g[r];
-    S.U[4 * kg + r][ti] = (4 * kg + r == ti) ? 1.0f : 0.0f;
-  }
-  wave_lds_sync();
-
-  // ---- parallel cyclic Jacobi
-  for (int sweep = 0; sweep < kMaxSweeps; ++sweep) {
-    float off = 0.f, tot = 0.f;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int e = lane + 64 * u, r = e >> 4, c = e & 15;
-      const float v = S.A[r][c];
-      tot = fmaf(v, v, tot);
-      if (r != c) off = fmaf(v, v, off);
+    for (int i = 0; i < kPage; ++i) {
+      d0[i] -= mu0;
+      d1[i] -= mu1;
     }
-    off = wave_sum(off);
-    tot = wave_sum(tot);
-    if (!(off > 1.6e-13f * tot)) break;  // off-diagonal norm below ~4e-7 of the whole
-    for (int round = 0; round < 15; ++round) {
-      if (lane < 8) {
-        const int p = (lane == 0) ? 15 : (round + lane) % 15;
-        const int q = (lane == 0) ? round : (round - lane + 15) % 15;
-        const float app = S.A[p][p], aqq = S.A[q][q], apq = S.A[p][q];
-        float c = 1.f, s = 0.f;
-        if (apq != 0.f) {
-          const float tau = (aqq - app) / (2.f * apq);
-          const float t = copysignf(1.0f, tau) / (fabsf(tau) + sqrtf(fmaf(tau, tau, 1.f)));
-          c = 1.0f / sqrtf(fmaf(t, t, 1.f));
-          s = t * c;
+    const float lam0 = S.lam[pg][0];
+    const float en = S.energy[pg];
+    // ---- basis V[:,k] = D^T u_k / sqrt(lambda_k) for d = 2*lane, 2*lane+1
+    float v[kRank][2];
+#pragma unroll
+    for (int k = 0; k < kRank; ++k) {
+      const float lk = S.lam[pg][k];
+      const bool keep = lam0 > 0.f && lk > 1e-6f * lam0 && lk > 1e-10f * en;
+      const int col = S.perm[pg][k];
+      float s0 = 0.f, s1 = 0.f;
+      if (keep) {
+        const float4* uc = reinterpret_cast<const float4*>(&S.UT[pg][col][0]);
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const float4 uq = uc[q4];
+          const float us[4] = {uq.x, uq.y, uq.z, uq.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            s0 = fmaf(d0[4 * q4 + e], us[e], s0);
+            s1 = fmaf(d1[4 * q4 + e], us[e], s1);
+          }
         }
-        S.mate[p] = q; S.cx[p] = c; S.sx[p] = -s;
-        S.mate[q] = p; S.cx[q] = c; S.sx[q] = s;
+        const float inv = 1.0f / sqrtf(lk);
+        s0 *= inv;
+        s1 *= inv;
       }
-      wave_lds_sync();
-      // columns: A <- A J, U <- U J
-      float na[4], nu[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int e = lane + 64 * u, r = e >> 4, x = e & 15;
-        const int mt = S.mate[x];
-        const float cxv = S.cx[x], sxv = S.sx[x];
-        na[u] = cxv * S.A[r][x] + sxv * S.A[r][mt];
-        nu[u] = cxv * S.U[r][x] + sxv * S.U[r][mt];
-      }
-      wave_lds_sync();
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int e = lane + 64 * u, r = e >> 4, x = e & 15;
-        S.A[r][x] = na[u];
-        S.U[r][x] = nu[u];
-      }
-      wave_lds_sync();
-      // rows: A <- J^T A
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int e = lane + 64 * u, x = e >> 4, c = e & 15;
-        const int mt = S.mate[x];
-        na[u] = S.cx[x] * S.A[x][c] + S.sx[x] * S.A[mt][c];
-      }
-      wave_lds_sync();
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int e = lane + 64 * u, x = e >> 4, c = e & 15;
-        S.A[x][c] = (S.mate[x] == c) ? 0.0f : na[u];  // the rotated pair is exactly zeroed
-      }
-      wave_lds_sync();
+      v[k][0] = s0;
+      v[k][1] = s1;
     }
-  }
+    // ---- sign: largest-|.| entry of each basis vector positive (lowest d on ties)
+    float sgn[kRank];
+#pragma unroll
+    for (int k = 0; k < kRank; ++k) {
+      float best = fabsf(v[k][0]);
+      int bd = 2 * lane;
+      float bv = v[k][0];
+      if (fabsf(v[k][1]) > best) { best = fabsf(v[k][1]); bd = 2 * lane + 1; bv = v[k][1]; }
+      // wave argmax of |v| (lowest d on ties); every step pairs lanes
+      // symmetrically, so all lanes end with the same winner
+      auto take = [&](float ob, int od, float ov) {
+        if (ob > best || (ob == best && od < bd)) { best = ob; bd = od; bv = ov; }
+      };
+      take(dpp_mov<kDppXor1>(best), (int)dpp_mov<kDppXor1>((uint32_t)bd), dpp_mov<kDppXor1>(bv));
+      take(dpp_mov<kDppXor2>(best), (int)dpp_mov<kDppXor2>((uint32_t)bd), dpp_mov<kDppXor2>(bv));
+      take(dpp_mov<kDppHalfMirror>(best), (int)dpp_mov<kDppHalfMirror>((uint32_t)bd),
+           dpp_mov<kDppHalfMirror>(bv));
+      take(dpp_mov<kDppMirror>(best), (int)dpp_mov<kDppMirror>((uint32_t)bd), dpp_mov<kDppMirror>(bv));
+      {
+        const auto rb = __builtin_amdgcn_permlane16_swap(__float_as_uint(best), __float_as_uint(best), false, false);
+        const auto rd = __builtin_amdgcn_permlane16_swap((uint32_t)bd, (uint32_t)bd, false, false);
+        const auto rv = __builtin_amdgcn_permlane16_swap(__float_as_uint(bv), __float_as_uint(bv), false, false);
+        best = __uint_as_float(rb[0]); bd = (int)rd[0]; bv = __uint_as_float(rv[0]);
+        take(__uint_as_float(rb[1]), (int)rd[1], __uint_as_float(rv[1]));
+      }
+      {
+        const auto rb = __builtin_amdgcn_permlane32_swap(__float_as_uint(best), __float_as_uint(best), false, false);
+        const auto rd = __builtin_amdgcn_permlane32_swap((uint32_t)bd, (uint32_t)bd, false, false);
+        const auto rv = __builtin_amdgcn_permlane32_swap(__float_as_uint(bv), __float_as_uint(bv), false, false);
+        best = __uint_as_float(rb[0]); bd = (int)rd[0]; bv = __uint_as_float(rv[0]);
+        take(__uint_as_float(rb[1]), (int)rd[1], __uint_as_float(rv[1]));
+      }
+      sgn[k] = (bv < 0.f) ? -1.0f : 1.0f;
+      v[k][0] *= sgn[k];
+      v[k][1] *= sgn[k];
+    }
+    // ---- coefficients C[i][k] = sqrt(lambda_k) u_k[i]: lane owns (i, k) pairs lane, lane+64
+    float cval[2];
+#pragma unroll
+    for (int uu = 0; uu < 2; ++uu) {
+      const int e = lane + 64 * uu, i = e >> 3, k = e & 7;
+      const float lk = S.lam[pg][k];
+      const bool keep = lam0 > 0.f && lk > 1e-6f * lam0 && lk > 1e-10f * en;
+      cval[uu] = keep ? sqrtf(lk) * S.UT[pg][S.perm[pg][k]][i] * sgn[k] : 0.f;
+    }
+    // ---- absmax scales
+    float am_mu = fmaxf(fabsf(mu0), fabsf(mu1));
+    float am_v = 0.f;
+#pragma unroll
+    for (int k = 0; k < kRank; ++k) am_v = fmaxf(am_v, fmaxf(fabsf(v[k][0]), fabsf(v[k][1])));
+    float am_c = fmaxf(fabsf(cval[0]), fabsf(cval[1]));
+    am_mu = wave_max(am_mu);
+    am_v = wave_max(am_v);
+    am_c = wave_max(am_c);
+    const float s_mu = f16_round(am_mu / 127.0f), s_v = f16_round(am_v / 7.0f),
+                s_c = f16_round(am_c / 127.0f);
 
-  // ---- eigenvalues in descending order, equal values keep index order
-  if (lane < kPage) {
-    const float lx = S.A[lane][lane];
-    int rank = 0;
-    for (int y = 0; y < kPage; ++y) {
-      const float ly = S.A[y][y];
-      rank += (ly > lx) || (ly == lx && y < lane);
+    // ---- codes into the LDS record
+#pragma unroll
+    for (int k = 0; k < kRank; ++k) {
+      S.vq[k][2 * lane] = (int8_t)quant(v[k][0], s_v, 7);
+      S.vq[k][2 * lane + 1] = (int8_t)quant(v[k][1], s_v, 7);
     }
-    S.perm[rank] = lane;
-    S.lam[rank] = lx;
-  }
-  wave_lds_sync();
-  const float lam0 = S.lam[0];
-  // ---- basis V[:,k] = D^T u_k / sqrt(lambda_k) for d = 2*lane, 2*lane+1
-  float v[kRank][2];
+    S.rec[kMuOff + 2 * lane] = (uint8_t)(int8_t)quant(mu0, s_mu, 127);
+    S.rec[kMuOff + 2 * lane + 1] = (uint8_t)(int8_t)quant(mu1, s_mu, 127);
 #pragma unroll
-  for (int k = 0; k < kRank; ++k) {
-    const float lk = S.lam[k];
-    const bool keep = lam0 > 0.f && lk > 1e-6f * lam0 && lk > 1e-10f * energy;
-    const int col = S.perm[k];
-    float s0 = 0.f, s1 = 0.f;
-    if (keep) {
+    for (int uu = 0; uu < 2; ++uu) S.rec[kCOff + lane + 64 * uu] = (uint8_t)(int8_t)quant(cval[uu], s_c, 127);
+    if (lane < (kStride - kSOff) / 4) {  // bytes [768, 784): scales then zero padding, as dwords
+      uint32_t w = 0;
+      if (lane == 0) w = f16_bits(s_mu) | (f16_bits(s_v) << 16);
+      if (lane == 1) w = f16_bits(s_c);
+      *reinterpret_cast<uint32_t*>(&S.rec[kSOff + 4 * lane]) = w;
+    }
+    wave_lds_sync();
+    // V words: word w of row k, byte b = V[8w+b][k] (low nibble) | V[8w+4+b][k] (high nibble)
 #pragma unroll
-      for (int i = 0; i < kPage; ++i) {
-        const float uik = S.U[i][col];
-        s0 = fmaf(S.D[i][2 * lane], uik, s0);
-        s1 = fmaf(S.D[i][2 * lane + 1], uik, s1);
+    for (int uu = 0; uu < 2; ++uu) {
+      const int e = lane + 64 * uu, k = e >> 4, w = e & 15;
+      uint32_t word = 0;
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) {
+        const uint32_t lo = (uint32_t)S.vq[k][8 * w + bb] & 0xFu;
+        const uint32_t hi = (uint32_t)S.vq[k][8 * w + 4 + bb] & 0xFu;
+        word |= (lo | (hi << 4)) << (8 * bb);
       }
-      const float inv = 1.0f / sqrtf(lk);
-      s0 *= inv;
-      s1 *= inv;
+      *reinterpret_cast<uint32_t*>(&S.rec[kVOff + k * 64 + w * 4]) = word;
     }
-    v[k][0] = s0;
-    v[k][1] = s1;
+    wave_lds_sync();
+    uint32_t* dst = reinterpret_cast<uint32_t*>(a.summ + ((size_t)blk * a.Hkv + kvh) * kStride);
+    const uint32_t* srcw = reinterpret_cast<const uint32_t*>(S.rec);
+    for (int e = lane; e < kStride / 4; e += 64) dst[e] = srcw[e];
+    wave_lds_sync();  // the record buffer is reused by the next page
   }
-  // ---- sign: largest-|.| entry of each basis vector positive (lowest d on ties)
-  float sgn[kRank];
-#pragma unroll
-  for (int k = 0; k < kRank; ++k) {
-    float best = fabsf(v[k][0]);
-    int bd = 2 * lane;
-    float bv = v[k][0];
-    if (fabsf(v[k][1]) > best) { best = fabsf(v[k][1]); bd = 2 * lane + 1; bv = v[k][1]; }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ob = __shfl_xor(best, o);
-      const int od = __shfl_xor(bd, o);
-      const float ov = __shfl_xor(bv, o);
-      if (ob > best || (ob == best && od < bd)) { best = ob; bd = od; bv = ov; }
-    }
-    sgn[k] = (bv < 0.f) ? -1.0f : 1.0f;
-    v[k][0] *= sgn[k];
-    v[k][1] *= sgn[k];
-  }
-  // ---- coefficients C[i][k] = sqrt(lambda_k) u_k[i]: lane owns (i, k) pairs lane, lane+64
-  float cval[2];
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int e = lane + 64 * u, i = e >> 3, k = e & 7;
-    const float lk = S.lam[k];
-    const bool keep = lam0 > 0.f && lk > 1e-6f * lam0 && lk > 1e-10f * energy;
-    cval[u] = keep ? sqrtf(lk) * S.U[i][S.perm[k]] * sgn[k] : 0.f;
-  }
-  // ---- absmax scales
-  float am_mu = fmaxf(fabsf(S.mu[2 * lane]), fabsf(S.mu[2 * lane + 1]));
-  float am_v = 0.f;
-#pragma unroll
-  for (int k = 0; k < kRank; ++k) am_v = fmaxf(am_v, fmaxf(fabsf(v[k][0]), fabsf(v[k][1])));
-  float am_c = fmaxf(fabsf(cval[0]), fabsf(cval[1]));
-  am_mu = wave_max(am_mu);
-  am_v = wave_max(am_v);
-  am_c = wave_max(am_c);
-  const float s_mu = f16_round(am_mu / 127.0f), s_v = f16_round(am_v / 7.0f),
-              s_c = f16_round(am_c / 127.0f);
-
-  // ---- codes into the LDS record
-#pragma unroll
-  for (int k = 0; k < kRank; ++k) {
-    S.vq[k][2 * lane] = (int8_t)quant(v[k][0], s_v, 7);
-    S.vq[k][2 * lane + 1] = (int8_t)quant(v[k][1], s_v, 7);
-  }
-  S.rec[kMuOff + 2 * lane] = (uint8_t)(int8_t)quant(S.mu[2 * lane], s_mu, 127);
-  S.rec[kMuOff + 2 * lane + 1] = (uint8_t)(int8_t)quant(S.mu[2 * lane + 1], s_mu, 127);
-#pragma unroll
-  for (int u = 0; u < 2; ++u) S.rec[kCOff + lane + 64 * u] = (uint8_t)(int8_t)quant(cval[u], s_c, 127);
-  if (lane < (kStride - kSOff) / 4) {  // bytes [768, 784): scales then zero padding, as dwords
-    uint32_t w = 0;
-    if (lane == 0) w = f16_bits(s_mu) | (f16_bits(s_v) << 16);
-    if (lane == 1) w = f16_bits(s_c);
-    *reinterpret_cast<uint32_t*>(&S.rec[kSOff + 4 * lane]) = w;
-  }
-  wave_lds_sync();
-  // V words: word w of row k, byte b = V[8w+b][k] (low nibble) | V[8w+4+b][k] (high nibble)
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int e = lane + 64 * u, k = e >> 4, w = e & 15;
-    uint32_t word = 0;
-#pragma unroll
-    for (int bb = 0; bb < 4; ++bb) {
-      const uint32_t lo = (uint32_t)S.vq[k][8 * w + bb] & 0xFu;
-      const uint32_t hi = (uint32_t)S.vq[k][8 * w + 4 + bb] & 0xFu;
-      word |= (lo | (hi << 4)) << (8 * bb);
-    }
-    *reinterpret_cast<uint32_t*>(&S.rec[kVOff + k * 64 + w * 4]) = word;
-  }
-  wave_lds_sync();
-  uint32_t* dst = reinterpret_cast<uint32_t*>(a.summ + ((size_t)blk * a.Hkv + kvh) * kStride);
-  const uint32_t* srcw = reinterpret_cast<const uint32_t*>(S.rec);
-  for (int e = lane; e < kStride / 4; e += 64) dst[e] = srcw[e];
 }
 
 }  // namespace
@@ -314,8 +418,9 @@ hipError_t launch_build(const locks_dims& d, const uint16_t* kc, const int32_t* 
   a.Hkv = d.n_kv_heads;
   a.N = d.max_pages_per_seq;
   a.num_blocks = d.num_blocks;
-  const long long items = (long long)d.batch * d.max_pages_per_seq * d.n_kv_heads;
-  const long long wgs = (items + kWaves - 1) / kWaves;
+  a.items = (long long)d.batch * d.max_pages_per_seq * d.n_kv_heads;
+  const long long per_wg = (long long)kWaves * kPagesPerWave;
+  const long long wgs = (a.items + per_wg - 1) / per_wg;
   if (wgs <= 0) return hipSuccess;
   hipLaunchKernelGGL(build_kernel, dim3((unsigned)wgs), dim3(64 * kWaves), 0, s, a);
   return hipGetLastError();
