@@ -16,7 +16,9 @@
 //       (coalesced 256-byte rows) and takes each token's weight by readlane.
 // Waves merge in LDS into one (max, sum, o[128]) partial per head and split; a
 // second launch, one workgroup per (sequence, query head), merges the splits
-// in fixed order and writes the output. No float atomics.
+// in fixed order and writes the output. No float atomics. For G >= 8 (and the
+// dense comparator at G = 4) the per-page products run on MFMA instead
+// (attend_mfma_kernel below).
 #include "device_common.h"
 #include "internal.h"
 
@@ -171,6 +173,175 @@ __global__ __launch_bounds__(256) void attend_kernel(AttnArgs a) {
   }
 }
 
+typedef __bf16 bf8_t __attribute__((ext_vector_type(8)));
+typedef short s4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ short bf16_bits(float x) {
+  return __builtin_bit_cast(short, (__bf16)x);
+}
+
+// MFMA flash-decode for G >= 4 query heads per KV head: each page is a
+// (16 tokens x 128) x (128 x G heads) contraction and back.
+//   S^T = K Q^T on v_mfma_f32_16x16x32_bf16: A = the key rows as stored
+//     (lane: token l%16, dims 8(l/16)+e of a 32-wide chunk), B = q as bf16
+//     hi + lo (~16 significant bits), heads padded to 16 with zeros; a lane
+//     then holds the base-2 logits of tokens 4(l/16)+r for head l%16.
+//   softmax over the page's tokens: in-lane over r, then two permlane swaps.
+//   O += P V on v_mfma_f32_16x16x16_bf16: those same registers are the A
+//     operand (P[head][token]) as bf16 hi + lo; B = V[token][dim], read from a
+//     per-wave LDS copy of the tile whose 272-byte rows make the 4-token
+//     column reads bank-conflict free; a lane accumulates O[head 4(l/16)+r]
+//     [dim 16 blk + l%16].
+template <int G>
+__global__ __launch_bounds__(256) void attend_mfma_kernel(AttnArgs a) {
+  static_assert(G >= 4 && G <= 16, "MFMA rows are the query heads of a group");
+  constexpr int kVRow = kDim + 8;  // staged V row in bf16 (272 bytes)
+  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int li = lane & 15, lj = lane >> 4;
+  const int N = a.N;
+  const int n_b = full_pages(a.seq_lens, b, N);
+  const int list_len = a.sel ? a.k : n_b;
+  const int s0 = split * a.pages_per_split;
+  const int s1 = min(s0 + a.pages_per_split, list_len);
+
+  // V staging during the page loop; the waves' O rows for the merge after it
+  union AttnLds {
+    __bf16 v[4][kPage][kVRow];
+    float wo[4][G][kDim];
+  };
+  __shared__ __align__(16) AttnLds U;
+  __shared__ float wm_s[4][G], wl_s[4][G];
+
+  auto page_block = [&](int s) -> int {
+    int blk;
+    if (a.sel_blk) {
+      blk = a.sel_blk[((size_t)b * a.Hkv + kvh) * a.k + s];
+    } else {
+      const int j = a.sel ? a.sel[((size_t)b * a.Hkv + kvh) * a.k + s] : s;
+      if (j < 0 || j >= n_b) return -1;
+      blk = a.page_table[(size_t)b * N + j];
+    }
+    return (blk >= 0 && blk < a.num_blocks) ? blk : -1;
+  };
+  int blk_next = (s0 + wave < s1) ? page_block(s0 + wave) : -1;
+
+  // q of head li (zero for li >= G), base-2 logit scale, bf16 hi + lo
+  bf8_t qh[4], ql[4];
+  {
+    const float qscale = kLog2e * kInvSqrtD;
+    const float* qrow = a.q + ((size_t)b * a.Hq + (size_t)kvh * G + (li < G ? li : 0)) * kDim;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float4 x0 = *reinterpret_cast<const float4*>(qrow + 32 * c + 8 * lj);
+      const float4 x1 = *reinterpret_cast<const float4*>(qrow + 32 * c + 8 * lj + 4);
+      const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = (li < G) ? xs[e] * qscale : 0.f;
+        const __bf16 h = (__bf16)x;
+        qh[c][e] = h;
+        ql[c][e] = (__bf16)(x - (float)h);
+      }
+    }
+  }
+
+  float m_run = -INFINITY, l_run = 0.f;  // head li
+  v4f oacc[8];
+#pragma unroll
+  for (int k8 = 0; k8 < 8; ++k8) oacc[k8] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  for (int s = s0 + wave; s < s1; s += 4) {
+    const int blk = blk_next;
+    blk_next = (s + 4 < s1) ? page_block(s + 4) : -1;
+    if (blk < 0) continue;
+    const size_t tile = ((size_t)blk * a.Hkv + kvh) * (kPage * kDim);
+    const uint4* krow = reinterpret_cast<const uint4*>(a.kc + tile + li * kDim + 8 * lj);
+    const uint4* vrow = reinterpret_cast<const uint4*>(a.vc + tile + li * kDim + 8 * lj);
+    uint4 kr[4], vr[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      kr[c] = krow[4 * c];
+      vr[c] = vrow[4 * c];
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) *reinterpret_cast<uint4*>(&U.v[wave][li][32 * c + 8 * lj]) = vr[c];
+
+    v4f sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const bf8_t kk = __builtin_bit_cast(bf8_t, kr[c]);
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk, qh[c], sacc, 0, 0, 0);
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk, ql[c], sacc, 0, 0, 0);
+    }
+    // online softmax for head li over the page's 16 tokens
+    float mx = fmaxf(fmaxf(sacc[0], sacc[1]), fmaxf(sacc[2], sacc[3]));
+    mx = xor32_max(xor16_max(mx));
+    const float mn = fmaxf(m_run, mx);
+    const float alpha = fast_exp2(m_run - mn);  // m_run = -inf -> 0
+    float pr[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(sacc[r] - mn);
+    float ps = (pr[0] + pr[1]) + (pr[2] + pr[3]);
+    ps = xor32_sum(xor16_sum(ps));
+    l_run = fmaf(l_run, alpha, ps);
+    m_run = mn;
+    // O rows are heads 4lj + r: their rescale factors sit in lanes 4lj + r
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float al = __shfl(alpha, 4 * lj + r);
+#pragma unroll
+      for (int k8 = 0; k8 < 8; ++k8) oacc[k8][r] *= al;
+    }
+    s4_t ph, pl;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const __bf16 h = (__bf16)pr[r];
+      ph[r] = __builtin_bit_cast(short, h);
+      pl[r] = bf16_bits(pr[r] - (float)h);
+    }
+    wave_lds_sync();  // the V tile is staged
+#pragma unroll
+    for (int k8 = 0; k8 < 8; ++k8) {
+      s4_t vb;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vb[e] = __builtin_bit_cast(short, U.v[wave][4 * lj + e][16 * k8 + li]);
+      oacc[k8] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ph, vb, oacc[k8], 0, 0, 0);
+      oacc[k8] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pl, vb, oacc[k8], 0, 0, 0);
+    }
+    wave_lds_sync();  // every lane has read the tile before the next one lands
+  }
+
+  // ---- merge the 4 waves of this split (the V staging area becomes O rows)
+  __syncthreads();
+  if (lj == 0 && li < G) { wm_s[wave][li] = m_run; wl_s[wave][li] = l_run; }
+#pragma unroll
+  for (int k8 = 0; k8 < 8; ++k8)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (4 * lj + r < G) U.wo[wave][4 * lj + r][16 * k8 + li] = oacc[k8][r];
+  __syncthreads();
+  float* part = a.partials + (((size_t)b * a.Hq + (size_t)kvh * G) * a.n_split + split) * kPartialFloats;
+  for (int i = tid; i < G * kDim; i += 256) {
+    const int h = i / kDim, d = i % kDim;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, wm_s[w][h]);
+    float L = 0.f, O = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float f = exp2f(wm_s[w][h] - M);
+        L += wl_s[w][h] * f;
+        O += U.wo[w][h][d] * f;
+      }
+    }
+    float* ph2 = part + (size_t)h * a.n_split * kPartialFloats;
+    ph2[2 + d] = O;
+    if (d == 0) { ph2[0] = M; ph2[1] = L; }
+  }
+}
+
 // Merge of the split partials of one (sequence, query head): 256 threads =
 // 128 output dims x 2 halves of the split list. Each half folds its splits in
 // fixed order with an online rescale, 8 splits' loads in flight at a time;
@@ -240,7 +411,18 @@ hipError_t launch_g(const locks_dims& d, const WsLayout& L, const DevPtrs& P, co
   a.k = L.k;
   a.pages_per_split = dense ? L.dense_pages_per_split : kSparsePagesPerSplit;
   a.n_split = dense ? L.n_dense_split : L.n_att_split;
-  hipLaunchKernelGGL(attend_kernel<G>, dim3(a.n_split, d.n_kv_heads, d.batch), dim3(256), 0, s, a);
+  // MFMA where a query group fills enough of the 16 rows: G >= 8 always, and
+  // G = 4 for the long dense splits; a sparse split at G = 4 (one page per
+  // wave, 3/4 of the rows padding) is faster on VALU (measured)
+  const dim3 grid(a.n_split, d.n_kv_heads, d.batch);
+  if constexpr (G >= 8) {
+    hipLaunchKernelGGL(attend_mfma_kernel<G>, grid, dim3(256), 0, s, a);
+  } else if constexpr (G == 4) {
+    if (dense) hipLaunchKernelGGL(attend_mfma_kernel<G>, grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(attend_kernel<G>, grid, dim3(256), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(attend_kernel<G>, grid, dim3(256), 0, s, a);
+  }
   hipLaunchKernelGGL(attend_merge_kernel, dim3(d.n_q_heads, d.batch), dim3(256), 0, s, a.partials,
                      out, d.n_q_heads, a.n_split);
   return hipGetLastError();
