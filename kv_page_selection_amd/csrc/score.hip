@@ -90,27 +90,44 @@ struct ScoreLds {
   float esc[4][16];
 };
 
-template <int G>
+// GROUP = query heads per KV head; a wave scores G = min(GROUP, 8) of them
+// (larger groups are split into slices of 8 heads, one wave each, which share
+// the record loads through the cache and fill the stage-2 MFMA columns)
+template <int GROUP>
 __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
+  constexpr int G = GROUP > 8 ? 8 : GROUP;
+  constexpr int NS = GROUP / G;           // head slices per KV head
   constexpr int RB = G < 4 ? 1 : G / 4;   // stage-1 row blocks (4 heads each)
   constexpr int PG = 16 / G;              // pages per stage-2 pass
   __shared__ ScoreLds<G> S;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = lane & 15, kg = lane >> 4;
   const int b = blockIdx.z;
-  // waves -> (KV head, page range): up to 4 KV heads share the same pages
-  const int hw = a.Hkv < 4 ? a.Hkv : 4;
-  const int slots = 4 / hw;
+  // waves -> (KV head, head slice, page range): the waves of a workgroup take
+  // the same pages of up to 4 KV heads (or slices), whose records are adjacent
+  const int hw = a.Hkv < 4 / NS ? a.Hkv : 4 / NS;
+  const int slots = 4 / (hw * NS);
   const int kvh = blockIdx.y * hw + wave % hw;
-  const int range = blockIdx.x * slots + wave / hw;
-  if (wave / hw >= slots || kvh >= a.Hkv || range >= a.n_ranges) return;  // whole wave
+  const int slice = (wave / hw) % NS;
+  const int range = blockIdx.x * slots + wave / (hw * NS);
+  if (wave / (hw * NS) >= slots || kvh >= a.Hkv || range >= a.n_ranges) return;  // whole wave
+  const int hbase = kvh * GROUP + slice * G;  // first query head of this wave
   const int N = a.N;
   const int n_b = full_pages(a.seq_lens, b, N);
   TileLds<G>& T = S.w[wave].t;
 
+  // page table of this wave's 64 pages, one entry per lane; issued first, so
+  // its latency overlaps the q prologue below
+  const int p0 = range * kScorePagesPerWave;
+  int myblk = -1;
+  {
+    const int j = p0 + lane;
+    if (j < n_b) myblk = a.page_table[(size_t)b * N + j];
+  }
+
   // ---- q of the group -> per-head exponent -> three int8 digit planes (wave-local)
   {
-    const float* qg = a.q + ((size_t)b * a.Hq + (size_t)kvh * G) * kDim;
+    const float* qg = a.q + ((size_t)b * a.Hq + (size_t)hbase) * kDim;
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const float q0 = qg[h * kDim + lane], q1 = qg[h * kDim + 64 + lane];
@@ -151,21 +168,13 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
   wave_lds_sync();  // digit planes consumed; the storage becomes tile staging
   if (lane < 8) T.zero[lane] = (_Float16)0.0f;
 
+  if (myblk < 0 || myblk >= a.num_blocks) myblk = -1;  // absent page
+
   // stage-2 output column col = (page pc of the pass, head hc)
   const int pc = row / G, hc = row % G;
   const float es = S.esc[wave][hc];
   float run_m = -1e30f, run_s = 0.f;  // head hc, base 2; -1e30 = empty
 
-  // page table of this wave's 64 pages, one entry per lane
-  const int p0 = range * kScorePagesPerWave;
-  int myblk = -1;
-  {
-    const int j = p0 + lane;
-    if (j < n_b) {
-      myblk = a.page_table[(size_t)b * N + j];
-      if (myblk < 0 || myblk >= a.num_blocks) myblk = -1;
-    }
-  }
 
   float myscore[G];  // lane = page of this wave: its score for every head
 #pragma unroll
@@ -301,7 +310,7 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
   // of the launch
 #pragma unroll
   for (int h = 0; h < G; ++h)
-    if (p0 + lane < n_b) __builtin_nontemporal_store(myscore[h], &a.scores[((size_t)b * a.Hq + (size_t)kvh * G + h) * N + p0 + lane]);
+    if (p0 + lane < n_b) __builtin_nontemporal_store(myscore[h], &a.scores[((size_t)b * a.Hq + (size_t)hbase + h) * N + p0 + lane]);
 
   // ---- per-head (max, sum) over this wave's pages: lanes 0..15, head = lane % G
 #pragma unroll
@@ -312,7 +321,7 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
     run_m = mn;
   }
   if (lane < G) {
-    float* dst = a.partials + (((size_t)b * a.Hq + (size_t)kvh * G + lane) * a.n_ranges + range) * 2;
+    float* dst = a.partials + (((size_t)b * a.Hq + (size_t)hbase + lane) * a.n_ranges + range) * 2;
     dst[0] = (run_s > 0.f) ? run_m : -INFINITY;
     dst[1] = run_s;
   }
@@ -333,8 +342,9 @@ hipError_t launch_g(const locks_dims& d, const WsLayout& L, const DevPtrs& P, co
   a.N = d.max_pages_per_seq;
   a.num_blocks = d.num_blocks;
   a.n_ranges = L.n_score_wg;
-  const int hw = d.n_kv_heads < 4 ? d.n_kv_heads : 4;
-  const int slots = 4 / hw;
+  constexpr int NS = G > 8 ? G / 8 : 1;
+  const int hw = d.n_kv_heads < 4 / NS ? d.n_kv_heads : 4 / NS;
+  const int slots = 4 / (hw * NS);
   dim3 grid((L.n_score_wg + slots - 1) / slots, (d.n_kv_heads + hw - 1) / hw, d.batch);
   hipLaunchKernelGGL(score_kernel<G>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
