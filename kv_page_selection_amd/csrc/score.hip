@@ -6,10 +6,10 @@
 //   s_hat = log sum_{i<16} exp((q.mu + (V^T q).c_i) / sqrt(128))
 // from the page's summary record alone (no key or value is read).
 //
-// Mapping. A workgroup is 4 waves; wave w scores 64 consecutive pages (4 tiles
-// of 16) of one KV head, and the waves of a workgroup take consecutive KV
-// heads of the same pages, so the records of one physical block (adjacent in
-// memory) are fetched together.
+// Mapping. A workgroup is 4 waves of one KV head (and one slice of at most 8
+// of its query heads); wave w scores 64 consecutive pages (4 tiles of 16), and
+// the waves take 4 consecutive page ranges. The q prologue (fixed-point digits
+// of the group's query heads) is split over the 4 waves and shared in LDS.
 //
 // Stage 1, mu.q and V^T q, on v_mfma_i32_16x16x64_i8, exact: the row operand is
 // each query head as a 22-bit fixed-point integer in three signed int8 digits
@@ -76,18 +76,11 @@ struct TileLds {
   float out[G][16];                     // the tile's page scores, [head][page], natural log
 };
 
-// Per wave: the q digit planes are dead once the row operands are in
-// registers, so they share storage with the tile staging.
-template <int G>
-union WaveLds {
-  TileLds<G> t;
-  __align__(16) int8_t dig[3][G][kDim];
-};
-
 template <int G>
 struct ScoreLds {
-  WaveLds<G> w[4];
-  float esc[4][16];
+  TileLds<G> w[4];
+  __align__(16) int8_t dig[3][G][kDim];  // q digit planes of the workgroup's heads
+  float esc[16];                         // per head: 2^-e log2(e) / sqrt(128)
 };
 
 // GROUP = query heads per KV head; a wave scores G = min(GROUP, 8) of them
@@ -103,18 +96,17 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = lane & 15, kg = lane >> 4;
   const int b = blockIdx.z;
-  // waves -> (KV head, head slice, page range): the waves of a workgroup take
-  // the same pages of up to 4 KV heads (or slices), whose records are adjacent
-  const int hw = a.Hkv < 4 / NS ? a.Hkv : 4 / NS;
-  const int slots = 4 / (hw * NS);
-  const int kvh = blockIdx.y * hw + wave % hw;
-  const int slice = (wave / hw) % NS;
-  const int range = blockIdx.x * slots + wave / (hw * NS);
-  if (wave / (hw * NS) >= slots || kvh >= a.Hkv || range >= a.n_ranges) return;  // whole wave
-  const int hbase = kvh * GROUP + slice * G;  // first query head of this wave
+  // workgroup -> (KV head, head slice, 4 page ranges). Slices are the slow
+  // grid dimension y = kvh * NS + slice over an x extent padded to a multiple
+  // of 8: workgroups are dealt round-robin to the 8 XCDs, so every slice of a
+  // range group lands on the XCD (and L2) that fetched its records first.
+  const int kvh = blockIdx.y / NS;
+  const int slice = blockIdx.y % NS;
+  const int range = blockIdx.x * 4 + wave;
+  const int hbase = kvh * GROUP + slice * G;  // first query head of this workgroup
   const int N = a.N;
   const int n_b = full_pages(a.seq_lens, b, N);
-  TileLds<G>& T = S.w[wave].t;
+  TileLds<G>& T = S.w[wave];
 
   // page table of this wave's 64 pages, one entry per lane; issued first, so
   // its latency overlaps the q prologue below
@@ -122,14 +114,14 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
   int myblk = -1;
   {
     const int j = p0 + lane;
-    if (j < n_b) myblk = a.page_table[(size_t)b * N + j];
+    if (range < a.n_ranges && j < n_b) myblk = a.page_table[(size_t)b * N + j];
   }
 
-  // ---- q of the group -> per-head exponent -> three int8 digit planes (wave-local)
+  // ---- q of the group -> per-head exponent -> three int8 digit planes;
+  // wave w converts heads w, w+4, ...
   {
     const float* qg = a.q + ((size_t)b * a.Hq + (size_t)hbase) * kDim;
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
+    for (int h = wave; h < G; h += 4) {
       const float q0 = qg[h * kDim + lane], q1 = qg[h * kDim + 64 + lane];
       const float qm = wave_max(fmaxf(fabsf(q0), fabsf(q1)));
       int e = 0;
@@ -146,14 +138,15 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
         const int r1 = (qf - d0) / 256;
         const int d1 = ((r1 + 128) & 255) - 128;
         const int d2 = (r1 - d1) / 256;
-        S.w[wave].dig[0][h][lane + 64 * u] = (int8_t)d0;
-        S.w[wave].dig[1][h][lane + 64 * u] = (int8_t)d1;
-        S.w[wave].dig[2][h][lane + 64 * u] = (int8_t)d2;
+        S.dig[0][h][lane + 64 * u] = (int8_t)d0;
+        S.dig[1][h][lane + 64 * u] = (int8_t)d1;
+        S.dig[2][h][lane + 64 * u] = (int8_t)d2;
       }
-      if (lane == 0) S.esc[wave][h] = ldexpf(1.0f, -e) * (kLog2e * kInvSqrtD);
+      if (lane == 0) S.esc[h] = ldexpf(1.0f, -e) * (kLog2e * kInvSqrtD);
     }
   }
-  wave_lds_sync();
+  __syncthreads();
+  if (range >= a.n_ranges) return;  // whole wave; no workgroup barrier follows
   // row operands: lane (row = (head 4rb + row/4, digit row%4), K group kg), d in [32kg+16m, +16)
   v4i aop[RB][2];
 #pragma unroll
@@ -162,17 +155,16 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
 #pragma unroll
     for (int m = 0; m < 2; ++m)
       aop[rb][m] = (h < G && dg < 3)
-                       ? *reinterpret_cast<const v4i*>(&S.w[wave].dig[dg < 3 ? dg : 0][h < G ? h : 0][32 * kg + 16 * m])
+                       ? *reinterpret_cast<const v4i*>(&S.dig[dg < 3 ? dg : 0][h < G ? h : 0][32 * kg + 16 * m])
                        : v4i{0, 0, 0, 0};
   }
-  wave_lds_sync();  // digit planes consumed; the storage becomes tile staging
   if (lane < 8) T.zero[lane] = (_Float16)0.0f;
 
   if (myblk < 0 || myblk >= a.num_blocks) myblk = -1;  // absent page
 
   // stage-2 output column col = (page pc of the pass, head hc)
   const int pc = row / G, hc = row % G;
-  const float es = S.esc[wave][hc];
+  const float es = S.esc[hc];
   float run_m = -1e30f, run_s = 0.f;  // head hc, base 2; -1e30 = empty
 
 
@@ -343,9 +335,8 @@ hipError_t launch_g(const locks_dims& d, const WsLayout& L, const DevPtrs& P, co
   a.num_blocks = d.num_blocks;
   a.n_ranges = L.n_score_wg;
   constexpr int NS = G > 8 ? G / 8 : 1;
-  const int hw = d.n_kv_heads < 4 / NS ? d.n_kv_heads : 4 / NS;
-  const int slots = 4 / (hw * NS);
-  dim3 grid((L.n_score_wg + slots - 1) / slots, (d.n_kv_heads + hw - 1) / hw, d.batch);
+  const int nrg = (L.n_score_wg + 3) / 4;
+  dim3 grid(NS == 1 ? nrg : (nrg + 7) / 8 * 8, d.n_kv_heads * NS, d.batch);
   hipLaunchKernelGGL(score_kernel<G>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }

@@ -62,6 +62,11 @@ def test_workspace_sizing_and_validation(L):
         with pytest.raises(L.LocksError) as e:
             L.workspace_bytes(dims(L, **bad), 512)
         assert e.value.status == L.ERR_UNSUPPORTED, bad
+    for bad in (dict(batch=2, n_kv_heads=40000, n_q_heads=40000),
+                dict(batch=1, n_kv_heads=40000, n_q_heads=640000)):  # launch-grid limits
+        with pytest.raises(L.LocksError) as e:
+            L.workspace_bytes(dims(L, **bad), 512)
+        assert e.value.status == L.ERR_UNSUPPORTED, bad
     with pytest.raises(L.LocksError) as e:
         L.workspace_bytes(dims(L, n_q_heads=30), 512)
     assert e.value.status == L.ERR_INVALID_ARG
