@@ -22,8 +22,14 @@
 // f16 hi + lo pair (about 22 significant bits); 16/G pages are packed
 // block-diagonally along K so one pass fills the 16 output columns. The
 // 16-token log-sum-exp is one in-lane step and two cross-row swaps, in base 2.
-// Every wave also leaves, per head, the (max, sum) of exp over its 64 pages,
-// which the group combine needs for every head's total mass.
+// The wave keeps its 64 x G scores in LDS; at the end it writes them once and
+// leaves, per head, the (max, sum) of exp2 over its pages, which the group
+// combine needs for every head's total mass.
+//
+// Loads. Each wave turns its 64 page-table entries into record offsets once
+// (an LDS table); every tile then issues its 13 record loads back to back in
+// a fixed order (V rows first) and consumes them in that order, so the first
+// MFMAs run while the tail of the tile is still arriving.
 #include "device_common.h"
 #include "internal.h"
 
@@ -72,15 +78,18 @@ struct TileLds {
   __align__(16) _Float16 pl[16][G][8];  // low part
   __align__(16) _Float16 zero[8];       // masked B operand
   float a[16][G + 1];                   // mu . q (exact integer), [page][head]; column G spare
-  float sc[16][4];                      // s_mu, s_V/16 * s_C, valid
-  float out[G][16];                     // the tile's page scores, [head][page], natural log
+  float sc[32][2];                      // s_mu, s_V/16 * s_C; rows 16.. take the other lanes' copies
+  __align__(16) float out[kScorePagesPerWave][G];  // the wave's page scores, [page][head], base 2
 };
 
 template <int G>
 struct ScoreLds {
   TileLds<G> w[4];
-  __align__(16) int8_t dig[3][G][kDim];  // q digit planes of the workgroup's heads
-  float esc[16];                         // per head: 2^-e log2(e) / sqrt(128)
+  union {
+    __align__(16) int8_t dig[3][G][kDim];  // q digit planes of the workgroup's heads,
+    uint32_t off[4][kScorePagesPerWave];   // then each wave's page record offsets
+  } u;
+  float esc[16];                           // per head: 2^-e log2(e) / sqrt(128)
 };
 
 // GROUP = query heads per KV head; a wave scores G = min(GROUP, 8) of them
@@ -138,15 +147,14 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
         const int r1 = (qf - d0) / 256;
         const int d1 = ((r1 + 128) & 255) - 128;
         const int d2 = (r1 - d1) / 256;
-        S.dig[0][h][lane + 64 * u] = (int8_t)d0;
-        S.dig[1][h][lane + 64 * u] = (int8_t)d1;
-        S.dig[2][h][lane + 64 * u] = (int8_t)d2;
+        S.u.dig[0][h][lane + 64 * u] = (int8_t)d0;
+        S.u.dig[1][h][lane + 64 * u] = (int8_t)d1;
+        S.u.dig[2][h][lane + 64 * u] = (int8_t)d2;
       }
       if (lane == 0) S.esc[h] = ldexpf(1.0f, -e) * (kLog2e * kInvSqrtD);
     }
   }
   __syncthreads();
-  if (range >= a.n_ranges) return;  // whole wave; no workgroup barrier follows
   // row operands: lane (row = (head 4rb + row/4, digit row%4), K group kg), d in [32kg+16m, +16)
   v4i aop[RB][2];
 #pragma unroll
@@ -155,65 +163,60 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
 #pragma unroll
     for (int m = 0; m < 2; ++m)
       aop[rb][m] = (h < G && dg < 3)
-                       ? *reinterpret_cast<const v4i*>(&S.dig[dg < 3 ? dg : 0][h < G ? h : 0][32 * kg + 16 * m])
+                       ? *reinterpret_cast<const v4i*>(&S.u.dig[dg < 3 ? dg : 0][h < G ? h : 0][32 * kg + 16 * m])
                        : v4i{0, 0, 0, 0};
   }
+  __syncthreads();  // digit planes consumed: the space takes the record offsets
+  if (range >= a.n_ranges) return;  // whole wave; no workgroup barrier follows
   if (lane < 8) T.zero[lane] = (_Float16)0.0f;
 
-  if (myblk < 0 || myblk >= a.num_blocks) myblk = -1;  // absent page
+  // An absent page (past the sequence's full pages, or a table entry out of
+  // range) reads block 0's record in its place, so every load is
+  // unconditional; its score is replaced by -inf at the end.
+  if (myblk < 0 || myblk >= a.num_blocks) myblk = -1;
+  const unsigned long long present = __ballot(myblk >= 0);  // bit i: page p0 + i
+  // the lane's page record, as an offset from summ in 16-byte units (the
+  // library limits num_blocks * n_kv_heads * 49 to 32 bits)
+  S.u.off[wave][lane] = (uint32_t)((myblk < 0 ? 0 : myblk) * a.Hkv + kvh) * (uint32_t)(kStride / 16);
+  const uint8_t* vbase = a.summ + kVOff + (row & 7) * 64 + kg * 16;  // V row of the lane
+  const uint8_t* rbase = a.summ + kg * 32;                           // mu, C slice of the lane
 
   // stage-2 output column col = (page pc of the pass, head hc)
   const int pc = row / G, hc = row % G;
   const float es = S.esc[hc];
-  float run_m = -1e30f, run_s = 0.f;  // head hc, base 2; -1e30 = empty
 
+  wave_lds_sync();
 
-  float myscore[G];  // lane = page of this wave: its score for every head
-#pragma unroll
-  for (int h = 0; h < G; ++h) myscore[h] = 0.f;
   for (int t = 0; t < kTiles; ++t) {
-    const int pbase = p0 + t * 16;
-    const int blk = __shfl(myblk, t * 16 + row);  // page pbase + row
-    // ---- loads: V rows (page 2vt + row/8, basis vector row%8), mu, C, scales
+    // record offsets of the tile's pages as this lane addresses them: the V
+    // row of page 2vt + row/8 for each vt, and the mu/C/scales of page row
+    uint32_t ov[8];
+#pragma unroll
+    for (int vt = 0; vt < 8; ++vt) ov[vt] = S.u.off[wave][t * 16 + 2 * vt + (row >> 3)];
+    const uint32_t om = S.u.off[wave][t * 16 + row];
+    // ---- loads: V rows (page 2vt + row/8, basis vector row%8), mu, C, scales.
+    // Issued in this order, pinned (the order is worth ~5% of the gather
+    // rate at 4-head groups: the V rows first, the tail of each record last).
+    const uint8_t* rec = rbase + ((size_t)om << 4);  // page t*16 + row
+    __builtin_amdgcn_sched_barrier(0);
     uint4 vraw[8];
 #pragma unroll
     for (int vt = 0; vt < 8; ++vt) {
-      const int blk2 = __shfl(myblk, t * 16 + 2 * vt + (row >> 3));
-      vraw[vt] = make_uint4(0, 0, 0, 0);
-      if (blk2 >= 0)
-        vraw[vt] = *reinterpret_cast<const uint4*>(
-            a.summ + ((size_t)blk2 * a.Hkv + kvh) * kStride + kVOff + (row & 7) * 64 + kg * 16);
+      vraw[vt] = *reinterpret_cast<const uint4*>(vbase + ((size_t)ov[vt] << 4));
+      __builtin_amdgcn_sched_barrier(0);
     }
-    uint4 mu0 = make_uint4(0, 0, 0, 0), mu1 = mu0, c0 = mu0, c1 = mu0;
-    uint2 scl = make_uint2(0, 0);
-    if (blk >= 0) {
-      const uint8_t* rec = a.summ + ((size_t)blk * a.Hkv + kvh) * kStride;
-      mu0 = *reinterpret_cast<const uint4*>(rec + kMuOff + kg * 32);
-      mu1 = *reinterpret_cast<const uint4*>(rec + kMuOff + kg * 32 + 16);
-      c0 = *reinterpret_cast<const uint4*>(rec + kCOff + kg * 32);
-      c1 = *reinterpret_cast<const uint4*>(rec + kCOff + kg * 32 + 16);
-      if (kg == 0) scl = *reinterpret_cast<const uint2*>(rec + kSOff);
-    }
-    *reinterpret_cast<uint4*>(&T.c[row][kg * 32]) = c0;
-    *reinterpret_cast<uint4*>(&T.c[row][kg * 32 + 16]) = c1;
-    if (kg == 0) {
-      T.sc[row][0] = f16bits_to_float(scl.x);
-      T.sc[row][1] = f16bits_to_float(scl.x >> 16) * (1.0f / 16.0f) * f16bits_to_float(scl.y);
-      T.sc[row][2] = (blk >= 0) ? 1.0f : 0.0f;
-    }
-
-    // ---- stage 1: mu tile (columns = the 16 pages); lane (page row, kg) -> head 4rb + kg
-    {
-      const v4i B0 = {(int)mu0.x, (int)mu0.y, (int)mu0.z, (int)mu0.w};
-      const v4i B1 = {(int)mu1.x, (int)mu1.y, (int)mu1.z, (int)mu1.w};
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        v4i acc = mfma_i8(aop[rb][0], B0, v4i{0, 0, 0, 0});
-        acc = mfma_i8(aop[rb][1], B1, acc);
-        const int h = 4 * rb + kg;
-        T.a[row][h < G ? h : G] = (float)(acc[2] * 256 + acc[1]) * 256.0f + (float)acc[0];
-      }
-    }
+    const uint4 mu1 = *reinterpret_cast<const uint4*>(rec + kMuOff + 16);
+    __builtin_amdgcn_sched_barrier(0);
+    const uint4 mu0 = *reinterpret_cast<const uint4*>(rec + kMuOff);
+    __builtin_amdgcn_sched_barrier(0);
+    const uint4 c1 = *reinterpret_cast<const uint4*>(rec + kCOff + 16);
+    __builtin_amdgcn_sched_barrier(0);
+    const uint4 c0 = *reinterpret_cast<const uint4*>(rec + kCOff);
+    __builtin_amdgcn_sched_barrier(0);
+    const uint2 scl = *reinterpret_cast<const uint2*>(rec - kg * 32 + kSOff);
+    __builtin_amdgcn_sched_barrier(0);
+    // consumed in the order the loads were issued, so work starts on the
+    // first records while the rest are still arriving
     // ---- stage 1: V tiles (columns = (page 2vt + row/8, basis vector row%8))
 #pragma unroll
     for (int vt = 0; vt < 8; ++vt) {
@@ -234,6 +237,29 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
           T.pl[2 * vt + (row >> 3)][h < G ? h : 0][row & 7] = xl;
         }
       }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- stage 1: mu tile (columns = the 16 pages); lane (page row, kg) -> head 4rb + kg
+    {
+      const v4i B0 = {(int)mu0.x, (int)mu0.y, (int)mu0.z, (int)mu0.w};
+      const v4i B1 = {(int)mu1.x, (int)mu1.y, (int)mu1.z, (int)mu1.w};
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        v4i acc = mfma_i8(aop[rb][0], B0, v4i{0, 0, 0, 0});
+        acc = mfma_i8(aop[rb][1], B1, acc);
+        const int h = 4 * rb + kg;
+        T.a[row][h < G ? h : G] = (float)(acc[2] * 256 + acc[1]) * 256.0f + (float)acc[0];
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    *reinterpret_cast<uint4*>(&T.c[row][kg * 32]) = c0;
+    *reinterpret_cast<uint4*>(&T.c[row][kg * 32 + 16]) = c1;
+    {
+      // every lane stores (lanes kg > 0 into the spare rows), so that the
+      // scale load is issued with the others rather than behind a branch
+      const int r = kg == 0 ? row : 16 + row;
+      T.sc[r][0] = f16bits_to_float(scl.x);
+      T.sc[r][1] = f16bits_to_float(scl.x >> 16) * (1.0f / 16.0f) * f16bits_to_float(scl.y);
     }
     wave_lds_sync();
 
@@ -278,19 +304,7 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
       mx = xor32_max(xor16_max(mx));
       float ssum = fast_exp2(t0 - mx) + fast_exp2(t1 - mx) + fast_exp2(t2 - mx) + fast_exp2(t3 - mx);
       ssum = xor32_sum(xor16_sum(ssum));
-      const float shat2 = mx + fast_log2(ssum);
-      const bool valid = T.sc[pp][2] != 0.0f;
-      if (kg == 0) T.out[hc][pp] = valid ? shat2 * kLn2 : -INFINITY;  // absent pages: -inf
-      // running (max, sum) of this head, branch-free; absent pages add nothing
-      const float x = valid ? shat2 : -1e30f;
-      const float mn = fmaxf(run_m, x);
-      run_s = run_s * fast_exp2(run_m - mn) + fast_exp2(x - mn);
-      run_m = mn;
-    }
-    wave_lds_sync();
-    if ((lane >> 4) == t) {
-#pragma unroll
-      for (int h = 0; h < G; ++h) myscore[h] = T.out[h][lane & 15];
+      if (kg == 0) T.out[t * 16 + pp][hc] = mx + fast_log2(ssum);
     }
     wave_lds_sync();
   }
@@ -300,22 +314,41 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
   // covers both); whole 256-byte rows per head coalesce, and streaming
   // (non-temporal) stores keep them from sitting dirty in L2 until the end
   // of the launch
+  const bool mine = (present >> lane) & 1ull;
 #pragma unroll
-  for (int h = 0; h < G; ++h)
-    if (p0 + lane < n_b) __builtin_nontemporal_store(myscore[h], &a.scores[((size_t)b * a.Hq + (size_t)hbase + h) * N + p0 + lane]);
+  for (int h = 0; h < G; ++h) {
+    const float sc = mine ? T.out[lane][h] * kLn2 : -INFINITY;  // natural log; absent: -inf
+    if (p0 + lane < n_b) __builtin_nontemporal_store(sc, &a.scores[((size_t)b * a.Hq + (size_t)hbase + h) * N + p0 + lane]);
+  }
 
-  // ---- per-head (max, sum) over this wave's pages: lanes 0..15, head = lane % G
+  // ---- per-head (max, sum) of exp2 over the wave's pages: lane takes head
+  // lane % G and pages i * 64/G + lane / G, then lanes of one head merge
+  constexpr int LPH = kScorePagesPerWave / G;
+  float m = -INFINITY, v[G];
 #pragma unroll
-  for (int off = G; off < 16; off <<= 1) {
-    const float m2 = __shfl_xor(run_m, off), s2 = __shfl_xor(run_s, off);
-    const float mn = fmaxf(run_m, m2);
-    run_s = run_s * fast_exp2(run_m - mn) + s2 * fast_exp2(m2 - mn);
-    run_m = mn;
+  for (int i = 0; i < G; ++i) {
+    const int pg = i * LPH + lane / G;
+    v[i] = ((present >> pg) & 1ull) ? T.out[pg][lane % G] : -INFINITY;
+    m = fmaxf(m, v[i]);
+  }
+  float ssum = 0.f;
+  {
+    const float ms = m == -INFINITY ? 0.f : m;
+#pragma unroll
+    for (int i = 0; i < G; ++i) ssum += fast_exp2(v[i] - ms);
+  }
+#pragma unroll
+  for (int off = G; off < 64; off <<= 1) {
+    const float m2 = __shfl_xor(m, off), s2 = __shfl_xor(ssum, off);
+    const float mn = fmaxf(m, m2);
+    const float ms = mn == -INFINITY ? 0.f : mn;
+    ssum = ssum * fast_exp2(m - ms) + s2 * fast_exp2(m2 - ms);
+    m = mn;
   }
   if (lane < G) {
     float* dst = a.partials + (((size_t)b * a.Hq + (size_t)hbase + lane) * a.n_ranges + range) * 2;
-    dst[0] = (run_s > 0.f) ? run_m : -INFINITY;
-    dst[1] = run_s;
+    dst[0] = (ssum > 0.f) ? m : -INFINITY;
+    dst[1] = ssum;
   }
 }
 

@@ -63,7 +63,8 @@ def test_workspace_sizing_and_validation(L):
             L.workspace_bytes(dims(L, **bad), 512)
         assert e.value.status == L.ERR_UNSUPPORTED, bad
     for bad in (dict(batch=2, n_kv_heads=40000, n_q_heads=40000),
-                dict(batch=1, n_kv_heads=40000, n_q_heads=640000)):  # launch-grid limits
+                dict(batch=1, n_kv_heads=40000, n_q_heads=640000),  # launch-grid limits
+                dict(n_kv_heads=8, n_q_heads=32, num_blocks=11_000_000)):  # 32-bit record offsets
         with pytest.raises(L.LocksError) as e:
             L.workspace_bytes(dims(L, **bad), 512)
         assert e.value.status == L.ERR_UNSUPPORTED, bad
