@@ -187,34 +187,56 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
 
   wave_lds_sync();
 
-  for (int t = 0; t < kTiles; ++t) {
-    // record offsets of the tile's pages as this lane addresses them: the V
-    // row of page 2vt + row/8 for each vt, and the mu/C/scales of page row
+  // one tile's records as this lane holds them: V rows (page 2vt + row/8,
+  // basis vector row%8), and the mu, C and scales of page row
+  struct TileRec {
+    uint4 v[8], mu1, mu0, c1, c0;
+    uint2 scl;
+  };
+  // The 13 loads of tile t go out in a pinned order (the order is worth ~5%
+  // of the gather rate at 4-head groups): issue_v the 8 V rows, issue_tail
+  // the mu, C and scales after them. Offsets come from the wave's LDS table.
+  auto issue_v = [&](int t, TileRec& r) {
     uint32_t ov[8];
 #pragma unroll
     for (int vt = 0; vt < 8; ++vt) ov[vt] = S.u.off[wave][t * 16 + 2 * vt + (row >> 3)];
-    const uint32_t om = S.u.off[wave][t * 16 + row];
-    // ---- loads: V rows (page 2vt + row/8, basis vector row%8), mu, C, scales.
-    // Issued in this order, pinned (the order is worth ~5% of the gather
-    // rate at 4-head groups: the V rows first, the tail of each record last).
-    const uint8_t* rec = rbase + ((size_t)om << 4);  // page t*16 + row
     __builtin_amdgcn_sched_barrier(0);
-    uint4 vraw[8];
 #pragma unroll
     for (int vt = 0; vt < 8; ++vt) {
-      vraw[vt] = *reinterpret_cast<const uint4*>(vbase + ((size_t)ov[vt] << 4));
+      r.v[vt] = *reinterpret_cast<const uint4*>(vbase + ((size_t)ov[vt] << 4));
       __builtin_amdgcn_sched_barrier(0);
     }
-    const uint4 mu1 = *reinterpret_cast<const uint4*>(rec + kMuOff + 16);
+  };
+  auto issue_tail = [&](int t, TileRec& r) {
+    const uint32_t om = S.u.off[wave][t * 16 + row];
+    const uint8_t* rec = rbase + ((size_t)om << 4);  // page t*16 + row
     __builtin_amdgcn_sched_barrier(0);
-    const uint4 mu0 = *reinterpret_cast<const uint4*>(rec + kMuOff);
+    r.mu1 = *reinterpret_cast<const uint4*>(rec + kMuOff + 16);
     __builtin_amdgcn_sched_barrier(0);
-    const uint4 c1 = *reinterpret_cast<const uint4*>(rec + kCOff + 16);
+    r.mu0 = *reinterpret_cast<const uint4*>(rec + kMuOff);
     __builtin_amdgcn_sched_barrier(0);
-    const uint4 c0 = *reinterpret_cast<const uint4*>(rec + kCOff);
+    r.c1 = *reinterpret_cast<const uint4*>(rec + kCOff + 16);
     __builtin_amdgcn_sched_barrier(0);
-    const uint2 scl = *reinterpret_cast<const uint2*>(rec - kg * 32 + kSOff);
+    r.c0 = *reinterpret_cast<const uint4*>(rec + kCOff);
     __builtin_amdgcn_sched_barrier(0);
+    r.scl = *reinterpret_cast<const uint2*>(rec - kg * 32 + kSOff);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // With up to 4 heads per wave (little compute per byte), the next tile's V
+  // rows are issued as soon as stage 1 has consumed the current ones, so they
+  // travel during stage 2; 8-head waves are compute-bound and skip this (the
+  // extra registers cost more than the overlap gains).
+  constexpr bool kPrefetchV = G <= 4;
+  TileRec cur;
+  issue_v(0, cur);
+#pragma unroll
+  for (int t = 0; t < kTiles; ++t) {
+    if (!kPrefetchV && t > 0) issue_v(t, cur);
+    issue_tail(t, cur);
+    const uint4* vraw = cur.v;
+    const uint4 mu0 = cur.mu0, mu1 = cur.mu1, c0 = cur.c0, c1 = cur.c1;
+    const uint2 scl = cur.scl;
     // consumed in the order the loads were issued, so work starts on the
     // first records while the rest are still arriving
     // ---- stage 1: V tiles (columns = (page 2vt + row/8, basis vector row%8))
@@ -261,6 +283,7 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
       T.sc[r][0] = f16bits_to_float(scl.x);
       T.sc[r][1] = f16bits_to_float(scl.x >> 16) * (1.0f / 16.0f) * f16bits_to_float(scl.y);
     }
+    if (kPrefetchV && t + 1 < kTiles) issue_v(t + 1, cur);
     wave_lds_sync();
 
     // ---- stage 2 + LSE, one pass per PG pages
