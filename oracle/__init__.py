@@ -190,6 +190,20 @@ def build_summaries(k_cache_bits: np.ndarray, page_table: np.ndarray, seq_lens: 
     return summaries
 
 
+def build_blocks(k_cache_bits: np.ndarray, blocks, summaries: np.ndarray) -> np.ndarray:
+    """The records of the listed physical blocks (every KV head) rebuilt in a
+    copy of `summaries`, as when those pages fill (A "How LOCKS works": a
+    page's summary is built once, when its 16th token lands). Entries < 0 or
+    >= num_blocks are skipped; the other records are left as they were."""
+    kc = _as(k_cache_bits, np.uint16)
+    out = np.array(summaries, dtype=np.uint8, copy=True)
+    for blk in np.asarray(blocks, dtype=np.int64).ravel():
+        if 0 <= blk < kc.shape[0]:
+            for h in range(kc.shape[1]):
+                out[blk, h] = build_record(kc[blk, h])[0]
+    return out
+
+
 # ---------------------------------------------------------------- decode
 
 def page_score_f64(q: np.ndarray, mu: np.ndarray, V: np.ndarray, C: np.ndarray) -> float:
@@ -238,7 +252,8 @@ def select(keys: np.ndarray, k: int) -> np.ndarray:
 
 
 def attention(q, k_cache_bits, v_cache_bits, page_table, seq_lens, selected=None) -> np.ndarray:
-    """Attention over the listed pages (selected[b, kvh, :]) or, with None, every full page."""
+    """Attention over the listed pages (selected[b, kvh, :]) or, with None, every full
+    page, plus each sequence's tail (the seq_len % 16 tokens of its partly filled page)."""
     q = _as(q, np.float32)
     B, Hq, _ = q.shape
     kc = _as(k_cache_bits, np.uint16)

@@ -28,7 +28,8 @@
  * (int8) and +-7 (int4), round half to even; coefficients taken from the
  * unquantised basis; Jacobi on the 16x16 Gram of the centred keys; group key =
  * log of the group-mean normalised mass share; top-k ties to the lower page
- * id; ids output ascending.
+ * id; ids output ascending; the tokens of the last, partly filled page (no
+ * summary yet: summaries are built when a page fills) are always attended.
  */
 #include <math.h>
 #include <stdint.h>
@@ -471,10 +472,19 @@ void oracle_select(int B, int Hkv, int max_pages, const double* keys, int k, int
 /* kept pages; with every page kept it is the dense full-KV attention)  */
 /* ------------------------------------------------------------------ */
 
+/* Tokens of sequence b past its last full page: they sit in logical page
+ * n_b, which has no summary yet (a summary is built when its page fills). */
+static int tail_tokens(const int32_t* seq_lens, int b, int max_pages) {
+  int n = valid_pages(seq_lens, b, max_pages);
+  if (n >= max_pages || seq_lens[b] <= 0) return 0;
+  return seq_lens[b] - n * OP;
+}
+
 /* out[b][h][128] = softmax_t(q_h . k_t / sqrt(128)) v_t over the tokens of the
- * pages listed in sel[b][kvh][0..k) (entries < 0 or >= n_b skipped). With
- * sel == NULL every full page of the sequence is used (dense attention).
- * Heads with no token get 0. */
+ * pages listed in sel[b][kvh][0..k) (entries < 0 or >= n_b skipped) and the
+ * tail tokens of the partly filled page n_b. With sel == NULL every full page
+ * of the sequence is used (dense attention over all seq_len tokens). Heads
+ * with no token get 0. */
 void oracle_attention(int B, int Hq, int Hkv, int max_pages, int num_blocks, const float* q,
                       const uint16_t* k_cache, const uint16_t* v_cache,
                       const int32_t* page_table, const int32_t* seq_lens, const int32_t* sel,
@@ -483,21 +493,37 @@ void oracle_attention(int B, int Hq, int Hkv, int max_pages, int num_blocks, con
   const double scale = 1.0 / sqrt((double)OD);
   for (int b = 0; b < B; b++) {
     int n = valid_pages(seq_lens, b, max_pages);
+    int tail = tail_tokens(seq_lens, b, max_pages);
 #pragma omp parallel for schedule(dynamic, 1)
     for (int h = 0; h < Hq; h++) {
       int kvh = h / G;
       int npg = sel ? k : n;
-      double qd[OD];
-      for (int d = 0; d < OD; d++) qd[d] = q[((size_t)b * Hq + h) * OD + d];
-      /* pass 1: the maximum logit */
-      double m = -INFINITY;
+      /* the attended (block, token count) list: listed pages, then the tail */
+      int* blk_of = (int*)malloc(sizeof(int) * (npg + 1));
+      int* ntok_of = (int*)malloc(sizeof(int) * (npg + 1));
+      int ne = 0;
       for (int s = 0; s < npg; s++) {
         int j = sel ? sel[((size_t)b * Hkv + kvh) * k + s] : s;
         if (j < 0 || j >= n) continue;
         int blk = page_table[(size_t)b * max_pages + j];
         if (blk < 0 || blk >= num_blocks) continue;
-        const uint16_t* kt = k_cache + ((size_t)blk * Hkv + kvh) * OP * OD;
-        for (int i = 0; i < OP; i++) {
+        blk_of[ne] = blk;
+        ntok_of[ne++] = OP;
+      }
+      if (tail > 0) {
+        int blk = page_table[(size_t)b * max_pages + n];
+        if (blk >= 0 && blk < num_blocks) {
+          blk_of[ne] = blk;
+          ntok_of[ne++] = tail;
+        }
+      }
+      double qd[OD];
+      for (int d = 0; d < OD; d++) qd[d] = q[((size_t)b * Hq + h) * OD + d];
+      /* pass 1: the maximum logit */
+      double m = -INFINITY;
+      for (int e = 0; e < ne; e++) {
+        const uint16_t* kt = k_cache + ((size_t)blk_of[e] * Hkv + kvh) * OP * OD;
+        for (int i = 0; i < ntok_of[e]; i++) {
           double l = 0;
           for (int d = 0; d < OD; d++) l += qd[d] * oracle_bf16_to_double(kt[i * OD + d]);
           m = fmax(m, l * scale);
@@ -507,14 +533,10 @@ void oracle_attention(int B, int Hq, int Hkv, int max_pages, int num_blocks, con
       for (int d = 0; d < OD; d++) o[d] = 0;
       if (m > -INFINITY) {
         /* pass 2: softmax weights and the weighted sum of values */
-        for (int s = 0; s < npg; s++) {
-          int j = sel ? sel[((size_t)b * Hkv + kvh) * k + s] : s;
-          if (j < 0 || j >= n) continue;
-          int blk = page_table[(size_t)b * max_pages + j];
-          if (blk < 0 || blk >= num_blocks) continue;
-          const uint16_t* kt = k_cache + ((size_t)blk * Hkv + kvh) * OP * OD;
-          const uint16_t* vt = v_cache + ((size_t)blk * Hkv + kvh) * OP * OD;
-          for (int i = 0; i < OP; i++) {
+        for (int e = 0; e < ne; e++) {
+          const uint16_t* kt = k_cache + ((size_t)blk_of[e] * Hkv + kvh) * OP * OD;
+          const uint16_t* vt = v_cache + ((size_t)blk_of[e] * Hkv + kvh) * OP * OD;
+          for (int i = 0; i < ntok_of[e]; i++) {
             double l = 0;
             for (int d = 0; d < OD; d++) l += qd[d] * oracle_bf16_to_double(kt[i * OD + d]);
             double w = exp(l * scale - m);
@@ -525,6 +547,8 @@ void oracle_attention(int B, int Hq, int Hkv, int max_pages, int num_blocks, con
       }
       for (int d = 0; d < OD; d++)
         out[((size_t)b * Hq + h) * OD + d] = (den > 0) ? o[d] / den : 0.0;
+      free(blk_of);
+      free(ntok_of);
     }
   }
 }

@@ -196,6 +196,22 @@ def test_record_format_matches_documented_layout(orc):
     assert np.array_equal(C, cc * float(s[2]))
 
 
+def test_build_blocks_rebuilds_only_the_listed_blocks(orc):
+    """Building the records of a block list (pages that just filled) gives each
+    listed block's records as the whole-cache build does and leaves the rest."""
+    r = rng(35)
+    B, Hkv, N = 2, 2, 4
+    kb, kd, vb, vd, pt = small_cache(r, B, Hkv, N, extra=2)
+    lens = np.full(B, N * PAGE, dtype=np.int32)
+    full = orc.build_summaries(kb, pt, lens)
+    stale = np.full_like(full, 0xAB)
+    blocks = np.array([pt[1, 2], -1, pt[0, 0], kb.shape[0], pt[1, 2]], dtype=np.int32)
+    got = orc.build_blocks(kb, blocks, stale)
+    for blk in range(kb.shape[0]):
+        want = full[blk] if blk in (pt[1, 2], pt[0, 0]) else stale[blk]
+        assert np.array_equal(got[blk], want), blk
+
+
 def test_summary_payload_is_about_ten_percent(orc):
     """(A "How LOCKS works"; B mechanism 1): the summary is about 10% of the
     page's KV bytes. Payload 776 B vs 16 tokens x 128 x bf16 x (K+V)."""
@@ -277,17 +293,15 @@ def test_dense_attention_matches_sdpa(orc):
     B, Hq, Hkv, N = 2, 4, 2, 5
     kb, kd, vb, vd, pt = small_cache(r, B, Hkv, N)
     q = r.standard_normal((B, Hq, DIM)).astype(np.float32)
-    lens = np.array([N * PAGE, 3 * PAGE + 7], dtype=np.int32)  # second: ragged tail ignored
+    lens = np.array([N * PAGE, 3 * PAGE + 7], dtype=np.int32)  # second: 7-token tail
     out = orc.attention(q, kb, vb, pt, lens)
     G = Hq // Hkv
     for b in range(B):
-        n = lens[b] // PAGE
+        # every token of the sequence, i.e. its full pages and then its tail
+        flat = lambda x: x[pt[b], h // G].reshape(-1, DIM)[: lens[b]]
         for h in range(Hq):
-            blks = pt[b, :n]
-            keys = kd[blks, h // G].reshape(-1, DIM)
-            vals = vd[blks, h // G].reshape(-1, DIM)
-            assert np.allclose(out[b, h], sdpa_ref(q[b, h].astype(np.float64), keys, vals),
-                               atol=1e-12)
+            ref = sdpa_ref(q[b, h].astype(np.float64), flat(kd), flat(vd))
+            assert np.allclose(out[b, h], ref, atol=1e-12)
 
 
 def test_sparse_attention_matches_sdpa_on_gathered_tokens(orc):
@@ -305,6 +319,52 @@ def test_sparse_attention_matches_sdpa_on_gathered_tokens(orc):
         assert np.allclose(out[0, h], ref, atol=1e-12)
     empty = orc.attention(q, kb, vb, pt, lens, np.full((1, 1, 4), -1, dtype=np.int32))
     assert np.all(empty == 0)
+
+
+def test_sparse_attention_adds_the_tail_and_never_reads_past_it(orc):
+    """The partly filled page has no summary (summaries are built when a page
+    fills) and is always attended: the selected pages' tokens plus the tail's,
+    nothing after seq_len (planted NaNs there must not reach the output)."""
+    r = rng(45)
+    B, Hq, Hkv, N = 2, 4, 2, 9
+    kb, kd, vb, vd, pt = small_cache(r, B, Hkv, N)
+    q = r.standard_normal((B, Hq, DIM)).astype(np.float32)
+    lens = np.array([5 * PAGE + 11, 1 * PAGE + 1], dtype=np.int32)
+    for b in range(B):  # NaN keys and values after each sequence's last token
+        n, t = lens[b] // PAGE, lens[b] % PAGE
+        kb[pt[b, n], :, t:] = 0x7FC0
+        vb[pt[b, n], :, t:] = 0x7FC0
+        kb[pt[b, n + 1:], :] = 0x7FC0
+        vb[pt[b, n + 1:], :] = 0x7FC0
+    sel = np.array([[[0, 3, 4]] * Hkv, [[0, -1, -1]] * Hkv], dtype=np.int32)
+    out = orc.attention(q, kb, vb, pt, lens, sel)
+    G = Hq // Hkv
+    for b in range(B):
+        n, t = lens[b] // PAGE, lens[b] % PAGE
+        for h in range(Hq):
+            pages = [j for j in sel[b, h // G] if 0 <= j < n]
+            keys = np.concatenate([kd[pt[b, pages], h // G].reshape(-1, DIM),
+                                   kd[pt[b, n], h // G, :t]])
+            vals = np.concatenate([vd[pt[b, pages], h // G].reshape(-1, DIM),
+                                   vd[pt[b, n], h // G, :t]])
+            ref = sdpa_ref(q[b, h].astype(np.float64), keys, vals)
+            assert np.all(np.isfinite(out[b, h]))
+            assert np.allclose(out[b, h], ref, atol=1e-12)
+
+
+def test_tail_only_sequence_attends_its_tokens(orc):
+    """A sequence shorter than one page: no page can be selected; the output
+    is the softmax over its few tokens (one token: exactly that value row)."""
+    r = rng(47)
+    kb, kd, vb, vd, pt = small_cache(r, 1, 1, 3)
+    q = r.standard_normal((1, 2, DIM)).astype(np.float32)
+    one = orc.attention(q, kb, vb, pt, np.array([1], dtype=np.int32),
+                        np.full((1, 1, 2), -1, dtype=np.int32))
+    assert np.array_equal(one[0, 0], vd[pt[0, 0], 0, 0]) and np.array_equal(one[0, 1], vd[pt[0, 0], 0, 0])
+    five = orc.attention(q, kb, vb, pt, np.array([5], dtype=np.int32))
+    for h in range(2):
+        ref = sdpa_ref(q[0, h].astype(np.float64), kd[pt[0, 0], 0, :5], vd[pt[0, 0], 0, :5])
+        assert np.allclose(five[0, h], ref, atol=1e-12)
 
 
 # ------------------------------------------------------------ whole step
