@@ -16,9 +16,11 @@
  *      (B mechanism 3);
  *   3. keep the k = budget/16 pages with the largest key (A "Code", top-k);
  *   4. run exact softmax attention over the kept pages only, renormalised
- *      over the kept tokens (A "Code", sparse attention).
+ *      over the kept tokens (A "Code", sparse attention), plus the tokens of
+ *      the sequence's partly filled last page, which has no summary yet.
  * The summary build (A "How LOCKS works", summary list; B mechanism 1) is a
- * separate, off-critical-path call.
+ * separate, off-critical-path call, for the whole cache or for the pages that
+ * just filled.
  *
  * Conventions for every entry point:
  *  - All array arguments are DEVICE pointers owned by the caller; the library
@@ -38,10 +40,14 @@
  *  - q must be finite.
  *  - Page table: page_table[b*max_pages_per_seq + j] is the physical block
  *    that holds logical page j of sequence b. Sequence b has
- *    n_b = min(seq_lens[b] / 16, max_pages_per_seq) full pages; tokens after
- *    the last full page are ignored (summaries exist only for full pages,
- *    A "How LOCKS works"). A block id outside [0, num_blocks) marks an absent
- *    page: it is never read, never scored and never selected.
+ *    n_b = min(seq_lens[b] / 16, max_pages_per_seq) full pages. Only full
+ *    pages have summaries (a page's summary is built when its 16th token
+ *    lands, A "How LOCKS works"), so only they are scored and selected. The
+ *    t_b = seq_lens[b] - 16 n_b tokens after them (when n_b <
+ *    max_pages_per_seq) sit in logical page n_b, the tail page: attention
+ *    always includes them, and reads nothing of that page past token t_b.
+ *    A block id outside [0, num_blocks) marks an absent page: it is never
+ *    read, never scored, never selected and never attended.
  *  - Query head h uses KV head h / G, G = n_q_heads / n_kv_heads.
  *
  * Layouts (row-major, C order):
@@ -128,6 +134,20 @@ locks_status locks_build_summaries(const locks_dims* dims, const void* k_cache,
                                    const int32_t* page_table, const int32_t* seq_lens,
                                    void* summaries, hipStream_t stream);
 
+/* Builds the records of an explicit list of physical blocks, every KV head of
+ * each: the pages that just filled (A "How LOCKS works": a page's summary is
+ * built once, when its 16th token lands; B mechanism 1: when a page is
+ * finalised). Same record as locks_build_summaries writes for that block.
+ *  blocks    device i32[n_blocks]; an entry outside [0, num_blocks) is
+ *            skipped (e.g. -1 for "no page filled in this sequence"), so a
+ *            captured decode graph can pass a fixed-length list. A block
+ *            listed twice is written twice with identical bytes.
+ *  n_blocks  >= 0 (0: nothing is enqueued); blocks may be NULL only then.
+ * Records of unlisted blocks are left untouched. */
+locks_status locks_build_blocks(const locks_dims* dims, const void* k_cache,
+                                const int32_t* blocks, int32_t n_blocks, void* summaries,
+                                hipStream_t stream);
+
 /* One LOCKS decode step = locks_score_pages + locks_select_pages +
  * locks_sparse_attention on the same workspace.
  *  q            f32 queries, one token per sequence.
@@ -135,7 +155,8 @@ locks_status locks_build_summaries(const locks_dims* dims, const void* k_cache,
  *               the documented format).
  *  budget_tokens  positive multiple of 16; k = budget_tokens / 16 pages are
  *               kept per (sequence, KV head).
- *  out          f32 attention output; heads of a sequence with n_b == 0 get 0.
+ *  out          f32 attention output over the kept pages and the tail; heads of
+ *               a sequence with no token (seq_lens[b] == 0) get 0.
  *  selected     kept logical page ids per (sequence, KV head) in ascending
  *               order; when fewer than k pages exist, the tail is -1.
  *  page_scores  optional (NULL = not written): per-head page score s_hat
@@ -170,18 +191,19 @@ locks_status locks_select_pages(const locks_dims* dims, const int32_t* page_tabl
                                 size_t workspace_bytes, hipStream_t stream);
 
 /* Phase 3: exact attention over the selected pages only (A "Code": attention
- * over the gathered tokens of the kept pages, softmax scale 1/sqrt(128)).
- * `selected` may come from locks_select_pages or from the caller: entries < 0
- * or >= n_b are skipped; ids should be distinct. */
+ * over the gathered tokens of the kept pages, softmax scale 1/sqrt(128)),
+ * plus the tail page's t_b tokens. `selected` may come from
+ * locks_select_pages or from the caller: entries < 0 or >= n_b are skipped;
+ * ids should be distinct. */
 locks_status locks_sparse_attention(const locks_dims* dims, const float* q,
                                     const void* k_cache, const void* v_cache,
                                     const int32_t* page_table, const int32_t* seq_lens,
                                     int32_t budget_tokens, const int32_t* selected, float* out,
                                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Dense decode attention over every full page (A "Code": the full-KV
- * comparison; A "Results": the dense baseline the speed-ups are quoted
- * against). Same layouts and workspace rules as locks_decode_step; size the
+/* Dense decode attention over all seq_lens[b] tokens: every full page and the
+ * tail (A "Code": the full-KV comparison; A "Results": the dense baseline the
+ * speed-ups are quoted against). Same layouts and workspace rules as locks_decode_step; size the
  * workspace with budget_tokens = 16. */
 locks_status locks_dense_attention(const locks_dims* dims, const float* q, const void* k_cache,
                                    const void* v_cache, const int32_t* page_table,

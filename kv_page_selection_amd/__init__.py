@@ -58,12 +58,14 @@ def lib() -> ctypes.CDLL:
         L.locks_last_error.restype = ctypes.c_char_p
         L.locks_workspace_bytes.argtypes = [D, I, ctypes.POINTER(S)]
         L.locks_build_summaries.argtypes = [D, P, P, P, P, P]
+        L.locks_build_blocks.argtypes = [D, P, P, I, P, P]
         L.locks_decode_step.argtypes = [D, P, P, P, P, P, P, I, P, P, P, P, S, P]
         L.locks_score_pages.argtypes = [D, P, P, P, P, I, P, P, S, P]
         L.locks_select_pages.argtypes = [D, P, P, I, P, P, P, S, P]
         L.locks_sparse_attention.argtypes = [D, P, P, P, P, P, I, P, P, P, S, P]
         L.locks_dense_attention.argtypes = [D, P, P, P, P, P, P, P, S, P]
-        for name in ("locks_workspace_bytes", "locks_build_summaries", "locks_decode_step",
+        for name in ("locks_workspace_bytes", "locks_build_summaries", "locks_build_blocks",
+                     "locks_decode_step",
                      "locks_score_pages", "locks_select_pages", "locks_sparse_attention",
                      "locks_dense_attention"):
             getattr(L, name).restype = ctypes.c_int
@@ -142,6 +144,24 @@ def build_summaries(k_cache: torch.Tensor, page_table: torch.Tensor, seq_lens: t
                                 dtype=torch.uint8, device=k_cache.device)
     _check(lib().locks_build_summaries(ctypes.byref(dims), _ptr(k_cache), _ptr(page_table),
                                        _ptr(seq_lens), _ptr(summaries), _stream(k_cache.device)))
+    return summaries
+
+
+def build_blocks(k_cache: torch.Tensor, blocks: torch.Tensor, summaries: torch.Tensor) -> torch.Tensor:
+    """Rebuilds, in place, the records of the listed physical blocks (every KV
+    head): the pages that just filled. blocks: int32 [n] on the device;
+    entries outside [0, num_blocks) are skipped."""
+    _check_common(None, k_cache, torch.zeros(1, 1, dtype=torch.int32, device=k_cache.device),
+                  torch.zeros(1, dtype=torch.int32, device=k_cache.device))
+    if blocks.dtype != torch.int32 or blocks.dim() != 1 or blocks.device != k_cache.device:
+        raise ValueError("blocks must be int32 [n] on the caches' device")
+    if summaries.dtype != torch.uint8 or tuple(summaries.shape) != (
+            k_cache.shape[0], k_cache.shape[1], summary_record_bytes()):
+        raise ValueError("summaries must be uint8 [num_blocks, Hkv, 784]")
+    blocks = blocks.contiguous()
+    dims = Dims(1, k_cache.shape[1], k_cache.shape[1], HEAD_DIM, 16, 8, 1, k_cache.shape[0])
+    _check(lib().locks_build_blocks(ctypes.byref(dims), _ptr(k_cache), _ptr(blocks),
+                                    blocks.numel(), _ptr(summaries), _stream(k_cache.device)))
     return summaries
 
 

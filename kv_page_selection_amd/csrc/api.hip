@@ -42,15 +42,16 @@ bool ws_layout(const locks_dims& d, int k, WsLayout* L, const char** why) {
   }
   L->sel_chunk = (int)M;
   L->n_sel_chunks = (int)((N + M - 1) / M);
-  L->n_att_split = (k + kSparsePagesPerSplit - 1) / kSparsePagesPerSplit;
+  // list entries: k selected pages, then the tail (tokens of the partly filled page)
+  L->n_att_split = (k + 1 + kSparsePagesPerSplit - 1) / kSparsePagesPerSplit;
   if (L->n_att_split > kMaxSplits) {
     *why = "budget/16 above the sparse-attention split capacity";
     return false;
   }
-  long long dps = kDensePagesPerSplit;
-  while ((N + dps - 1) / dps > kMaxSplits) dps *= 2;
+  long long dps = kDensePagesPerSplit;  // dense list: N pages, then the tail
+  while ((N + 1 + dps - 1) / dps > kMaxSplits) dps *= 2;
   L->dense_pages_per_split = (int)dps;
-  L->n_dense_split = (int)((N + dps - 1) / dps);
+  L->n_dense_split = (int)((N + 1 + dps - 1) / dps);
   size_t off = 0;
   L->dense_part = off; off = align_up(off + (size_t)(B * Hq) * L->n_dense_split * kPartialFloats * 4);
   L->score_part = off; off = align_up(off + (size_t)(B * Hq * L->n_score_wg) * 2 * 4);
@@ -187,10 +188,29 @@ locks_status locks_build_summaries(const locks_dims* dims, const void* k_cache,
   LOCKS_TRY(need(page_table, 4, "page_table"));
   LOCKS_TRY(need(seq_lens, 4, "seq_lens"));
   LOCKS_TRY(need(summaries, 16, "summaries"));
+  if ((long long)dims->batch * dims->max_pages_per_seq * dims->n_kv_heads > (1LL << 35))
+    return fail(LOCKS_ERR_UNSUPPORTED, "batch * max_pages_per_seq * n_kv_heads above 2^35");
   (void)hipGetLastError();
   return hip_status(launch_build(*dims, static_cast<const uint16_t*>(k_cache), page_table, seq_lens,
-                                 static_cast<uint8_t*>(summaries), stream),
+                                 nullptr, 0, static_cast<uint8_t*>(summaries), stream),
                     "summary build launch");
+}
+
+locks_status locks_build_blocks(const locks_dims* dims, const void* k_cache, const int32_t* blocks,
+                                int32_t n_blocks, void* summaries, hipStream_t stream) {
+  g_err.clear();
+  LOCKS_TRY(check_dims(dims));
+  if (n_blocks < 0) return fail(LOCKS_ERR_INVALID_ARG, "n_blocks must be >= 0");
+  LOCKS_TRY(need(k_cache, 16, "k_cache"));
+  LOCKS_TRY(need(summaries, 16, "summaries"));
+  if ((long long)n_blocks * dims->n_kv_heads > (1LL << 35))
+    return fail(LOCKS_ERR_UNSUPPORTED, "n_blocks * n_kv_heads above 2^35");
+  if (n_blocks == 0) return LOCKS_OK;
+  LOCKS_TRY(need(blocks, 4, "blocks"));
+  (void)hipGetLastError();
+  return hip_status(launch_build(*dims, static_cast<const uint16_t*>(k_cache), nullptr, nullptr,
+                                 blocks, n_blocks, static_cast<uint8_t*>(summaries), stream),
+                    "block build launch");
 }
 
 locks_status locks_score_pages(const locks_dims* dims, const float* q, const void* summaries,

@@ -4,7 +4,10 @@
 // its (sequence, KV head) (blog post, "Code": attention over the gathered
 // tokens of the selected pages; softmax scale 1/sqrt(128), renormalised over
 // those tokens). Dense mode: the same over every full page, the full-KV
-// comparison of the same section.
+// comparison of the same section. Both modes also attend the sequence's tail,
+// the tokens of its partly filled last page (no summary exists for it until
+// it fills: "How LOCKS works"), as one more list entry whose rows past the
+// tail are neither read nor weighted.
 //
 // Grid (split, KV head, sequence); a split is a run of pages of the list and a
 // wave handles one page at a time for all G heads of the group:
@@ -46,7 +49,9 @@ __global__ __launch_bounds__(256) void attend_kernel(AttnArgs a) {
   const int tok = lane & 15, c = lane >> 4;
   const int N = a.N;
   const int n_b = full_pages(a.seq_lens, b, N);
-  const int list_len = a.sel ? a.k : n_b;
+  const int tail = tail_tokens(a.seq_lens, b, N);
+  const int base_len = a.sel ? a.k : n_b;  // entry base_len is the tail, if any
+  const int list_len = base_len + (tail > 0 ? 1 : 0);
   const int s0 = split * a.pages_per_split;
   const int s1 = min(s0 + a.pages_per_split, list_len);
 
@@ -58,7 +63,9 @@ __global__ __launch_bounds__(256) void attend_kernel(AttnArgs a) {
   // list, through the page table, or (dense) page s itself
   auto page_block = [&](int s) -> int {
     int blk;
-    if (a.sel_blk) {
+    if (s == base_len) {
+      blk = a.page_table[(size_t)b * N + n_b];  // the tail page (n_b < N here)
+    } else if (a.sel_blk) {
       blk = a.sel_blk[((size_t)b * a.Hkv + kvh) * a.k + s];
     } else {
       const int j = a.sel ? a.sel[((size_t)b * a.Hkv + kvh) * a.k + s] : s;
@@ -82,15 +89,16 @@ __global__ __launch_bounds__(256) void attend_kernel(AttnArgs a) {
     const int blk = blk_next;
     blk_next = (s + 4 < s1) ? page_block(s + 4) : -1;
     if (blk < 0) continue;
+    const int ntok = (s == base_len) ? tail : kPage;  // rows >= ntok: not read, not weighted
     const size_t tile = ((size_t)blk * a.Hkv + kvh) * (kPage * kDim);
     const uint4* krow = reinterpret_cast<const uint4*>(a.kc + tile + tok * kDim + c * 32);
     uint4 kr[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) kr[u] = krow[u];
+    for (int u = 0; u < 4; ++u) kr[u] = (tok < ntok) ? krow[u] : make_uint4(0u, 0u, 0u, 0u);
     uint32_t vr[kPage];
     const uint32_t* vbase = reinterpret_cast<const uint32_t*>(a.vc + tile) + lane;
 #pragma unroll
-    for (int i = 0; i < kPage; ++i) vr[i] = vbase[i * (kDim / 2)];
+    for (int i = 0; i < kPage; ++i) vr[i] = (i < ntok) ? vbase[i * (kDim / 2)] : 0u;
 
     // ---- logits of token `tok`, partial over d in [32c, 32c+32)
     float lg[G];
@@ -120,6 +128,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttnArgs a) {
     for (int h = 0; h < G; ++h) {
       float x = xor16_sum(lg[h]);  // the four d-chunks of token `tok`
       x = xor32_sum(x);
+      if (tok >= ntok) x = -INFINITY;
       const float pm = row16_reduce(x, [](float u, float v) { return fmaxf(u, v); });
       const float mn = fmaxf(m[h], pm);
       const float alpha = exp2f(m[h] - mn);  // m = -inf -> 0
@@ -201,7 +210,9 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(AttnArgs a) {
   const int li = lane & 15, lj = lane >> 4;
   const int N = a.N;
   const int n_b = full_pages(a.seq_lens, b, N);
-  const int list_len = a.sel ? a.k : n_b;
+  const int tail = tail_tokens(a.seq_lens, b, N);
+  const int base_len = a.sel ? a.k : n_b;  // entry base_len is the tail, if any
+  const int list_len = base_len + (tail > 0 ? 1 : 0);
   const int s0 = split * a.pages_per_split;
   const int s1 = min(s0 + a.pages_per_split, list_len);
 
@@ -215,7 +226,9 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(AttnArgs a) {
 
   auto page_block = [&](int s) -> int {
     int blk;
-    if (a.sel_blk) {
+    if (s == base_len) {
+      blk = a.page_table[(size_t)b * N + n_b];  // the tail page (n_b < N here)
+    } else if (a.sel_blk) {
       blk = a.sel_blk[((size_t)b * a.Hkv + kvh) * a.k + s];
     } else {
       const int j = a.sel ? a.sel[((size_t)b * a.Hkv + kvh) * a.k + s] : s;
@@ -255,14 +268,15 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(AttnArgs a) {
     const int blk = blk_next;
     blk_next = (s + 4 < s1) ? page_block(s + 4) : -1;
     if (blk < 0) continue;
+    const int ntok = (s == base_len) ? tail : kPage;  // rows >= ntok: not read, not weighted
     const size_t tile = ((size_t)blk * a.Hkv + kvh) * (kPage * kDim);
     const uint4* krow = reinterpret_cast<const uint4*>(a.kc + tile + li * kDim + 8 * lj);
     const uint4* vrow = reinterpret_cast<const uint4*>(a.vc + tile + li * kDim + 8 * lj);
     uint4 kr[4], vr[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      kr[c] = krow[4 * c];
-      vr[c] = vrow[4 * c];
+      kr[c] = (li < ntok) ? krow[4 * c] : make_uint4(0u, 0u, 0u, 0u);
+      vr[c] = (li < ntok) ? vrow[4 * c] : make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
     for (int c = 0; c < 4; ++c) *reinterpret_cast<uint4*>(&U.v[wave][li][32 * c + 8 * lj]) = vr[c];
@@ -274,7 +288,10 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(AttnArgs a) {
       sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk, qh[c], sacc, 0, 0, 0);
       sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk, ql[c], sacc, 0, 0, 0);
     }
-    // online softmax for head li over the page's 16 tokens
+    // online softmax for head li over the page's 16 tokens (4lj + r)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (4 * lj + r >= ntok) sacc[r] = -INFINITY;
     float mx = fmaxf(fmaxf(sacc[0], sacc[1]), fmaxf(sacc[2], sacc[3]));
     mx = xor32_max(xor16_max(mx));
     const float mn = fmaxf(m_run, mx);

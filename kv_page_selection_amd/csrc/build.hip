@@ -43,6 +43,7 @@ struct BuildArgs {
   const uint16_t* kc;
   const int32_t* page_table;
   const int32_t* seq_lens;
+  const int32_t* blocks;  // non-null: build these blocks (every KV head) instead
   uint8_t* summ;
   int B, Hkv, N, num_blocks;
   long long items;
@@ -154,11 +155,16 @@ __device__ __forceinline__ void jacobi_sweep(float (&a)[kPage], float (&u)[kPage
   jacobi_round<15>(a, u, i, rot);
 }
 
-// (b, j, kvh) of work item `item`; blk < 0 when there is nothing to build
+// (b, j, kvh) of work item `item` (or (list entry, kvh) for a block list);
+// blk < 0 when there is nothing to build
 __device__ __forceinline__ int item_block(const BuildArgs& a, long long item, int* kvh) {
   *kvh = 0;
   if (item >= a.items) return -1;
   *kvh = (int)(item % a.Hkv);
+  if (a.blocks) {
+    const int blk = a.blocks[item / a.Hkv];
+    return (blk >= 0 && blk < a.num_blocks) ? blk : -1;
+  }
   const long long bj = item / a.Hkv;
   const int j = (int)(bj % a.N);
   const int b = (int)(bj / a.N);
@@ -408,17 +414,20 @@ __global__ __launch_bounds__(64 * kWaves) void build_kernel(BuildArgs a) {
 }  // namespace
 
 hipError_t launch_build(const locks_dims& d, const uint16_t* kc, const int32_t* pt,
-                        const int32_t* sl, uint8_t* summ, hipStream_t s) {
+                        const int32_t* sl, const int32_t* blocks, int n_blocks, uint8_t* summ,
+                        hipStream_t s) {
   BuildArgs a;
   a.kc = kc;
   a.page_table = pt;
   a.seq_lens = sl;
+  a.blocks = blocks;
   a.summ = summ;
   a.B = d.batch;
   a.Hkv = d.n_kv_heads;
   a.N = d.max_pages_per_seq;
   a.num_blocks = d.num_blocks;
-  a.items = (long long)d.batch * d.max_pages_per_seq * d.n_kv_heads;
+  a.items = blocks ? (long long)n_blocks * d.n_kv_heads
+                   : (long long)d.batch * d.max_pages_per_seq * d.n_kv_heads;
   const long long per_wg = (long long)kWaves * kPagesPerWave;
   const long long wgs = (a.items + per_wg - 1) / per_wg;
   if (wgs <= 0) return hipSuccess;

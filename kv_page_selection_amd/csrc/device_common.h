@@ -38,6 +38,15 @@ __device__ __forceinline__ int full_pages(const int32_t* seq_lens, int b, int ma
   return n > max_pages ? max_pages : n;
 }
 
+// Tokens of sequence b after its last full page: they sit in logical page
+// full_pages(), which has no summary yet (a page's summary is built when its
+// 16th token lands); 0 when the full pages already reach max_pages.
+__device__ __forceinline__ int tail_tokens(const int32_t* seq_lens, int b, int max_pages) {
+  const int len = seq_lens[b];
+  const int n = full_pages(seq_lens, b, max_pages);
+  return (len <= 0 || n >= max_pages) ? 0 : len - n * kPage;
+}
+
 // Orders LDS traffic of one wave around a point where lanes exchange data
 // through LDS (a wave's LDS operations complete in issue order).
 __device__ __forceinline__ void wave_lds_sync() {

@@ -65,7 +65,10 @@ hipError_t launch_attend(const locks_dims& d, const WsLayout& L, const DevPtrs& 
                          const uint16_t* kc, const uint16_t* vc, const int32_t* page_table,
                          const int32_t* seq_lens, const int32_t* selected,
                          const int32_t* selected_blocks, float* out, bool dense, hipStream_t s);
+// Whole cache (blocks == nullptr: every full page through the page table) or
+// the n_blocks listed blocks, every KV head of each.
 hipError_t launch_build(const locks_dims& d, const uint16_t* kc, const int32_t* page_table,
-                        const int32_t* seq_lens, uint8_t* summ, hipStream_t s);
+                        const int32_t* seq_lens, const int32_t* blocks, int n_blocks,
+                        uint8_t* summ, hipStream_t s);
 
 }  // namespace locks

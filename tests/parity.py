@@ -30,16 +30,22 @@ def host(w: workloads.Workload):
 
 
 def compact_cache(w: workloads.Workload, sel: np.ndarray):
-    """Host bits of only the blocks the selection touches, with a page table
-    remapped onto them (unlisted pages become absent). Keeps full-size parity
+    """Host bits of only the blocks the selection (and each sequence's tail
+    page) touches, with a page table remapped onto them (unlisted pages become
+    absent). Keeps full-size parity
     cheap: the oracle reads the same bytes the GPU read."""
     pt = w.page_table.cpu().numpy()
+    sl = w.seq_lens.cpu().numpy()
     B, Hkv, k = sel.shape
+    N = pt.shape[1]
     blocks = set()
     for b in range(B):
         ids = sel[b].reshape(-1)
-        ids = ids[(ids >= 0) & (ids < pt.shape[1])]
+        ids = ids[(ids >= 0) & (ids < N)]
         blocks.update(pt[b, np.unique(ids)].tolist())
+        n = min(int(sl[b]) // 16, N)
+        if n < N and sl[b] > 16 * n:  # the tail page is attended too
+            blocks.add(int(pt[b, n]))
     blocks = sorted(b for b in blocks if 0 <= b < w.num_blocks)
     remap = -np.ones(w.num_blocks, dtype=np.int64)
     remap[blocks] = np.arange(len(blocks))

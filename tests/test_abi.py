@@ -28,7 +28,8 @@ def declared_symbols():
 
 def test_header_declares_the_boundary():
     syms = declared_symbols()
-    for name in ("locks_build_summaries", "locks_decode_step", "locks_score_pages",
+    for name in ("locks_build_summaries", "locks_build_blocks", "locks_decode_step",
+                 "locks_score_pages",
                  "locks_select_pages", "locks_sparse_attention", "locks_dense_attention",
                  "locks_workspace_bytes", "locks_summary_record_bytes", "locks_last_error"):
         assert name in syms
@@ -92,6 +93,12 @@ def test_entry_points_reject_null_and_small_workspace_on_host(L):
     assert st == L.ERR_INVALID_ARG and b"aligned" in lib.locks_last_error()
     st = lib.locks_build_summaries(ctypes.byref(d), None, fake, fake, fake, None)
     assert st == L.ERR_INVALID_ARG
+    # block-list build: n < 0 refused, n == 0 enqueues nothing, NULL list refused
+    st = lib.locks_build_blocks(ctypes.byref(d), fake, fake, -1, fake, None)
+    assert st == L.ERR_INVALID_ARG and b"n_blocks" in lib.locks_last_error()
+    assert lib.locks_build_blocks(ctypes.byref(d), fake, None, 0, fake, None) == L.OK
+    st = lib.locks_build_blocks(ctypes.byref(d), fake, None, 4, fake, None)
+    assert st == L.ERR_INVALID_ARG and b"blocks is NULL" in lib.locks_last_error()
     st = lib.locks_dense_attention(None, fake, fake, fake, fake, fake, fake, fake, 1 << 40, None)
     assert st == L.ERR_INVALID_ARG and b"dims is NULL" in lib.locks_last_error()
 

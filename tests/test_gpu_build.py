@@ -120,3 +120,31 @@ def test_full_size_build_glm_layer(locks):
     compare_builds(w, summ, n_sample=2000)
     del w, summ
     torch.cuda.empty_cache()
+
+
+def test_build_blocks_matches_whole_cache_build(locks):
+    """Rebuilding a block list (pages that just filled) writes exactly the
+    records the whole-cache build writes for those blocks and nothing else;
+    a build made only from block lists meets the oracle bars."""
+    w = workloads.make(2, device=DEV, ctx=16 * 200, batch=2, seed=9)
+    full = locks.build_summaries(w.k_cache, w.page_table, w.seq_lens)
+    pt = w.page_table.cpu().numpy()
+    stale = torch.full_like(full, 0xAB)
+    listed = [int(pt[1, 7]), -1, int(pt[0, 0]), w.num_blocks, int(pt[1, 7]), int(pt[0, 199])]
+    locks.build_blocks(w.k_cache, torch.tensor(listed, dtype=torch.int32, device=DEV), stale)
+    torch.cuda.synchronize()
+    f, g = full.cpu().numpy(), stale.cpu().numpy()
+    for blk in range(w.num_blocks):
+        if blk in listed:
+            assert np.array_equal(g[blk], f[blk]), blk
+        else:
+            assert np.all(g[blk] == 0xAB), blk
+    # every page built through block lists of 64, one list per page fill
+    fresh = torch.zeros_like(full)
+    order = torch.from_numpy(pt.T.reshape(-1).copy()).to(DEV)
+    for i in range(0, order.numel(), 64):
+        locks.build_blocks(w.k_cache, order[i:i + 64].contiguous(), fresh)
+    torch.cuda.synchronize()
+    assert torch.equal(fresh, full)
+    compare_builds(w, fresh, n_sample=400)
+

@@ -97,6 +97,57 @@ def test_edge_cases(locks):
     assert 5 not in sel[1] and 200 not in sel[1]
 
 
+def plant_nan_after_seq_len(w):
+    """bf16 NaN in every key and value row after each sequence's last token:
+    the tail page's rows past the tail and every later page of the table."""
+    pt = w.page_table.cpu().numpy()
+    sl = w.seq_lens.cpu().numpy()
+    for b in range(w.batch):
+        n = min(int(sl[b]) // 16, w.max_pages)
+        t = int(sl[b]) - 16 * n
+        for j in range(n, w.max_pages):
+            blk = int(pt[b, j])
+            if not 0 <= blk < w.num_blocks:
+                continue
+            first = t if j == n else 0
+            w.k_cache[blk, :, first:] = float("nan")
+            w.v_cache[blk, :, first:] = float("nan")
+
+
+@pytest.mark.parametrize("config,hkv,hq", [(1, 1, 1), (2, 16, 32), (2, 8, 32), (2, 4, 32), (5, 2, 32)],
+                         ids=["G1", "G2", "G4", "G8", "G16"])
+def test_tail_tokens_are_attended_and_nothing_after_seq_len_is_read(locks, config, hkv, hq):
+    """The partly filled last page has no summary: it is never scored or
+    selected, but its tokens are attended in the decode step, in sparse
+    attention on a given selection and in dense attention. Rows past seq_len
+    hold NaN; none may reach the output."""
+    w = workloads.make(config, device=DEV, ctx=16 * 160, batch=4, budget=512, n_kv_heads=hkv,
+                       n_q_heads=hq, seq_lens=[16 * 90 + 5, 16 * 160, 7, 16 * 33 + 15], seed=17)
+    plant_nan_after_seq_len(w)
+    summ = locks.build_summaries(w.k_cache, w.page_table, w.seq_lens)
+    r = decode_and_check(w, summ)
+    out = r["out"].cpu().numpy()
+    assert np.all(np.isfinite(out))
+    assert np.all(r["sel"].cpu().numpy()[2] == -1)  # 7 tokens: no full page to select
+    q, pt, sl = host(w)
+    kb, vb = workloads.bf16_bits(w.k_cache), workloads.bf16_bits(w.v_cache)
+    given = r["sel"].clone()
+    given[:, :, 1::2] = -1  # a thinner caller-provided selection
+    att = torch.empty_like(w.q)
+    ws = locks.new_workspace(locks.make_dims(w.q, w.k_cache, w.page_table), w.budget, DEV)
+    locks.sparse_attention(w.q, w.k_cache, w.v_cache, w.page_table, w.seq_lens, w.budget,
+                           given, att, ws)
+    dense = locks.dense_attention(w.q, w.k_cache, w.v_cache, w.page_table, w.seq_lens)
+    torch.cuda.synchronize()
+    for name, g, ref in (("sparse", att, oracle.attention(q, kb, vb, pt, sl, given.cpu().numpy())),
+                         ("dense", dense, oracle.attention(q, kb, vb, pt, sl))):
+        g = g.cpu().numpy()
+        assert np.all(np.isfinite(g)), name
+        err, cos = out_ok(g, ref)
+        say(f"  tail {name} G={hq // hkv}: max-abs {err:.2e} cos {cos:.7f}")
+        assert err < 1e-4, name
+
+
 def test_sparse_attention_on_given_selection(locks):
     w = workloads.make(4, device=DEV, ctx=16 * 1024, seed=3)
     q, pt, sl = host(w)
