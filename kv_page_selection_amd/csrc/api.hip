@@ -24,10 +24,15 @@ bool ws_layout(const locks_dims& d, int k, WsLayout* L, const char** why) {
   L->n_score_wg = (int)((N + kScorePagesPerWave - 1) / kScorePagesPerWave);
   {
     const int G = d.n_q_heads / d.n_kv_heads;
+    // bound units, pooled into super-ranges of S units: 64-page ranges, or
+    // 16-page tiles when there are fewer than 2k ranges (a bound over so few
+    // units prunes little: most pages would reach the merge)
+    L->bound_tiles = L->n_score_wg < 2LL * k;
+    const long long nt = (L->bound_tiles ? 4LL : 1LL) * L->n_score_wg;
     int S = 1;
-    while ((long long)G * ((L->n_score_wg + S - 1) / S) > kBoundSlots) S *= 2;
+    while ((long long)G * ((nt + S - 1) / S) > kBoundSlots) S *= 2;
     L->bound_sup = S;
-    L->bound_n_sup = (L->n_score_wg + S - 1) / S;
+    L->bound_n_sup = (int)((nt + S - 1) / S);
   }
   // select chunks of up to 1024 pages; every page's sort key fits the chunk's slots
   if (k > kSelectMaxK) {
@@ -55,6 +60,7 @@ bool ws_layout(const locks_dims& d, int k, WsLayout* L, const char** why) {
   size_t off = 0;
   L->dense_part = off; off = align_up(off + (size_t)(B * Hq) * L->n_dense_split * kPartialFloats * 4);
   L->score_part = off; off = align_up(off + (size_t)(B * Hq * L->n_score_wg) * 2 * 4);
+  L->tile_max = off;   off = align_up(off + (size_t)(B * Hq * L->n_score_wg) * 4 * 4);
   L->scores = off;     off = align_up(off + (size_t)(B * Hq * N) * 4);
   L->cand = off;       off = align_up(off + (size_t)(B * Hkv * L->n_sel_chunks) * L->sel_chunk * 8);
   L->cand_blk = off;   off = align_up(off + (size_t)(B * Hkv * L->n_sel_chunks) * L->sel_chunk * 4);
@@ -72,6 +78,7 @@ DevPtrs ws_ptrs(const locks_dims& d, const WsLayout& L, void* ws, float* page_sc
   P.ws = w;
   P.scores = page_scores ? page_scores : reinterpret_cast<float*>(w + L.scores);
   P.score_part = reinterpret_cast<float*>(w + L.score_part);
+  P.tile_max = reinterpret_cast<float*>(w + L.tile_max);
   P.cand = reinterpret_cast<unsigned long long*>(w + L.cand);
   P.cand_blk = reinterpret_cast<int32_t*>(w + L.cand_blk);
   P.cand_count = reinterpret_cast<int32_t*>(w + L.cand_count);

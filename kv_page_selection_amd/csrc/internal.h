@@ -24,6 +24,7 @@ constexpr int kPartialFloats = 130;     // (m, l, o[128]) per head and split
 struct WsLayout {
   size_t scores = 0;       // f32 [B][Hq][N]   page scores when the caller passes none
   size_t score_part = 0;   // f32 [B][Hq][n_score_wg][2]  (max, sum) per 64-page range, base 2
+  size_t tile_max = 0;     // f32 [B][Hq][4 n_score_wg]   max per 16-page tile, base 2
   size_t cand = 0;         // u64 [B][Hkv][n_sel_chunks][chunk] survivors of each chunk
   size_t cand_blk = 0;     // i32 [B][Hkv][n_sel_chunks][chunk] their physical blocks
   size_t cand_count = 0;   // i32 [B][Hkv][n_sel_chunks]
@@ -33,7 +34,8 @@ struct WsLayout {
   size_t total = 0;
   int k = 0;
   int n_score_wg = 0;
-  int bound_sup = 0, bound_n_sup = 0;  // ranges per super-range, super-ranges per head
+  bool bound_tiles = false;            // bound units: 16-page tiles (else 64-page ranges)
+  int bound_sup = 0, bound_n_sup = 0;  // units per super-range, super-ranges per head
   int sel_chunk = 0, n_sel_chunks = 0;
   int n_att_split = 0, n_dense_split = 0, dense_pages_per_split = 0;
 };
@@ -45,6 +47,7 @@ struct DevPtrs {
   uint8_t* ws;
   float* scores;
   float* score_part;
+  float* tile_max;
   unsigned long long* cand;
   int32_t* cand_blk;
   int32_t* cand_count;

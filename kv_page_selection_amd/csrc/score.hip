@@ -24,7 +24,8 @@
 // 16-token log-sum-exp is one in-lane step and two cross-row swaps, in base 2.
 // The wave keeps its 64 x G scores in LDS; at the end it writes them once and
 // leaves, per head, the (max, sum) of exp2 over its pages, which the group
-// combine needs for every head's total mass.
+// combine needs for every head's total mass, and the max of each 16-page tile,
+// the units of the selection's pruning bound.
 //
 // Loads. Each wave turns its 64 page-table entries into record offsets once
 // (an LDS table); every tile then issues its 13 record loads back to back in
@@ -50,6 +51,7 @@ struct ScoreArgs {
   const int32_t* seq_lens;
   float* scores;
   float* partials;
+  float* tile_max;
   int Hq, Hkv, N, num_blocks, n_ranges;
 };
 
@@ -373,6 +375,19 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
     dst[0] = (ssum > 0.f) ? m : -INFINITY;
     dst[1] = ssum;
   }
+  // ---- per head and 16-page tile: the max of s_hat (base 2; -inf if no page),
+  // when the selection bounds by tiles
+  if (a.tile_max && lane < kTiles * G) {
+    const int tt = lane / G, hh = lane % G;
+    float tm = -INFINITY;
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+      const int pg = tt * 16 + p;
+      if ((present >> pg) & 1ull) tm = fmaxf(tm, T.out[pg][hh]);
+    }
+    a.tile_max[((size_t)b * a.Hq + (size_t)hbase + hh) * ((size_t)a.n_ranges * kTiles) +
+               (size_t)range * kTiles + tt] = tm;
+  }
 }
 
 template <int G>
@@ -385,6 +400,7 @@ hipError_t launch_g(const locks_dims& d, const WsLayout& L, const DevPtrs& P, co
   a.seq_lens = sl;
   a.scores = P.scores;
   a.partials = P.score_part;
+  a.tile_max = L.bound_tiles ? P.tile_max : nullptr;
   a.Hq = d.n_q_heads;
   a.Hkv = d.n_kv_heads;
   a.N = d.max_pages_per_seq;

@@ -11,15 +11,17 @@
 //  1. chunk pass, grid (chunk, KV head, sequence), 1024 threads:
 //     a. bound: every workgroup folds the scoring pass's per-range (max, sum)
 //        partials (a few tens of KB, L2-resident) into L_g, and from the
-//        per-range maxima a lower bound T on the k-th largest key: every
-//        64-page range holds a page whose key is at least max_g(range max of
-//        s_hat_g - L_g) - log2 G, so the k-th largest of these per-range
-//        bounds (over distinct ranges) cannot exceed the k-th largest key. One
-//        2048-bucket histogram that keeps each bucket's smallest member gives
-//        that k-th largest bound. Ranges are pooled into super-ranges when the
-//        (head, range) maxima exceed what LDS holds (the maximum over a
-//        super-range still bounds one of its pages). Computing this in every
-//        workgroup costs less than a launch of its own.
+//        maxima of s_hat over bound units (the 64-page ranges, or 16-page
+//        tiles when a sequence has fewer than 2k ranges) a lower bound T on
+//        the k-th largest key: every unit holds a page whose key is at least
+//        max_g(unit max of s_hat_g - L_g) - log2 G, so the k-th largest of
+//        these per-unit bounds (over distinct units) cannot exceed the k-th
+//        largest key. One 2048-bucket histogram that keeps each bucket's
+//        smallest member gives that k-th largest bound. Units are pooled into
+//        super-ranges when the (head, unit) maxima exceed what LDS holds (the
+//        maximum over a super-range still bounds one of its pages).
+//        Computing this in every workgroup costs less than a launch of its
+//        own.
 //     b. the keys of the workgroup's <= 4096 pages as 64-bit sort keys
 //        (order-preserving key bits << 32 | ~page id, so one integer
 //        comparison applies "larger key, then lower id"); those with key >= T
@@ -53,6 +55,7 @@ constexpr int kMergeEpt = kSelectMaxElems / kThreads;     // 8 candidates per th
 struct SelectArgs {
   const float* scores;
   const float* score_part;
+  const float* tile_max;
   const int32_t* page_table;
   const int32_t* seq_lens;
   unsigned long long* cand;
@@ -60,7 +63,7 @@ struct SelectArgs {
   int32_t* cand_count;
   int32_t* selected;
   int32_t* sel_blk;
-  int Hq, Hkv, N, k, n_ranges, sup, n_sup, chunk, n_chunks;
+  int Hq, Hkv, N, k, n_ranges, n_tiles, sup, n_sup, chunk, n_chunks;
 };
 
 struct BoundLds {
@@ -193,7 +196,7 @@ __global__ __launch_bounds__(kThreads) void select_chunk_kernel(SelectArgs a) {
   constexpr int kLbPt = kBoundSlots / G / kThreads;  // super-ranges per thread at most
   const int chunk = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int N = a.N, nr = a.n_ranges, S = a.sup, nR = a.n_sup;
+  const int N = a.N, nr = a.n_ranges, nt = a.n_tiles, S = a.sup, nR = a.n_sup;
   const int n_b = full_pages(a.seq_lens, b, N);
   const size_t head = (size_t)b * a.Hkv + kvh;
   __shared__ ChunkShared sh;
@@ -224,6 +227,7 @@ __global__ __launch_bounds__(kThreads) void select_chunk_kernel(SelectArgs a) {
   }
   const float2* part =
       reinterpret_cast<const float2*>(a.score_part) + ((size_t)b * a.Hq + (size_t)kvh * G + g) * nr;
+  const bool tiles = a.tile_max != nullptr;  // bound units: tiles, else the ranges
   float lm = -1e30f, ls = 0.f;
   for (int r0 = 0; r0 < nr; r0 += 8 * P) {
     float2 v[8];
@@ -237,10 +241,33 @@ __global__ __launch_bounds__(kThreads) void select_chunk_kernel(SelectArgs a) {
       const int r = r0 + j + i * P;
       const bool ne = v[i].y > 0.f;  // range holds a present page
       if (ne) lse2_acc(lm, ls, v[i].x, v[i].y);
+      if (tiles) continue;
       if (S == 1) {
         if (r < nr) sh.bound.msup[g * nR + r] = ne ? key_order_bits(v[i].x) : 0u;
       } else if (ne) {
         atomicMax(&sh.bound.msup[g * nR + r / S], key_order_bits(v[i].x));
+      }
+    }
+  }
+  // tile units: the 16-page tiles' maxima (-inf: no present page)
+  if (tiles) {
+    const float* tmx = a.tile_max + ((size_t)b * a.Hq + (size_t)kvh * G + g) * nt;
+    for (int u0 = 0; u0 < nt; u0 += 8 * P) {
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int u = u0 + j + i * P;
+        v[i] = (u < nt) ? tmx[u] : -INFINITY;
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int u = u0 + j + i * P;
+        const bool ne = v[i] > -INFINITY;
+        if (S == 1) {
+          if (u < nt) sh.bound.msup[g * nR + u] = ne ? key_order_bits(v[i]) : 0u;
+        } else if (ne) {
+          atomicMax(&sh.bound.msup[g * nR + u / S], key_order_bits(v[i]));
+        }
       }
     }
   }
@@ -280,7 +307,7 @@ __global__ __launch_bounds__(kThreads) void select_chunk_kernel(SelectArgs a) {
   big_reduce3(cnt, lo, hi, sh.red3);
   float tlb;
   if ((int)cnt < a.k) {
-    tlb = -INFINITY;  // fewer ranges than k: no pruning
+    tlb = -INFINITY;  // fewer bound units than k: no pruning
   } else if (lo == hi) {
     tlb = key_from_order_bits(lo) - 1e-3f;
   } else {
@@ -699,6 +726,7 @@ hipError_t launch_select(const locks_dims& d, const WsLayout& L, const DevPtrs& 
   SelectArgs a;
   a.scores = P.scores;
   a.score_part = P.score_part;
+  a.tile_max = L.bound_tiles ? P.tile_max : nullptr;
   a.page_table = pt;
   a.seq_lens = sl;
   a.cand = P.cand;
@@ -711,6 +739,7 @@ hipError_t launch_select(const locks_dims& d, const WsLayout& L, const DevPtrs& 
   a.N = d.max_pages_per_seq;
   a.k = L.k;
   a.n_ranges = L.n_score_wg;
+  a.n_tiles = 4 * L.n_score_wg;
   a.sup = L.bound_sup;
   a.n_sup = L.bound_n_sup;
   a.chunk = L.sel_chunk;
