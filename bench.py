@@ -273,6 +273,58 @@ def main():
     score_us, select_us, attend_us = phase_us["score"], phase_us["select"], phase_us["attend"]
     score_gbs = sb / (score_us * 1e-6) / 1e9
 
+    # ---- page-fill build: the records of one just-filled block per sequence
+    # (every KV head), as a decode graph runs it when its pages fill; timed
+    # like the phases (graph of back-to-back launches)
+    fill_blocks = w.page_table[:, N // 2].contiguous()
+    fill_summ = torch.zeros_like(summ)
+
+    def fill_fn(r):
+        locks.build_blocks(reps[r][1], fill_blocks, fill_summ)
+
+    g = phase_graph(fill_fn)
+    g.replay()
+    torch.cuda.synchronize()
+    samples = []
+    for _ in range(5):
+        ts.record()
+        g.replay()
+        te.record()
+        torch.cuda.synchronize()
+        samples.append(ts.elapsed_time(te) * 1e3 / PHASE_REPS)
+    fill_us = float(np.median(samples))
+    del g
+
+    # ---- the same step with a ragged tail (seq_len - 5 tokens: 11 tokens on
+    # the partly filled last page, attended on top of the selected pages)
+    sl_tail = (w.seq_lens - 5).clamp(min=0)
+
+    def step_tail(r):
+        s_, kc_, vc_ = reps[r]
+        locks.decode_step(w.q, s_, kc_, vc_, w.page_table, sl_tail, w.budget,
+                          out=outs[r], selected=sels[r], workspace=ws[r])
+
+    tgraphs = []
+    for r in range(R):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step_tail(r)
+        tgraphs.append(g)
+    for i in range(args.warmup):
+        tgraphs[i % R].replay()
+    torch.cuda.synchronize()
+    ts.record()
+    for i in range(args.steps):
+        tgraphs[i % R].replay()
+    te.record()
+    torch.cuda.synchronize()
+    tail_step_us = ts.elapsed_time(te) * 1e3 / args.steps
+    del tgraphs
+    # restore the full-page selection for anything below that reads it
+    for i in range(R):
+        graphs[i].replay()
+    torch.cuda.synchronize()
+
     traffic = None
     if os.path.exists(PROFILE_TRAFFIC):
         t = json.load(open(PROFILE_TRAFFIC))
@@ -369,6 +421,9 @@ def main():
         "page_heads_scored_per_s": round(B * Hkv * N / (step_ms * 1e-3), 1),
         "phases_us": {"score": round(score_us, 2), "select": round(select_us, 2),
                       "attend": round(attend_us, 2)},
+        "page_fill_build": {"us": round(fill_us, 2), "page_heads": B * Hkv,
+                            "blocks": "one per sequence, every KV head"},
+        "ragged_tail_step": {"us_per_step": round(tail_step_us, 2), "tail_tokens": "seq_len % 16 = 11"},
         "summary_build": {"us": round(build_us, 1), "page_heads": B * Hkv * N,
                           "page_heads_per_s": round(B * Hkv * N / (build_us * 1e-6), 1)},
         "dense": dense,

@@ -173,16 +173,21 @@ __device__ __forceinline__ int item_block(const BuildArgs& a, long long item, in
   return (blk >= 0 && blk < a.num_blocks) ? blk : -1;
 }
 
+// PPW pages per wave: 4 for throughput; 1 when there are few items (a list of
+// pages that just filled), so phases 1 and 3, which walk a wave's pages one
+// after another, take a quarter of the time and more waves share the work.
+template <int PPW>
 __global__ __launch_bounds__(64 * kWaves) void build_kernel(BuildArgs a) {
+  static_assert(PPW == 1 || PPW == kPagesPerWave, "pages per wave");
   __shared__ WaveLds lds_all[kWaves];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   WaveLds& S = lds_all[wave];
-  const long long item0 = ((long long)blockIdx.x * kWaves + wave) * kPagesPerWave;
+  const long long item0 = ((long long)blockIdx.x * kWaves + wave) * PPW;
   const int ti = lane & 15, kg = lane >> 4;
 
   // ================================================ 1. centroid, deviations, Gram
 #pragma unroll 1
-  for (int pg = 0; pg < kPagesPerWave; ++pg) {
+  for (int pg = 0; pg < PPW; ++pg) {
     int kvh;
     const int blk = item_block(a, item0 + pg, &kvh);
     float kf[32];
@@ -225,6 +230,7 @@ __global__ __launch_bounds__(64 * kWaves) void build_kernel(BuildArgs a) {
   // ================================================ 2. four eigenproblems, 16 lanes each
   {
     const int pg = lane >> 4, i = lane & 15;
+    const bool live = pg < PPW;  // lanes of unused page slots do not vote
     float a_[kPage], u_[kPage];
 #pragma unroll
     for (int tt = 0; tt < kPage; ++tt) {
@@ -239,7 +245,7 @@ __global__ __launch_bounds__(64 * kWaves) void build_kernel(BuildArgs a) {
       const auto add = [](float x, float y) { return x + y; };
       off = row16_reduce(off, add);
       tot = row16_reduce(tot, add);
-      if (__ballot(off > kOffTol * tot) == 0) break;  // all 4 pages converged
+      if (__ballot(live && off > kOffTol * tot) == 0) break;  // every page converged
       jacobi_sweep(a_, u_, i, S.rot[pg]);
     }
     S.diag[pg][i] = a_[0];
@@ -264,7 +270,7 @@ __global__ __launch_bounds__(64 * kWaves) void build_kernel(BuildArgs a) {
 
   // ================================================ 3. basis, coefficients, codes, record
 #pragma unroll 1
-  for (int pg = 0; pg < kPagesPerWave; ++pg) {
+  for (int pg = 0; pg < PPW; ++pg) {
     int kvh;
     const int blk = item_block(a, item0 + pg, &kvh);
     if (blk < 0) continue;  // wave-uniform
@@ -428,10 +434,15 @@ hipError_t launch_build(const locks_dims& d, const uint16_t* kc, const int32_t* 
   a.num_blocks = d.num_blocks;
   a.items = blocks ? (long long)n_blocks * d.n_kv_heads
                    : (long long)d.batch * d.max_pages_per_seq * d.n_kv_heads;
-  const long long per_wg = (long long)kWaves * kPagesPerWave;
+  // few items (up to one page per wave of a full chip): latency mode
+  const bool few = a.items <= 4096;
+  const long long per_wg = (long long)kWaves * (few ? 1 : kPagesPerWave);
   const long long wgs = (a.items + per_wg - 1) / per_wg;
   if (wgs <= 0) return hipSuccess;
-  hipLaunchKernelGGL(build_kernel, dim3((unsigned)wgs), dim3(64 * kWaves), 0, s, a);
+  if (few)
+    hipLaunchKernelGGL(build_kernel<1>, dim3((unsigned)wgs), dim3(64 * kWaves), 0, s, a);
+  else
+    hipLaunchKernelGGL(build_kernel<kPagesPerWave>, dim3((unsigned)wgs), dim3(64 * kWaves), 0, s, a);
   return hipGetLastError();
 }
 
