@@ -223,6 +223,19 @@ def exact_page_lse(q: np.ndarray, keys: np.ndarray) -> float:
                                              _ptr(_as(keys, np.float64))))
 
 
+def exact_scores(q, k_cache_bits, page_table, seq_lens) -> np.ndarray:
+    """Exact page scores log sum_i exp(q.k_i / sqrt(128)) over every full page's
+    real keys (the exact-mass selector; -inf for absent pages and j >= n_b)."""
+    q = _as(q, np.float32)
+    B, Hq, _ = q.shape
+    kc = _as(k_cache_bits, np.uint16)
+    pt = _as(page_table, np.int32)
+    out = np.zeros((B, Hq, pt.shape[1]))
+    lib().oracle_exact_scores(B, Hq, kc.shape[1], pt.shape[1], kc.shape[0], _ptr(q), _ptr(kc),
+                              _ptr(pt), _ptr(_as(seq_lens, np.int32)), _ptr(out))
+    return out
+
+
 def scores(q, summaries, page_table, seq_lens, num_kv_heads: int) -> np.ndarray:
     """s_hat[b, h, j] (float64; -inf for absent pages and j >= n_b)."""
     q = _as(q, np.float32)

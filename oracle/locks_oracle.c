@@ -394,6 +394,37 @@ void oracle_scores(int B, int Hq, int Hkv, int max_pages, int num_blocks, const 
   }
 }
 
+/* Exact page scores: the log-sum-exp of q.k/sqrt(d) over every full page's
+ * real keys (the exact-mass selector that Theorem 1 compares LOCKS against,
+ * A "How LOCKS works"; B section 3). scores: [B][Hq][max_pages]; pages
+ * j >= n_b and absent pages get -inf. */
+void oracle_exact_scores(int B, int Hq, int Hkv, int max_pages, int num_blocks, const float* q,
+                         const uint16_t* k_cache, const int32_t* page_table,
+                         const int32_t* seq_lens, double* scores) {
+  int G = Hq / Hkv;
+  for (int b = 0; b < B; b++) {
+    int n = valid_pages(seq_lens, b, max_pages);
+#pragma omp parallel for schedule(dynamic, 64)
+    for (int u = 0; u < max_pages * Hkv; u++) {
+      int j = u / Hkv, kvh = u % Hkv;
+      int blk = (j < n) ? page_table[(size_t)b * max_pages + j] : -1;
+      int present = blk >= 0 && blk < num_blocks;
+      double keys[OP * OD];
+      if (present) {
+        const uint16_t* kt = k_cache + ((size_t)blk * Hkv + kvh) * OP * OD;
+        for (int x = 0; x < OP * OD; x++) keys[x] = oracle_bf16_to_double(kt[x]);
+      }
+      for (int g = 0; g < G; g++) {
+        int h = kvh * G + g;
+        double qd[OD];
+        for (int d = 0; d < OD; d++) qd[d] = q[((size_t)b * Hq + h) * OD + d];
+        scores[((size_t)b * Hq + h) * max_pages + j] =
+            present ? oracle_exact_page_lse(qd, keys) : -INFINITY;
+      }
+    }
+  }
+}
+
 /* ------------------------------------------------------------------ */
 /* Group-shared selection (B mechanism 3) and top-k (A "Code")          */
 /* ------------------------------------------------------------------ */

@@ -223,6 +223,27 @@ def test_summary_payload_is_about_ten_percent(orc):
 
 # ------------------------------------------------------------ group keys + top-k
 
+def test_exact_scores_match_scipy_logsumexp_on_real_keys(orc):
+    """The exact-mass selector's page scores: scipy's logsumexp over each full
+    page's real keys; absent pages and pages past the full ones are -inf."""
+    r = rng(29)
+    B, Hq, Hkv, N = 2, 4, 2, 6
+    kb, kd, vb, vd, pt = small_cache(r, B, Hkv, N)
+    q = r.standard_normal((B, Hq, DIM)).astype(np.float32)
+    lens = np.array([N * PAGE, 3 * PAGE + 9], dtype=np.int32)
+    pt[0, 2] = -1
+    got = orc.exact_scores(q, kb, pt, lens)
+    G = Hq // Hkv
+    for b in range(B):
+        for h in range(Hq):
+            for j in range(N):
+                if j >= lens[b] // PAGE or pt[b, j] < 0:
+                    assert got[b, h, j] == -np.inf
+                else:
+                    ref = exact_lse(q[b, h].astype(np.float64), kd[pt[b, j], h // G])
+                    assert abs(got[b, h, j] - ref) < 1e-12
+
+
 def test_group_keys_are_log_mean_shares(orc):
     r = rng(21)
     B, Hkv, G, N = 2, 3, 4, 37
