@@ -181,6 +181,20 @@ locks_status locks_score_pages(const locks_dims* dims, const float* q, const voi
                                int32_t budget_tokens, float* page_scores, void* workspace,
                                size_t workspace_bytes, hipStream_t stream);
 
+/* Reference selector: the exact page masses, s*[b][h][j] = log sum_i
+ * exp(q_h . k_i / sqrt(128)) over the 16 real keys of every full page — the
+ * exact mass selection that Theorem 1 bounds LOCKS's coverage against (A "How
+ * LOCKS works", Theorem 1; B section 3). It reads every key (4 KiB per
+ * page-head), so it is a quality reference, not a decode path. It leaves the
+ * workspace as locks_score_pages does, so locks_select_pages and
+ * locks_sparse_attention can follow it unchanged (then selecting by exact
+ * mass). Same arguments as locks_score_pages with k_cache (bf16, 16-byte
+ * aligned) in place of the summaries; q must be 16-byte aligned. */
+locks_status locks_exact_score_pages(const locks_dims* dims, const float* q, const void* k_cache,
+                                     const int32_t* page_table, const int32_t* seq_lens,
+                                     int32_t budget_tokens, float* page_scores, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream);
+
 /* Phase 2: group combine (B mechanism 3: every head's mass share averaged over
  * the GQA group) and top-k (A "Code": top-k by score, ids sorted ascending).
  * Ties between equal keys go to the lower page id. Must follow

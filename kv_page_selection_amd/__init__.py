@@ -61,12 +61,14 @@ def lib() -> ctypes.CDLL:
         L.locks_build_blocks.argtypes = [D, P, P, I, P, P]
         L.locks_decode_step.argtypes = [D, P, P, P, P, P, P, I, P, P, P, P, S, P]
         L.locks_score_pages.argtypes = [D, P, P, P, P, I, P, P, S, P]
+        L.locks_exact_score_pages.argtypes = [D, P, P, P, P, I, P, P, S, P]
         L.locks_select_pages.argtypes = [D, P, P, I, P, P, P, S, P]
         L.locks_sparse_attention.argtypes = [D, P, P, P, P, P, I, P, P, P, S, P]
         L.locks_dense_attention.argtypes = [D, P, P, P, P, P, P, P, S, P]
         for name in ("locks_workspace_bytes", "locks_build_summaries", "locks_build_blocks",
                      "locks_decode_step",
-                     "locks_score_pages", "locks_select_pages", "locks_sparse_attention",
+                     "locks_score_pages", "locks_exact_score_pages", "locks_select_pages",
+                     "locks_sparse_attention",
                      "locks_dense_attention"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -193,6 +195,18 @@ def score_pages(q, summaries, k_cache, page_table, seq_lens, budget_tokens: int,
     _check(lib().locks_score_pages(ctypes.byref(dims), _ptr(q), _ptr(summaries), _ptr(page_table),
                                    _ptr(seq_lens), int(budget_tokens), _ptr(page_scores),
                                    _ptr(workspace), workspace.numel(), _stream(q.device)))
+
+
+def exact_score_pages(q, k_cache, page_table, seq_lens, budget_tokens: int, workspace,
+                      page_scores=None):
+    """Reference phase 1: exact page masses from the keys (then select_pages
+    selects by exact mass)."""
+    _check_common(q, k_cache, page_table, seq_lens)
+    dims = make_dims(q, k_cache, page_table)
+    _check(lib().locks_exact_score_pages(ctypes.byref(dims), _ptr(q), _ptr(k_cache),
+                                         _ptr(page_table), _ptr(seq_lens), int(budget_tokens),
+                                         _ptr(page_scores), _ptr(workspace), workspace.numel(),
+                                         _stream(q.device)))
 
 
 def select_pages(q, k_cache, page_table, seq_lens, budget_tokens: int, selected, workspace,

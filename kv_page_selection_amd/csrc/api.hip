@@ -242,6 +242,28 @@ locks_status locks_score_pages(const locks_dims* dims, const float* q, const voi
                     "score launch");
 }
 
+locks_status locks_exact_score_pages(const locks_dims* dims, const float* q, const void* k_cache,
+                                     const int32_t* page_table, const int32_t* seq_lens,
+                                     int32_t budget_tokens, float* page_scores, void* workspace,
+                                     size_t workspace_bytes, hipStream_t stream) {
+  g_err.clear();
+  LOCKS_TRY(check_dims(dims));
+  LOCKS_TRY(check_budget(budget_tokens));
+  LOCKS_TRY(need(q, 16, "q"));
+  LOCKS_TRY(need(k_cache, 16, "k_cache"));
+  LOCKS_TRY(need(page_table, 4, "page_table"));
+  LOCKS_TRY(need(seq_lens, 4, "seq_lens"));
+  if (page_scores) LOCKS_TRY(need(page_scores, 4, "page_scores"));
+  WsLayout L;
+  LOCKS_TRY(layout(dims, budget_tokens, &L));
+  LOCKS_TRY(check_ws(L, workspace, workspace_bytes));
+  const DevPtrs P = ws_ptrs(*dims, L, workspace, page_scores);
+  (void)hipGetLastError();
+  return hip_status(launch_exact_score(*dims, L, P, q, static_cast<const uint16_t*>(k_cache),
+                                       page_table, seq_lens, stream),
+                    "exact score launch");
+}
+
 locks_status locks_select_pages(const locks_dims* dims, const int32_t* page_table,
                                 const int32_t* seq_lens, int32_t budget_tokens, int32_t* selected,
                                 const float* page_scores, void* workspace, size_t workspace_bytes,

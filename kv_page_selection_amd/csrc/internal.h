@@ -61,6 +61,11 @@ DevPtrs ws_ptrs(const locks_dims& d, const WsLayout& L, void* ws, float* page_sc
 hipError_t launch_score(const locks_dims& d, const WsLayout& L, const DevPtrs& P, const float* q,
                         const uint8_t* summ, const int32_t* page_table, const int32_t* seq_lens,
                         hipStream_t s);
+// Exact-mass scores from the keys themselves (the reference selector); same
+// workspace outputs as launch_score.
+hipError_t launch_exact_score(const locks_dims& d, const WsLayout& L, const DevPtrs& P,
+                              const float* q, const uint16_t* kc, const int32_t* page_table,
+                              const int32_t* seq_lens, hipStream_t s);
 hipError_t launch_select(const locks_dims& d, const WsLayout& L, const DevPtrs& P,
                          const int32_t* page_table, const int32_t* seq_lens, int32_t* selected,
                          hipStream_t s);
