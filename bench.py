@@ -119,6 +119,8 @@ def main():
     ap.add_argument("--replicas", type=int, default=0, help="0 = enough to exceed 1 GB per cycle")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-quality", action="store_true",
+                    help="skip the selection-quality comparison with the exact-mass selector")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="host time the oracle baseline repeats the step for")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -332,6 +334,57 @@ def main():
                 and t.get("workload") == w.recipe):
             traffic = t.get("hbm_bytes_per_launch")
 
+    # ---- selection quality against the exact-mass selector (Theorem 1's
+    # reference): exact page masses from the keys, then the same select pass;
+    # coverage = the exact group mass the LOCKS selection keeps / the mass the
+    # exact selection keeps, per (sequence, KV head); recall = shared pages / k
+    quality = None
+    if not args.no_quality:
+        ex_scores = torch.empty(B, Hq, N, device=dev)
+        ex_sel = torch.empty_like(sels[0])
+        locks.exact_score_pages(w.q, reps[0][1], w.page_table, w.seq_lens, w.budget, ws[0],
+                                page_scores=ex_scores)
+        locks.select_pages(w.q, reps[0][1], w.page_table, w.seq_lens, w.budget, ex_sel, ws[0],
+                           page_scores=ex_scores)
+        torch.cuda.synchronize()
+        ex_ms = []
+        for i in range(3):
+            ts.record()
+            locks.exact_score_pages(w.q, reps[i % R][1], w.page_table, w.seq_lens, w.budget,
+                                    ws[0], page_scores=ex_scores)
+            te.record()
+            torch.cuda.synchronize()
+            ex_ms.append(ts.elapsed_time(te))
+        graphs[0].replay()  # the LOCKS selection of replica 0 (same inputs as above)
+        torch.cuda.synchronize()
+        es = ex_scores.double().cpu().numpy()
+        nb = np.minimum(w.seq_lens.cpu().numpy() // 16, N)
+        for b in range(B):
+            es[b, :, nb[b]:] = -np.inf
+        G = Hq // Hkv
+        L = np.log(np.exp(es - es.max(-1, keepdims=True)).sum(-1, keepdims=True)) + es.max(-1, keepdims=True)
+        share = np.exp(es - L).reshape(B, Hkv, G, N).mean(2)  # exact group mass share per page
+        ls, xs = sels[0].cpu().numpy(), ex_sel.cpu().numpy()
+        cov, rec = [], []
+        for b in range(B):
+            for h in range(Hkv):
+                a_ = ls[b, h][ls[b, h] >= 0]
+                x_ = xs[b, h][xs[b, h] >= 0]
+                if len(x_) == 0:
+                    continue
+                cov.append(share[b, h, a_].sum() / share[b, h, x_].sum())
+                rec.append(len(np.intersect1d(a_, x_)) / len(x_))
+        quality = {"exact_selector_us": round(float(np.median(ex_ms)) * 1e3, 1),
+                   "mass_coverage_min": round(float(np.min(cov)), 5),
+                   "mass_coverage_mean": round(float(np.mean(cov)), 5),
+                   "recall_mean": round(float(np.mean(rec)), 4),
+                   "groups": len(cov)}
+        if w.carrier is not None:
+            car = w.carrier.cpu().numpy()
+            quality["carrier_retained"] = float(np.mean(
+                [car[b] in ls[b, h] for b in range(B) for h in range(Hkv) if car[b] >= 0]))
+        del ex_scores, ex_sel
+
     # ---- dense flash-decode comparator on the same caches
     dense = None
     if not args.no_dense:
@@ -427,6 +480,7 @@ def main():
         "summary_build": {"us": round(build_us, 1), "page_heads": B * Hkv * N,
                           "page_heads_per_s": round(B * Hkv * N / (build_us * 1e-6), 1)},
         "dense": dense,
+        "selection_vs_exact_mass": quality,
         "roofline": {"bound": "hbm", "kernel": "score_kernel", "achieved": round(score_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(score_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "algorithmic_bytes_per_launch": sb,
