@@ -490,5 +490,113 @@ def main():
     print(json.dumps(line), flush=True)
 
 
+def sweep(args):
+    """Batch-scaling sweep with variable sequence lengths (not the default
+    line): per batch size, L decode layers (independent caches) in one graph,
+    sequence lengths seeded log-uniform in [32K, 512K) tokens and not page
+    multiples (every sequence has a tail). One JSON line per batch size."""
+    import numpy as np
+    import torch
+
+    import kv_page_selection_amd as locks
+    import workloads
+
+    dev = torch.device("cuda:0")
+    L = args.layers
+    budget = 2048
+    for B in [int(x) for x in args.sweep.split(",")]:
+        rng = np.random.default_rng(7000 + B)
+        lens = np.exp(rng.uniform(np.log(32768), np.log(524288), B)).astype(np.int64)
+        lens = lens - lens % 16 + rng.integers(1, 16, B)  # ragged tails
+        ctx = int((lens.max() + 15) // 16 * 16)
+        print(f"[sweep] batch {B}: generating {L} layers, max seq_len {int(lens.max())}",
+              file=sys.stderr, flush=True)
+        layers = [workloads.make(2, device=dev, ctx=ctx, batch=B, budget=budget, seed=8000 + 10 * B + l,
+                                 seq_lens=[int(x) for x in lens]) for l in range(L)]
+        w0 = layers[0]
+        Hq, Hkv, N, k = w0.n_q_heads, w0.n_kv_heads, w0.max_pages, w0.k_pages
+        nb = np.minimum(lens // 16, N)
+        summs = [locks.build_summaries(w.k_cache, w.page_table, w.seq_lens) for w in layers]
+        dims = locks.make_dims(w0.q, w0.k_cache, w0.page_table)
+        scored = int(nb.sum()) * Hkv
+        step_bytes = L * (scored * REC_PAYLOAD + int(nb.sum()) * 4 +
+                          B * Hkv * min(k, int(nb.min())) * 8192 + B * Hq * 128 * 8)
+        R = max(1, math.ceil(1.0e9 / step_bytes))
+        sets = [[(summs[l], layers[l].k_cache, layers[l].v_cache) for l in range(L)]]
+        for _ in range(R - 1):
+            sets.append([(s_.clone(), kc.clone(), vc.clone()) for s_, kc, vc in sets[0]])
+        ws = [locks.new_workspace(dims, budget, dev) for _ in range(L)]
+        outs = [torch.empty_like(w0.q) for _ in range(L)]
+        sels = [torch.empty(B, Hkv, k, dtype=torch.int32, device=dev) for _ in range(L)]
+
+        def model_step(r):
+            for l, (s_, kc, vc) in enumerate(sets[r]):
+                w = layers[l]
+                locks.decode_step(w.q, s_, kc, vc, w.page_table, w.seq_lens, budget,
+                                  out=outs[l], selected=sels[l], workspace=ws[l])
+
+        cs = torch.cuda.Stream()
+        cs.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cs):
+            model_step(0)
+        torch.cuda.current_stream().wait_stream(cs)
+        torch.cuda.synchronize()
+        graphs = []
+        for r in range(R):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                model_step(r)
+            graphs.append(g)
+        for i in range(10):
+            graphs[i % R].replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n = max(20, args.steps // 4)
+        e0.record()
+        for i in range(n):
+            graphs[i % R].replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / n
+        # dense comparator over the same layers (all seq_len tokens)
+        dws = locks.new_workspace(dims, 16, dev)
+        dout = torch.empty_like(w0.q)
+        for r in range(min(R, 2)):
+            for l, (s_, kc, vc) in enumerate(sets[r]):
+                locks.dense_attention(layers[l].q, kc, vc, layers[l].page_table, layers[l].seq_lens,
+                                      out=dout, workspace=dws)
+        torch.cuda.synchronize()
+        nd = 5
+        e0.record()
+        for i in range(nd):
+            for l, (s_, kc, vc) in enumerate(sets[i % R]):
+                locks.dense_attention(layers[l].q, kc, vc, layers[l].page_table, layers[l].seq_lens,
+                                      out=dout, workspace=dws)
+        e1.record()
+        torch.cuda.synchronize()
+        dense_us = e0.elapsed_time(e1) * 1e3 / nd
+        print(json.dumps({
+            "mode": "batch_sweep", "batch": B, "layers": L, "budget_tokens": budget,
+            "workload": f"32 q / 8 kv heads, structured keys, seq_len log-uniform in [32K, 512K) "
+                        f"with ragged tails; seeds 8000+10B+layer",
+            "seq_len_min": int(lens.min()), "seq_len_median": int(np.median(lens)),
+            "seq_len_max": int(lens.max()), "replicas": R,
+            "us_per_step": round(us, 2), "us_per_layer": round(us / L, 2),
+            "decode_tokens_per_s_per_layer": round(B / (us / L * 1e-6), 1),
+            "alg_gbs": round(step_bytes / (us * 1e-6) / 1e9, 1),
+            "dense_us_per_step": round(dense_us, 2), "speedup_vs_dense": round(dense_us / us, 3),
+        }), flush=True)
+        del graphs, sets, layers, summs, ws, outs, sels, dws, dout
+        torch.cuda.empty_cache()
+
+
 if __name__ == "__main__":
-    main()
+    if "--sweep" in sys.argv:
+        ap = argparse.ArgumentParser()
+        ap.add_argument("--sweep", default="1,2,4,8,16,32",
+                        help="comma-separated batch sizes (variable-length batch-scaling mode)")
+        ap.add_argument("--layers", type=int, default=2)
+        ap.add_argument("--steps", type=int, default=200)
+        sweep(ap.parse_args())
+    else:
+        main()

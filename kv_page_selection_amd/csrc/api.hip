@@ -8,6 +8,8 @@
 
 #include "device_common.h"
 #include "internal.h"
+
+#include <algorithm>
 #include "locks.h"
 
 namespace locks {
@@ -24,15 +26,17 @@ bool ws_layout(const locks_dims& d, int k, WsLayout* L, const char** why) {
   L->n_score_wg = (int)((N + kScorePagesPerWave - 1) / kScorePagesPerWave);
   {
     const int G = d.n_q_heads / d.n_kv_heads;
-    // bound units, pooled into super-ranges of S units: 64-page ranges, or
-    // 16-page tiles when there are fewer than 2k ranges (a bound over so few
-    // units prunes little: most pages would reach the merge)
-    L->bound_tiles = L->n_score_wg < 2LL * k;
-    const long long nt = (L->bound_tiles ? 4LL : 1LL) * L->n_score_wg;
-    int S = 1;
-    while ((long long)G * ((nt + S - 1) / S) > kBoundSlots) S *= 2;
-    L->bound_sup = S;
-    L->bound_n_sup = (int)((nt + S - 1) / S);
+    // bound units, pooled into super-ranges of S units so that every head's
+    // unit maxima fit the LDS slots: 64-page ranges, or (for a sequence of
+    // fewer than kTileBoundPages * k pages, where a bound over its ranges
+    // would prune little) 16-page tiles, at most 8k of them
+    auto pool = [&](long long units) {
+      int S = 1;
+      while ((long long)G * ((units + S - 1) / S) > kBoundSlots) S *= 2;
+      return S;
+    };
+    L->sup_r = pool(L->n_score_wg);
+    L->sup_t = pool(std::min(4LL * L->n_score_wg, (long long)kTileBoundPages / 16 * k));
   }
   // select chunks of up to 1024 pages; every page's sort key fits the chunk's slots
   if (k > kSelectMaxK) {

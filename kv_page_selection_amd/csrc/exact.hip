@@ -31,8 +31,8 @@ struct ExactArgs {
   const int32_t* seq_lens;
   float* scores;
   float* partials;
-  float* tile_max;  // nullptr: the selection bounds by ranges
-  int Hq, Hkv, N, num_blocks, n_ranges;
+  float* tile_max;
+  int Hq, Hkv, N, num_blocks, n_ranges, tile_pages;  // tile maxima for n_b < tile_pages
 };
 
 template <int G>
@@ -146,8 +146,8 @@ __global__ __launch_bounds__(256) void exact_score_kernel(ExactArgs a) {
       dst[0] = (ssum > 0.f) ? m : -INFINITY;
       dst[1] = ssum;
     }
-    // ---- per head and 16-page tile: the max (when the selection bounds by tiles)
-    if (a.tile_max && lane < 4 * G) {
+    // ---- per head and 16-page tile: the max (for a sequence bounded by tiles)
+    if (n_b < a.tile_pages && lane < 4 * G) {
       const int tt = lane / G, hh = lane % G;
       float tm = -INFINITY;
 #pragma unroll
@@ -168,7 +168,8 @@ hipError_t launch_g(const locks_dims& d, const WsLayout& L, const DevPtrs& P, co
   a.seq_lens = sl;
   a.scores = P.scores;
   a.partials = P.score_part;
-  a.tile_max = L.bound_tiles ? P.tile_max : nullptr;
+  a.tile_max = P.tile_max;
+  a.tile_pages = kTileBoundPages * L.k;
   a.Hq = d.n_q_heads;
   a.Hkv = d.n_kv_heads;
   a.N = d.max_pages_per_seq;

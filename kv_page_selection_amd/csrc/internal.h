@@ -19,6 +19,7 @@ constexpr int kSparsePagesPerSplit = 4; // one page per wave
 constexpr int kDensePagesPerSplit = 256; // at least; grows so that splits <= kMaxSplits
 constexpr int kMaxSplits = 2048;        // split partials one merge workgroup combines
 constexpr int kPartialFloats = 130;     // (m, l, o[128]) per head and split
+constexpr int kTileBoundPages = 128;    // per selected page: sequences with fewer pages bound by tiles
 
 // Byte offsets of the regions of the caller's workspace (each 256-aligned).
 struct WsLayout {
@@ -34,8 +35,10 @@ struct WsLayout {
   size_t total = 0;
   int k = 0;
   int n_score_wg = 0;
-  bool bound_tiles = false;            // bound units: 16-page tiles (else 64-page ranges)
-  int bound_sup = 0, bound_n_sup = 0;  // units per super-range, super-ranges per head
+  // selection bound units, chosen per sequence on the device: 16-page tiles
+  // when the sequence has fewer than 2k ranges (< kTileBoundRanges * k
+  // pages), else 64-page ranges; units per super-range for each kind
+  int sup_r = 1, sup_t = 1;
   int sel_chunk = 0, n_sel_chunks = 0;
   int n_att_split = 0, n_dense_split = 0, dense_pages_per_split = 0;
 };

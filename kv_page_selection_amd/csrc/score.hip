@@ -52,7 +52,7 @@ struct ScoreArgs {
   float* scores;
   float* partials;
   float* tile_max;
-  int Hq, Hkv, N, num_blocks, n_ranges;
+  int Hq, Hkv, N, num_blocks, n_ranges, tile_pages;
 };
 
 __device__ __forceinline__ int nib_lo(uint32_t x) { return (int)((x << 4) & 0xF0F0F0F0u); }
@@ -118,10 +118,15 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
   const int N = a.N;
   const int n_b = full_pages(a.seq_lens, b, N);
   TileLds<G>& T = S.w[wave];
+  const int p0 = range * kScorePagesPerWave;
+
+  // A range wholly past the sequence's full pages (shorter sequences of a
+  // batch) has no work and writes nothing (its partials are never read);
+  // the whole workgroup leaves at once when none of its ranges has a page.
+  if (blockIdx.x * 4 * kScorePagesPerWave >= n_b) return;  // workgroup-uniform
 
   // page table of this wave's 64 pages, one entry per lane; issued first, so
   // its latency overlaps the q prologue below
-  const int p0 = range * kScorePagesPerWave;
   int myblk = -1;
   {
     const int j = p0 + lane;
@@ -170,6 +175,7 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
   }
   __syncthreads();  // digit planes consumed: the space takes the record offsets
   if (range >= a.n_ranges) return;  // whole wave; no workgroup barrier follows
+  if (p0 >= n_b) return;            // whole wave: past the sequence's full pages
   if (lane < 8) T.zero[lane] = (_Float16)0.0f;
 
   // An absent page (past the sequence's full pages, or a table entry out of
@@ -376,8 +382,8 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
     dst[1] = ssum;
   }
   // ---- per head and 16-page tile: the max of s_hat (base 2; -inf if no page),
-  // when the selection bounds by tiles
-  if (a.tile_max && lane < kTiles * G) {
+  // for a sequence whose selection bounds by tiles
+  if (n_b < a.tile_pages && lane < kTiles * G) {
     const int tt = lane / G, hh = lane % G;
     float tm = -INFINITY;
 #pragma unroll
@@ -400,7 +406,8 @@ hipError_t launch_g(const locks_dims& d, const WsLayout& L, const DevPtrs& P, co
   a.seq_lens = sl;
   a.scores = P.scores;
   a.partials = P.score_part;
-  a.tile_max = L.bound_tiles ? P.tile_max : nullptr;
+  a.tile_max = P.tile_max;
+  a.tile_pages = kTileBoundPages * L.k;
   a.Hq = d.n_q_heads;
   a.Hkv = d.n_kv_heads;
   a.N = d.max_pages_per_seq;

@@ -63,7 +63,7 @@ struct SelectArgs {
   int32_t* cand_count;
   int32_t* selected;
   int32_t* sel_blk;
-  int Hq, Hkv, N, k, n_ranges, n_tiles, sup, n_sup, chunk, n_chunks;
+  int Hq, Hkv, N, k, n_ranges, n_tiles, sup_r, sup_t, chunk, n_chunks;
 };
 
 struct BoundLds {
@@ -196,10 +196,23 @@ __global__ __launch_bounds__(kThreads) void select_chunk_kernel(SelectArgs a) {
   constexpr int kLbPt = kBoundSlots / G / kThreads;  // super-ranges per thread at most
   const int chunk = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int N = a.N, nr = a.n_ranges, nt = a.n_tiles, S = a.sup, nR = a.n_sup;
+  const int N = a.N, nt = a.n_tiles;
   const int n_b = full_pages(a.seq_lens, b, N);
+  // bound units of this sequence: 16-page tiles when it has fewer than 2k
+  // ranges (a bound over so few units prunes little; the scoring pass wrote
+  // tile maxima exactly for such sequences), else 64-page ranges; only the
+  // ranges and tiles that hold its pages are read
+  const bool tiles = n_b < kTileBoundPages * a.k;
+  const int nr = (n_b + kScorePagesPerWave - 1) / kScorePagesPerWave;
+  const int nu = tiles ? (n_b + 15) / 16 : nr;
+  const int S = tiles ? a.sup_t : a.sup_r;
+  const int nR = (nu + S - 1) / S;  // super-ranges (G * nR fits the LDS slots)
   const size_t head = (size_t)b * a.Hkv + kvh;
   __shared__ ChunkShared sh;
+  if (chunk * a.chunk >= n_b) {  // workgroup-uniform: no page of the sequence here
+    if (tid == 0) a.cand_count[head * a.n_chunks + chunk] = 0;
+    return;
+  }
 
   // ---- this chunk's scores and page-table entries, in flight during the bound pass
   const int ept = a.chunk / kThreads;  // 1, 2 or 4 slabs of 1024 consecutive pages
@@ -226,8 +239,7 @@ __global__ __launch_bounds__(kThreads) void select_chunk_kernel(SelectArgs a) {
     __syncthreads();
   }
   const float2* part =
-      reinterpret_cast<const float2*>(a.score_part) + ((size_t)b * a.Hq + (size_t)kvh * G + g) * nr;
-  const bool tiles = a.tile_max != nullptr;  // bound units: tiles, else the ranges
+      reinterpret_cast<const float2*>(a.score_part) + ((size_t)b * a.Hq + (size_t)kvh * G + g) * a.n_ranges;
   float lm = -1e30f, ls = 0.f;
   for (int r0 = 0; r0 < nr; r0 += 8 * P) {
     float2 v[8];
@@ -252,19 +264,19 @@ __global__ __launch_bounds__(kThreads) void select_chunk_kernel(SelectArgs a) {
   // tile units: the 16-page tiles' maxima (-inf: no present page)
   if (tiles) {
     const float* tmx = a.tile_max + ((size_t)b * a.Hq + (size_t)kvh * G + g) * nt;
-    for (int u0 = 0; u0 < nt; u0 += 8 * P) {
+    for (int u0 = 0; u0 < nu; u0 += 8 * P) {
       float v[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int u = u0 + j + i * P;
-        v[i] = (u < nt) ? tmx[u] : -INFINITY;
+        v[i] = (u < nu) ? tmx[u] : -INFINITY;
       }
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int u = u0 + j + i * P;
         const bool ne = v[i] > -INFINITY;
         if (S == 1) {
-          if (u < nt) sh.bound.msup[g * nR + u] = ne ? key_order_bits(v[i]) : 0u;
+          if (u < nu) sh.bound.msup[g * nR + u] = ne ? key_order_bits(v[i]) : 0u;
         } else if (ne) {
           atomicMax(&sh.bound.msup[g * nR + u / S], key_order_bits(v[i]));
         }
@@ -726,7 +738,7 @@ hipError_t launch_select(const locks_dims& d, const WsLayout& L, const DevPtrs& 
   SelectArgs a;
   a.scores = P.scores;
   a.score_part = P.score_part;
-  a.tile_max = L.bound_tiles ? P.tile_max : nullptr;
+  a.tile_max = P.tile_max;
   a.page_table = pt;
   a.seq_lens = sl;
   a.cand = P.cand;
@@ -740,8 +752,8 @@ hipError_t launch_select(const locks_dims& d, const WsLayout& L, const DevPtrs& 
   a.k = L.k;
   a.n_ranges = L.n_score_wg;
   a.n_tiles = 4 * L.n_score_wg;
-  a.sup = L.bound_sup;
-  a.n_sup = L.bound_n_sup;
+  a.sup_r = L.sup_r;
+  a.sup_t = L.sup_t;
   a.chunk = L.sel_chunk;
   a.n_chunks = L.n_sel_chunks;
   const dim3 grid(L.n_sel_chunks, d.n_kv_heads, d.batch);
