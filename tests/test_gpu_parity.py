@@ -97,6 +97,20 @@ def test_edge_cases(locks):
     assert 5 not in sel[1] and 200 not in sel[1]
 
 
+@pytest.mark.parametrize("budget", [512, 2048])
+def test_mixed_lengths_use_both_bound_units(locks, budget):
+    """One batch whose sequences bound their selection differently: sequences
+    with >= 128 k pages by 64-page ranges, shorter ones by 16-page tiles;
+    the shortest has fewer pages than k (no bound) and one is empty."""
+    k = budget // 16
+    long_pages = 128 * k + 37
+    w = workloads.make(2, device=DEV, ctx=16 * long_pages, batch=4, budget=budget, seed=23,
+                       seq_lens=[16 * long_pages, 16 * 700 + 3, 16 * (k // 2) + 9, 0])
+    summ = locks.build_summaries(w.k_cache, w.page_table, w.seq_lens)
+    r = decode_and_check(w, summ)
+    assert np.all(r["sel"].cpu().numpy()[3] == -1)
+
+
 def plant_nan_after_seq_len(w):
     """bf16 NaN in every key and value row after each sequence's last token:
     the tail page's rows past the tail and every later page of the table."""
