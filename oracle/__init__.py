@@ -87,6 +87,18 @@ def lib() -> ctypes.CDLL:
         L.oracle_attention.restype = None
         L.oracle_decode_step.argtypes = [I, I, I, I, I, P, P, P, P, P, P, I, P, P, P, P]
         L.oracle_decode_step.restype = None
+        L.oracle_exact_scores.argtypes = [I, I, I, I, I, P, P, P, P, P]
+        L.oracle_exact_scores.restype = None
+        L.oracle_variant_record_bytes.argtypes = [I, I]
+        L.oracle_variant_record_bytes.restype = ctypes.c_size_t
+        L.oracle_build_record_variant.argtypes = [P, I, I, P]
+        L.oracle_build_record_variant.restype = None
+        L.oracle_unpack_record_variant.argtypes = [P, I, I, P, P, P]
+        L.oracle_unpack_record_variant.restype = None
+        L.oracle_build_summaries_variant.argtypes = [I, I, I, I, P, P, P, I, I, P]
+        L.oracle_build_summaries_variant.restype = None
+        L.oracle_scores_variant.argtypes = [I, I, I, I, I, P, P, I, I, P, P, P]
+        L.oracle_scores_variant.restype = None
         L.oracle_num_threads.argtypes = []
         L.oracle_num_threads.restype = I
         _lib = L
@@ -141,7 +153,7 @@ def page_summary_f64(keys: np.ndarray, rank: int = RANK):
 
     Returns mu[128], V[128, r], C[16, r], lam[16] (descending)."""
     keys = _as(keys, np.float64)
-    assert keys.shape == (PAGE, DIM) and 1 <= rank <= 15
+    assert keys.shape == (PAGE, DIM) and 1 <= rank <= 16
     mu = np.zeros(DIM)
     V = np.zeros((DIM, rank))
     C = np.zeros((PAGE, rank))
@@ -201,6 +213,65 @@ def build_blocks(k_cache_bits: np.ndarray, blocks, summaries: np.ndarray) -> np.
         if 0 <= blk < kc.shape[0]:
             for h in range(kc.shape[1]):
                 out[blk, h] = build_record(kc[blk, h])[0]
+    return out
+
+
+# ------------------------------------------ variant formats (precision / rank ablation)
+
+VARIANT_RANKS = (4, 8, 16)
+VARIANT_VBITS = (2, 4, 16)
+
+
+def variant_record_bytes(rank: int, vbits: int) -> int:
+    """Bytes per record of the (rank, V bits) variant format."""
+    assert rank in VARIANT_RANKS and vbits in VARIANT_VBITS
+    return int(lib().oracle_variant_record_bytes(rank, vbits))
+
+
+def build_record_variant(keys_bf16: np.ndarray, rank: int, vbits: int) -> np.ndarray:
+    """Variant record of one page from its 16x128 bf16 bits (the same
+    unquantised summary as build_record, stored at rank `rank` with V in
+    `vbits` bits: 2 or 4 = integer codes, 16 = fp16; mu and C int8 or fp16)."""
+    kb = _as(keys_bf16, np.uint16)
+    assert kb.shape == (PAGE, DIM)
+    rec = np.zeros(variant_record_bytes(rank, vbits), dtype=np.uint8)
+    lib().oracle_build_record_variant(_ptr(kb), rank, vbits, _ptr(rec))
+    return rec
+
+
+def unpack_record_variant(rec: np.ndarray, rank: int, vbits: int):
+    """Decoded (mu[128], V[128, rank], C[16, rank]) of one variant record."""
+    rec = _as(rec, np.uint8)
+    assert rec.shape == (variant_record_bytes(rank, vbits),)
+    mu, V, C = np.zeros(DIM), np.zeros((DIM, rank)), np.zeros((PAGE, rank))
+    lib().oracle_unpack_record_variant(_ptr(rec), rank, vbits, _ptr(mu), _ptr(V), _ptr(C))
+    return mu, V, C
+
+
+def build_summaries_variant(k_cache_bits, page_table, seq_lens, rank: int, vbits: int,
+                            summaries: np.ndarray | None = None) -> np.ndarray:
+    """Variant records [num_blocks, Hkv, variant_record_bytes] of every full page."""
+    kc = _as(k_cache_bits, np.uint16)
+    nb, hkv = kc.shape[0], kc.shape[1]
+    pt = _as(page_table, np.int32)
+    if summaries is None:
+        summaries = np.zeros((nb, hkv, variant_record_bytes(rank, vbits)), dtype=np.uint8)
+    lib().oracle_build_summaries_variant(pt.shape[0], hkv, pt.shape[1], nb, _ptr(kc), _ptr(pt),
+                                         _ptr(_as(seq_lens, np.int32)), rank, vbits,
+                                         _ptr(summaries))
+    return summaries
+
+
+def scores_variant(q, summaries, page_table, seq_lens, num_kv_heads: int, rank: int,
+                   vbits: int) -> np.ndarray:
+    """s_hat[b, h, j] from variant records (-inf for absent pages and j >= n_b)."""
+    q = _as(q, np.float32)
+    B, Hq, _ = q.shape
+    pt = _as(page_table, np.int32)
+    sm = _as(summaries, np.uint8)
+    out = np.zeros((B, Hq, pt.shape[1]))
+    lib().oracle_scores_variant(B, Hq, num_kv_heads, pt.shape[1], sm.shape[0], _ptr(q), _ptr(sm),
+                                rank, vbits, _ptr(pt), _ptr(_as(seq_lens, np.int32)), _ptr(out))
     return out
 
 

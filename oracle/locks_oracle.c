@@ -174,7 +174,8 @@ int oracle_jacobi_eigh(int n, double* a, double* w, double* u) {
 /* Unquantised rank-r summary of one 16x128 key tile.
  * keys: 16*128 doubles. Outputs mu[128], V[128*r] (column k = basis vector k),
  * C[16*r] (row i = coefficients of token i), lam[16] eigenvalues of the
- * centred Gram, descending. r in 1..15. */
+ * centred Gram, descending. r in 1..16 (the centred keys have rank <= 15, so
+ * a 16th direction has zero energy and a zero column). */
 void oracle_page_summary_f64(const double* keys, int r, double* mu, double* V, double* C,
                              double* lam) {
   double D[OP * OD], G[OP * OP], w[OP], U[OP * OP];
@@ -293,6 +294,125 @@ void oracle_unpack_record(const uint8_t* rec, double* mu, double* V, double* C) 
       }
   for (int d = 0; d < OD; d++) mu[d] = s_mu * (int8_t)rec[OMU_OFF + d];
   for (int i = 0; i < OP * OR; i++) C[i] = s_c * (int8_t)rec[OC_OFF + i];
+}
+
+/* ------------------------------------------------------------------ */
+/* Variant record formats: the precision / rank ablation (A "Caveats": */
+/* Theorem 1 holds for unquantised summaries; int4 loses a few recall   */
+/* points, int2 collapses)                                              */
+/* ------------------------------------------------------------------ */
+
+/* Rank r in {4, 8, 16}; V in vbits in {2, 4} (signed integer codes, range
+ * +-(2^(vbits-1) - 1)) or 16 (fp16 values). mu and C are int8 codes (range
+ * +-127) in the integer formats and fp16 values in the fp16 format. Bytes:
+ * V [d][k] row-major, element e = d*r + k in bits [e*vbits, (e+1)*vbits)
+ * (little-endian; two's complement for codes); then mu[128]; then C[16][r];
+ * then fp16 scales {s_mu, s_V, s_C, 0} (1.0 where values are stored as
+ * fp16); zero padding to a multiple of 16 bytes. */
+static int variant_mbits(int vbits) { return vbits == 16 ? 16 : 8; }
+
+size_t oracle_variant_record_bytes(int r, int vbits) {
+  size_t b = (size_t)OD * r * vbits / 8 + (size_t)OD * variant_mbits(vbits) / 8 +
+             (size_t)OP * r * variant_mbits(vbits) / 8 + 8;
+  return (b + 15) / 16 * 16;
+}
+
+static void put_bits(uint8_t* base, size_t e, int bits, uint32_t v) {
+  for (int t = 0; t < bits; t++) {
+    size_t bit = e * bits + t;
+    if ((v >> t) & 1u) base[bit / 8] |= (uint8_t)(1u << (bit % 8));
+  }
+}
+
+static uint32_t get_bits(const uint8_t* base, size_t e, int bits) {
+  uint32_t v = 0;
+  for (int t = 0; t < bits; t++) {
+    size_t bit = e * bits + t;
+    v |= (uint32_t)((base[bit / 8] >> (bit % 8)) & 1u) << t;
+  }
+  return v;
+}
+
+/* One tensor stored as codes (bits < 16, with its quantiser scale) or fp16
+ * values (bits = 16, scale 1.0). Returns the scale's fp16 bits. */
+static uint16_t store_tensor(const double* x, int n, int bits, uint8_t* dst) {
+  if (bits == 16) {
+    for (int i = 0; i < n; i++) put_bits(dst, i, 16, oracle_double_to_f16(x[i]));
+    return 0x3C00; /* 1.0 */
+  }
+  int* codes = (int*)malloc(sizeof(int) * n);
+  uint16_t sb;
+  quantize_block(x, n, (1 << (bits - 1)) - 1, codes, &sb);
+  for (int i = 0; i < n; i++) put_bits(dst, i, bits, (uint32_t)codes[i] & ((1u << bits) - 1));
+  free(codes);
+  return sb;
+}
+
+static void load_tensor(const uint8_t* src, int n, int bits, double scale, double* x) {
+  for (int i = 0; i < n; i++) {
+    uint32_t v = get_bits(src, i, bits);
+    if (bits == 16) {
+      x[i] = oracle_f16_to_double((uint16_t)v);
+    } else {
+      int c = (int)v;
+      if (c >= (1 << (bits - 1))) c -= 1 << bits; /* two's complement */
+      x[i] = scale * c;
+    }
+  }
+}
+
+void oracle_build_record_variant(const uint16_t* keys_bf16, int r, int vbits, uint8_t* rec) {
+  double keys[OP * OD], mu[OD], V[OD * 16], C[OP * 16], lam[OP];
+  for (int i = 0; i < OP * OD; i++) keys[i] = oracle_bf16_to_double(keys_bf16[i]);
+  oracle_page_summary_f64(keys, r, mu, V, C, lam);
+  int mb = variant_mbits(vbits);
+  size_t ov = 0, om = (size_t)OD * r * vbits / 8, oc = om + (size_t)OD * mb / 8,
+         os = oc + (size_t)OP * r * mb / 8;
+  memset(rec, 0, oracle_variant_record_bytes(r, vbits));
+  uint16_t sc[3];
+  sc[1] = store_tensor(V, OD * r, vbits, rec + ov);
+  sc[0] = store_tensor(mu, OD, mb, rec + om);
+  sc[2] = store_tensor(C, OP * r, mb, rec + oc);
+  for (int t = 0; t < 3; t++) {
+    rec[os + 2 * t] = (uint8_t)(sc[t] & 0xff);
+    rec[os + 2 * t + 1] = (uint8_t)(sc[t] >> 8);
+  }
+}
+
+/* Decode a variant record: mu[128], V[128*r], C[16*r]. */
+void oracle_unpack_record_variant(const uint8_t* rec, int r, int vbits, double* mu, double* V,
+                                  double* C) {
+  int mb = variant_mbits(vbits);
+  size_t om = (size_t)OD * r * vbits / 8, oc = om + (size_t)OD * mb / 8,
+         os = oc + (size_t)OP * r * mb / 8;
+  double s_mu = oracle_f16_to_double((uint16_t)(rec[os] | (rec[os + 1] << 8)));
+  double s_v = oracle_f16_to_double((uint16_t)(rec[os + 2] | (rec[os + 3] << 8)));
+  double s_c = oracle_f16_to_double((uint16_t)(rec[os + 4] | (rec[os + 5] << 8)));
+  load_tensor(rec, OD * r, vbits, s_v, V);
+  load_tensor(rec + om, OD, mb, s_mu, mu);
+  load_tensor(rec + oc, OP * r, mb, s_c, C);
+}
+
+/* Variant records of every full page of every sequence (stride = the
+ * variant's record bytes); records of unreferenced blocks are untouched. */
+void oracle_build_summaries_variant(int B, int Hkv, int max_pages, int num_blocks,
+                                    const uint16_t* k_cache, const int32_t* page_table,
+                                    const int32_t* seq_lens, int r, int vbits,
+                                    uint8_t* summaries) {
+  size_t stride = oracle_variant_record_bytes(r, vbits);
+  for (int b = 0; b < B; b++) {
+    int n = seq_lens[b] / OP;
+    if (n > max_pages) n = max_pages;
+    if (n < 0) n = 0;
+#pragma omp parallel for schedule(dynamic, 64)
+    for (int u = 0; u < n * Hkv; u++) {
+      int j = u / Hkv, kvh = u % Hkv;
+      int blk = page_table[(size_t)b * max_pages + j];
+      if (blk < 0 || blk >= num_blocks) continue;
+      const uint16_t* tile = k_cache + ((size_t)blk * Hkv + kvh) * OP * OD;
+      oracle_build_record_variant(tile, r, vbits, summaries + ((size_t)blk * Hkv + kvh) * stride);
+    }
+  }
 }
 
 /* Summaries of every full page of every sequence; records of unreferenced
@@ -420,6 +540,33 @@ void oracle_exact_scores(int B, int Hq, int Hkv, int max_pages, int num_blocks, 
         for (int d = 0; d < OD; d++) qd[d] = q[((size_t)b * Hq + h) * OD + d];
         scores[((size_t)b * Hq + h) * max_pages + j] =
             present ? oracle_exact_page_lse(qd, keys) : -INFINITY;
+      }
+    }
+  }
+}
+
+/* Page scores from variant records (the page-score equation at rank r). */
+void oracle_scores_variant(int B, int Hq, int Hkv, int max_pages, int num_blocks, const float* q,
+                           const uint8_t* summaries, int r, int vbits,
+                           const int32_t* page_table, const int32_t* seq_lens, double* scores) {
+  int G = Hq / Hkv;
+  size_t stride = oracle_variant_record_bytes(r, vbits);
+  for (int b = 0; b < B; b++) {
+    int n = valid_pages(seq_lens, b, max_pages);
+#pragma omp parallel for schedule(dynamic, 64)
+    for (int u = 0; u < max_pages * Hkv; u++) {
+      int j = u / Hkv, kvh = u % Hkv;
+      int blk = (j < n) ? page_table[(size_t)b * max_pages + j] : -1;
+      double mu[OD], V[OD * 16], C[OP * 16];
+      int present = blk >= 0 && blk < num_blocks;
+      if (present)
+        oracle_unpack_record_variant(summaries + ((size_t)blk * Hkv + kvh) * stride, r, vbits, mu, V, C);
+      for (int g = 0; g < G; g++) {
+        int h = kvh * G + g;
+        double qd[OD];
+        for (int d = 0; d < OD; d++) qd[d] = q[((size_t)b * Hq + h) * OD + d];
+        scores[((size_t)b * Hq + h) * max_pages + j] =
+            present ? oracle_page_score_f64(qd, mu, V, C, r) : -INFINITY;
       }
     }
   }

@@ -212,6 +212,84 @@ def test_build_blocks_rebuilds_only_the_listed_blocks(orc):
         assert np.array_equal(got[blk], want), blk
 
 
+# ------------------------------------------------------------ variant formats
+
+def decode_variant_numpy(rec, r, vb):
+    """Independent decoder of the documented variant layout (V [d][k] then mu
+    then C [16][r], little-endian bit fields, then fp16 scales)."""
+    mb = 16 if vb == 16 else 8
+    nv, nm, nc = DIM * r * vb // 8, DIM * mb // 8, PAGE * r * mb // 8
+    bits = np.unpackbits(rec, bitorder="little").astype(np.int64)
+
+    def field(off, n, b):
+        return (bits[off * 8: off * 8 + n * b].reshape(n, b) << np.arange(b)).sum(1)
+
+    sc = rec[nv + nm + nc: nv + nm + nc + 6].view(np.float16).astype(np.float64)
+
+    def values(v, b, scale):
+        if b == 16:
+            return v.astype(np.uint16).view(np.float16).astype(np.float64), None
+        c = np.where(v >= 2 ** (b - 1), v - 2 ** b, v)
+        return scale * c, c
+
+    V, vc = values(field(0, DIM * r, vb), vb, sc[1])
+    mu, mc = values(field(nv, DIM, mb), mb, sc[0])
+    C, cc = values(field(nv + nm, PAGE * r, mb), mb, sc[2])
+    assert np.all(rec[nv + nm + nc + 6:] == 0)  # fourth scale slot and padding
+    return mu, V.reshape(DIM, r), C.reshape(PAGE, r), (mc, vc, cc), sc
+
+
+@pytest.mark.parametrize("r", [4, 8, 16])
+@pytest.mark.parametrize("vb", [2, 4, 16])
+def test_variant_records_decode_independently_and_quantise_correctly(orc, r, vb):
+    rr = rng(300 + 10 * r + vb)
+    keys = planted_page(rr, 8, noise=0.05)
+    kb, kd = bf16_round(keys)
+    rec = orc.build_record_variant(kb, r, vb)
+    mu, V, C, codes, sc = decode_variant_numpy(rec, r, vb)
+    mu_o, V_o, C_o = orc.unpack_record_variant(rec, r, vb)
+    assert np.array_equal(mu, mu_o) and np.array_equal(V, V_o) and np.array_equal(C, C_o)
+    mu_u, V_u, C_u, _ = orc.page_summary_f64(kd, rank=r)
+    if vb == 16:  # stored values are numpy's fp16 rounding of the unquantised summary
+        for got, want in ((mu, mu_u), (V, V_u), (C, C_u)):
+            assert np.array_equal(got, want.astype(np.float16).astype(np.float64))
+        assert np.all(sc[:3] == 1.0)
+    else:
+        qv = 2 ** (vb - 1) - 1
+        for (c, q, x, s) in ((codes[1], qv, V_u, sc[1]), (codes[0], 127, mu_u, sc[0]),
+                             (codes[2], 127, C_u, sc[2])):
+            assert s == np.float16(np.abs(x).max() / q)
+            assert np.abs(c).max() <= q
+            inside = np.abs(x.ravel()) <= s * q
+            assert np.all(np.abs(x.ravel()[inside] - s * c[inside]) <= s / 2 * (1 + 1e-9))
+        if vb == 2:
+            assert set(np.unique(codes[1])) <= {-1, 0, 1}
+
+
+def test_variant_int4_rank8_holds_the_shipped_values(orc):
+    """Same quantiser, another byte layout: the int4 rank-8 variant decodes to
+    exactly the values of the shipped 784-byte record."""
+    rr = rng(321)
+    for _ in range(3):
+        kb, _ = bf16_round(planted_page(rr, 8, noise=0.05))
+        a = orc.unpack_record(orc.build_record(kb)[0])
+        b = orc.unpack_record_variant(orc.build_record_variant(kb, 8, 4), 8, 4)
+        for x, y in zip(a, b):
+            assert np.array_equal(x, y)
+
+
+def test_variant_fp16_rank16_scores_track_the_exact_page_lse(orc):
+    """Rank 16 spans every centred page (rank <= 15), so an fp16-stored rank-16
+    summary scores within fp16 rounding of the exact LSE on the real keys."""
+    rr = rng(331)
+    for _ in range(4):
+        kb, kd = bf16_round(rr.standard_normal((PAGE, DIM)))
+        mu, V, C = orc.unpack_record_variant(orc.build_record_variant(kb, 16, 16), 16, 16)
+        for _ in range(3):
+            q = rr.standard_normal(DIM)
+            assert abs(orc.page_score_f64(q, mu, V, C) - exact_lse(q, kd)) < 2e-2
+
+
 def test_summary_payload_is_about_ten_percent(orc):
     """(A "How LOCKS works"; B mechanism 1): the summary is about 10% of the
     page's KV bytes. Payload 776 B vs 16 tokens x 128 x bf16 x (K+V)."""
