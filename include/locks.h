@@ -195,6 +195,30 @@ locks_status locks_exact_score_pages(const locks_dims* dims, const float* q, con
                                      int32_t budget_tokens, float* page_scores, void* workspace,
                                      size_t workspace_bytes, hipStream_t stream);
 
+/* Precision / rank ablation (A "Caveats": Theorem 1 covers unquantised
+ * summaries; int4 loses a few recall points; int2 collapses). Variant records
+ * hold the same summary at rank in {4, 8, 16} with V as int2 or int4 codes
+ * (v_bits = 2, 4; range +-(2^(v_bits-1) - 1)) or fp16 values (v_bits = 16),
+ * and mu, C as int8 codes (fp16 values when v_bits = 16). Layout per record:
+ * V [d][k] row-major, element e = d*rank + k in bits [e*v_bits, (e+1)*v_bits),
+ * little-endian, two's complement codes; mu[128]; C[16][rank]; fp16 scales
+ * {s_mu, s_V, s_C, 0} (1.0 for fp16 tensors); zero padding to a multiple of
+ * 16 bytes. Records are [num_blocks][n_kv_heads][locks_variant_record_bytes].
+ * A measurement path: locks_score_pages_variant leaves the workspace as
+ * locks_score_pages does, so locks_select_pages and locks_sparse_attention
+ * follow it unchanged; it is not tuned like the shipped format's scorer.
+ * Unsupported (rank, v_bits) return LOCKS_ERR_UNSUPPORTED. */
+locks_status locks_variant_record_bytes(int32_t rank, int32_t v_bits, size_t* out_bytes);
+locks_status locks_build_summaries_variant(const locks_dims* dims, const void* k_cache,
+                                           const int32_t* page_table, const int32_t* seq_lens,
+                                           int32_t rank, int32_t v_bits, void* summaries,
+                                           hipStream_t stream);
+locks_status locks_score_pages_variant(const locks_dims* dims, const float* q, const void* summaries,
+                                       const int32_t* page_table, const int32_t* seq_lens,
+                                       int32_t budget_tokens, int32_t rank, int32_t v_bits,
+                                       float* page_scores, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream);
+
 /* Phase 2: group combine (B mechanism 3: every head's mass share averaged over
  * the GQA group) and top-k (A "Code": top-k by score, ids sorted ascending).
  * Ties between equal keys go to the lower page id. Must follow

@@ -62,12 +62,17 @@ def lib() -> ctypes.CDLL:
         L.locks_decode_step.argtypes = [D, P, P, P, P, P, P, I, P, P, P, P, S, P]
         L.locks_score_pages.argtypes = [D, P, P, P, P, I, P, P, S, P]
         L.locks_exact_score_pages.argtypes = [D, P, P, P, P, I, P, P, S, P]
+        L.locks_variant_record_bytes.argtypes = [I, I, ctypes.POINTER(S)]
+        L.locks_build_summaries_variant.argtypes = [D, P, P, P, I, I, P, P]
+        L.locks_score_pages_variant.argtypes = [D, P, P, P, P, I, I, I, P, P, S, P]
         L.locks_select_pages.argtypes = [D, P, P, I, P, P, P, S, P]
         L.locks_sparse_attention.argtypes = [D, P, P, P, P, P, I, P, P, P, S, P]
         L.locks_dense_attention.argtypes = [D, P, P, P, P, P, P, P, S, P]
         for name in ("locks_workspace_bytes", "locks_build_summaries", "locks_build_blocks",
                      "locks_decode_step",
                      "locks_score_pages", "locks_exact_score_pages", "locks_select_pages",
+                     "locks_variant_record_bytes", "locks_build_summaries_variant",
+                     "locks_score_pages_variant",
                      "locks_sparse_attention",
                      "locks_dense_attention"):
             getattr(L, name).restype = ctypes.c_int
@@ -207,6 +212,39 @@ def exact_score_pages(q, k_cache, page_table, seq_lens, budget_tokens: int, work
                                          _ptr(page_table), _ptr(seq_lens), int(budget_tokens),
                                          _ptr(page_scores), _ptr(workspace), workspace.numel(),
                                          _stream(q.device)))
+
+
+def variant_record_bytes(rank: int, v_bits: int) -> int:
+    """Bytes per record of the (rank, V bits) variant format."""
+    n = ctypes.c_size_t(0)
+    _check(lib().locks_variant_record_bytes(rank, v_bits, ctypes.byref(n)))
+    return n.value
+
+
+def build_summaries_variant(k_cache, page_table, seq_lens, rank: int, v_bits: int,
+                            summaries=None):
+    """Variant records [num_blocks, Hkv, variant_record_bytes] of every full page."""
+    _check_common(None, k_cache, page_table, seq_lens)
+    dims = make_dims(page_table.shape[0], k_cache, page_table, n_q_heads=k_cache.shape[1])
+    if summaries is None:
+        summaries = torch.zeros(k_cache.shape[0], k_cache.shape[1],
+                                variant_record_bytes(rank, v_bits), dtype=torch.uint8,
+                                device=k_cache.device)
+    _check(lib().locks_build_summaries_variant(ctypes.byref(dims), _ptr(k_cache), _ptr(page_table),
+                                               _ptr(seq_lens), rank, v_bits, _ptr(summaries),
+                                               _stream(k_cache.device)))
+    return summaries
+
+
+def score_pages_variant(q, summaries, k_cache, page_table, seq_lens, budget_tokens: int, rank: int,
+                        v_bits: int, workspace, page_scores=None):
+    """Phase 1 from variant records (then select_pages / sparse_attention as usual)."""
+    _check_common(q, k_cache, page_table, seq_lens)
+    dims = make_dims(q, k_cache, page_table)
+    _check(lib().locks_score_pages_variant(ctypes.byref(dims), _ptr(q), _ptr(summaries),
+                                           _ptr(page_table), _ptr(seq_lens), int(budget_tokens),
+                                           rank, v_bits, _ptr(page_scores), _ptr(workspace),
+                                           workspace.numel(), _stream(q.device)))
 
 
 def select_pages(q, k_cache, page_table, seq_lens, budget_tokens: int, selected, workspace,

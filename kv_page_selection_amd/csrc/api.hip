@@ -268,6 +268,63 @@ locks_status locks_exact_score_pages(const locks_dims* dims, const float* q, con
                     "exact score launch");
 }
 
+locks_status locks_variant_record_bytes(int32_t rank, int32_t v_bits, size_t* out_bytes) {
+  g_err.clear();
+  if (!out_bytes) return fail(LOCKS_ERR_INVALID_ARG, "out_bytes is NULL");
+  const size_t n = variant_record_bytes(rank, v_bits);
+  if (!n) return fail(LOCKS_ERR_UNSUPPORTED, "variant format: rank must be 4, 8 or 16 and v_bits 2, 4 or 16");
+  *out_bytes = n;
+  return LOCKS_OK;
+}
+
+locks_status locks_build_summaries_variant(const locks_dims* dims, const void* k_cache,
+                                           const int32_t* page_table, const int32_t* seq_lens,
+                                           int32_t rank, int32_t v_bits, void* summaries,
+                                           hipStream_t stream) {
+  g_err.clear();
+  LOCKS_TRY(check_dims(dims));
+  size_t n = 0;
+  LOCKS_TRY(locks_variant_record_bytes(rank, v_bits, &n));
+  LOCKS_TRY(need(k_cache, 16, "k_cache"));
+  LOCKS_TRY(need(page_table, 4, "page_table"));
+  LOCKS_TRY(need(seq_lens, 4, "seq_lens"));
+  LOCKS_TRY(need(summaries, 16, "summaries"));
+  if ((long long)dims->batch * dims->max_pages_per_seq * dims->n_kv_heads > (1LL << 35))
+    return fail(LOCKS_ERR_UNSUPPORTED, "batch * max_pages_per_seq * n_kv_heads above 2^35");
+  (void)hipGetLastError();
+  return hip_status(launch_build_variant(*dims, static_cast<const uint16_t*>(k_cache), page_table,
+                                         seq_lens, rank, v_bits, static_cast<uint8_t*>(summaries),
+                                         stream),
+                    "variant build launch");
+}
+
+locks_status locks_score_pages_variant(const locks_dims* dims, const float* q, const void* summaries,
+                                       const int32_t* page_table, const int32_t* seq_lens,
+                                       int32_t budget_tokens, int32_t rank, int32_t v_bits,
+                                       float* page_scores, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream) {
+  g_err.clear();
+  LOCKS_TRY(check_dims(dims));
+  LOCKS_TRY(check_budget(budget_tokens));
+  size_t n = 0;
+  LOCKS_TRY(locks_variant_record_bytes(rank, v_bits, &n));
+  LOCKS_TRY(need(q, 4, "q"));
+  LOCKS_TRY(need(summaries, 16, "summaries"));
+  LOCKS_TRY(need(page_table, 4, "page_table"));
+  LOCKS_TRY(need(seq_lens, 4, "seq_lens"));
+  if (page_scores) LOCKS_TRY(need(page_scores, 4, "page_scores"));
+  if ((unsigned long long)dims->num_blocks * dims->n_kv_heads * n > (1ULL << 40))
+    return fail(LOCKS_ERR_UNSUPPORTED, "variant summaries above 1 TiB");
+  WsLayout L;
+  LOCKS_TRY(layout(dims, budget_tokens, &L));
+  LOCKS_TRY(check_ws(L, workspace, workspace_bytes));
+  const DevPtrs P = ws_ptrs(*dims, L, workspace, page_scores);
+  (void)hipGetLastError();
+  return hip_status(launch_score_variant(*dims, L, P, q, static_cast<const uint8_t*>(summaries),
+                                         page_table, seq_lens, rank, v_bits, stream),
+                    "variant score launch");
+}
+
 locks_status locks_select_pages(const locks_dims* dims, const int32_t* page_table,
                                 const int32_t* seq_lens, int32_t budget_tokens, int32_t* selected,
                                 const float* page_scores, void* workspace, size_t workspace_bytes,

@@ -64,6 +64,16 @@ DevPtrs ws_ptrs(const locks_dims& d, const WsLayout& L, void* ws, float* page_sc
 hipError_t launch_score(const locks_dims& d, const WsLayout& L, const DevPtrs& P, const float* q,
                         const uint8_t* summ, const int32_t* page_table, const int32_t* seq_lens,
                         hipStream_t s);
+// Variant record formats (precision / rank ablation): bytes per record (0 if
+// unsupported), whole-cache build, and scores (same workspace outputs as
+// launch_score).
+size_t variant_record_bytes(int rank, int v_bits);
+hipError_t launch_build_variant(const locks_dims& d, const uint16_t* kc, const int32_t* page_table,
+                                const int32_t* seq_lens, int rank, int v_bits, uint8_t* summ,
+                                hipStream_t s);
+hipError_t launch_score_variant(const locks_dims& d, const WsLayout& L, const DevPtrs& P,
+                                const float* q, const uint8_t* summ, const int32_t* page_table,
+                                const int32_t* seq_lens, int rank, int v_bits, hipStream_t s);
 // Exact-mass scores from the keys themselves (the reference selector); same
 // workspace outputs as launch_score.
 hipError_t launch_exact_score(const locks_dims& d, const WsLayout& L, const DevPtrs& P,

@@ -52,6 +52,19 @@ def test_record_size(L):
     assert L.summary_record_bytes() == 784
 
 
+def test_variant_record_sizes_match_the_oracle_layout(L):
+    """Host-side: the library's variant record sizes equal those of the
+    independently written oracle layout; unsupported formats are refused."""
+    import oracle
+    for r in (4, 8, 16):
+        for vb in (2, 4, 16):
+            assert L.variant_record_bytes(r, vb) == oracle.variant_record_bytes(r, vb)
+    for bad in ((8, 8), (2, 4), (32, 16)):
+        with pytest.raises(L.LocksError) as e:
+            L.variant_record_bytes(*bad)
+        assert e.value.status == L.ERR_UNSUPPORTED
+
+
 def test_workspace_sizing_and_validation(L):
     n = L.workspace_bytes(dims(L), 2048)
     assert n > 32 * 65536 * 4  # holds at least the per-head page scores
