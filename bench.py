@@ -590,8 +590,111 @@ def sweep(args):
         torch.cuda.empty_cache()
 
 
+def selection_quality(locks, w, summ_sel, ex_sel, ex_scores):
+    """Coverage of the exact group mass and recall of the exact selection by a
+    selection (host numpy on the exact scores)."""
+    import numpy as np
+    B, Hq, N = ex_scores.shape
+    Hkv = w.n_kv_heads
+    es = ex_scores.double().cpu().numpy()
+    nb = np.minimum(w.seq_lens.cpu().numpy() // 16, N)
+    for b in range(B):
+        es[b, :, nb[b]:] = -np.inf
+    mx = es.max(-1, keepdims=True)
+    L = np.log(np.exp(es - mx).sum(-1, keepdims=True)) + mx
+    share = np.exp(es - L).reshape(B, Hkv, Hq // Hkv, N).mean(2)
+    ls, xs = summ_sel.cpu().numpy(), ex_sel.cpu().numpy()
+    cov, rec, car = [], [], []
+    carrier = w.carrier.cpu().numpy() if w.carrier is not None else None
+    for b in range(B):
+        for h in range(Hkv):
+            a_ = ls[b, h][ls[b, h] >= 0]
+            x_ = xs[b, h][xs[b, h] >= 0]
+            if len(x_) == 0:
+                continue
+            cov.append(share[b, h, a_].sum() / share[b, h, x_].sum())
+            rec.append(len(np.intersect1d(a_, x_)) / len(x_))
+            if carrier is not None and carrier[b] >= 0:
+                car.append(carrier[b] in a_)
+    out = {"mass_coverage_min": round(float(np.min(cov)), 5),
+           "mass_coverage_mean": round(float(np.mean(cov)), 5),
+           "recall_mean": round(float(np.mean(rec)), 4)}
+    if car:
+        out["carrier_retained"] = round(float(np.mean(car)), 4)
+    return out
+
+
+def ablation(args):
+    """Precision / rank ablation (not the default line): per workload and
+    summary format (rank 4/8/16 x V int2/int4/fp16, plus the shipped int4
+    rank-8 path), the selection's coverage of the exact-mass selection, its
+    recall and carrier retention, and the scoring time. One JSON line each."""
+    import numpy as np
+    import torch
+
+    import kv_page_selection_amd as locks
+    import workloads
+
+    dev = torch.device("cuda:0")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, n=5):
+        fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n
+
+    for spec in args.ablation.split(","):
+        config, budget = (int(x) for x in spec.split(":"))
+        w = workloads.make(config, device=dev, budget=budget)
+        print(f"[ablation] {w.recipe}", file=sys.stderr, flush=True)
+        B, Hq, Hkv, N, k = w.batch, w.n_q_heads, w.n_kv_heads, w.max_pages, w.k_pages
+        ws = locks.new_workspace(locks.make_dims(w.q, w.k_cache, w.page_table), budget, dev)
+        ex_scores = torch.empty(B, Hq, N, device=dev)
+        ex_sel = torch.empty(B, Hkv, k, dtype=torch.int32, device=dev)
+        locks.exact_score_pages(w.q, w.k_cache, w.page_table, w.seq_lens, budget, ws,
+                                page_scores=ex_scores)
+        locks.select_pages(w.q, w.k_cache, w.page_table, w.seq_lens, budget, ex_sel, ws,
+                           page_scores=ex_scores)
+        sel = torch.empty_like(ex_sel)
+        rows = [("shipped", 8, 4)] + [("variant", r, vb) for r in (4, 8, 16) for vb in (16, 4, 2)]
+        for kind, r, vb in rows:
+            if kind == "shipped":
+                summ = locks.build_summaries(w.k_cache, w.page_table, w.seq_lens)
+                score = lambda: locks.score_pages(w.q, summ, w.k_cache, w.page_table, w.seq_lens,
+                                                  budget, ws)
+                rec_bytes = locks.summary_record_bytes()
+            else:
+                summ = locks.build_summaries_variant(w.k_cache, w.page_table, w.seq_lens, r, vb)
+                score = lambda: locks.score_pages_variant(w.q, summ, w.k_cache, w.page_table,
+                                                          w.seq_lens, budget, r, vb, ws)
+                rec_bytes = locks.variant_record_bytes(r, vb)
+            us = timed(score)
+            score()
+            locks.select_pages(w.q, w.k_cache, w.page_table, w.seq_lens, budget, sel, ws)
+            torch.cuda.synchronize()
+            line = {"mode": "ablation", "workload": w.recipe, "format": kind, "rank": r,
+                    "v_bits": vb, "mu_c_bits": 16 if vb == 16 else 8, "record_bytes": rec_bytes,
+                    "score_us": round(us, 1)}
+            line.update(selection_quality(locks, w, sel, ex_sel, ex_scores))
+            print(json.dumps(line), flush=True)
+            del summ
+            torch.cuda.empty_cache()
+        del w, ws
+        torch.cuda.empty_cache()
+
+
 if __name__ == "__main__":
-    if "--sweep" in sys.argv:
+    if "--ablation" in sys.argv:
+        ap = argparse.ArgumentParser()
+        ap.add_argument("--ablation", default="3:2048,3:512,4:512",
+                        help="comma-separated config:budget workloads (precision / rank ablation)")
+        ablation(ap.parse_args())
+    elif "--sweep" in sys.argv:
         ap = argparse.ArgumentParser()
         ap.add_argument("--sweep", default="1,2,4,8,16,32",
                         help="comma-separated batch sizes (variable-length batch-scaling mode)")
