@@ -69,12 +69,13 @@ def traffic_from(fetch_csv, write_csv, bench_log):
     flag adds, written to profiles/score_kernel_traffic.json together with the
     scoring sources' hash (a kernel change makes the numbers stale)."""
     import csv
+    import re
 
     def per_dispatch(path):
         score, copy = [], []
         for r in csv.DictReader(open(path)):
             name, v = r["Kernel_Name"], float(r["Counter_Value"])
-            if "score_kernel" in name:
+            if re.search(r"(^|::)score_kernel<", name):  # not exact_/variant scorers
                 score.append(v)
             elif "copyBuffer" in name:
                 copy.append((int(r["Dispatch_Id"]), v))
