@@ -33,10 +33,9 @@
  *  - Identical inputs give bitwise-identical outputs (no float atomics).
  *  - Supported shape: head_dim 128, page_size 16, rank 8, and a GQA group
  *    size G = n_q_heads / n_kv_heads in {1, 2, 4, 8, 16}; budget/16 <= 4096
- *    pages; max_pages_per_seq <= 2^20; batch * n_kv_heads <= 65535 (and
- *    n_kv_heads <= 32767 when G = 16); num_blocks * n_kv_heads <= 87652393
- *    (summary records within 64 GiB). Other values return
- *    LOCKS_ERR_UNSUPPORTED.
+ *    pages; max_pages_per_seq <= 2^20; batch * n_kv_heads <= 65535;
+ *    num_blocks * n_kv_heads <= 87652393 (summary records within 64 GiB).
+ *    Other values return LOCKS_ERR_UNSUPPORTED.
  *  - q must be finite.
  *  - Page table: page_table[b*max_pages_per_seq + j] is the physical block
  *    that holds logical page j of sequence b. Sequence b has

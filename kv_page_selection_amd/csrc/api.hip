@@ -125,8 +125,6 @@ locks_status check_dims(const locks_dims* d) {
     return fail(LOCKS_ERR_UNSUPPORTED, "batch * n_kv_heads above 65535");
   if ((long long)d->num_blocks * d->n_kv_heads * (kStride / 16) > 0xFFFFFFFFLL)
     return fail(LOCKS_ERR_UNSUPPORTED, "num_blocks * n_kv_heads above 87652393 (summaries above 64 GiB)");
-  if (G == 16 && d->n_kv_heads > 32767)
-    return fail(LOCKS_ERR_UNSUPPORTED, "n_kv_heads above 32767 with 16 query heads per KV head");
   return LOCKS_OK;
 }
 

@@ -6,22 +6,26 @@
 //   s_hat = log sum_{i<16} exp((q.mu + (V^T q).c_i) / sqrt(128))
 // from the page's summary record alone (no key or value is read).
 //
-// Mapping. A workgroup is 4 waves of one KV head (and one slice of at most 8
-// of its query heads); wave w scores 64 consecutive pages (4 tiles of 16), and
-// the waves take 4 consecutive page ranges. The q prologue (fixed-point digits
-// of the group's query heads) is split over the 4 waves and shared in LDS.
+// Mapping. A workgroup is 4 waves of one KV head and all G of its query heads;
+// wave w scores 64 consecutive pages (4 tiles of 16), and the waves take 4
+// consecutive page ranges. The q prologue (fixed-point digits of the group's
+// query heads) is split over the 4 waves and shared in LDS.
 //
 // Stage 1, mu.q and V^T q, on v_mfma_i32_16x16x64_i8, exact: the row operand is
-// each query head as a 22-bit fixed-point integer in three signed int8 digits
-// (rows = 4 heads x 4 digit slots, the 4th slot zero), the column operand is
-// the record's codes as stored (mu bytes; V nibbles widened to 16*code with
-// one shift and mask). A lane then holds all three digit sums of one value,
-// which it combines in int32 and one fp32 rounding.
+// each query head as a 22-bit fixed-point integer in three signed int8 digits,
+// the column operand is the record's codes as stored (mu bytes; V nibbles
+// widened to 16*code with one shift and mask). Up to 8 heads, a row block is 4
+// heads x 4 digit slots (the 4th zero), so a lane holds all three digit sums
+// of one value; with 16 heads a row block is one digit plane of all 16 heads,
+// and a lane finds the same 4 heads in the three planes' outputs. Either way
+// it combines the digit sums in int32 and one fp32 rounding.
 // Stage 2, the in-page contraction C p (16 tokens x 8 x G heads), on
 // v_mfma_f32_16x16x{32,16}_f16: C codes are exact in f16 and p enters as an
-// f16 hi + lo pair (about 22 significant bits); 16/G pages are packed
-// block-diagonally along K so one pass fills the 16 output columns. The
-// 16-token log-sum-exp is one in-lane step and two cross-row swaps, in base 2.
+// f16 hi + lo pair (about 22 significant bits). Up to 8 heads, 16/G pages are
+// packed block-diagonally along K so one pass fills the 16 output columns;
+// with 16 heads one page fills them, and hi and lo share one product (K =
+// 8 basis vectors x {hi, lo}). The 16-token log-sum-exp is one in-lane step
+// and two cross-row swaps, in base 2.
 // The wave keeps its 64 x G scores in LDS; at the end it writes them once and
 // leaves, per head, the (max, sum) of exp2 over its pages, which the group
 // combine needs for every head's total mass, and the max of each 16-page tile,
@@ -84,9 +88,9 @@ struct TileLds {
   __align__(16) float out[kScorePagesPerWave][G];  // the wave's page scores, [page][head], base 2
 };
 
-template <int G>
+template <int G, class TileT>
 struct ScoreLds {
-  TileLds<G> w[4];
+  TileT w[4];
   union {
     __align__(16) int8_t dig[3][G][kDim];  // q digit planes of the workgroup's heads,
     uint32_t off[4][kScorePagesPerWave];   // then each wave's page record offsets
@@ -94,27 +98,126 @@ struct ScoreLds {
   float esc[16];                           // per head: 2^-e log2(e) / sqrt(128)
 };
 
-// GROUP = query heads per KV head; a wave scores G = min(GROUP, 8) of them
-// (larger groups are split into slices of 8 heads, one wave each, which share
-// the record loads through the cache and fill the stage-2 MFMA columns)
-template <int GROUP>
+// q of the G heads at qg -> per-head exponent e (max |q| * 2^e in [2^21,
+// 2^22)) -> three signed int8 digit planes, q * 2^e = d0 + 256 d1 + 65536 d2;
+// wave w converts heads w, w+4, ...
+template <int G>
+__device__ __forceinline__ void q_digit_planes(const float* qg, int8_t (&dig)[3][G][kDim],
+                                               float* esc, int wave, int lane) {
+  for (int h = wave; h < G; h += 4) {
+    const float q0 = qg[h * kDim + lane], q1 = qg[h * kDim + 64 + lane];
+    const float qm = wave_max(fmaxf(fabsf(q0), fabsf(q1)));
+    int e = 0;
+    if (qm > 0.f) {
+      int E;
+      frexpf(qm, &E);
+      e = 22 - E;
+    }
+    const float qs[2] = {q0, q1};
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int qf = (int)rintf(ldexpf(qs[u], e));
+      const int d0 = ((qf + 128) & 255) - 128;
+      const int r1 = (qf - d0) / 256;
+      const int d1 = ((r1 + 128) & 255) - 128;
+      const int d2 = (r1 - d1) / 256;
+      dig[0][h][lane + 64 * u] = (int8_t)d0;
+      dig[1][h][lane + 64 * u] = (int8_t)d1;
+      dig[2][h][lane + 64 * u] = (int8_t)d2;
+    }
+    if (lane == 0) esc[h] = ldexpf(1.0f, -e) * (kLog2e * kInvSqrtD);
+  }
+}
+
+// The three digit sums of one value -> fp32 (|value| < 2^37; the top two
+// digits combine exactly in int32)
+__device__ __forceinline__ float digits_to_float(int s0, int s1, int s2) {
+  return (float)(s2 * 256 + s1) * 256.0f + (float)s0;
+}
+
+// A wave's outputs from its base-2 scores out[page][head] (pages p0 .. p0+63
+// of sequence b, query heads hbase ..): page scores in natural log (-inf for
+// an absent page), the per-head (max, sum of exp2) over the range, and, for a
+// sequence bounded by tiles, the max of each 16-page tile.
+template <int G>
+__device__ __forceinline__ void write_wave_outputs(const ScoreArgs& a, const float (&out)[kScorePagesPerWave][G],
+                                                   unsigned long long present, int b, int hbase,
+                                                   int range, int p0, int n_b, int lane) {
+  const int N = a.N;
+  // written once after the wave's last loads: a store in flight would hold
+  // up the wait for later loads (one in-order counter covers both); whole
+  // 256-byte rows per head coalesce, and streaming (non-temporal) stores keep
+  // them from sitting dirty in L2 until the end of the launch
+  const bool mine = (present >> lane) & 1ull;
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float sc = mine ? out[lane][h] * kLn2 : -INFINITY;
+    if (p0 + lane < n_b) __builtin_nontemporal_store(sc, &a.scores[((size_t)b * a.Hq + (size_t)hbase + h) * N + p0 + lane]);
+  }
+
+  // per-head (max, sum) of exp2 over the wave's pages: lane takes head
+  // lane % G and pages i * 64/G + lane / G, then lanes of one head merge
+  constexpr int LPH = kScorePagesPerWave / G;
+  float m = -INFINITY, v[G];
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    const int pg = i * LPH + lane / G;
+    v[i] = ((present >> pg) & 1ull) ? out[pg][lane % G] : -INFINITY;
+    m = fmaxf(m, v[i]);
+  }
+  float ssum = 0.f;
+  {
+    const float ms = m == -INFINITY ? 0.f : m;
+#pragma unroll
+    for (int i = 0; i < G; ++i) ssum += fast_exp2(v[i] - ms);
+  }
+#pragma unroll
+  for (int off = G; off < 64; off <<= 1) {
+    const float m2 = __shfl_xor(m, off), s2 = __shfl_xor(ssum, off);
+    const float mn = fmaxf(m, m2);
+    const float ms = mn == -INFINITY ? 0.f : mn;
+    ssum = ssum * fast_exp2(m - ms) + s2 * fast_exp2(m2 - ms);
+    m = mn;
+  }
+  if (lane < G) {
+    float* dst = a.partials + (((size_t)b * a.Hq + (size_t)hbase + lane) * a.n_ranges + range) * 2;
+    dst[0] = (ssum > 0.f) ? m : -INFINITY;
+    dst[1] = ssum;
+  }
+  // per head and 16-page tile: the max of s_hat (base 2; -inf if no page)
+  if (n_b < a.tile_pages && lane < kTiles * G) {
+    const int tt = lane / G, hh = lane % G;
+    float tm = -INFINITY;
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+      const int pg = tt * 16 + p;
+      if ((present >> pg) & 1ull) tm = fmaxf(tm, out[pg][hh]);
+    }
+    a.tile_max[((size_t)b * a.Hq + (size_t)hbase + hh) * ((size_t)a.n_ranges * kTiles) +
+               (size_t)range * kTiles + tt] = tm;
+  }
+}
+
+// One tile's records as a lane holds them: V rows (page 2vt + row/8, basis
+// vector row%8), and the mu, C and scales of page row
+struct TileRec {
+  uint4 v[8], mu1, mu0, c1, c0;
+  uint2 scl;
+};
+
+// G = query heads per KV head (at most 8)
+template <int G>
 __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
-  constexpr int G = GROUP > 8 ? 8 : GROUP;
-  constexpr int NS = GROUP / G;           // head slices per KV head
+  static_assert(G <= 8, "16-head groups use score16_kernel");
   constexpr int RB = G < 4 ? 1 : G / 4;   // stage-1 row blocks (4 heads each)
   constexpr int PG = 16 / G;              // pages per stage-2 pass
-  __shared__ ScoreLds<G> S;
+  __shared__ ScoreLds<G, TileLds<G>> S;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = lane & 15, kg = lane >> 4;
   const int b = blockIdx.z;
-  // workgroup -> (KV head, head slice, 4 page ranges). Slices are the slow
-  // grid dimension y = kvh * NS + slice over an x extent padded to a multiple
-  // of 8: workgroups are dealt round-robin to the 8 XCDs, so every slice of a
-  // range group lands on the XCD (and L2) that fetched its records first.
-  const int kvh = blockIdx.y / NS;
-  const int slice = blockIdx.y % NS;
+  const int kvh = blockIdx.y;
   const int range = blockIdx.x * 4 + wave;
-  const int hbase = kvh * GROUP + slice * G;  // first query head of this workgroup
+  const int hbase = kvh * G;  // first query head of the group
   const int N = a.N;
   const int n_b = full_pages(a.seq_lens, b, N);
   TileLds<G>& T = S.w[wave];
@@ -132,35 +235,7 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
     const int j = p0 + lane;
     if (range < a.n_ranges && j < n_b) myblk = a.page_table[(size_t)b * N + j];
   }
-
-  // ---- q of the group -> per-head exponent -> three int8 digit planes;
-  // wave w converts heads w, w+4, ...
-  {
-    const float* qg = a.q + ((size_t)b * a.Hq + (size_t)hbase) * kDim;
-    for (int h = wave; h < G; h += 4) {
-      const float q0 = qg[h * kDim + lane], q1 = qg[h * kDim + 64 + lane];
-      const float qm = wave_max(fmaxf(fabsf(q0), fabsf(q1)));
-      int e = 0;
-      if (qm > 0.f) {
-        int E;
-        frexpf(qm, &E);
-        e = 22 - E;  // max |q| * 2^e in [2^21, 2^22)
-      }
-      const float qs[2] = {q0, q1};
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int qf = (int)rintf(ldexpf(qs[u], e));
-        const int d0 = ((qf + 128) & 255) - 128;
-        const int r1 = (qf - d0) / 256;
-        const int d1 = ((r1 + 128) & 255) - 128;
-        const int d2 = (r1 - d1) / 256;
-        S.u.dig[0][h][lane + 64 * u] = (int8_t)d0;
-        S.u.dig[1][h][lane + 64 * u] = (int8_t)d1;
-        S.u.dig[2][h][lane + 64 * u] = (int8_t)d2;
-      }
-      if (lane == 0) S.esc[h] = ldexpf(1.0f, -e) * (kLog2e * kInvSqrtD);
-    }
-  }
+  q_digit_planes<G>(a.q + ((size_t)b * a.Hq + (size_t)hbase) * kDim, S.u.dig, S.esc, wave, lane);
   __syncthreads();
   // row operands: lane (row = (head 4rb + row/4, digit row%4), K group kg), d in [32kg+16m, +16)
   v4i aop[RB][2];
@@ -195,12 +270,6 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
 
   wave_lds_sync();
 
-  // one tile's records as this lane holds them: V rows (page 2vt + row/8,
-  // basis vector row%8), and the mu, C and scales of page row
-  struct TileRec {
-    uint4 v[8], mu1, mu0, c1, c0;
-    uint2 scl;
-  };
   // The 13 loads of tile t go out in a pinned order (the order is worth ~5%
   // of the gather rate at 4-head groups): issue_v the 8 V rows, issue_tail
   // the mu, C and scales after them. Offsets come from the wave's LDS table.
@@ -340,59 +409,295 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
     wave_lds_sync();
   }
 
-  // ---- the wave's scores, written once after its last loads: a store in
-  // flight would hold up the wait for later loads (one in-order counter
-  // covers both); whole 256-byte rows per head coalesce, and streaming
-  // (non-temporal) stores keep them from sitting dirty in L2 until the end
-  // of the launch
-  const bool mine = (present >> lane) & 1ull;
+  write_wave_outputs<G>(a, T.out, present, b, hbase, range, p0, n_b, lane);
+}
+
+// ---- 16 query heads per KV head: one wave decodes each record once for all
+// 16 heads.
+//
+// Work split. A 64-page range is two waves of 32 pages (2 tiles each), and a
+// workgroup takes two ranges: a 1M-token sequence with 2 KV heads then still
+// gives every SIMD four waves. LDS per wave stays under 10 KB (V^T q staged
+// half a tile at a time; the q digit planes share their space with the tile
+// buffers, which are not in use yet), so four workgroups fit a CU. The two
+// waves of a range merge their per-head (max, sum) through LDS at the end.
+//
+// Stage 1 row blocks are the digit planes (rows = the 16 heads): lane (column
+// j, group kg) finds heads 4kg .. 4kg+3 of column j in each plane's output.
+// V^T q goes to LDS as one word per (page, basis vector k, head) holding the
+// f16 hi part and, above it, the lo part, so the lane's 4 heads are one
+// 16-byte store. Stage 2 is one v_mfma_f32_16x16x16_f16 per page over K = 16
+// = (k, part): lane group kg supplies (k = kg, hi), (kg, lo), (kg + 4, hi),
+// (kg + 4, lo), so A repeats two C codes and B is two LDS words.
+// The 16-token log-sum-exp runs on the deviation term alone: the centroid
+// term is the same for the page's 16 tokens and is added after the log. A
+// page's deviations sum to about zero (its coefficients are centred), so the
+// sum of their exp2 is at least about 1 and does not underflow; a sum that
+// overflows gives a non-finite score, and that half tile is redone with the
+// max subtracted.
+constexpr int k16PagesPerWave = kScorePagesPerWave / 2;
+constexpr int k16Tiles = k16PagesPerWave / 16;
+
+struct Tile16Lds {
+  __align__(16) int8_t c[16][128];          // C codes + 128 per page (token-major)
+  __align__(16) uint32_t p[8][kRank][16];   // V^T q * 2^-22 of half a tile, [page][k][head]: f16 hi | lo << 16
+  __align__(16) float a[16][16];            // mu . q per (page, head), digit units
+  float sc[32][2];                          // s_mu, s_V/16 * s_C; rows 16.. take the other lanes' copies
+  float out[k16PagesPerWave][17];           // the wave's page scores, [page][head] (+1 pad), base 2
+};
+struct Score16Lds {
+  union {
+    __align__(16) int8_t dig[3][16][kDim];  // q digit planes (prologue only)
+    Tile16Lds w[4];
+  } u;
+  uint32_t off[4][k16PagesPerWave];         // each wave's page record offsets, 16-byte units
+  float2 ms[2][16];                         // second half of each range: per-head (max, sum of exp2)
+  float esc[16];                            // per head: 2^-e log2(e) / sqrt(128)
+};
+
+__global__ __launch_bounds__(256, 4) void score16_kernel(ScoreArgs a) {
+  constexpr int G = 16;
+  __shared__ Score16Lds S;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row = lane & 15, kg = lane >> 4;
+  const int b = blockIdx.z;
+  const int kvh = blockIdx.y;
+  const int range = blockIdx.x * 2 + (wave >> 1);
+  const int half = wave & 1;
+  const int hbase = kvh * G;
+  const int N = a.N;
+  const int n_b = full_pages(a.seq_lens, b, N);
+  const int p0 = range * kScorePagesPerWave + half * k16PagesPerWave;  // the wave's first page
+
+  if (blockIdx.x * 2 * kScorePagesPerWave >= n_b) return;  // workgroup-uniform
+
+  // A wave past the ranges or the sequence's full pages has no work but still
+  // reaches the workgroup barriers below (no wave returns after this point).
+  const bool active = range < a.n_ranges && p0 < n_b;  // wave-uniform
+  int myblk = -1;
+  if (active && lane < k16PagesPerWave && p0 + lane < n_b) myblk = a.page_table[(size_t)b * N + p0 + lane];
+  q_digit_planes<G>(a.q + ((size_t)b * a.Hq + (size_t)hbase) * kDim, S.u.dig, S.esc, wave, lane);
+  __syncthreads();
+  // row operands: digit plane dg, lane (row = head, kg), d in [32kg+16m, +16)
+  v4i aop[3][2];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const float sc = mine ? T.out[lane][h] * kLn2 : -INFINITY;  // natural log; absent: -inf
-    if (p0 + lane < n_b) __builtin_nontemporal_store(sc, &a.scores[((size_t)b * a.Hq + (size_t)hbase + h) * N + p0 + lane]);
+  for (int dg = 0; dg < 3; ++dg)
+#pragma unroll
+    for (int m = 0; m < 2; ++m) aop[dg][m] = *reinterpret_cast<const v4i*>(&S.u.dig[dg][row][32 * kg + 16 * m]);
+  // stage-2 scales of this lane's head (column row)
+  const float es = S.esc[row], es22 = es * 0x1p22f;
+  __syncthreads();  // digit planes consumed: their space becomes the tile buffers
+
+  Tile16Lds& T = S.u.w[wave];
+  if (myblk < 0 || myblk >= a.num_blocks) myblk = -1;
+  const unsigned long long present = __ballot(myblk >= 0);  // bit i: page p0 + i
+  if (active) {
+    if (lane < k16PagesPerWave)
+      S.off[wave][lane] = (uint32_t)((myblk < 0 ? 0 : myblk) * a.Hkv + kvh) * (uint32_t)(kStride / 16);
+    const uint8_t* vbase = a.summ + kVOff + (row & 7) * 64 + kg * 16;
+    const uint8_t* rbase = a.summ + kg * 32;
+    wave_lds_sync();
+
+    // a tile's loads in three groups, in the order they are consumed: V rows
+    // of pages 0-7, the mu, C and scales, V rows of pages 8-15
+    auto issue_v = [&](int t, int h, TileRec& r) {
+      uint32_t ov[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ov[i] = S.off[wave][t * 16 + 2 * (4 * h + i) + (row >> 3)];
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        r.v[4 * h + i] = *reinterpret_cast<const uint4*>(vbase + ((size_t)ov[i] << 4));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    auto issue_tail = [&](int t, TileRec& r) {
+      const uint8_t* rec = rbase + ((size_t)S.off[wave][t * 16 + row] << 4);  // page t*16 + row
+      __builtin_amdgcn_sched_barrier(0);
+      r.mu1 = *reinterpret_cast<const uint4*>(rec + kMuOff + 16);
+      r.mu0 = *reinterpret_cast<const uint4*>(rec + kMuOff);
+      r.c1 = *reinterpret_cast<const uint4*>(rec + kCOff + 16);
+      r.c0 = *reinterpret_cast<const uint4*>(rec + kCOff);
+      r.scl = *reinterpret_cast<const uint2*>(rec - kg * 32 + kSOff);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // stage 1 for the V rows of half h of the tile -> T.p (pages 8h .. 8h+7)
+    auto stage1 = [&](const TileRec& r, int h) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint4 v = r.v[4 * h + i];
+        const v4i B0 = {nib_lo(v.x), nib_hi(v.x), nib_lo(v.y), nib_hi(v.y)};
+        const v4i B1 = {nib_lo(v.z), nib_hi(v.z), nib_lo(v.w), nib_hi(v.w)};
+        v4i s[3];
+#pragma unroll
+        for (int dg = 0; dg < 3; ++dg) s[dg] = mfma_i8(aop[dg][1], B1, mfma_i8(aop[dg][0], B0, v4i{0, 0, 0, 0}));
+        uint32_t w[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float x = digits_to_float(s[0][j], s[1][j], s[2][j]) * 0x1p-22f;  // into f16 range
+          const _Float16 xh = (_Float16)x;
+          const _Float16 xl = (_Float16)(x - (float)xh);
+          w[j] = (uint32_t)__builtin_bit_cast(uint16_t, xh) | ((uint32_t)__builtin_bit_cast(uint16_t, xl) << 16);
+        }
+        *reinterpret_cast<uint4*>(&T.p[2 * i + (row >> 3)][row & 7][4 * kg]) = uint4{w[0], w[1], w[2], w[3]};
+      }
+    };
+
+    // stage 2 + LSE of tile page pp (T.p holds its half); lane (head row, kg)
+    // gets tokens 4kg .. 4kg+3. safe: subtract the page's max first.
+    const h2 bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+    const uint32_t csel = 0x04000400u | (uint32_t)kg | ((uint32_t)kg << 16);  // bytes kg, 0x64, kg, 0x64
+    auto pass = [&](int pp, bool safe) -> float {
+      const uint2 cw = *reinterpret_cast<const uint2*>(&T.c[pp][row * 8]);  // token row, k = 0..7
+      const h2 clo = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, cw.x, csel)) + bias;
+      const h2 chi = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, cw.y, csel)) + bias;
+      const h4 A = {clo[0], clo[1], chi[0], chi[1]};
+      const h2 p0v = __builtin_bit_cast(h2, T.p[pp & 7][kg][row]);
+      const h2 p1v = __builtin_bit_cast(h2, T.p[pp & 7][kg + 4][row]);
+      const h4 B = {p0v[0], p0v[1], p1v[0], p1v[1]};
+      const v4f acc = __builtin_amdgcn_mfma_f32_16x16x16f16(A, B, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      const float2 scv = *reinterpret_cast<const float2*>(&T.sc[pp][0]);
+      const float sv = scv.y * es22;
+      const float d0 = acc[0] * sv, d1 = acc[1] * sv, d2 = acc[2] * sv, d3 = acc[3] * sv;
+      float mx = 0.f;
+      if (safe) {
+        mx = fmaxf(fmaxf(d0, d1), fmaxf(d2, d3));
+        mx = xor32_max(xor16_max(mx));
+      }
+      float ssum = (fast_exp2(d0 - mx) + fast_exp2(d1 - mx)) + (fast_exp2(d2 - mx) + fast_exp2(d3 - mx));
+      ssum = xor32_sum(xor16_sum(ssum));
+      return fmaf(T.a[pp][row], scv.x * es, mx + fast_log2(ssum));
+    };
+    // the 8 passes of half h as one branch-free block; lane kg keeps pages
+    // 4i + kg (i = 2h, 2h + 1)
+    auto stage2 = [&](int h, float (&keep)[4]) {
+#pragma unroll
+      for (int pp = 8 * h; pp < 8 * h + 8; ++pp) {
+        const float r = pass(pp, false);
+        keep[pp >> 2] = ((pp & 3) == kg) ? r : keep[pp >> 2];
+      }
+      const bool redo = !__builtin_isfinite(keep[2 * h]) || !__builtin_isfinite(keep[2 * h + 1]);
+      if (__builtin_expect(__ballot(redo) != 0ull, 0)) {
+#pragma unroll 1
+        for (int pp = 8 * h; pp < 8 * h + 8; ++pp) {
+          const float r = pass(pp, true);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) keep[i] = (i == (pp >> 2) && (pp & 3) == kg) ? r : keep[i];
+        }
+      }
+    };
+
+    TileRec cur, nxt;
+    issue_v(0, 0, cur);
+    issue_tail(0, cur);
+    issue_v(0, 1, cur);
+#pragma unroll
+    for (int t = 0; t < k16Tiles; ++t) {
+      const bool more = t + 1 < k16Tiles;
+      stage1(cur, 0);
+      if (more) issue_v(t + 1, 0, nxt);
+      __builtin_amdgcn_sched_barrier(0);
+      // ---- stage 1: mu tile (columns = the 16 pages); lane (page row, kg) -> heads 4kg ..
+      {
+        const uint4 mu0 = cur.mu0, mu1 = cur.mu1;
+        const v4i B0 = {(int)mu0.x, (int)mu0.y, (int)mu0.z, (int)mu0.w};
+        const v4i B1 = {(int)mu1.x, (int)mu1.y, (int)mu1.z, (int)mu1.w};
+        v4i s[3];
+#pragma unroll
+        for (int dg = 0; dg < 3; ++dg) s[dg] = mfma_i8(aop[dg][1], B1, mfma_i8(aop[dg][0], B0, v4i{0, 0, 0, 0}));
+        float4 av;
+        av.x = digits_to_float(s[0][0], s[1][0], s[2][0]);
+        av.y = digits_to_float(s[0][1], s[1][1], s[2][1]);
+        av.z = digits_to_float(s[0][2], s[1][2], s[2][2]);
+        av.w = digits_to_float(s[0][3], s[1][3], s[2][3]);
+        *reinterpret_cast<float4*>(&T.a[row][4 * kg]) = av;
+        const uint4 c0 = cur.c0, c1 = cur.c1;
+        *reinterpret_cast<uint4*>(&T.c[row][kg * 32]) =
+            uint4{c0.x ^ 0x80808080u, c0.y ^ 0x80808080u, c0.z ^ 0x80808080u, c0.w ^ 0x80808080u};
+        *reinterpret_cast<uint4*>(&T.c[row][kg * 32 + 16]) =
+            uint4{c1.x ^ 0x80808080u, c1.y ^ 0x80808080u, c1.z ^ 0x80808080u, c1.w ^ 0x80808080u};
+        const uint2 scl = cur.scl;
+        const int r = kg == 0 ? row : 16 + row;
+        T.sc[r][0] = f16bits_to_float(scl.x);
+        T.sc[r][1] = f16bits_to_float(scl.x >> 16) * (1.0f / 16.0f) * f16bits_to_float(scl.y);
+      }
+      if (more) issue_tail(t + 1, nxt);
+      wave_lds_sync();
+      float keep[4] = {0.f, 0.f, 0.f, 0.f};
+      stage2(0, keep);
+      wave_lds_sync();  // half 0 of T.p read: half 1 takes its place
+      stage1(cur, 1);
+      if (more) issue_v(t + 1, 1, nxt);
+      wave_lds_sync();
+      stage2(1, keep);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) T.out[t * 16 + 4 * i + kg][row] = keep[i];
+      wave_lds_sync();
+      if (more) cur = nxt;
+    }
   }
 
-  // ---- per-head (max, sum) of exp2 over the wave's pages: lane takes head
-  // lane % G and pages i * 64/G + lane / G, then lanes of one head merge
-  constexpr int LPH = kScorePagesPerWave / G;
-  float m = -INFINITY, v[G];
+  // ---- per-head (max, sum of exp2) over the wave's present pages: lane
+  // (head row, kg) takes pages 4i + kg, then the 4 lanes of a head merge
+  float m = -INFINITY, ssum = 0.f;
+  if (active) {
+    float v[k16PagesPerWave / 4];
 #pragma unroll
-  for (int i = 0; i < G; ++i) {
-    const int pg = i * LPH + lane / G;
-    v[i] = ((present >> pg) & 1ull) ? T.out[pg][lane % G] : -INFINITY;
-    m = fmaxf(m, v[i]);
-  }
-  float ssum = 0.f;
-  {
+    for (int i = 0; i < k16PagesPerWave / 4; ++i) {
+      const int pg = 4 * i + kg;
+      v[i] = ((present >> pg) & 1ull) ? T.out[pg][row] : -INFINITY;
+      m = fmaxf(m, v[i]);
+    }
     const float ms = m == -INFINITY ? 0.f : m;
 #pragma unroll
-    for (int i = 0; i < G; ++i) ssum += fast_exp2(v[i] - ms);
-  }
+    for (int i = 0; i < k16PagesPerWave / 4; ++i) ssum += fast_exp2(v[i] - ms);
 #pragma unroll
-  for (int off = G; off < 64; off <<= 1) {
-    const float m2 = __shfl_xor(m, off), s2 = __shfl_xor(ssum, off);
-    const float mn = fmaxf(m, m2);
-    const float ms = mn == -INFINITY ? 0.f : mn;
-    ssum = ssum * fast_exp2(m - ms) + s2 * fast_exp2(m2 - ms);
-    m = mn;
+    for (int off = 16; off < 64; off <<= 1) {
+      const float m2 = __shfl_xor(m, off), s2 = __shfl_xor(ssum, off);
+      const float mn = fmaxf(m, m2);
+      const float mz = mn == -INFINITY ? 0.f : mn;
+      ssum = ssum * fast_exp2(m - mz) + s2 * fast_exp2(m2 - mz);
+      m = mn;
+    }
   }
-  if (lane < G) {
-    float* dst = a.partials + (((size_t)b * a.Hq + (size_t)hbase + lane) * a.n_ranges + range) * 2;
-    dst[0] = (ssum > 0.f) ? m : -INFINITY;
-    dst[1] = ssum;
+  if (half == 1 && lane < 16) S.ms[wave >> 1][row] = make_float2(m, ssum);
+  __syncthreads();
+  if (!active) return;
+  if (half == 0 && lane < 16) {
+    const float2 o = S.ms[wave >> 1][row];
+    const float mn = fmaxf(m, o.x);
+    const float mz = mn == -INFINITY ? 0.f : mn;
+    const float st = ssum * fast_exp2(m - mz) + o.y * fast_exp2(o.x - mz);
+    float* dst = a.partials + (((size_t)b * a.Hq + (size_t)hbase + row) * a.n_ranges + range) * 2;
+    dst[0] = (st > 0.f) ? mn : -INFINITY;
+    dst[1] = st;
   }
-  // ---- per head and 16-page tile: the max of s_hat (base 2; -inf if no page),
-  // for a sequence whose selection bounds by tiles
-  if (n_b < a.tile_pages && lane < kTiles * G) {
-    const int tt = lane / G, hh = lane % G;
+  // ---- page scores (natural log; -inf for an absent page): lane = page
+  // lane % 32, heads 2j + lane / 32, so each store covers 128 bytes of 2 heads
+  {
+    const int pg = lane & 31;
+    const bool mine = (present >> pg) & 1ull;
+    if (p0 + pg < n_b) {
+#pragma unroll
+      for (int j = 0; j < G / 2; ++j) {
+        const int h = 2 * j + (lane >> 5);
+        const float sc = mine ? T.out[pg][h] * kLn2 : -INFINITY;
+        __builtin_nontemporal_store(sc, &a.scores[((size_t)b * a.Hq + (size_t)hbase + h) * N + p0 + pg]);
+      }
+    }
+  }
+  // ---- per head and 16-page tile: the max of s_hat (base 2; -inf if no page)
+  if (n_b < a.tile_pages && lane < k16Tiles * 16) {
+    const int tt = lane >> 4;
     float tm = -INFINITY;
 #pragma unroll
     for (int p = 0; p < 16; ++p) {
       const int pg = tt * 16 + p;
-      if ((present >> pg) & 1ull) tm = fmaxf(tm, T.out[pg][hh]);
+      if ((present >> pg) & 1ull) tm = fmaxf(tm, T.out[pg][row]);
     }
-    a.tile_max[((size_t)b * a.Hq + (size_t)hbase + hh) * ((size_t)a.n_ranges * kTiles) +
-               (size_t)range * kTiles + tt] = tm;
+    a.tile_max[((size_t)b * a.Hq + (size_t)hbase + row) * ((size_t)a.n_ranges * kTiles) +
+               (size_t)range * kTiles + 2 * half + tt] = tm;
   }
 }
 
@@ -413,10 +718,13 @@ hipError_t launch_g(const locks_dims& d, const WsLayout& L, const DevPtrs& P, co
   a.N = d.max_pages_per_seq;
   a.num_blocks = d.num_blocks;
   a.n_ranges = L.n_score_wg;
-  constexpr int NS = G > 8 ? G / 8 : 1;
-  const int nrg = (L.n_score_wg + 3) / 4;
-  dim3 grid(NS == 1 ? nrg : (nrg + 7) / 8 * 8, d.n_kv_heads * NS, d.batch);
-  hipLaunchKernelGGL(score_kernel<G>, grid, dim3(256), 0, s, a);
+  if constexpr (G == 16) {
+    const dim3 grid((L.n_score_wg + 1) / 2, d.n_kv_heads, d.batch);  // two ranges per workgroup
+    hipLaunchKernelGGL(score16_kernel, grid, dim3(256), 0, s, a);
+  } else {
+    const dim3 grid((L.n_score_wg + 3) / 4, d.n_kv_heads, d.batch);  // four ranges per workgroup
+    hipLaunchKernelGGL(score_kernel<G>, grid, dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -80,9 +80,10 @@ def test_decode_parity_on_oracle_built_summaries(locks):
     decode_and_check(w, torch.from_numpy(summ).to(DEV))
 
 
-def test_edge_cases(locks):
+@pytest.mark.parametrize("hkv", [8, 2], ids=["G4", "G16"])
+def test_edge_cases(locks, hkv):
     """Empty sequence, partial last page, absent pages (block -1), budget >= pages."""
-    w = workloads.make(2, device=DEV, ctx=16 * 300, batch=4, budget=512,
+    w = workloads.make(2, device=DEV, ctx=16 * 300, batch=4, budget=512, n_kv_heads=hkv, n_q_heads=32,
                        seq_lens=[0, 16 * 300, 16 * 37 + 9, 16 * 20], seed=5)
     pt = w.page_table.clone()
     pt[1, 5] = -1
