@@ -349,9 +349,16 @@ __global__ __launch_bounds__(kThreads) void select_chunk_kernel(SelectArgs a) {
   unsigned long long x[kChunkEpt];
 #pragma unroll
   for (int i = 0; i < kChunkEpt; ++i) {
-    float km = -1e30f, ks = 0.f;
+    // log2 of sum_g exp2(s_hat_g - L_g): the max over the group first, then
+    // one exp2 per head
+    float v[G], km = -1e30f, ks = 0.f;
 #pragma unroll
-    for (int gg = 0; gg < G; ++gg) lse2_acc(km, ks, sc[gg][i] * kLog2e - L[gg], 1.0f);
+    for (int gg = 0; gg < G; ++gg) {
+      v[gg] = fmaf(sc[gg][i], kLog2e, -L[gg]);
+      km = fmaxf(km, v[gg]);
+    }
+#pragma unroll
+    for (int gg = 0; gg < G; ++gg) ks += fast_exp2(v[gg] - km);
     const bool in = i < ept && p0 + i * kThreads < n_b;
     // log2 of the summed shares minus log2 G; absent pages score -inf
     const float key2 = (in && ks > 0.f && km > -1e29f) ? km + fast_log2(ks) - log2G : -INFINITY;
