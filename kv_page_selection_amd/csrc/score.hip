@@ -205,9 +205,10 @@ struct TileRec {
   uint2 scl;
 };
 
-// G = query heads per KV head (at most 8)
+// G = query heads per KV head (at most 8). 8-head waves are held to 128
+// VGPRs (4 waves per SIMD; left alone they take a few more and drop to 3).
 template <int G>
-__global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
+__global__ __launch_bounds__(256, G == 8 ? 4 : 1) void score_kernel(ScoreArgs a) {
   static_assert(G <= 8, "16-head groups use score16_kernel");
   constexpr int RB = G < 4 ? 1 : G / 4;   // stage-1 row blocks (4 heads each)
   constexpr int PG = 16 / G;              // pages per stage-2 pass
@@ -266,7 +267,7 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
 
   // stage-2 output column col = (page pc of the pass, head hc)
   const int pc = row / G, hc = row % G;
-  const float es = S.esc[hc];
+  const float es = S.esc[hc], es22 = es * 0x1p22f;
 
   wave_lds_sync();
 
@@ -363,9 +364,12 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
     if (kPrefetchV && t + 1 < kTiles) issue_v(t + 1, cur);
     wave_lds_sync();
 
-    // ---- stage 2 + LSE, one pass per PG pages
-#pragma unroll
-    for (int gp = 0; gp < G; ++gp) {
+    // ---- stage 2 + LSE, one pass per PG pages. The G passes are one
+    // branch-free block (the 4 lanes of an output column store the same
+    // value), and the LSE sums exp2 of the deviation term alone, adding the
+    // centroid term after the log; a non-finite result (an overflowed sum)
+    // redoes the tile's passes with the page max subtracted.
+    auto pass = [&](int gp, bool safe) -> float {
       v4f acc = {0.f, 0.f, 0.f, 0.f};
       const int pp = gp * PG + pc;  // tile page of this lane's output column
       if constexpr (PG >= 4) {
@@ -396,15 +400,27 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a) {
         acc = __builtin_amdgcn_mfma_f32_16x16x16f16(A, Bl, acc, 0, 0, 0);
       }
       // lane (col = row, kg) holds tokens 4kg .. 4kg+3 of (page pp, head hc)
-      const float sa = T.sc[pp][0] * es, sv = T.sc[pp][1] * es * 0x1p22f;
-      const float base = T.a[pp][hc] * sa;
-      const float t0 = fmaf(acc[0], sv, base), t1 = fmaf(acc[1], sv, base);
-      const float t2 = fmaf(acc[2], sv, base), t3 = fmaf(acc[3], sv, base);
-      float mx = fmaxf(fmaxf(t0, t1), fmaxf(t2, t3));
-      mx = xor32_max(xor16_max(mx));
-      float ssum = fast_exp2(t0 - mx) + fast_exp2(t1 - mx) + fast_exp2(t2 - mx) + fast_exp2(t3 - mx);
+      const float sv = T.sc[pp][1] * es22;
+      const float d0 = acc[0] * sv, d1 = acc[1] * sv, d2 = acc[2] * sv, d3 = acc[3] * sv;
+      float mx = 0.f;
+      if (safe) {
+        mx = fmaxf(fmaxf(d0, d1), fmaxf(d2, d3));
+        mx = xor32_max(xor16_max(mx));
+      }
+      float ssum = (fast_exp2(d0 - mx) + fast_exp2(d1 - mx)) + (fast_exp2(d2 - mx) + fast_exp2(d3 - mx));
       ssum = xor32_sum(xor16_sum(ssum));
-      if (kg == 0) T.out[t * 16 + pp][hc] = mx + fast_log2(ssum);
+      return fmaf(T.a[pp][hc], T.sc[pp][0] * es, mx + fast_log2(ssum));
+    };
+    bool redo = false;
+#pragma unroll
+    for (int gp = 0; gp < G; ++gp) {
+      const float r = pass(gp, false);
+      redo |= !__builtin_isfinite(r);
+      T.out[t * 16 + gp * PG + pc][hc] = r;
+    }
+    if (__builtin_expect(__ballot(redo) != 0ull, 0)) {
+#pragma unroll 1
+      for (int gp = 0; gp < G; ++gp) T.out[t * 16 + gp * PG + pc][hc] = pass(gp, true);
     }
     wave_lds_sync();
   }
