@@ -97,8 +97,15 @@ template <int M>
 __device__ __forceinline__ void jacobi_round(float (&a)[kPage], float (&u)[kPage], int i,
                                              float2* rot) {
   const bool lower = i < (i ^ M);
-  const float d_me = a[0], d_other = swz<M>(a[0]);
-  const float o_me = a[M], o_other = swz<M>(a[M]);
+  // the partner row, slot-permuted: pa[t] = partner's slot t ^ M (column i ^ t).
+  // All 16 swizzles go out before any is used, so the round waits on LDS
+  // latency once rather than once per element.
+  float pa[kPage];
+#pragma unroll
+  for (int tt = 0; tt < kPage; ++tt) pa[tt] = swz<M>(a[tt ^ M]);
+  __builtin_amdgcn_sched_barrier(0);
+  const float d_me = a[0], d_other = pa[M];
+  const float o_me = a[M], o_other = pa[0];
   // both lanes of a pair take the same inputs, hence the same angle
   const float app = lower ? d_me : d_other, aqq = lower ? d_other : d_me;
   const float apq = lower ? o_me : o_other;
@@ -115,16 +122,21 @@ __device__ __forceinline__ void jacobi_round(float (&a)[kPage], float (&u)[kPage
   // rows: row_i <- c row_i + sg row_partner; the partner's slot t ^ M is column i ^ t
   float ar[kPage];
 #pragma unroll
-  for (int tt = 0; tt < kPage; ++tt) ar[tt] = fmaf(c, a[tt], sg * swz<M>(a[tt ^ M]));
+  for (int tt = 0; tt < kPage; ++tt) ar[tt] = fmaf(c, a[tt], sg * pa[tt]);
   rot[i] = make_float2(c, sg);
   wave_lds_sync();
+  // the angles of all 16 columns this lane's slots hold, read together
+  float2 rc[kPage];
+#pragma unroll
+  for (int tt = 0; tt < kPage; ++tt) rc[tt] = rot[i ^ tt];
+  __builtin_amdgcn_sched_barrier(0);
   // columns: slot t is column x = i ^ t, rotated with column x ^ M (slot t ^ M);
   // updated in place one slot pair at a time
 #pragma unroll
   for (int tt = 0; tt < kPage; ++tt) {
     if (tt < (tt ^ M)) {
       const int t2 = tt ^ M;
-      const float2 r1 = rot[i ^ tt], r2 = rot[i ^ t2];
+      const float2 r1 = rc[tt], r2 = rc[t2];
       a[tt] = fmaf(r1.x, ar[tt], r1.y * ar[t2]);
       a[t2] = fmaf(r2.x, ar[t2], r2.y * ar[tt]);
       const float u1 = u[tt], u2 = u[t2];
