@@ -98,6 +98,30 @@ def test_edge_cases(locks, hkv):
     assert 5 not in sel[1] and 200 not in sel[1]
 
 
+@pytest.mark.parametrize("hkv", [32, 16, 8, 4, 2], ids=["G1", "G2", "G4", "G8", "G16"])
+def test_overflowing_deviation_terms(locks, hkv):
+    """Keys scaled by 300: on some pages a token's deviation term (its logit
+    minus the page's centroid logit) exceeds 128 in base 2, so the scoring
+    kernels' sum of exp2 over the deviations alone overflows and those pages
+    are scored again with the page max subtracted. Same bars as everywhere."""
+    w = workloads.make(2, device=DEV, ctx=16 * 300, budget=512, n_kv_heads=hkv, n_q_heads=32, seed=41)
+    w.k_cache = (w.k_cache.float() * 300.0).to(torch.bfloat16)
+    summ = locks.build_summaries(w.k_cache, w.page_table, w.seq_lens)
+    q, pt, sl = host(w)
+    sm = summ.cpu().numpy()
+    G = 32 // hkv
+    dev_max = 0.0  # largest deviation term over a sample of pages, base 2
+    for j in range(0, w.max_pages, 7):
+        for h in range(hkv):
+            mu, V, C = oracle.unpack_record(sm[pt[0, j], h])
+            for g in range(G):
+                dev = C @ (V.T @ q[0, h * G + g].astype(np.float64)) / np.sqrt(128.0) / np.log(2.0)
+                dev_max = max(dev_max, float(dev.max()))
+    assert dev_max > 130.0, f"premise: the largest deviation term is only {dev_max:.1f} (base 2)"
+    say(f"overflowing deviation terms, G={G}: largest sampled {dev_max:.0f} (base 2)")
+    decode_and_check(w, summ)
+
+
 @pytest.mark.parametrize("budget", [512, 2048])
 def test_mixed_lengths_use_both_bound_units(locks, budget):
     """One batch whose sequences bound their selection differently: sequences
