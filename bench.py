@@ -53,9 +53,16 @@ def algorithmic_bytes(B, Hq, Hkv, N, k, n_sel):
 
 
 def source_hash(paths):
+    """Hash of the sources' code: comments and whitespace are left out, so a
+    change of documentation does not mark counter figures stale, any change of
+    code does."""
+    import re
     h = hashlib.sha256()
     for p in paths:
-        h.update(open(p, "rb").read())
+        text = open(p, encoding="utf-8").read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()
 
 

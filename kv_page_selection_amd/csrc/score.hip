@@ -7,9 +7,11 @@
 // from the page's summary record alone (no key or value is read).
 //
 // Mapping. A workgroup is 4 waves of one KV head and all G of its query heads;
-// wave w scores 64 consecutive pages (4 tiles of 16), and the waves take 4
-// consecutive page ranges. The q prologue (fixed-point digits of the group's
-// query heads) is split over the 4 waves and shared in LDS.
+// up to 8 heads, wave w scores 64 consecutive pages (4 tiles of 16) and the
+// waves take 4 consecutive page ranges; with 16 heads two waves share a
+// 64-page range (32 pages each) and a workgroup takes 2 ranges. The q
+// prologue (fixed-point digits of the group's query heads) is split over the
+// 4 waves and shared in LDS.
 //
 // Stage 1, mu.q and V^T q, on v_mfma_i32_16x16x64_i8, exact: the row operand is
 // each query head as a 22-bit fixed-point integer in three signed int8 digits,
@@ -31,9 +33,9 @@
 // combine needs for every head's total mass, and the max of each 16-page tile,
 // the units of the selection's pruning bound.
 //
-// Loads. Each wave turns its 64 page-table entries into record offsets once
-// (an LDS table); every tile then issues its 13 record loads back to back in
-// a fixed order (V rows first) and consumes them in that order, so the first
+// Loads. Each wave turns its page-table entries into record offsets once (an
+// LDS table); every tile then issues its 13 record loads back to back in a
+// fixed order (V rows first) and consumes them in that order, so the first
 // MFMAs run while the tail of the tile is still arriving.
 #include "device_common.h"
 #include "internal.h"
