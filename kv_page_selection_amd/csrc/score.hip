@@ -137,6 +137,29 @@ __device__ __forceinline__ float digits_to_float(int s0, int s1, int s2) {
   return (float)(s2 * 256 + s1) * 256.0f + (float)s0;
 }
 
+// Reduce-scatter of 4 passes' per-lane partial sums over the 4 lane groups (16
+// lanes each) of a wave: one v_permlane16_swap pairs groups (0, 1) and (2, 3),
+// one v_permlane32_swap pairs the halves, and each swap leaves a lane two
+// copies of one pass, its own and its partner's. A lane ends with the total of
+// pass reduce_scatter4_pass() of the four.
+__device__ __forceinline__ float swap16_sum(float x, float y) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float swap32_sum(float x, float y) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float reduce_scatter4(float s0, float s1, float s2, float s3) {
+  return swap32_sum(swap16_sum(s0, s1), swap16_sum(s2, s3));
+}
+// the pass a lane keeps: the same two swaps applied to pass tags
+__device__ __forceinline__ int reduce_scatter4_pass() {
+  const auto a = __builtin_amdgcn_permlane16_swap(0u, 1u, false, false);
+  const auto b = __builtin_amdgcn_permlane32_swap(0u, 1u, false, false);
+  return (int)a[0] + 2 * (int)b[0];
+}
+
 // A wave's outputs from its base-2 scores out[page][head] (pages p0 .. p0+63
 // of sequence b, query heads hbase ..): page scores in natural log (-inf for
 // an absent page), the per-head (max, sum of exp2) over the range, and, for a
@@ -270,6 +293,7 @@ __global__ __launch_bounds__(256, G == 8 ? 4 : 1) void score_kernel(ScoreArgs a)
   // stage-2 output column col = (page pc of the pass, head hc)
   const int pc = row / G, hc = row % G;
   const float es = S.esc[hc], es22 = es * 0x1p22f;
+  const int jpass = reduce_scatter4_pass();  // with G >= 4: which pass of each 4 this lane finishes
 
   wave_lds_sync();
 
@@ -366,12 +390,14 @@ __global__ __launch_bounds__(256, G == 8 ? 4 : 1) void score_kernel(ScoreArgs a)
     if (kPrefetchV && t + 1 < kTiles) issue_v(t + 1, cur);
     wave_lds_sync();
 
-    // ---- stage 2 + LSE, one pass per PG pages. The G passes are one
-    // branch-free block (the 4 lanes of an output column store the same
-    // value), and the LSE sums exp2 of the deviation term alone, adding the
-    // centroid term after the log; a non-finite result (an overflowed sum)
-    // redoes the tile's passes with the page max subtracted.
-    auto pass = [&](int gp, bool safe) -> float {
+    // ---- stage 2 + LSE, one pass per PG pages, as one branch-free block.
+    // The LSE sums exp2 of the deviation term alone and adds the centroid
+    // term after the log; a non-finite result (an overflowed sum) redoes the
+    // tile's passes with the page max subtracted. With 4 or more passes, each
+    // 4 share one reduce-scatter over the lane groups and each lane group
+    // finishes one of them; with fewer, every lane of a column reduces and
+    // stores the same value.
+    auto deviations = [&](int gp) -> v4f {
       v4f acc = {0.f, 0.f, 0.f, 0.f};
       const int pp = gp * PG + pc;  // tile page of this lane's output column
       if constexpr (PG >= 4) {
@@ -403,26 +429,48 @@ __global__ __launch_bounds__(256, G == 8 ? 4 : 1) void score_kernel(ScoreArgs a)
       }
       // lane (col = row, kg) holds tokens 4kg .. 4kg+3 of (page pp, head hc)
       const float sv = T.sc[pp][1] * es22;
-      const float d0 = acc[0] * sv, d1 = acc[1] * sv, d2 = acc[2] * sv, d3 = acc[3] * sv;
+      return v4f{acc[0] * sv, acc[1] * sv, acc[2] * sv, acc[3] * sv};
+    };
+    auto part_sum = [&](int gp) -> float {
+      const v4f d = deviations(gp);
+      return (fast_exp2(d[0]) + fast_exp2(d[1])) + (fast_exp2(d[2]) + fast_exp2(d[3]));
+    };
+    // pass gp's score (every lane of the column); safe: page max subtracted first
+    auto score_full = [&](int gp, bool safe) -> float {
+      const v4f d = deviations(gp);
+      const int pp = gp * PG + pc;
       float mx = 0.f;
       if (safe) {
-        mx = fmaxf(fmaxf(d0, d1), fmaxf(d2, d3));
+        mx = fmaxf(fmaxf(d[0], d[1]), fmaxf(d[2], d[3]));
         mx = xor32_max(xor16_max(mx));
       }
-      float ssum = (fast_exp2(d0 - mx) + fast_exp2(d1 - mx)) + (fast_exp2(d2 - mx) + fast_exp2(d3 - mx));
+      float ssum = (fast_exp2(d[0] - mx) + fast_exp2(d[1] - mx)) + (fast_exp2(d[2] - mx) + fast_exp2(d[3] - mx));
       ssum = xor32_sum(xor16_sum(ssum));
       return fmaf(T.a[pp][hc], T.sc[pp][0] * es, mx + fast_log2(ssum));
     };
     bool redo = false;
+    if constexpr (G >= 4) {
 #pragma unroll
-    for (int gp = 0; gp < G; ++gp) {
-      const float r = pass(gp, false);
-      redo |= !__builtin_isfinite(r);
-      T.out[t * 16 + gp * PG + pc][hc] = r;
+      for (int g = 0; g < G / 4; ++g) {
+        const float s0 = part_sum(4 * g), s1 = part_sum(4 * g + 1);
+        const float s2 = part_sum(4 * g + 2), s3 = part_sum(4 * g + 3);
+        const float tot = reduce_scatter4(s0, s1, s2, s3);
+        const int pp = (4 * g + jpass) * PG + pc;
+        const float r = fmaf(T.a[pp][hc], T.sc[pp][0] * es, fast_log2(tot));
+        redo |= !__builtin_isfinite(r);
+        T.out[t * 16 + pp][hc] = r;
+      }
+    } else {
+#pragma unroll
+      for (int gp = 0; gp < G; ++gp) {
+        const float r = score_full(gp, false);
+        redo |= !__builtin_isfinite(r);
+        T.out[t * 16 + gp * PG + pc][hc] = r;
+      }
     }
     if (__builtin_expect(__ballot(redo) != 0ull, 0)) {
 #pragma unroll 1
-      for (int gp = 0; gp < G; ++gp) T.out[t * 16 + gp * PG + pc][hc] = pass(gp, true);
+      for (int gp = 0; gp < G; ++gp) T.out[t * 16 + gp * PG + pc][hc] = score_full(gp, true);
     }
     wave_lds_sync();
   }
@@ -504,6 +552,7 @@ __global__ __launch_bounds__(256, 4) void score16_kernel(ScoreArgs a) {
     for (int m = 0; m < 2; ++m) aop[dg][m] = *reinterpret_cast<const v4i*>(&S.u.dig[dg][row][32 * kg + 16 * m]);
   // stage-2 scales of this lane's head (column row)
   const float es = S.esc[row], es22 = es * 0x1p22f;
+  const int jpass = reduce_scatter4_pass();  // which page of each 4 this lane finishes
   __syncthreads();  // digit planes consumed: their space becomes the tile buffers
 
   Tile16Lds& T = S.u.w[wave];
@@ -562,11 +611,11 @@ __global__ __launch_bounds__(256, 4) void score16_kernel(ScoreArgs a) {
       }
     };
 
-    // stage 2 + LSE of tile page pp (T.p holds its half); lane (head row, kg)
-    // gets tokens 4kg .. 4kg+3. safe: subtract the page's max first.
+    // stage 2 of tile page pp (T.p holds its half): lane (head row, kg) gets
+    // the deviation terms of tokens 4kg .. 4kg+3
     const h2 bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
     const uint32_t csel = 0x04000400u | (uint32_t)kg | ((uint32_t)kg << 16);  // bytes kg, 0x64, kg, 0x64
-    auto pass = [&](int pp, bool safe) -> float {
+    auto deviations = [&](int pp) -> v4f {
       const uint2 cw = *reinterpret_cast<const uint2*>(&T.c[pp][row * 8]);  // token row, k = 0..7
       const h2 clo = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, cw.x, csel)) + bias;
       const h2 chi = __builtin_bit_cast(h2, __builtin_amdgcn_perm(0x64646464u, cw.y, csel)) + bias;
@@ -575,34 +624,40 @@ __global__ __launch_bounds__(256, 4) void score16_kernel(ScoreArgs a) {
       const h2 p1v = __builtin_bit_cast(h2, T.p[pp & 7][kg + 4][row]);
       const h4 B = {p0v[0], p0v[1], p1v[0], p1v[1]};
       const v4f acc = __builtin_amdgcn_mfma_f32_16x16x16f16(A, B, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-      const float2 scv = *reinterpret_cast<const float2*>(&T.sc[pp][0]);
-      const float sv = scv.y * es22;
-      const float d0 = acc[0] * sv, d1 = acc[1] * sv, d2 = acc[2] * sv, d3 = acc[3] * sv;
-      float mx = 0.f;
-      if (safe) {
-        mx = fmaxf(fmaxf(d0, d1), fmaxf(d2, d3));
-        mx = xor32_max(xor16_max(mx));
-      }
-      float ssum = (fast_exp2(d0 - mx) + fast_exp2(d1 - mx)) + (fast_exp2(d2 - mx) + fast_exp2(d3 - mx));
-      ssum = xor32_sum(xor16_sum(ssum));
-      return fmaf(T.a[pp][row], scv.x * es, mx + fast_log2(ssum));
+      const float sv = T.sc[pp][1] * es22;
+      return v4f{acc[0] * sv, acc[1] * sv, acc[2] * sv, acc[3] * sv};
     };
-    // the 8 passes of half h as one branch-free block; lane kg keeps pages
-    // 4i + kg (i = 2h, 2h + 1)
-    auto stage2 = [&](int h, float (&keep)[4]) {
+    // the lane's part of sum_i exp2(deviation_i) for page pp
+    auto part_sum = [&](int pp) -> float {
+      const v4f d = deviations(pp);
+      return (fast_exp2(d[0]) + fast_exp2(d[1])) + (fast_exp2(d[2]) + fast_exp2(d[3]));
+    };
+    // page pp's score with the page max subtracted first (every lane of the head)
+    auto score_safe = [&](int pp) -> float {
+      const v4f d = deviations(pp);
+      float mx = fmaxf(fmaxf(d[0], d[1]), fmaxf(d[2], d[3]));
+      mx = xor32_max(xor16_max(mx));
+      float ssum = (fast_exp2(d[0] - mx) + fast_exp2(d[1] - mx)) + (fast_exp2(d[2] - mx) + fast_exp2(d[3] - mx));
+      ssum = xor32_sum(xor16_sum(ssum));
+      return fmaf(T.a[pp][row], T.sc[pp][0] * es, mx + fast_log2(ssum));
+    };
+    // the 8 pages of half h of tile t, 4 at a time: one reduce-scatter leaves
+    // each lane group the sum of one page, whose score it finishes and stores
+    auto stage2 = [&](int t, int h) {
+      bool redo = false;
 #pragma unroll
-      for (int pp = 8 * h; pp < 8 * h + 8; ++pp) {
-        const float r = pass(pp, false);
-        keep[pp >> 2] = ((pp & 3) == kg) ? r : keep[pp >> 2];
+      for (int g = 2 * h; g < 2 * h + 2; ++g) {
+        const float s0 = part_sum(4 * g), s1 = part_sum(4 * g + 1);
+        const float s2 = part_sum(4 * g + 2), s3 = part_sum(4 * g + 3);
+        const float tot = reduce_scatter4(s0, s1, s2, s3);
+        const int pp = 4 * g + jpass;
+        const float r = fmaf(T.a[pp][row], T.sc[pp][0] * es, fast_log2(tot));
+        redo |= !__builtin_isfinite(r);
+        T.out[t * 16 + pp][row] = r;
       }
-      const bool redo = !__builtin_isfinite(keep[2 * h]) || !__builtin_isfinite(keep[2 * h + 1]);
       if (__builtin_expect(__ballot(redo) != 0ull, 0)) {
 #pragma unroll 1
-        for (int pp = 8 * h; pp < 8 * h + 8; ++pp) {
-          const float r = pass(pp, true);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) keep[i] = (i == (pp >> 2) && (pp & 3) == kg) ? r : keep[i];
-        }
+        for (int pp = 8 * h; pp < 8 * h + 8; ++pp) T.out[t * 16 + pp][row] = score_safe(pp);
       }
     };
 
@@ -642,15 +697,12 @@ __global__ __launch_bounds__(256, 4) void score16_kernel(ScoreArgs a) {
       }
       if (more) issue_tail(t + 1, nxt);
       wave_lds_sync();
-      float keep[4] = {0.f, 0.f, 0.f, 0.f};
-      stage2(0, keep);
+      stage2(t, 0);
       wave_lds_sync();  // half 0 of T.p read: half 1 takes its place
       stage1(cur, 1);
       if (more) issue_v(t + 1, 1, nxt);
       wave_lds_sync();
-      stage2(1, keep);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) T.out[t * 16 + 4 * i + kg][row] = keep[i];
+      stage2(t, 1);
       wave_lds_sync();
       if (more) cur = nxt;
     }
