@@ -354,10 +354,11 @@ __global__ __launch_bounds__(256, G == 8 ? 4 : 1) void score_kernel(ScoreArgs a)
         v4i acc = mfma_i8(aop[rb][0], B0, v4i{0, 0, 0, 0});
         acc = mfma_i8(aop[rb][1], B1, acc);
         const int h = 4 * rb + kg;
-        // exact integer (|.| < 2^37) -> fp32 -> scaled into f16 range, split hi + lo
-        const float x = ((float)(acc[2] * 256 + acc[1]) * 256.0f + (float)acc[0]) * 0x1p-22f;
-        const _Float16 xh = (_Float16)x;
-        const _Float16 xl = (_Float16)(x - (float)xh);
+        // exact integer (|.| < 2^37) -> fp32 -> split hi + lo, both scaled by
+        // 2^-22 into f16 range as they are rounded (the scaling is exact)
+        const float x = digits_to_float(acc[0], acc[1], acc[2]);
+        const _Float16 xh = (_Float16)(x * 0x1p-22f);
+        const _Float16 xl = (_Float16)fmaf(x, 0x1p-22f, -(float)xh);
         if (h < G) {
           T.ph[2 * vt + (row >> 3)][h < G ? h : 0][row & 7] = xh;
           T.pl[2 * vt + (row >> 3)][h < G ? h : 0][row & 7] = xl;
@@ -602,10 +603,12 @@ __global__ __launch_bounds__(256, 4) void score16_kernel(ScoreArgs a) {
         uint32_t w[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float x = digits_to_float(s[0][j], s[1][j], s[2][j]) * 0x1p-22f;  // into f16 range
-          const _Float16 xh = (_Float16)x;
-          const _Float16 xl = (_Float16)(x - (float)xh);
-          w[j] = (uint32_t)__builtin_bit_cast(uint16_t, xh) | ((uint32_t)__builtin_bit_cast(uint16_t, xl) << 16);
+          // hi + lo, both scaled by 2^-22 into f16 range as they are rounded;
+          // lo goes straight into the high half
+          const float x = digits_to_float(s[0][j], s[1][j], s[2][j]);
+          const _Float16 xh = (_Float16)(x * 0x1p-22f);
+          const h2 hl = {xh, (_Float16)fmaf(x, 0x1p-22f, -(float)xh)};
+          w[j] = __builtin_bit_cast(uint32_t, hl);
         }
         *reinterpret_cast<uint4*>(&T.p[2 * i + (row >> 3)][row & 7][4 * kg]) = uint4{w[0], w[1], w[2], w[3]};
       }
