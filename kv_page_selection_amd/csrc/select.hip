@@ -189,8 +189,10 @@ __device__ void big_exclusive_scan2(uint32_t& a, uint32_t& b, uint32_t* ta, uint
   *tb = sb;
 }
 
-template <int G>
+// EPT = pages per thread (1, 2 or 4 slabs of 1024), fixed by the chunk size
+template <int G, int EPT>
 __global__ __launch_bounds__(kThreads) void select_chunk_kernel(SelectArgs a) {
+  static_assert(EPT >= 1 && EPT <= kChunkEpt, "pages per thread");
   constexpr int P = kThreads / G;  // threads per head in the bound pass
   constexpr int WPG = P / 64;      // waves per head
   constexpr int kLbPt = kBoundSlots / G / kThreads;  // super-ranges per thread at most
@@ -215,13 +217,12 @@ __global__ __launch_bounds__(kThreads) void select_chunk_kernel(SelectArgs a) {
   }
 
   // ---- this chunk's scores and page-table entries, in flight during the bound pass
-  const int ept = a.chunk / kThreads;  // 1, 2 or 4 slabs of 1024 consecutive pages
   const int p0 = chunk * a.chunk + tid;  // page of slab i: p0 + 1024 i (coalesced loads)
-  float sc[G][kChunkEpt];
-  int blk[kChunkEpt];
+  float sc[G][EPT];
+  int blk[EPT];
 #pragma unroll
-  for (int i = 0; i < kChunkEpt; ++i) {
-    const bool in = i < ept && p0 + i * kThreads < n_b;
+  for (int i = 0; i < EPT; ++i) {
+    const bool in = p0 + i * kThreads < n_b;
     const int p = in ? p0 + i * kThreads : 0;
     blk[i] = a.page_table[(size_t)b * N + p];
 #pragma unroll
@@ -302,12 +303,13 @@ __global__ __launch_bounds__(kThreads) void select_chunk_kernel(SelectArgs a) {
     lb[i] = 0u;
     const int R = tid + i * kThreads;
     if (R < nR) {
+      uint32_t mu[G];  // all G maxima read before any is used
+#pragma unroll
+      for (int gg = 0; gg < G; ++gg) mu[gg] = sh.bound.msup[gg * nR + R];
       float v = -INFINITY;
 #pragma unroll
-      for (int gg = 0; gg < G; ++gg) {
-        const uint32_t u = sh.bound.msup[gg * nR + R];
-        if (u) v = fmaxf(v, key_from_order_bits(u) - L[gg]);
-      }
+      for (int gg = 0; gg < G; ++gg)
+        if (mu[gg]) v = fmaxf(v, key_from_order_bits(mu[gg]) - L[gg]);
       if (v > -INFINITY) {
         lb[i] = key_order_bits(v - log2G);
         ++cnt;
@@ -346,9 +348,11 @@ __global__ __launch_bounds__(kThreads) void select_chunk_kernel(SelectArgs a) {
   }
 
   // ================================================================ 2. chunk
-  unsigned long long x[kChunkEpt];
+  unsigned long long x[kChunkEpt];  // slots past EPT stay 0 (no candidate)
 #pragma unroll
-  for (int i = 0; i < kChunkEpt; ++i) {
+  for (int i = 0; i < kChunkEpt; ++i) x[i] = 0;
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) {
     // log2 of sum_g exp2(s_hat_g - L_g): the max over the group first, then
     // one exp2 per head
     float v[G], km = -1e30f, ks = 0.f;
@@ -359,10 +363,9 @@ __global__ __launch_bounds__(kThreads) void select_chunk_kernel(SelectArgs a) {
     }
 #pragma unroll
     for (int gg = 0; gg < G; ++gg) ks += fast_exp2(v[gg] - km);
-    const bool in = i < ept && p0 + i * kThreads < n_b;
+    const bool in = p0 + i * kThreads < n_b;
     // log2 of the summed shares minus log2 G; absent pages score -inf
     const float key2 = (in && ks > 0.f && km > -1e29f) ? km + fast_log2(ks) - log2G : -INFINITY;
-    x[i] = 0;
     if (key2 > -INFINITY && key2 >= tlb) {
       const uint32_t jj = (uint32_t)(p0 + i * kThreads);
       x[i] = ((unsigned long long)key_order_bits(key2) << 32) | (unsigned long long)(0xffffffffu - jj);
@@ -381,7 +384,7 @@ __global__ __launch_bounds__(kThreads) void select_chunk_kernel(SelectArgs a) {
                              T0 + T1 + T2 + (e23 >> 16)};
     const size_t base = (head * a.n_chunks + chunk) * a.chunk;
 #pragma unroll
-    for (int i = 0; i < kChunkEpt; ++i)
+    for (int i = 0; i < EPT; ++i)
       if (x[i] != 0) {
         a.cand[base + off[i]] = x[i];
         a.cand_blk[base + off[i]] = blk[i];
@@ -764,14 +767,19 @@ hipError_t launch_select(const locks_dims& d, const WsLayout& L, const DevPtrs& 
   a.chunk = L.sel_chunk;
   a.n_chunks = L.n_sel_chunks;
   const dim3 grid(L.n_sel_chunks, d.n_kv_heads, d.batch);
+  const int ept = L.sel_chunk / kThreads;  // 1, 2 or 4
+#define LOCKS_CHUNK(GG)                                                                               \
+  case GG:                                                                                            \
+    if (ept == 1) hipLaunchKernelGGL((select_chunk_kernel<GG, 1>), grid, dim3(kThreads), 0, s, a);   \
+    else if (ept == 2) hipLaunchKernelGGL((select_chunk_kernel<GG, 2>), grid, dim3(kThreads), 0, s, a); \
+    else if (ept == 4) hipLaunchKernelGGL((select_chunk_kernel<GG, 4>), grid, dim3(kThreads), 0, s, a); \
+    else return hipErrorInvalidValue;                                                                 \
+    break;
   switch (d.n_q_heads / d.n_kv_heads) {
-    case 1: hipLaunchKernelGGL(select_chunk_kernel<1>, grid, dim3(kThreads), 0, s, a); break;
-    case 2: hipLaunchKernelGGL(select_chunk_kernel<2>, grid, dim3(kThreads), 0, s, a); break;
-    case 4: hipLaunchKernelGGL(select_chunk_kernel<4>, grid, dim3(kThreads), 0, s, a); break;
-    case 8: hipLaunchKernelGGL(select_chunk_kernel<8>, grid, dim3(kThreads), 0, s, a); break;
-    case 16: hipLaunchKernelGGL(select_chunk_kernel<16>, grid, dim3(kThreads), 0, s, a); break;
+    LOCKS_CHUNK(1) LOCKS_CHUNK(2) LOCKS_CHUNK(4) LOCKS_CHUNK(8) LOCKS_CHUNK(16)
     default: return hipErrorInvalidValue;
   }
+#undef LOCKS_CHUNK
   hipLaunchKernelGGL(select_merge_kernel, dim3(d.n_kv_heads, d.batch), dim3(64), 0, s, a);
   return hipGetLastError();
 }
