@@ -152,6 +152,69 @@ __device__ __forceinline__ void jacobi_round(float (&a)[kPage], float (&u)[kPage
   wave_lds_sync();  // every lane has read this round's angles
 }
 
+// The same round for a wave that holds one page: lanes 0-15 hold the rows of
+// A and lanes 16-31 the rows of U (slot-permuted alike), so one column
+// rotation updates both. Rows of U skip the row rotation (c = 1, s = 0) and
+// only rows of A publish their angles; lanes 32-63 hold zeros.
+template <int M>
+__device__ __forceinline__ void jacobi_round_shared(float (&x)[kPage], int i, bool arow, float2* rot) {
+  const bool lower = i < (i ^ M);
+  float pa[kPage];
+#pragma unroll
+  for (int tt = 0; tt < kPage; ++tt) pa[tt] = swz<M>(x[tt ^ M]);
+  __builtin_amdgcn_sched_barrier(0);
+  const float d_me = x[0], d_other = pa[M];
+  const float o_me = x[M], o_other = pa[0];
+  const float app = lower ? d_me : d_other, aqq = lower ? d_other : d_me;
+  const float apq = lower ? o_me : o_other;
+  const float safe = (apq != 0.f) ? apq : 1.f;
+  const float tau = (aqq - app) * __builtin_amdgcn_rcpf(2.f * safe);
+  const float t = copysignf(1.0f, tau) *
+                  __builtin_amdgcn_rcpf(fabsf(tau) + __builtin_amdgcn_sqrtf(fmaf(tau, tau, 1.f)));
+  const float c = (apq != 0.f) ? __builtin_amdgcn_rsqf(fmaf(t, t, 1.f)) : 1.f;
+  const float s = (apq != 0.f) ? t * c : 0.f;
+  const float sg = lower ? -s : s;
+  const float cr = arow ? c : 1.f, sr = arow ? sg : 0.f;
+  float ar[kPage];
+#pragma unroll
+  for (int tt = 0; tt < kPage; ++tt) ar[tt] = fmaf(cr, x[tt], sr * pa[tt]);
+  if (arow) rot[i] = make_float2(c, sg);
+  wave_lds_sync();
+  float2 rc[kPage];
+#pragma unroll
+  for (int tt = 0; tt < kPage; ++tt) rc[tt] = rot[i ^ tt];
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int tt = 0; tt < kPage; ++tt) {
+    if (tt < (tt ^ M)) {
+      const int t2 = tt ^ M;
+      const float2 r1 = rc[tt], r2 = rc[t2];
+      x[tt] = fmaf(r1.x, ar[tt], r1.y * ar[t2]);
+      x[t2] = fmaf(r2.x, ar[t2], r2.y * ar[tt]);
+    }
+  }
+  x[M] = arow ? 0.f : x[M];
+  wave_lds_sync();  // every lane has read this round's angles
+}
+
+__device__ __forceinline__ void jacobi_sweep_shared(float (&x)[kPage], int i, bool arow, float2* rot) {
+  jacobi_round_shared<1>(x, i, arow, rot);
+  jacobi_round_shared<2>(x, i, arow, rot);
+  jacobi_round_shared<3>(x, i, arow, rot);
+  jacobi_round_shared<4>(x, i, arow, rot);
+  jacobi_round_shared<5>(x, i, arow, rot);
+  jacobi_round_shared<6>(x, i, arow, rot);
+  jacobi_round_shared<7>(x, i, arow, rot);
+  jacobi_round_shared<8>(x, i, arow, rot);
+  jacobi_round_shared<9>(x, i, arow, rot);
+  jacobi_round_shared<10>(x, i, arow, rot);
+  jacobi_round_shared<11>(x, i, arow, rot);
+  jacobi_round_shared<12>(x, i, arow, rot);
+  jacobi_round_shared<13>(x, i, arow, rot);
+  jacobi_round_shared<14>(x, i, arow, rot);
+  jacobi_round_shared<15>(x, i, arow, rot);
+}
+
 __device__ __forceinline__ void jacobi_sweep(float (&a)[kPage], float (&u)[kPage], int i,
                                              float2* rot) {
   jacobi_round<1>(a, u, i, rot);
@@ -240,41 +303,70 @@ __device__ __forceinline__ void eigen_phases(const BuildArgs& a, LdsT& S, long l
   // ================================================ 2. four eigenproblems, 16 lanes each
   {
     const int pg = lane >> 4, i = lane & 15;
-    const bool live = pg < PPW;  // lanes of unused page slots do not vote
-    float a_[kPage], u_[kPage];
+    const auto add = [](float x, float y) { return x + y; };
+    float a_[kPage];
+    if constexpr (PPW == 1) {
+      // one page: A in lanes 0-15, U in lanes 16-31 (identity: U[i][i ^ t] =
+      // (t == 0)), rotated by the same instructions; lanes 32-63 hold zeros
+      const bool arow = lane < 16;
 #pragma unroll
-    for (int tt = 0; tt < kPage; ++tt) {
-      a_[tt] = S.A[pg][i][tt];
-      u_[tt] = (tt == 0) ? 1.0f : 0.0f;  // identity: U[i][i ^ t] = (t == 0)
+      for (int tt = 0; tt < kPage; ++tt)
+        a_[tt] = arow ? S.A[0][i][tt] : ((lane < 32 && tt == 0) ? 1.0f : 0.0f);
+      for (int sweep = 0; sweep < kMaxSweeps; ++sweep) {
+        float off = 0.f, tot = a_[0] * a_[0];
+#pragma unroll
+        for (int tt = 1; tt < kPage; ++tt) off = fmaf(a_[tt], a_[tt], off);
+        tot += off;
+        off = row16_reduce(off, add);
+        tot = row16_reduce(tot, add);
+        if (__ballot(arow && off > kOffTol * tot) == 0) break;  // converged
+        jacobi_sweep_shared(a_, i, arow, S.rot[0]);
+      }
+      if (arow) S.diag[0][i] = a_[0];
+      // (storage shared with the Gram rows read above: one wave's LDS
+      // operations complete in order, and the union keeps the compiler from
+      // reordering them)
+      if (lane >= 16 && lane < 32) {
+#pragma unroll
+        for (int tt = 0; tt < kPage; ++tt) S.UT[0][i ^ tt][i] = a_[tt];
+      }
+    } else {
+      float u_[kPage];
+#pragma unroll
+      for (int tt = 0; tt < kPage; ++tt) {
+        a_[tt] = S.A[pg][i][tt];
+        u_[tt] = (tt == 0) ? 1.0f : 0.0f;  // identity: U[i][i ^ t] = (t == 0)
+      }
+      for (int sweep = 0; sweep < kMaxSweeps; ++sweep) {
+        float off = 0.f, tot = a_[0] * a_[0];
+#pragma unroll
+        for (int tt = 1; tt < kPage; ++tt) off = fmaf(a_[tt], a_[tt], off);
+        tot += off;
+        off = row16_reduce(off, add);
+        tot = row16_reduce(tot, add);
+        if (__ballot(off > kOffTol * tot) == 0) break;  // every page converged
+        jacobi_sweep(a_, u_, i, S.rot[pg]);
+      }
+      S.diag[pg][i] = a_[0];
+      // (storage shared with the Gram rows this wave read above: one wave's LDS
+      // operations complete in order, and the union keeps the compiler from
+      // reordering them)
+#pragma unroll
+      for (int tt = 0; tt < kPage; ++tt) S.UT[pg][i ^ tt][i] = u_[tt];
     }
-    for (int sweep = 0; sweep < kMaxSweeps; ++sweep) {
-      float off = 0.f, tot = a_[0] * a_[0];
-#pragma unroll
-      for (int tt = 1; tt < kPage; ++tt) off = fmaf(a_[tt], a_[tt], off);
-      tot += off;
-      const auto add = [](float x, float y) { return x + y; };
-      off = row16_reduce(off, add);
-      tot = row16_reduce(tot, add);
-      if (__ballot(live && off > kOffTol * tot) == 0) break;  // every page converged
-      jacobi_sweep(a_, u_, i, S.rot[pg]);
-    }
-    S.diag[pg][i] = a_[0];
-    // (storage shared with the Gram rows this wave read above: one wave's LDS
-    // operations complete in order, and the union keeps the compiler from
-    // reordering them)
-#pragma unroll
-    for (int tt = 0; tt < kPage; ++tt) S.UT[pg][i ^ tt][i] = u_[tt];
     wave_lds_sync();
     // eigenvalues in descending order, equal values keep index order
-    const float lx = a_[0];
-    int rank = 0;
+    if (pg < PPW) {
+      const float lx = a_[0];
+      int rank = 0;
 #pragma unroll
-    for (int y = 0; y < kPage; ++y) {
-      const float ly = S.diag[pg][y];
-      rank += (ly > lx) || (ly == lx && y < i);
+      for (int y = 0; y < kPage; ++y) {
+        const float ly = S.diag[pg][y];
+        rank += (ly > lx) || (ly == lx && y < i);
+      }
+      S.perm[pg][rank] = i;
+      S.lam[pg][rank] = lx;
     }
-    S.perm[pg][rank] = i;
-    S.lam[pg][rank] = lx;
   }
   wave_lds_sync();
 
