@@ -34,6 +34,7 @@ SMALL = [
     dict(config=5, ctx=16 * 3000, budget=512),                  # G = 16
     dict(config=2, ctx=16 * 640, n_kv_heads=16, n_q_heads=32),  # G = 2
     dict(config=2, ctx=16 * 640, n_kv_heads=4, n_q_heads=32),   # G = 8
+    dict(config=2, ctx=16 * 7000),                              # 2048-page select chunks
 ]
 
 
@@ -58,6 +59,8 @@ SELECT_PATHS = [
     # G = 16 with 2048 ranges: the 32768 (head, range) maxima exceed what the
     # bound pass holds, so it pools ranges in pairs
     dict(config=5, ctx=16 * 131072, budget=512, n_kv_heads=1, n_q_heads=16),
+    # G = 16 with 2048-page select chunks (two pages per chunk-pass thread)
+    dict(config=5, ctx=16 * 32768, batch=4, budget=512),
 ]
 
 
