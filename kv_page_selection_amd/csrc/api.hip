@@ -65,7 +65,14 @@ bool ws_layout(const locks_dims& d, int k, WsLayout* L, const char** why) {
     *why = "budget/16 above the sparse-attention split capacity";
     return false;
   }
-  long long dps = kDensePagesPerSplit;  // dense list: N pages, then the tail
+  // dense list: N pages, then the tail. Splits of >= kDensePagesPerSplit pages
+  // (one per wave), doubled while the grid would exceed a target number of
+  // workgroups: enough to fill the GPU, few enough partials to merge. The MFMA
+  // kernel of 8- and 16-head groups holds 3 workgroups per CU and does more
+  // work per page, so it takes fewer, longer splits (measured).
+  const long long target = (d.n_q_heads / d.n_kv_heads) >= 8 ? kDenseTargetWgs / 4 : kDenseTargetWgs;
+  long long dps = kDensePagesPerSplit;
+  while (dps < N + 1 && B * Hkv * ((N + 1 + dps - 1) / dps) > target) dps *= 2;
   while ((N + 1 + dps - 1) / dps > kMaxSplits) dps *= 2;
   L->dense_pages_per_split = (int)dps;
   L->n_dense_split = (int)((N + 1 + dps - 1) / dps);
