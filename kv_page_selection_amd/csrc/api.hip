@@ -65,14 +65,15 @@ bool ws_layout(const locks_dims& d, int k, WsLayout* L, const char** why) {
     *why = "budget/16 above the sparse-attention split capacity";
     return false;
   }
-  // dense list: N pages, then the tail. Splits of >= kDensePagesPerSplit pages
-  // (one per wave), doubled while the grid would exceed a target number of
-  // workgroups: enough to fill the GPU, few enough partials to merge. The MFMA
-  // kernel of 8- and 16-head groups holds 3 workgroups per CU and does more
-  // work per page, so it takes fewer, longer splits (measured).
-  const long long target = (d.n_q_heads / d.n_kv_heads) >= 8 ? kDenseTargetWgs / 4 : kDenseTargetWgs;
+  // dense list: N pages, then the tail, in splits of kDensePagesPerSplit
+  // pages; halved (down to one page per wave) while the grid has fewer than
+  // kDenseMinWgs workgroups, so short contexts and small batches still fill
+  // the GPU (the MFMA kernel of 8- and 16-head groups holds 3 workgroups per
+  // CU and does more work per page: a quarter of that). Filled grids keep the
+  // long splits, which ragged batches need (measured).
+  const long long min_wgs = (d.n_q_heads / d.n_kv_heads) >= 8 ? kDenseMinWgs / 4 : kDenseMinWgs;
   long long dps = kDensePagesPerSplit;
-  while (dps < N + 1 && B * Hkv * ((N + 1 + dps - 1) / dps) > target) dps *= 2;
+  while (dps > 4 && B * Hkv * ((N + 1 + dps - 1) / dps) < min_wgs) dps /= 2;
   while ((N + 1 + dps - 1) / dps > kMaxSplits) dps *= 2;
   L->dense_pages_per_split = (int)dps;
   L->n_dense_split = (int)((N + 1 + dps - 1) / dps);

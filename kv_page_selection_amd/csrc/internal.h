@@ -16,8 +16,8 @@ constexpr int kSelectMaxK = 4096;       // budget/16 limit (the merge keeps up t
 constexpr int kSelectChunk = 4096;      // pages per select workgroup at most (4 per thread)
 constexpr int kBoundSlots = 16384;      // (head, super-range) maxima the bound pass holds in LDS
 constexpr int kSparsePagesPerSplit = 4; // one page per wave
-constexpr int kDensePagesPerSplit = 4;   // at least (one page per wave); grows with the grid
-constexpr int kDenseTargetWgs = 4096;    // dense splits are sized so the grid stays near this
+constexpr int kDensePagesPerSplit = 256; // usual dense split; smaller for small grids, larger past kMaxSplits
+constexpr int kDenseMinWgs = 1024;       // dense splits shrink while the grid has fewer workgroups
 constexpr int kMaxSplits = 2048;        // split partials one merge workgroup combines
 constexpr int kPartialFloats = 130;     // (m, l, o[128]) per head and split
 constexpr int kTileBoundPages = 128;    // per selected page: sequences with fewer pages bound by tiles
