@@ -1,4 +1,5 @@
-// build.hip — summary build (gfx950): 4 pages per wave.
+// build.hip — summary build (gfx950): 4 pages per wave (1 for a short list
+// of pages that just filled).
 //
 // Steps (blog post, "How LOCKS works" and "Code" build loop; technical summary,
 // section 2 mechanism 1): centroid mu = mean of the page's 16 keys; centred
@@ -21,7 +22,9 @@
 //     rotated element is slot m, the partner row is one ds_swizzle (XOR m)
 //     away and reads slot-permuted by XOR m, and the column rotation of slot
 //     t uses the angle of column i ^ t, published through a 16-entry LDS
-//     table: no register is indexed per lane.
+//     table: no register is indexed per lane. A wave with one page holds the
+//     eigenvector rows in lanes 16-31 instead, so the same instructions
+//     rotate both matrices.
 //  3. per page, all 64 lanes: lane owns d = 2*lane, 2*lane+1 of all 16 keys
 //     (reloaded, L2-resident), forms V, the sign rule, C, the scales and the
 //     codes, and writes the record.
