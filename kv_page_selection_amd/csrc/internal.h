@@ -11,7 +11,6 @@
 namespace locks {
 
 constexpr int kScorePagesPerWave = 64;  // 4 tiles x 16 pages per wave and KV head
-constexpr int kSelectMaxElems = 8192;   // candidates ranked per merge round (8 per thread)
 constexpr int kSelectMaxK = 4096;       // budget/16 limit (the merge keeps up to k between rounds)
 constexpr int kSelectChunk = 4096;      // pages per select workgroup at most (4 per thread)
 constexpr int kBoundSlots = 16384;      // (head, super-range) maxima the bound pass holds in LDS

@@ -50,7 +50,6 @@ constexpr int kThreads = 1024;
 constexpr int kNW = kThreads / 64;
 constexpr int kHistBuckets = 2 * kThreads;                // 2 buckets per thread
 constexpr int kChunkEpt = kSelectChunk / kThreads;        // <= 4 pages per thread
-constexpr int kMergeEpt = kSelectMaxElems / kThreads;     // 8 candidates per thread per round
 
 struct SelectArgs {
   const float* scores;
