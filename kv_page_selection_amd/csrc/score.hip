@@ -483,11 +483,15 @@ __global__ __launch_bounds__(256, G == 8 ? 4 : 1) void score_kernel(ScoreArgs a)
 // 16 heads.
 //
 // Work split. A 64-page range is two waves of 32 pages (2 tiles each), and a
-// workgroup takes two ranges: a 1M-token sequence with 2 KV heads then still
-// gives every SIMD four waves. LDS per wave stays under 10 KB (V^T q staged
-// half a tile at a time; the q digit planes share their space with the tile
-// buffers, which are not in use yet), so four workgroups fit a CU. The two
-// waves of a range merge their per-head (max, sum) through LDS at the end.
+// workgroup takes two ranges: a 1M-token sequence with 2 KV heads then gives
+// every SIMD four waves, one round. Smaller grids (B * Hkv * ranges <= 1024)
+// run 16 pages per wave, a range per workgroup, for twice the waves: at 7000
+// pages that scores in 9.6 us instead of 11.8, while at 65536 pages the
+// second round costs more than it hides (33.3 us against 29.0). LDS per wave
+// stays under 10 KB (V^T q staged half a tile at a time; the q digit planes
+// share their space with the tile buffers, which are not in use yet), so four
+// workgroups fit a CU. The waves of a range merge their per-head (max, sum)
+// through LDS at the end.
 //
 // Stage 1 row blocks are the digit planes (rows = the 16 heads): lane (column
 // j, group kg) finds heads 4kg .. 4kg+3 of column j in each plane's output.
@@ -502,41 +506,47 @@ __global__ __launch_bounds__(256, G == 8 ? 4 : 1) void score_kernel(ScoreArgs a)
 // sum of their exp2 is at least about 1 and does not underflow; a sum that
 // overflows gives a non-finite score, and that half tile is redone with the
 // max subtracted.
-constexpr int k16PagesPerWave = kScorePagesPerWave / 2;
-constexpr int k16Tiles = k16PagesPerWave / 16;
+constexpr long long k16ShortGridRanges = 1024;  // 16 pages per wave up to this many (seq, KV head, range)
 
+template <int PPW>
 struct Tile16Lds {
   __align__(16) int8_t c[16][128];          // C codes + 128 per page (token-major)
   __align__(16) uint32_t p[8][kRank][16];   // V^T q * 2^-22 of half a tile, [page][k][head]: f16 hi | lo << 16
   __align__(16) float a[16][16];            // mu . q per (page, head), digit units
   float sc[32][2];                          // s_mu, s_V/16 * s_C; rows 16.. take the other lanes' copies
-  float out[k16PagesPerWave][17];           // the wave's page scores, [page][head] (+1 pad), base 2
+  float out[PPW][17];                       // the wave's page scores, [page][head] (+1 pad), base 2
 };
+template <int PPW>
 struct Score16Lds {
   union {
     __align__(16) int8_t dig[3][16][kDim];  // q digit planes (prologue only)
-    Tile16Lds w[4];
+    Tile16Lds<PPW> w[4];
   } u;
-  uint32_t off[4][k16PagesPerWave];         // each wave's page record offsets, 16-byte units
-  float2 ms[2][16];                         // second half of each range: per-head (max, sum of exp2)
+  uint32_t off[4][PPW];                     // each wave's page record offsets, 16-byte units
+  float2 ms[4][16];                         // per wave and head: (max, sum of exp2) over its pages
   float esc[16];                            // per head: 2^-e log2(e) / sqrt(128)
 };
 
+template <int PPW>
 __global__ __launch_bounds__(256, 4) void score16_kernel(ScoreArgs a) {
   constexpr int G = 16;
-  __shared__ Score16Lds S;
+  constexpr int k16PagesPerWave = PPW;
+  constexpr int k16Tiles = PPW / 16;
+  constexpr int k16WavesPerRange = kScorePagesPerWave / PPW;  // 2 or 4
+  constexpr int k16RangesPerWg = 4 / k16WavesPerRange;
+  __shared__ Score16Lds<PPW> S;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = lane & 15, kg = lane >> 4;
   const int b = blockIdx.z;
   const int kvh = blockIdx.y;
-  const int range = blockIdx.x * 2 + (wave >> 1);
-  const int half = wave & 1;
+  const int range = blockIdx.x * k16RangesPerWg + wave / k16WavesPerRange;
+  const int half = wave % k16WavesPerRange;  // the wave's part of its range
   const int hbase = kvh * G;
   const int N = a.N;
   const int n_b = full_pages(a.seq_lens, b, N);
   const int p0 = range * kScorePagesPerWave + half * k16PagesPerWave;  // the wave's first page
 
-  if (blockIdx.x * 2 * kScorePagesPerWave >= n_b) return;  // workgroup-uniform
+  if (blockIdx.x * k16RangesPerWg * kScorePagesPerWave >= n_b) return;  // workgroup-uniform
 
   // A wave past the ranges or the sequence's full pages has no work but still
   // reaches the workgroup barriers below (no wave returns after this point).
@@ -556,7 +566,7 @@ __global__ __launch_bounds__(256, 4) void score16_kernel(ScoreArgs a) {
   const int jpass = reduce_scatter4_pass();  // which page of each 4 this lane finishes
   __syncthreads();  // digit planes consumed: their space becomes the tile buffers
 
-  Tile16Lds& T = S.u.w[wave];
+  Tile16Lds<PPW>& T = S.u.w[wave];
   if (myblk < 0 || myblk >= a.num_blocks) myblk = -1;
   const unsigned long long present = __ballot(myblk >= 0);  // bit i: page p0 + i
   if (active) {
@@ -734,27 +744,36 @@ __global__ __launch_bounds__(256, 4) void score16_kernel(ScoreArgs a) {
       m = mn;
     }
   }
-  if (half == 1 && lane < 16) S.ms[wave >> 1][row] = make_float2(m, ssum);
-  __syncthreads();
+  if constexpr (k16WavesPerRange > 1) {
+    if (half > 0 && lane < 16) S.ms[wave][row] = make_float2(m, ssum);
+    __syncthreads();
+  }
   if (!active) return;
   if (half == 0 && lane < 16) {
-    const float2 o = S.ms[wave >> 1][row];
-    const float mn = fmaxf(m, o.x);
-    const float mz = mn == -INFINITY ? 0.f : mn;
-    const float st = ssum * fast_exp2(m - mz) + o.y * fast_exp2(o.x - mz);
+    float mn = m, st = ssum;
+#pragma unroll
+    for (int w = 1; w < k16WavesPerRange; ++w) {
+      const float2 o = S.ms[wave + w][row];
+      const float mx = fmaxf(mn, o.x);
+      const float mz = mx == -INFINITY ? 0.f : mx;
+      st = st * fast_exp2(mn - mz) + o.y * fast_exp2(o.x - mz);
+      mn = mx;
+    }
     float* dst = a.partials + (((size_t)b * a.Hq + (size_t)hbase + row) * a.n_ranges + range) * 2;
     dst[0] = (st > 0.f) ? mn : -INFINITY;
     dst[1] = st;
   }
   // ---- page scores (natural log; -inf for an absent page): lane = page
-  // lane % 32, heads 2j + lane / 32, so each store covers 128 bytes of 2 heads
+  // lane % P, heads HP j + lane / P (P pages per wave, HP = 64 / P heads per
+  // store), so each store covers HP runs of 4P bytes
   {
-    const int pg = lane & 31;
+    constexpr int HP = 64 / k16PagesPerWave;
+    const int pg = lane % k16PagesPerWave;
     const bool mine = (present >> pg) & 1ull;
     if (p0 + pg < n_b) {
 #pragma unroll
-      for (int j = 0; j < G / 2; ++j) {
-        const int h = 2 * j + (lane >> 5);
+      for (int j = 0; j < G / HP; ++j) {
+        const int h = HP * j + lane / k16PagesPerWave;
         const float sc = mine ? T.out[pg][h] * kLn2 : -INFINITY;
         __builtin_nontemporal_store(sc, &a.scores[((size_t)b * a.Hq + (size_t)hbase + h) * N + p0 + pg]);
       }
@@ -770,7 +789,7 @@ __global__ __launch_bounds__(256, 4) void score16_kernel(ScoreArgs a) {
       if ((present >> pg) & 1ull) tm = fmaxf(tm, T.out[pg][row]);
     }
     a.tile_max[((size_t)b * a.Hq + (size_t)hbase + row) * ((size_t)a.n_ranges * kTiles) +
-               (size_t)range * kTiles + 2 * half + tt] = tm;
+               (size_t)range * kTiles + k16Tiles * half + tt] = tm;
   }
 }
 
@@ -792,8 +811,15 @@ hipError_t launch_g(const locks_dims& d, const WsLayout& L, const DevPtrs& P, co
   a.num_blocks = d.num_blocks;
   a.n_ranges = L.n_score_wg;
   if constexpr (G == 16) {
-    const dim3 grid((L.n_score_wg + 1) / 2, d.n_kv_heads, d.batch);  // two ranges per workgroup
-    hipLaunchKernelGGL(score16_kernel, grid, dim3(256), 0, s, a);
+    // 32 pages per wave (two ranges per workgroup); 16 (one range per
+    // workgroup) when that grid still fits one round of resident waves
+    if ((long long)d.batch * d.n_kv_heads * L.n_score_wg <= k16ShortGridRanges) {
+      const dim3 grid(L.n_score_wg, d.n_kv_heads, d.batch);
+      hipLaunchKernelGGL(score16_kernel<16>, grid, dim3(256), 0, s, a);
+    } else {
+      const dim3 grid((L.n_score_wg + 1) / 2, d.n_kv_heads, d.batch);
+      hipLaunchKernelGGL(score16_kernel<32>, grid, dim3(256), 0, s, a);
+    }
   } else {
     const dim3 grid((L.n_score_wg + 3) / 4, d.n_kv_heads, d.batch);  // four ranges per workgroup
     hipLaunchKernelGGL(score_kernel<G>, grid, dim3(256), 0, s, a);
