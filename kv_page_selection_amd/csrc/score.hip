@@ -9,9 +9,13 @@
 // Mapping. A workgroup is 4 waves of one KV head and all G of its query heads;
 // up to 8 heads, wave w scores 64 consecutive pages (4 tiles of 16) and the
 // waves take 4 consecutive page ranges; with 16 heads two waves share a
-// 64-page range (32 pages each) and a workgroup takes 2 ranges. The q
-// prologue (fixed-point digits of the group's query heads) is split over the
-// 4 waves and shared in LDS.
+// 64-page range (32 pages each) and a workgroup takes 2 ranges. Grids of at
+// most 1024 (sequence, KV head, range) triples, which would leave SIMDs with
+// one wave or none, split each range over four waves of 16 pages instead
+// (a workgroup per range), still one round of resident waves. The waves of a
+// range merge their per-head (max, sum) in LDS. The q prologue (fixed-point
+// digits of the group's query heads) is split over the 4 waves and shared in
+// LDS.
 //
 // Stage 1, mu.q and V^T q, on v_mfma_i32_16x16x64_i8, exact: the row operand is
 // each query head as a 22-bit fixed-point integer in three signed int8 digits,
@@ -49,6 +53,7 @@ typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 
 constexpr int kTiles = kScorePagesPerWave / 16;
+constexpr long long kScoreRoundWaves = 4096;  // 4 waves per SIMD x 1024 SIMDs: one round of a scorer grid
 
 struct ScoreArgs {
   const float* q;
@@ -78,8 +83,8 @@ __device__ __forceinline__ v4i mfma_i8(v4i a, v4i b, v4i c) {
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }
 
-// Per-wave LDS staging of one 16-page tile.
-template <int G>
+// Per-wave LDS staging of one 16-page tile; the wave's P page scores.
+template <int G, int P>
 struct TileLds {
   __align__(16) int8_t c[16][144];      // C codes per page (token-major), padded rows
   __align__(16) _Float16 ph[16][G][8];  // p (scaled by 2^-22) high part, [page][head][k]
@@ -87,7 +92,7 @@ struct TileLds {
   __align__(16) _Float16 zero[8];       // masked B operand
   float a[16][G + 1];                   // mu . q (exact integer), [page][head]; column G spare
   float sc[32][2];                      // s_mu, s_V/16 * s_C; rows 16.. take the other lanes' copies
-  __align__(16) float out[kScorePagesPerWave][G];  // the wave's page scores, [page][head], base 2
+  __align__(16) float out[P][G];        // the wave's page scores, [page][head], base 2
 };
 
 template <int G, class TileT>
@@ -98,6 +103,7 @@ struct ScoreLds {
     uint32_t off[4][kScorePagesPerWave];   // then each wave's page record offsets
   } u;
   float esc[16];                           // per head: 2^-e log2(e) / sqrt(128)
+  float2 ms[4][8];                         // per wave and head: (max, sum of exp2) over its pages
 };
 
 // q of the G heads at qg -> per-head exponent e (max |q| * 2^e in [2^21,
@@ -160,41 +166,58 @@ __device__ __forceinline__ int reduce_scatter4_pass() {
   return (int)a[0] + 2 * (int)b[0];
 }
 
-// A wave's outputs from its base-2 scores out[page][head] (pages p0 .. p0+63
+// A wave's outputs from its base-2 scores out[page][head] (pages p0 .. p0+P-1
 // of sequence b, query heads hbase ..): page scores in natural log (-inf for
 // an absent page), the per-head (max, sum of exp2) over the range, and, for a
-// sequence bounded by tiles, the max of each 16-page tile.
-template <int G>
-__device__ __forceinline__ void write_wave_outputs(const ScoreArgs& a, const float (&out)[kScorePagesPerWave][G],
-                                                   unsigned long long present, int b, int hbase,
-                                                   int range, int p0, int n_b, int lane) {
+// sequence bounded by tiles, the max of each 16-page tile. With W waves per
+// 64-page range (P = 64 / W), waves part > 0 leave their (max, sum) in LDS
+// and part 0 merges them; every wave of the workgroup calls this (the merge
+// has a barrier), those without pages with present = 0. Nothing but page
+// scores is written for a range without pages (live = false).
+template <int G, int P, class Lds>
+__device__ __forceinline__ void write_wave_outputs(const ScoreArgs& a, const float (&out)[P][G], Lds& S,
+                                                   unsigned long long present, bool live, int b, int hbase,
+                                                   int range, int part, int p0, int n_b, int wave,
+                                                   int lane) {
+  constexpr int W = kScorePagesPerWave / P;
+  constexpr int HP = 64 / P;  // heads per store pass
   const int N = a.N;
   // written once after the wave's last loads: a store in flight would hold
-  // up the wait for later loads (one in-order counter covers both); whole
-  // 256-byte rows per head coalesce, and streaming (non-temporal) stores keep
-  // them from sitting dirty in L2 until the end of the launch
-  const bool mine = (present >> lane) & 1ull;
+  // up the wait for later loads (one in-order counter covers both); lane =
+  // page lane % P of head group lane / P, so whole runs of 4P bytes per head
+  // coalesce, and streaming (non-temporal) stores keep them from sitting
+  // dirty in L2 until the end of the launch
+  {
+    const int pg = lane % P;
+    const bool mine = (present >> pg) & 1ull;
+    if (p0 + pg < n_b) {
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const float sc = mine ? out[lane][h] * kLn2 : -INFINITY;
-    if (p0 + lane < n_b) __builtin_nontemporal_store(sc, &a.scores[((size_t)b * a.Hq + (size_t)hbase + h) * N + p0 + lane]);
+      for (int j = 0; j < (G + HP - 1) / HP; ++j) {
+        const int h = HP * j + lane / P;
+        if (HP * j + HP <= G || h < G) {
+          const float sc = mine ? out[pg][h < G ? h : 0] * kLn2 : -INFINITY;
+          __builtin_nontemporal_store(sc, &a.scores[((size_t)b * a.Hq + (size_t)hbase + h) * N + p0 + pg]);
+        }
+      }
+    }
   }
 
   // per-head (max, sum) of exp2 over the wave's pages: lane takes head
   // lane % G and pages i * 64/G + lane / G, then lanes of one head merge
   constexpr int LPH = kScorePagesPerWave / G;
-  float m = -INFINITY, v[G];
+  constexpr int PPL = (P + LPH - 1) / LPH;  // pages per lane
+  float m = -INFINITY, v[PPL];
 #pragma unroll
-  for (int i = 0; i < G; ++i) {
+  for (int i = 0; i < PPL; ++i) {
     const int pg = i * LPH + lane / G;
-    v[i] = ((present >> pg) & 1ull) ? out[pg][lane % G] : -INFINITY;
+    v[i] = (pg < P && ((present >> pg) & 1ull)) ? out[pg < P ? pg : 0][lane % G] : -INFINITY;
     m = fmaxf(m, v[i]);
   }
   float ssum = 0.f;
   {
     const float ms = m == -INFINITY ? 0.f : m;
 #pragma unroll
-    for (int i = 0; i < G; ++i) ssum += fast_exp2(v[i] - ms);
+    for (int i = 0; i < PPL; ++i) ssum += fast_exp2(v[i] - ms);
   }
 #pragma unroll
   for (int off = G; off < 64; off <<= 1) {
@@ -204,13 +227,28 @@ __device__ __forceinline__ void write_wave_outputs(const ScoreArgs& a, const flo
     ssum = ssum * fast_exp2(m - ms) + s2 * fast_exp2(m2 - ms);
     m = mn;
   }
-  if (lane < G) {
+  if constexpr (W > 1) {
+    if (part > 0 && lane < G) S.ms[wave][lane] = make_float2(m, ssum);
+    __syncthreads();
+    if (part == 0 && lane < G) {
+#pragma unroll
+      for (int w = 1; w < W; ++w) {
+        const float2 o = S.ms[wave + w][lane];
+        const float mn = fmaxf(m, o.x);
+        const float ms = mn == -INFINITY ? 0.f : mn;
+        ssum = ssum * fast_exp2(m - ms) + o.y * fast_exp2(o.x - ms);
+        m = mn;
+      }
+    }
+  }
+  if (live && part == 0 && lane < G) {
     float* dst = a.partials + (((size_t)b * a.Hq + (size_t)hbase + lane) * a.n_ranges + range) * 2;
     dst[0] = (ssum > 0.f) ? m : -INFINITY;
     dst[1] = ssum;
   }
   // per head and 16-page tile: the max of s_hat (base 2; -inf if no page)
-  if (n_b < a.tile_pages && lane < kTiles * G) {
+  constexpr int TPW = P / 16;  // tiles per wave
+  if (live && n_b < a.tile_pages && lane < TPW * G) {
     const int tt = lane / G, hh = lane % G;
     float tm = -INFINITY;
 #pragma unroll
@@ -219,7 +257,7 @@ __device__ __forceinline__ void write_wave_outputs(const ScoreArgs& a, const flo
       if ((present >> pg) & 1ull) tm = fmaxf(tm, out[pg][hh]);
     }
     a.tile_max[((size_t)b * a.Hq + (size_t)hbase + hh) * ((size_t)a.n_ranges * kTiles) +
-               (size_t)range * kTiles + tt] = tm;
+               (size_t)range * kTiles + part * TPW + tt] = tm;
   }
 }
 
@@ -230,36 +268,41 @@ struct TileRec {
   uint2 scl;
 };
 
-// G = query heads per KV head (at most 8). 8-head waves are held to 128
-// VGPRs (4 waves per SIMD; left alone they take a few more and drop to 3).
-template <int G>
+// G = query heads per KV head (at most 8); P = pages per wave: 64 (a range
+// per wave, four per workgroup) or, for grids that would leave SIMDs idle,
+// 16 (a range over four waves). 8-head waves are held to 128 VGPRs (4 waves
+// per SIMD; left alone they take a few more and drop to 3).
+template <int G, int P>
 __global__ __launch_bounds__(256, G == 8 ? 4 : 1) void score_kernel(ScoreArgs a) {
   static_assert(G <= 8, "16-head groups use score16_kernel");
   constexpr int RB = G < 4 ? 1 : G / 4;   // stage-1 row blocks (4 heads each)
   constexpr int PG = 16 / G;              // pages per stage-2 pass
-  __shared__ ScoreLds<G, TileLds<G>> S;
+  constexpr int W = kScorePagesPerWave / P;  // waves per range
+  constexpr int TPW = P / 16;                // tiles per wave
+  __shared__ ScoreLds<G, TileLds<G, P>> S;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = lane & 15, kg = lane >> 4;
   const int b = blockIdx.z;
   const int kvh = blockIdx.y;
-  const int range = blockIdx.x * 4 + wave;
+  const int range = blockIdx.x * (4 / W) + wave / W;
+  const int part = wave % W;  // the wave's part of its range
   const int hbase = kvh * G;  // first query head of the group
   const int N = a.N;
   const int n_b = full_pages(a.seq_lens, b, N);
-  TileLds<G>& T = S.w[wave];
-  const int p0 = range * kScorePagesPerWave;
+  TileLds<G, P>& T = S.w[wave];
+  const int p0 = range * kScorePagesPerWave + part * P;
 
   // A range wholly past the sequence's full pages (shorter sequences of a
   // batch) has no work and writes nothing (its partials are never read);
   // the whole workgroup leaves at once when none of its ranges has a page.
-  if (blockIdx.x * 4 * kScorePagesPerWave >= n_b) return;  // workgroup-uniform
+  if (blockIdx.x * (4 / W) * kScorePagesPerWave >= n_b) return;  // workgroup-uniform
 
-  // page table of this wave's 64 pages, one entry per lane; issued first, so
+  // page table of this wave's P pages, one entry per lane; issued first, so
   // its latency overlaps the q prologue below
   int myblk = -1;
   {
     const int j = p0 + lane;
-    if (range < a.n_ranges && j < n_b) myblk = a.page_table[(size_t)b * N + j];
+    if (range < a.n_ranges && lane < P && j < n_b) myblk = a.page_table[(size_t)b * N + j];
   }
   q_digit_planes<G>(a.q + ((size_t)b * a.Hq + (size_t)hbase) * kDim, S.u.dig, S.esc, wave, lane);
   __syncthreads();
@@ -275,8 +318,12 @@ __global__ __launch_bounds__(256, G == 8 ? 4 : 1) void score_kernel(ScoreArgs a)
                        : v4i{0, 0, 0, 0};
   }
   __syncthreads();  // digit planes consumed: the space takes the record offsets
-  if (range >= a.n_ranges) return;  // whole wave; no workgroup barrier follows
-  if (p0 >= n_b) return;            // whole wave: past the sequence's full pages
+  // A wave past the ranges or the sequence's full pages has no work. With one
+  // wave per range it leaves here (no workgroup barrier follows); with
+  // several, it still reaches the merge barrier at the end.
+  const bool live = range < a.n_ranges && range * kScorePagesPerWave < n_b;  // the range has pages
+  const bool active = live && p0 < n_b;                                      // this wave has pages
+  if (W == 1 && !active) return;
   if (lane < 8) T.zero[lane] = (_Float16)0.0f;
 
   // An absent page (past the sequence's full pages, or a table entry out of
@@ -284,199 +331,202 @@ __global__ __launch_bounds__(256, G == 8 ? 4 : 1) void score_kernel(ScoreArgs a)
   // unconditional; its score is replaced by -inf at the end.
   if (myblk < 0 || myblk >= a.num_blocks) myblk = -1;
   const unsigned long long present = __ballot(myblk >= 0);  // bit i: page p0 + i
-  // the lane's page record, as an offset from summ in 16-byte units (the
-  // library limits num_blocks * n_kv_heads * 49 to 32 bits)
-  S.u.off[wave][lane] = (uint32_t)((myblk < 0 ? 0 : myblk) * a.Hkv + kvh) * (uint32_t)(kStride / 16);
-  const uint8_t* vbase = a.summ + kVOff + (row & 7) * 64 + kg * 16;  // V row of the lane
-  const uint8_t* rbase = a.summ + kg * 32;                           // mu, C slice of the lane
+  if (active) {
+    // the lane's page record, as an offset from summ in 16-byte units (the
+    // library limits num_blocks * n_kv_heads * 49 to 32 bits)
+    S.u.off[wave][lane] = (uint32_t)((myblk < 0 ? 0 : myblk) * a.Hkv + kvh) * (uint32_t)(kStride / 16);
+    const uint8_t* vbase = a.summ + kVOff + (row & 7) * 64 + kg * 16;  // V row of the lane
+    const uint8_t* rbase = a.summ + kg * 32;                           // mu, C slice of the lane
 
-  // stage-2 output column col = (page pc of the pass, head hc)
-  const int pc = row / G, hc = row % G;
-  const float es = S.esc[hc], es22 = es * 0x1p22f;
-  const int jpass = reduce_scatter4_pass();  // with G >= 4: which pass of each 4 this lane finishes
+    // stage-2 output column col = (page pc of the pass, head hc)
+    const int pc = row / G, hc = row % G;
+    const float es = S.esc[hc], es22 = es * 0x1p22f;
+    const int jpass = reduce_scatter4_pass();  // with G >= 4: which pass of each 4 this lane finishes
 
-  wave_lds_sync();
-
-  // The 13 loads of tile t go out in a pinned order (the order is worth ~5%
-  // of the gather rate at 4-head groups): issue_v the 8 V rows, issue_tail
-  // the mu, C and scales after them. Offsets come from the wave's LDS table.
-  auto issue_v = [&](int t, TileRec& r) {
-    uint32_t ov[8];
-#pragma unroll
-    for (int vt = 0; vt < 8; ++vt) ov[vt] = S.u.off[wave][t * 16 + 2 * vt + (row >> 3)];
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int vt = 0; vt < 8; ++vt) {
-      r.v[vt] = *reinterpret_cast<const uint4*>(vbase + ((size_t)ov[vt] << 4));
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-  auto issue_tail = [&](int t, TileRec& r) {
-    const uint32_t om = S.u.off[wave][t * 16 + row];
-    const uint8_t* rec = rbase + ((size_t)om << 4);  // page t*16 + row
-    __builtin_amdgcn_sched_barrier(0);
-    r.mu1 = *reinterpret_cast<const uint4*>(rec + kMuOff + 16);
-    __builtin_amdgcn_sched_barrier(0);
-    r.mu0 = *reinterpret_cast<const uint4*>(rec + kMuOff);
-    __builtin_amdgcn_sched_barrier(0);
-    r.c1 = *reinterpret_cast<const uint4*>(rec + kCOff + 16);
-    __builtin_amdgcn_sched_barrier(0);
-    r.c0 = *reinterpret_cast<const uint4*>(rec + kCOff);
-    __builtin_amdgcn_sched_barrier(0);
-    r.scl = *reinterpret_cast<const uint2*>(rec - kg * 32 + kSOff);
-    __builtin_amdgcn_sched_barrier(0);
-  };
-
-  // With up to 4 heads per wave (little compute per byte), the next tile's V
-  // rows are issued as soon as stage 1 has consumed the current ones, so they
-  // travel during stage 2; 8-head waves are compute-bound and skip this (the
-  // extra registers cost more than the overlap gains).
-  constexpr bool kPrefetchV = G <= 4;
-  TileRec cur;
-  issue_v(0, cur);
-#pragma unroll
-  for (int t = 0; t < kTiles; ++t) {
-    if (!kPrefetchV && t > 0) issue_v(t, cur);
-    issue_tail(t, cur);
-    const uint4* vraw = cur.v;
-    const uint4 mu0 = cur.mu0, mu1 = cur.mu1, c0 = cur.c0, c1 = cur.c1;
-    const uint2 scl = cur.scl;
-    // consumed in the order the loads were issued, so work starts on the
-    // first records while the rest are still arriving
-    // ---- stage 1: V tiles (columns = (page 2vt + row/8, basis vector row%8))
-#pragma unroll
-    for (int vt = 0; vt < 8; ++vt) {
-      const uint4 v = vraw[vt];
-      const v4i B0 = {nib_lo(v.x), nib_hi(v.x), nib_lo(v.y), nib_hi(v.y)};
-      const v4i B1 = {nib_lo(v.z), nib_hi(v.z), nib_lo(v.w), nib_hi(v.w)};
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        v4i acc = mfma_i8(aop[rb][0], B0, v4i{0, 0, 0, 0});
-        acc = mfma_i8(aop[rb][1], B1, acc);
-        const int h = 4 * rb + kg;
-        // exact integer (|.| < 2^37) -> fp32 -> split hi + lo, both scaled by
-        // 2^-22 into f16 range as they are rounded (the scaling is exact)
-        const float x = digits_to_float(acc[0], acc[1], acc[2]);
-        const _Float16 xh = (_Float16)(x * 0x1p-22f);
-        const _Float16 xl = (_Float16)fmaf(x, 0x1p-22f, -(float)xh);
-        if (h < G) {
-          T.ph[2 * vt + (row >> 3)][h < G ? h : 0][row & 7] = xh;
-          T.pl[2 * vt + (row >> 3)][h < G ? h : 0][row & 7] = xl;
-        }
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // ---- stage 1: mu tile (columns = the 16 pages); lane (page row, kg) -> head 4rb + kg
-    {
-      const v4i B0 = {(int)mu0.x, (int)mu0.y, (int)mu0.z, (int)mu0.w};
-      const v4i B1 = {(int)mu1.x, (int)mu1.y, (int)mu1.z, (int)mu1.w};
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        v4i acc = mfma_i8(aop[rb][0], B0, v4i{0, 0, 0, 0});
-        acc = mfma_i8(aop[rb][1], B1, acc);
-        const int h = 4 * rb + kg;
-        T.a[row][h < G ? h : G] = (float)(acc[2] * 256 + acc[1]) * 256.0f + (float)acc[0];
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    *reinterpret_cast<uint4*>(&T.c[row][kg * 32]) = c0;
-    *reinterpret_cast<uint4*>(&T.c[row][kg * 32 + 16]) = c1;
-    {
-      // every lane stores (lanes kg > 0 into the spare rows), so that the
-      // scale load is issued with the others rather than behind a branch
-      const int r = kg == 0 ? row : 16 + row;
-      T.sc[r][0] = f16bits_to_float(scl.x);
-      T.sc[r][1] = f16bits_to_float(scl.x >> 16) * (1.0f / 16.0f) * f16bits_to_float(scl.y);
-    }
-    if (kPrefetchV && t + 1 < kTiles) issue_v(t + 1, cur);
     wave_lds_sync();
 
-    // ---- stage 2 + LSE, one pass per PG pages, as one branch-free block.
-    // The LSE sums exp2 of the deviation term alone and adds the centroid
-    // term after the log; a non-finite result (an overflowed sum) redoes the
-    // tile's passes with the page max subtracted. With 4 or more passes, each
-    // 4 share one reduce-scatter over the lane groups and each lane group
-    // finishes one of them; with fewer, every lane of a column reduces and
-    // stores the same value.
-    auto deviations = [&](int gp) -> v4f {
-      v4f acc = {0.f, 0.f, 0.f, 0.f};
-      const int pp = gp * PG + pc;  // tile page of this lane's output column
-      if constexpr (PG >= 4) {
-        // K = 32 per MFMA = 4 page slots x 8 basis vectors; lane group kg = slot
-#pragma unroll
-        for (int ch = 0; ch < PG / 4; ++ch) {
-          const int slot = 4 * ch + kg;
-          const uint2 cw = *reinterpret_cast<const uint2*>(&T.c[gp * PG + slot][row * 8]);
-          const h4 c_lo = codes_to_h4(cw.x), c_hi = codes_to_h4(cw.y);
-          const h8 A = {c_lo[0], c_lo[1], c_lo[2], c_lo[3], c_hi[0], c_hi[1], c_hi[2], c_hi[3]};
+    // The 13 loads of tile t go out in a pinned order (the order is worth ~5%
+    // of the gather rate at 4-head groups): issue_v the 8 V rows, issue_tail
+    // the mu, C and scales after them. Offsets come from the wave's LDS table.
+    auto issue_v = [&](int t, TileRec& r) {
+      uint32_t ov[8];
+  #pragma unroll
+      for (int vt = 0; vt < 8; ++vt) ov[vt] = S.u.off[wave][t * 16 + 2 * vt + (row >> 3)];
+      __builtin_amdgcn_sched_barrier(0);
+  #pragma unroll
+      for (int vt = 0; vt < 8; ++vt) {
+        r.v[vt] = *reinterpret_cast<const uint4*>(vbase + ((size_t)ov[vt] << 4));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    auto issue_tail = [&](int t, TileRec& r) {
+      const uint32_t om = S.u.off[wave][t * 16 + row];
+      const uint8_t* rec = rbase + ((size_t)om << 4);  // page t*16 + row
+      __builtin_amdgcn_sched_barrier(0);
+      r.mu1 = *reinterpret_cast<const uint4*>(rec + kMuOff + 16);
+      __builtin_amdgcn_sched_barrier(0);
+      r.mu0 = *reinterpret_cast<const uint4*>(rec + kMuOff);
+      __builtin_amdgcn_sched_barrier(0);
+      r.c1 = *reinterpret_cast<const uint4*>(rec + kCOff + 16);
+      __builtin_amdgcn_sched_barrier(0);
+      r.c0 = *reinterpret_cast<const uint4*>(rec + kCOff);
+      __builtin_amdgcn_sched_barrier(0);
+      r.scl = *reinterpret_cast<const uint2*>(rec - kg * 32 + kSOff);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // With up to 4 heads per wave (little compute per byte), the next tile's V
+    // rows are issued as soon as stage 1 has consumed the current ones, so they
+    // travel during stage 2; 8-head waves are compute-bound and skip this (the
+    // extra registers cost more than the overlap gains).
+    constexpr bool kPrefetchV = G <= 4;
+    TileRec cur;
+    issue_v(0, cur);
+  #pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      if (!kPrefetchV && t > 0) issue_v(t, cur);
+      issue_tail(t, cur);
+      const uint4* vraw = cur.v;
+      const uint4 mu0 = cur.mu0, mu1 = cur.mu1, c0 = cur.c0, c1 = cur.c1;
+      const uint2 scl = cur.scl;
+      // consumed in the order the loads were issued, so work starts on the
+      // first records while the rest are still arriving
+      // ---- stage 1: V tiles (columns = (page 2vt + row/8, basis vector row%8))
+  #pragma unroll
+      for (int vt = 0; vt < 8; ++vt) {
+        const uint4 v = vraw[vt];
+        const v4i B0 = {nib_lo(v.x), nib_hi(v.x), nib_lo(v.y), nib_hi(v.y)};
+        const v4i B1 = {nib_lo(v.z), nib_hi(v.z), nib_lo(v.w), nib_hi(v.w)};
+  #pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          v4i acc = mfma_i8(aop[rb][0], B0, v4i{0, 0, 0, 0});
+          acc = mfma_i8(aop[rb][1], B1, acc);
+          const int h = 4 * rb + kg;
+          // exact integer (|.| < 2^37) -> fp32 -> split hi + lo, both scaled by
+          // 2^-22 into f16 range as they are rounded (the scaling is exact)
+          const float x = digits_to_float(acc[0], acc[1], acc[2]);
+          const _Float16 xh = (_Float16)(x * 0x1p-22f);
+          const _Float16 xl = (_Float16)fmaf(x, 0x1p-22f, -(float)xh);
+          if (h < G) {
+            T.ph[2 * vt + (row >> 3)][h < G ? h : 0][row & 7] = xh;
+            T.pl[2 * vt + (row >> 3)][h < G ? h : 0][row & 7] = xl;
+          }
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // ---- stage 1: mu tile (columns = the 16 pages); lane (page row, kg) -> head 4rb + kg
+      {
+        const v4i B0 = {(int)mu0.x, (int)mu0.y, (int)mu0.z, (int)mu0.w};
+        const v4i B1 = {(int)mu1.x, (int)mu1.y, (int)mu1.z, (int)mu1.w};
+  #pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          v4i acc = mfma_i8(aop[rb][0], B0, v4i{0, 0, 0, 0});
+          acc = mfma_i8(aop[rb][1], B1, acc);
+          const int h = 4 * rb + kg;
+          T.a[row][h < G ? h : G] = (float)(acc[2] * 256 + acc[1]) * 256.0f + (float)acc[0];
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      *reinterpret_cast<uint4*>(&T.c[row][kg * 32]) = c0;
+      *reinterpret_cast<uint4*>(&T.c[row][kg * 32 + 16]) = c1;
+      {
+        // every lane stores (lanes kg > 0 into the spare rows), so that the
+        // scale load is issued with the others rather than behind a branch
+        const int r = kg == 0 ? row : 16 + row;
+        T.sc[r][0] = f16bits_to_float(scl.x);
+        T.sc[r][1] = f16bits_to_float(scl.x >> 16) * (1.0f / 16.0f) * f16bits_to_float(scl.y);
+      }
+      if (kPrefetchV && t + 1 < TPW) issue_v(t + 1, cur);
+      wave_lds_sync();
+
+      // ---- stage 2 + LSE, one pass per PG pages, as one branch-free block.
+      // The LSE sums exp2 of the deviation term alone and adds the centroid
+      // term after the log; a non-finite result (an overflowed sum) redoes the
+      // tile's passes with the page max subtracted. With 4 or more passes, each
+      // 4 share one reduce-scatter over the lane groups and each lane group
+      // finishes one of them; with fewer, every lane of a column reduces and
+      // stores the same value.
+      auto deviations = [&](int gp) -> v4f {
+        v4f acc = {0.f, 0.f, 0.f, 0.f};
+        const int pp = gp * PG + pc;  // tile page of this lane's output column
+        if constexpr (PG >= 4) {
+          // K = 32 per MFMA = 4 page slots x 8 basis vectors; lane group kg = slot
+  #pragma unroll
+          for (int ch = 0; ch < PG / 4; ++ch) {
+            const int slot = 4 * ch + kg;
+            const uint2 cw = *reinterpret_cast<const uint2*>(&T.c[gp * PG + slot][row * 8]);
+            const h4 c_lo = codes_to_h4(cw.x), c_hi = codes_to_h4(cw.y);
+            const h8 A = {c_lo[0], c_lo[1], c_lo[2], c_lo[3], c_hi[0], c_hi[1], c_hi[2], c_hi[3]};
+            const bool on = (pc == slot);
+            const h8 Bh = *reinterpret_cast<const h8*>(on ? &T.ph[pp][hc][0] : &T.zero[0]);
+            const h8 Bl = *reinterpret_cast<const h8*>(on ? &T.pl[pp][hc][0] : &T.zero[0]);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bh, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bl, acc, 0, 0, 0);
+          }
+        } else {
+          // K = 16 per MFMA = 2 page slots x 8; lane group kg = (slot kg/2, half kg%2)
+          const int slot = kg >> 1, half = kg & 1;
+          const int pg = gp * PG + (slot < PG ? slot : 0);
+          const uint32_t cw = *reinterpret_cast<const uint32_t*>(&T.c[pg][row * 8 + 4 * half]);
+          const h4 cv = codes_to_h4(cw);
+          const h4 A = (slot < PG) ? cv : h4{0, 0, 0, 0};
           const bool on = (pc == slot);
-          const h8 Bh = *reinterpret_cast<const h8*>(on ? &T.ph[pp][hc][0] : &T.zero[0]);
-          const h8 Bl = *reinterpret_cast<const h8*>(on ? &T.pl[pp][hc][0] : &T.zero[0]);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bh, acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, Bl, acc, 0, 0, 0);
+          const h4 Bh = *reinterpret_cast<const h4*>(on ? &T.ph[pp][hc][4 * half] : &T.zero[0]);
+          const h4 Bl = *reinterpret_cast<const h4*>(on ? &T.pl[pp][hc][4 * half] : &T.zero[0]);
+          acc = __builtin_amdgcn_mfma_f32_16x16x16f16(A, Bh, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x16f16(A, Bl, acc, 0, 0, 0);
+        }
+        // lane (col = row, kg) holds tokens 4kg .. 4kg+3 of (page pp, head hc)
+        const float sv = T.sc[pp][1] * es22;
+        return v4f{acc[0] * sv, acc[1] * sv, acc[2] * sv, acc[3] * sv};
+      };
+      auto part_sum = [&](int gp) -> float {
+        const v4f d = deviations(gp);
+        return (fast_exp2(d[0]) + fast_exp2(d[1])) + (fast_exp2(d[2]) + fast_exp2(d[3]));
+      };
+      // pass gp's score (every lane of the column); safe: page max subtracted first
+      auto score_full = [&](int gp, bool safe) -> float {
+        const v4f d = deviations(gp);
+        const int pp = gp * PG + pc;
+        float mx = 0.f;
+        if (safe) {
+          mx = fmaxf(fmaxf(d[0], d[1]), fmaxf(d[2], d[3]));
+          mx = xor32_max(xor16_max(mx));
+        }
+        float ssum = (fast_exp2(d[0] - mx) + fast_exp2(d[1] - mx)) + (fast_exp2(d[2] - mx) + fast_exp2(d[3] - mx));
+        ssum = xor32_sum(xor16_sum(ssum));
+        return fmaf(T.a[pp][hc], T.sc[pp][0] * es, mx + fast_log2(ssum));
+      };
+      bool redo = false;
+      if constexpr (G >= 4) {
+  #pragma unroll
+        for (int g = 0; g < G / 4; ++g) {
+          const float s0 = part_sum(4 * g), s1 = part_sum(4 * g + 1);
+          const float s2 = part_sum(4 * g + 2), s3 = part_sum(4 * g + 3);
+          const float tot = reduce_scatter4(s0, s1, s2, s3);
+          const int pp = (4 * g + jpass) * PG + pc;
+          const float r = fmaf(T.a[pp][hc], T.sc[pp][0] * es, fast_log2(tot));
+          redo |= !__builtin_isfinite(r);
+          T.out[t * 16 + pp][hc] = r;
         }
       } else {
-        // K = 16 per MFMA = 2 page slots x 8; lane group kg = (slot kg/2, half kg%2)
-        const int slot = kg >> 1, half = kg & 1;
-        const int pg = gp * PG + (slot < PG ? slot : 0);
-        const uint32_t cw = *reinterpret_cast<const uint32_t*>(&T.c[pg][row * 8 + 4 * half]);
-        const h4 cv = codes_to_h4(cw);
-        const h4 A = (slot < PG) ? cv : h4{0, 0, 0, 0};
-        const bool on = (pc == slot);
-        const h4 Bh = *reinterpret_cast<const h4*>(on ? &T.ph[pp][hc][4 * half] : &T.zero[0]);
-        const h4 Bl = *reinterpret_cast<const h4*>(on ? &T.pl[pp][hc][4 * half] : &T.zero[0]);
-        acc = __builtin_amdgcn_mfma_f32_16x16x16f16(A, Bh, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x16f16(A, Bl, acc, 0, 0, 0);
+  #pragma unroll
+        for (int gp = 0; gp < G; ++gp) {
+          const float r = score_full(gp, false);
+          redo |= !__builtin_isfinite(r);
+          T.out[t * 16 + gp * PG + pc][hc] = r;
+        }
       }
-      // lane (col = row, kg) holds tokens 4kg .. 4kg+3 of (page pp, head hc)
-      const float sv = T.sc[pp][1] * es22;
-      return v4f{acc[0] * sv, acc[1] * sv, acc[2] * sv, acc[3] * sv};
-    };
-    auto part_sum = [&](int gp) -> float {
-      const v4f d = deviations(gp);
-      return (fast_exp2(d[0]) + fast_exp2(d[1])) + (fast_exp2(d[2]) + fast_exp2(d[3]));
-    };
-    // pass gp's score (every lane of the column); safe: page max subtracted first
-    auto score_full = [&](int gp, bool safe) -> float {
-      const v4f d = deviations(gp);
-      const int pp = gp * PG + pc;
-      float mx = 0.f;
-      if (safe) {
-        mx = fmaxf(fmaxf(d[0], d[1]), fmaxf(d[2], d[3]));
-        mx = xor32_max(xor16_max(mx));
+      if (__builtin_expect(__ballot(redo) != 0ull, 0)) {
+  #pragma unroll 1
+        for (int gp = 0; gp < G; ++gp) T.out[t * 16 + gp * PG + pc][hc] = score_full(gp, true);
       }
-      float ssum = (fast_exp2(d[0] - mx) + fast_exp2(d[1] - mx)) + (fast_exp2(d[2] - mx) + fast_exp2(d[3] - mx));
-      ssum = xor32_sum(xor16_sum(ssum));
-      return fmaf(T.a[pp][hc], T.sc[pp][0] * es, mx + fast_log2(ssum));
-    };
-    bool redo = false;
-    if constexpr (G >= 4) {
-#pragma unroll
-      for (int g = 0; g < G / 4; ++g) {
-        const float s0 = part_sum(4 * g), s1 = part_sum(4 * g + 1);
-        const float s2 = part_sum(4 * g + 2), s3 = part_sum(4 * g + 3);
-        const float tot = reduce_scatter4(s0, s1, s2, s3);
-        const int pp = (4 * g + jpass) * PG + pc;
-        const float r = fmaf(T.a[pp][hc], T.sc[pp][0] * es, fast_log2(tot));
-        redo |= !__builtin_isfinite(r);
-        T.out[t * 16 + pp][hc] = r;
-      }
-    } else {
-#pragma unroll
-      for (int gp = 0; gp < G; ++gp) {
-        const float r = score_full(gp, false);
-        redo |= !__builtin_isfinite(r);
-        T.out[t * 16 + gp * PG + pc][hc] = r;
-      }
+      wave_lds_sync();
     }
-    if (__builtin_expect(__ballot(redo) != 0ull, 0)) {
-#pragma unroll 1
-      for (int gp = 0; gp < G; ++gp) T.out[t * 16 + gp * PG + pc][hc] = score_full(gp, true);
-    }
-    wave_lds_sync();
+
   }
 
-  write_wave_outputs<G>(a, T.out, present, b, hbase, range, p0, n_b, lane);
+  write_wave_outputs<G, P>(a, T.out, S, present, live, b, hbase, range, part, p0, n_b, wave, lane);
 }
 
 // ---- 16 query heads per KV head: one wave decodes each record once for all
@@ -506,7 +556,6 @@ __global__ __launch_bounds__(256, G == 8 ? 4 : 1) void score_kernel(ScoreArgs a)
 // sum of their exp2 is at least about 1 and does not underflow; a sum that
 // overflows gives a non-finite score, and that half tile is redone with the
 // max subtracted.
-constexpr long long k16ShortGridRanges = 1024;  // 16 pages per wave up to this many (seq, KV head, range)
 
 template <int PPW>
 struct Tile16Lds {
@@ -813,7 +862,7 @@ hipError_t launch_g(const locks_dims& d, const WsLayout& L, const DevPtrs& P, co
   if constexpr (G == 16) {
     // 32 pages per wave (two ranges per workgroup); 16 (one range per
     // workgroup) when that grid still fits one round of resident waves
-    if ((long long)d.batch * d.n_kv_heads * L.n_score_wg <= k16ShortGridRanges) {
+    if ((long long)d.batch * d.n_kv_heads * L.n_score_wg * 4 <= kScoreRoundWaves) {
       const dim3 grid(L.n_score_wg, d.n_kv_heads, d.batch);
       hipLaunchKernelGGL(score16_kernel<16>, grid, dim3(256), 0, s, a);
     } else {
@@ -821,8 +870,18 @@ hipError_t launch_g(const locks_dims& d, const WsLayout& L, const DevPtrs& P, co
       hipLaunchKernelGGL(score16_kernel<32>, grid, dim3(256), 0, s, a);
     }
   } else {
-    const dim3 grid((L.n_score_wg + 3) / 4, d.n_kv_heads, d.batch);  // four ranges per workgroup
-    hipLaunchKernelGGL(score_kernel<G>, grid, dim3(256), 0, s, a);
+    // 64 pages per wave (four ranges per workgroup); 16 (a range over four
+    // waves) when that grid still fits one round of resident waves: four
+    // times the waves to hide latency with where the 64-page grid leaves a
+    // SIMD one wave or none
+    const long long units = (long long)d.batch * d.n_kv_heads * L.n_score_wg;  // (seq, KV head, range)
+    if (units * 4 <= kScoreRoundWaves) {
+      const dim3 grid(L.n_score_wg, d.n_kv_heads, d.batch);
+      hipLaunchKernelGGL((score_kernel<G, 16>), grid, dim3(256), 0, s, a);
+    } else {
+      const dim3 grid((L.n_score_wg + 3) / 4, d.n_kv_heads, d.batch);
+      hipLaunchKernelGGL((score_kernel<G, 64>), grid, dim3(256), 0, s, a);
+    }
   }
   return hipGetLastError();
 }
