@@ -12,10 +12,13 @@ Sources, cited by title and section:
   (B) "LOCKS – 효율적인 롱 컨텍스트 디코딩을 위한 페이지 로컬 압축 키 요약"
       (gist.science, paper 2607.24555) — section 2, mechanisms 1-3.
 
-Parity pins for every function are in ``tests/test_oracle_pins.py``. The QUANTISED scores and selections have no pin
-other than their pieces (the quantiser, the pack format and the unquantised
-score each are pinned; their composition is not): "parity unpinned" for the
-quantised end-to-end numbers.
+Parity pins for every function are in ``tests/test_oracle_pins.py``. The
+quantised path is pinned in pieces (the quantiser against numpy's fp16
+rounding, the record layout against a record packed with numpy, the
+unquantised score against the exact page LSE) and end to end from the record
+on: the decode step's scores equal scipy's log-sum-exp over the keys a record
+reconstructs (decoded there independently), and its selection is the stable
+top-k of group keys formed there from them.
 """
 from __future__ import annotations
 

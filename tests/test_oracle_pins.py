@@ -513,6 +513,54 @@ def test_scores_from_records_match_unpacked_formula_and_selection_order(orc):
         assert list(sel[0, kvh]) == sorted(order)
 
 
+def np_decode_record(rec):
+    """Decoder of the documented record layout written here with numpy bit
+    operations; it shares nothing with the oracle's unpacking."""
+    rec = np.asarray(rec, dtype=np.uint8)
+    s = rec[768:774].copy().view(np.float16).astype(np.float64)  # s_mu, s_V, s_C
+    w = rec[:512].reshape(8, 16, 4).astype(np.int64)             # [k][word][byte]
+    nib = np.stack([w & 0xF, w >> 4], axis=2)                    # [k][word][half][byte]
+    nib = np.where(nib > 7, nib - 16, nib)                       # 4-bit two's complement
+    V = nib.reshape(8, DIM).T * s[1]                             # d = 8 word + 4 half + byte
+    mu = rec[512:640].view(np.int8).astype(np.float64) * s[0]
+    C = rec[640:768].view(np.int8).astype(np.float64).reshape(PAGE, 8) * s[2]
+    return mu, V, C
+
+
+def test_quantised_scores_and_selection_match_reconstructed_keys(orc):
+    """End to end on quantised records (A "How LOCKS works": the score is the
+    log-sum-exp of the page's reconstructed logits; B mechanism 3: the group
+    key averages each head's mass share): every page score of the oracle's
+    decode step equals scipy's log-sum-exp over the 16 keys the record
+    reconstructs, mu + V c_i, with the record decoded here independently; and
+    its selection is the stable top-k of group keys formed here from those
+    scores. This ties the quantised composition (build -> record -> score ->
+    key -> top-k) to the definition rather than to the oracle's factored form
+    q.mu + (V^T q).c_i."""
+    r = rng(71)
+    B, Hq, Hkv, N, k = 2, 8, 2, 24, 6
+    kb, kd, vb, vd, pt, q = oracle_inputs(r, B, Hq, Hkv, N)
+    lens = np.array([N * PAGE, N * PAGE - 21], dtype=np.int32)  # the second ends in a tail
+    summ = orc.build_summaries(kb, pt, lens)
+    out, sel, sc, ky = orc.decode_step(q, summ, kb, vb, pt, lens, k * PAGE)
+    G = Hq // Hkv
+    for b in range(B):
+        n = int(lens[b]) // PAGE
+        ref = np.empty((Hq, n))
+        for h in range(Hq):
+            qh = q[b, h].astype(np.float64)
+            for j in range(n):
+                mu, V, C = np_decode_record(summ[pt[b, j], h // G])
+                ref[h, j] = exact_lse(qh, mu + C @ V.T)
+        assert np.allclose(sc[b, :, :n], ref, rtol=0, atol=1e-9)
+        for kvh in range(Hkv):
+            s = ref[kvh * G:(kvh + 1) * G]
+            share = np.exp(s - logsumexp(s, axis=1, keepdims=True))  # per head, sums to 1
+            key = np.log(share.mean(axis=0))
+            top = np.lexsort((np.arange(n), -key))[:k]
+            assert list(sel[b, kvh]) == sorted(top.tolist())
+
+
 @pytest.mark.parametrize("rank", [2, 4, 8])
 def test_theorem1_mass_retention_bound(orc, rank):
     """(A "How LOCKS works", Theorem 1; B section 3 retention guarantees.)
