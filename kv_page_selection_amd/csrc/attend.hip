@@ -53,6 +53,13 @@ __global__ __launch_bounds__(256) void attend_kernel(AttnArgs a) {
   const int base_len = a.sel ? a.k : n_b;  // entry base_len is the tail, if any
   const int list_len = base_len + (tail > 0 ? 1 : 0);
   const int s0 = split * a.pages_per_split;
+  // the first entry's block id: a selected page (entry < k) needs no sequence
+  // length, so its load goes out together with the length's
+  int blk_first = -1;
+  if (a.sel_blk && s0 + wave < a.k) {
+    const int blk = a.sel_blk[((size_t)b * a.Hkv + kvh) * a.k + s0 + wave];
+    blk_first = (blk >= 0 && blk < a.num_blocks) ? blk : -1;
+  }
   const int s1 = min(s0 + a.pages_per_split, list_len);
 
   __shared__ __align__(16) float q_s[G][kDim];
@@ -74,7 +81,10 @@ __global__ __launch_bounds__(256) void attend_kernel(AttnArgs a) {
     }
     return (blk >= 0 && blk < a.num_blocks) ? blk : -1;
   };
-  int blk_next = (s0 + wave < s1) ? page_block(s0 + wave) : -1;  // in flight during q staging
+  // a selected entry's block id was loaded above; others (the tail, dense
+  // lists, caller-given ids) are looked up here
+  int blk_next = blk_first;
+  if (!(a.sel_blk && s0 + wave < a.k)) blk_next = (s0 + wave < s1) ? page_block(s0 + wave) : -1;
 
   const float qscale = kLog2e * kInvSqrtD;  // logits in base-2 units
   for (int i = tid; i < G * kDim; i += 256)
@@ -214,6 +224,13 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(AttnArgs a) {
   const int base_len = a.sel ? a.k : n_b;  // entry base_len is the tail, if any
   const int list_len = base_len + (tail > 0 ? 1 : 0);
   const int s0 = split * a.pages_per_split;
+  // the first entry's block id: a selected page (entry < k) needs no sequence
+  // length, so its load goes out together with the length's
+  int blk_first = -1;
+  if (a.sel_blk && s0 + wave < a.k) {
+    const int blk = a.sel_blk[((size_t)b * a.Hkv + kvh) * a.k + s0 + wave];
+    blk_first = (blk >= 0 && blk < a.num_blocks) ? blk : -1;
+  }
   const int s1 = min(s0 + a.pages_per_split, list_len);
 
   // V staging during the page loop; the waves' O rows for the merge after it
@@ -237,7 +254,8 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(AttnArgs a) {
     }
     return (blk >= 0 && blk < a.num_blocks) ? blk : -1;
   };
-  int blk_next = (s0 + wave < s1) ? page_block(s0 + wave) : -1;
+  int blk_next = blk_first;
+  if (!(a.sel_blk && s0 + wave < a.k)) blk_next = (s0 + wave < s1) ? page_block(s0 + wave) : -1;
 
   // q of head li (zero for li >= G), base-2 logit scale, bf16 hi + lo
   bf8_t qh[4], ql[4];
@@ -371,11 +389,12 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(const float* partials
   const float* ph = partials + ((size_t)b * Hq + h) * n_split * kPartialFloats;
   const int per = (n_split + 1) / 2;
   const int s0 = half * per, s1 = min(n_split, s0 + per);
+  constexpr int MB = 8;  // splits' loads in flight at a time (16 or 32 measured slower)
   float M = -1e30f, L = 0.f, O = 0.f;  // (-1e30, 0, 0) = empty
-  for (int sb = s0; sb < s1; sb += 8) {
-    float mv[8], lv[8], ov[8];
+  for (int sb = s0; sb < s1; sb += MB) {
+    float mv[MB], lv[MB], ov[MB];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < MB; ++i) {
       const int sp = (sb + i < s1) ? sb + i : s0;
       const float* p = ph + (size_t)sp * kPartialFloats;
       mv[i] = p[0];
@@ -383,7 +402,7 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(const float* partials
       ov[i] = p[2 + d];
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < MB; ++i) {
       const float mi = (sb + i < s1) ? fmaxf(mv[i], -1e30f) : -1e30f;
       const float mn = fmaxf(M, mi);
       const float fa = fast_exp2(M - mn), fb = (sb + i < s1) ? fast_exp2(mi - mn) : 0.f;
