@@ -235,6 +235,30 @@ def test_full_budget_equals_dense(locks):
     assert float((out - dense).abs().max()) < 1e-5
 
 
+@pytest.mark.parametrize("config,hkv,pages", [(2, 8, 6400), (2, 4, 12800), (5, 2, 25600)],
+                         ids=["G4", "G8", "G16"])
+def test_scorer_splits_agree_bitwise(locks, config, hkv, pages):
+    """The scorer runs 16 pages per wave on grids of at most 1024 (sequence,
+    KV head, 64-page range) triples and 64 (32 at 16 heads) on larger ones.
+    A sequence decoded alone (800 triples) and in a batch of two (1600) goes
+    through both and gets bit-identical scores, selection and output."""
+    say(f"scorer split agreement config {config} hkv {hkv} pages {pages}")
+    w = workloads.make(config, device=DEV, ctx=16 * pages, batch=2, budget=512, n_kv_heads=hkv,
+                       n_q_heads=32, seed=43, seq_lens=[16 * pages - 21, 16 * pages])
+    summ = locks.build_summaries(w.k_cache, w.page_table, w.seq_lens)
+    runs = []
+    for nb in (2, 1):
+        q, pt, sl = (t[:nb].contiguous() for t in (w.q, w.page_table, w.seq_lens))
+        ps = torch.full((nb, w.n_q_heads, w.max_pages), float("nan"), device=DEV)
+        o, s = locks.decode_step(q, summ, w.k_cache, w.v_cache, pt, sl, w.budget, page_scores=ps)
+        runs.append((o[0].clone(), s[0].clone(), ps[0].clone()))
+    torch.cuda.synchronize()
+    n = pages - 2  # full pages of sequence 0 (then an 11-token tail)
+    (o2, s2, p2), (o1, s1, p1) = runs
+    assert torch.equal(p1[:, :n], p2[:, :n])
+    assert torch.equal(s1, s2) and torch.equal(o1, o2)
+
+
 def test_deterministic_and_workspace_reuse(locks):
     """Bitwise-identical repeats; one workspace reused across budgets and the
     dense call (counters are left at zero by every call)."""
