@@ -235,8 +235,9 @@ def test_full_budget_equals_dense(locks):
     assert float((out - dense).abs().max()) < 1e-5
 
 
-@pytest.mark.parametrize("config,hkv,pages", [(2, 8, 6400), (2, 4, 12800), (5, 2, 25600)],
-                         ids=["G4", "G8", "G16"])
+@pytest.mark.parametrize("config,hkv,pages",
+                         [(2, 32, 1600), (2, 16, 3200), (2, 8, 6400), (2, 4, 12800), (5, 2, 25600)],
+                         ids=["G1", "G2", "G4", "G8", "G16"])
 def test_scorer_splits_agree_bitwise(locks, config, hkv, pages):
     """The scorer runs 16 pages per wave on grids of at most 1024 (sequence,
     KV head, 64-page range) triples and 64 (32 at 16 heads) on larger ones.
