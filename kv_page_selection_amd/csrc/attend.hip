@@ -449,7 +449,9 @@ hipError_t launch_g(const locks_dims& d, const WsLayout& L, const DevPtrs& P, co
   a.n_split = dense ? L.n_dense_split : L.n_att_split;
   // MFMA where a query group fills enough of the 16 rows: G >= 8 always, and
   // G = 4 for the long dense splits; a sparse split at G = 4 (one page per
-  // wave, 3/4 of the rows padding) is faster on VALU (measured)
+  // wave, 3/4 of the rows padding) stays on VALU: MFMA there showed no clear
+  // gain (1.0 us per step faster at one 1M-token sequence, 0.5 slower at
+  // eight of 256K tokens)
   const dim3 grid(a.n_split, d.n_kv_heads, d.batch);
   if constexpr (G >= 8) {
     hipLaunchKernelGGL(attend_mfma_kernel<G>, grid, dim3(256), 0, s, a);
