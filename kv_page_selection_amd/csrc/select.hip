@@ -393,25 +393,36 @@ __global__ __launch_bounds__(kThreads) void select_chunk_kernel(SelectArgs a) {
 
 }
 
-// ============================================================ merge (one wave)
+// ============================================================ merge
 //
-// One wave per (sequence, KV head) ranks the chunk lists, in page order, in
-// rounds of up to kRoundNew new candidates appended to the running top-k in
-// LDS; a wave needs no barriers, only the in-order completion of its own LDS
-// operations. Ranking: bucket refinement over the live key range with a
-// 2048-bucket LDS histogram (32 buckets per lane), elements above the bucket
-// of the need-th key in, below it out, until the count fits or the live keys
-// are all equal (then the earliest, i.e. lowest page ids, win).
+// One workgroup of kMergeThreads per (sequence, KV head). Fast path (every
+// chunk list fits the speculative slots, at most 1024 candidates): wave 0
+// alone ranks them in registers and the other waves leave. Otherwise the
+// whole workgroup ranks the chunk lists, in page order, in rounds: new
+// candidates are appended to the running top-k in LDS until the list's
+// kRoundCap entries are full, then ranked by bucket refinement over the live
+// key range with a 2048-bucket LDS histogram (4 buckets per thread):
+// elements above the bucket of the need-th key in, below it out, until the
+// count fits or the live keys are all equal (then the earliest, i.e. lowest
+// page ids, win).
 
-constexpr int kRoundNew = 512;                   // new candidates per round
+constexpr int kMergeThreads = 512;               // 8 waves: the fast path keeps its registers
+constexpr int kMW = kMergeThreads / 64;
+constexpr int kRoundNew = 512;                   // candidates gathered per load batch
 constexpr int kRoundCap = kSelectMaxK + kRoundNew;
+constexpr int kMergeBpt = kHistBuckets / kMergeThreads;           // histogram buckets per thread
+constexpr int kMergeEpt = (kRoundCap + kMergeThreads - 1) / kMergeThreads;  // list entries per thread
 
-struct WaveMergeLds {
+struct MergeLds {
   unsigned long long x[kRoundCap];  // sort keys; 0 = rejected
   int blk[kRoundCap];
   uint8_t state[kRoundCap];         // 0 live, 1 selected, 2 rejected
   uint32_t hist[kHistBuckets];
   int off[1025];
+  uint32_t red3[3][kMW];
+  uint32_t scn[kMW];
+  int bstar;
+  uint32_t babove;
 };
 
 // LDS slot of histogram bucket bk when lane l owns buckets [32l, 32l+32):
@@ -419,16 +430,31 @@ struct WaveMergeLds {
 // different banks.
 __device__ __forceinline__ int hslot(int bk) { return ((bk & 31) << 6) | (bk >> 5); }
 
-__device__ __forceinline__ uint32_t wave_ballot_count(bool p) {
-  return (uint32_t)__popcll(__ballot(p));
+// Exclusive prefix sum over the workgroup (thread order) of one u32; *total
+// gets the workgroup total. One barrier; scn is free again after the next.
+__device__ __forceinline__ uint32_t merge_excl_scan(uint32_t v, uint32_t* scn, uint32_t* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t inc = wave_incl_scan(v);
+  if (lane == 63) scn[wave] = inc;
+  __syncthreads();
+  uint32_t pre = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kMW; ++w) {
+    const uint32_t c = scn[w];
+    pre += (w < wave) ? c : 0u;
+    tot += c;
+  }
+  *total = tot;
+  return pre + inc - v;
 }
 
-// Ranks x[0..n) (state all live on entry) and marks the `need` largest selected.
-__device__ void wave_topk(WaveMergeLds& W, int n, int need) {
-  const int lane = threadIdx.x & 63;
+// Ranks x[0..n) (state all live on entry) and marks the `need` largest
+// selected; every thread of the workgroup takes part.
+__device__ void merge_topk(MergeLds& W, int n, int need) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int iter = 0; iter < 8 && need > 0; ++iter) {
     uint32_t cnt = 0, lo = 0xffffffffu, hi = 0u;
-    for (int e = lane; e < n; e += 64)
+    for (int e = tid; e < n; e += kMergeThreads)
       if (W.state[e] == 0) {
         const uint32_t v = (uint32_t)(W.x[e] >> 32);
         ++cnt;
@@ -438,102 +464,110 @@ __device__ void wave_topk(WaveMergeLds& W, int n, int need) {
     cnt = wave_sum_u32(cnt);
     lo = wave_min_u32(lo);
     hi = wave_max_u32(hi);
+    if (lane == 0) { W.red3[0][wave] = cnt; W.red3[1][wave] = lo; W.red3[2][wave] = hi; }
+    __syncthreads();
+    cnt = 0;
+    lo = 0xffffffffu;
+    hi = 0u;
+#pragma unroll
+    for (int w = 0; w < kMW; ++w) {
+      cnt += W.red3[0][w];
+      lo = min(lo, W.red3[1][w]);
+      hi = max(hi, W.red3[2][w]);
+    }
     if ((int)cnt <= need) {  // every live element is in
-      for (int e = lane; e < n; e += 64)
+      for (int e = tid; e < n; e += kMergeThreads)
         if (W.state[e] == 0) W.state[e] = 1;
-      wave_lds_sync();
+      __syncthreads();
       return;
     }
     if (lo == hi) break;
     const float scale = (float)kHistBuckets / ((float)(hi - lo) + 1.0f);
-    for (int i = lane; i < kHistBuckets; i += 64) W.hist[i] = 0u;  // layout-independent
-    wave_lds_sync();
-    for (int e = lane; e < n; e += 64)
-      if (W.state[e] == 0) atomicAdd(&W.hist[hslot(hbucket((uint32_t)(W.x[e] >> 32), lo, scale))], 1u);
-    wave_lds_sync();
-    // lane l owns buckets [32l, 32l+32); suffix counts from the top bucket down
-    uint32_t hb[32];
-    uint32_t mine = 0;
 #pragma unroll
-    for (int q = 0; q < 32; ++q) {
-      hb[q] = W.hist[(q << 6) | lane];
+    for (int q = 0; q < kMergeBpt; ++q) W.hist[kMergeBpt * tid + q] = 0u;
+    __syncthreads();
+    for (int e = tid; e < n; e += kMergeThreads)
+      if (W.state[e] == 0) atomicAdd(&W.hist[hbucket((uint32_t)(W.x[e] >> 32), lo, scale)], 1u);
+    __syncthreads();
+    // thread t owns buckets [4t, 4t+4): counts above them, then the bucket
+    // holding the need-th key from the top
+    uint32_t hb[kMergeBpt], mine = 0;
+#pragma unroll
+    for (int q = 0; q < kMergeBpt; ++q) {
+      hb[q] = W.hist[kMergeBpt * tid + q];
       mine += hb[q];
     }
-    const uint32_t pre = wave_incl_scan(mine);
-    const uint32_t total = __builtin_amdgcn_readlane(pre, 63);
-    uint32_t acc = total - pre;  // elements in buckets above this lane's
-    int bstar = -1;
-    uint32_t above = 0;
+    uint32_t tot;
+    const uint32_t pre = merge_excl_scan(mine, W.scn, &tot);
+    uint32_t acc = tot - pre - mine;
 #pragma unroll
-    for (int q = 31; q >= 0; --q) {
-      if (acc < (uint32_t)need && (uint32_t)need <= acc + hb[q]) { bstar = 32 * lane + q; above = acc; }
+    for (int q = kMergeBpt - 1; q >= 0; --q) {
+      if (acc < (uint32_t)need && (uint32_t)need <= acc + hb[q]) {
+        W.bstar = kMergeBpt * tid + q;  // exactly one thread finds it
+        W.babove = acc;
+      }
       acc += hb[q];
     }
-    // exactly one lane found the bucket: broadcast it
-    const uint64_t owner = __ballot(bstar >= 0);
-    if (owner == 0) break;  // unreachable: some bucket holds the need-th key
-    const int src = __builtin_ctzll(owner);
-    bstar = __builtin_amdgcn_readlane(bstar, src);
-    above = __builtin_amdgcn_readlane(above, src);
-    for (int e = lane; e < n; e += 64)
+    __syncthreads();
+    const int bstar = W.bstar;
+    const uint32_t above = W.babove;
+    for (int e = tid; e < n; e += kMergeThreads)
       if (W.state[e] == 0) {
         const int bk = hbucket((uint32_t)(W.x[e] >> 32), lo, scale);
         if (bk > bstar) W.state[e] = 1;
         else if (bk < bstar) W.state[e] = 2;
       }
-    wave_lds_sync();
     need -= (int)above;
+    __syncthreads();
   }
-  // live keys all equal (or, unreachably, out of passes): earliest live win
-  int base = 0;
-  for (int e0 = 0; e0 < n && need > 0; e0 += 64) {
-    const int e = e0 + lane;
-    const bool live = e < n && W.state[e] == 0;
-    const uint32_t before = wave_incl_scan(live ? 1u : 0u) - (live ? 1u : 0u);
-    if (live && (int)(base + before) < need) W.state[e] = 1;
-    base += (int)wave_ballot_count(live);
+  if (need > 0) {
+    // live keys all equal (or, unreachably, out of passes): earliest live
+    // win; thread t owns entries [t E, t E + E)
+    const int E = (n + kMergeThreads - 1) / kMergeThreads;
+    uint32_t nl = 0;
+    for (int i = 0; i < E; ++i) {
+      const int e = tid * E + i;
+      if (e < n && W.state[e] == 0) ++nl;
+    }
+    uint32_t tot;
+    uint32_t before = merge_excl_scan(nl, W.scn, &tot);
+    for (int i = 0; i < E; ++i) {
+      const int e = tid * E + i;
+      if (e < n && W.state[e] == 0) {
+        if ((int)before < need) W.state[e] = 1;
+        ++before;
+      }
+    }
+    __syncthreads();
   }
-  wave_lds_sync();
 }
 
-// The exact top-k of one (sequence, KV head)'s candidate lists, run by one
-// wave; leaves the kept sort keys and blocks, in page order, in W.x / W.blk
-// and returns their count.
-__device__ int wave_merge(WaveMergeLds& W, const unsigned long long* src, const int32_t* src_blk,
-                          const int32_t* counts, int n_chunks, int chunk, int k) {
-  const int lane = threadIdx.x & 63;
-  // chunk offsets: lane l sums chunks [l*cpl, (l+1)*cpl)
-  const int cpl = (n_chunks + 63) / 64;
-  int c_loc[16];
-  int mine = 0;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int c = lane * cpl + i;
-    c_loc[i] = (i < cpl && c < n_chunks) ? counts[c] : 0;
-    mine += c_loc[i];
-  }
-  const int pre = (int)wave_incl_scan((uint32_t)mine);
-  const int total = __builtin_amdgcn_readlane(pre, 63);
-  {
-    int o = pre - mine;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int c = lane * cpl + i;
-      if (i < cpl && c < n_chunks) W.off[c] = o;
-      o += c_loc[i];
-    }
-    if (lane == 0) W.off[n_chunks] = total;
-  }
-  wave_lds_sync();
+// The exact top-k of one (sequence, KV head)'s candidate lists, run by the
+// whole workgroup; leaves the kept sort keys and blocks, in page order, in
+// W.x / W.blk and returns their count.
+__device__ int merge_lists(MergeLds& W, const unsigned long long* src, const int32_t* src_blk,
+                           const int32_t* counts, int n_chunks, int chunk, int k) {
+  const int tid = threadIdx.x;
+  // chunk offsets (at most 1024 chunks: two per thread)
+  const uint32_t c0 = (2 * tid < n_chunks) ? (uint32_t)counts[2 * tid] : 0u;
+  const uint32_t c1 = (2 * tid + 1 < n_chunks) ? (uint32_t)counts[2 * tid + 1] : 0u;
+  uint32_t total_u;
+  const uint32_t o = merge_excl_scan(c0 + c1, W.scn, &total_u);
+  if (2 * tid < n_chunks) W.off[2 * tid] = (int)o;
+  if (2 * tid + 1 < n_chunks) W.off[2 * tid + 1] = (int)(o + c0);
+  if (tid == 0) W.off[n_chunks] = (int)total_u;
+  __syncthreads();
+  const int total = (int)total_u;
   int nkept = 0, consumed = 0;
   do {
-    const int take = min(total - consumed, kRoundNew);
-    // gather the next `take` candidates (8 per lane, all loads in flight together)
-    int slot[kRoundNew / 64];
+    // a round fills the LDS list: after the first, k kept plus what fits
+    const int take = min(total - consumed, kRoundCap - nkept);
+    unsigned long long xv[kMergeEpt];
+    int bv[kMergeEpt];
 #pragma unroll
-    for (int i = 0; i < kRoundNew / 64; ++i) {
-      const int e = lane + 64 * i;
-      slot[i] = -1;
+    for (int i = 0; i < kMergeEpt; ++i) {
+      const int e = tid + kMergeThreads * i;
+      int sidx = 0;
       if (e < take) {
         const int gidx = consumed + e;
         int c = 0;
@@ -541,47 +575,52 @@ __device__ int wave_merge(WaveMergeLds& W, const unsigned long long* src, const 
           const int mid = (lo + hi) >> 1;
           if (W.off[mid] <= gidx) { c = mid; lo = mid + 1; } else hi = mid - 1;
         }
-        slot[i] = c * chunk + (gidx - W.off[c]);
+        sidx = c * chunk + (gidx - W.off[c]);
       }
-    }
-    unsigned long long xv[kRoundNew / 64];
-    int bv[kRoundNew / 64];
-#pragma unroll
-    for (int i = 0; i < kRoundNew / 64; ++i) {
-      const int sidx = slot[i] >= 0 ? slot[i] : 0;
       xv[i] = src[sidx];
       bv[i] = src_blk[sidx];
     }
 #pragma unroll
-    for (int i = 0; i < kRoundNew / 64; ++i) {
-      const int e = lane + 64 * i;
+    for (int i = 0; i < kMergeEpt; ++i) {
+      const int e = tid + kMergeThreads * i;
       if (e < take) {
         W.x[nkept + e] = xv[i];
         W.blk[nkept + e] = bv[i];
       }
     }
     const int n = nkept + take;
-    for (int e = lane; e < n; e += 64) W.state[e] = 0;
-    wave_lds_sync();
-    wave_topk(W, n, k);
-    // keep the selected, in order (destinations never pass their sources)
-    int base = 0;
-    for (int e0 = 0; e0 < n; e0 += 64) {
-      const int e = e0 + lane;
-      const bool s = e < n && W.state[e] == 1;
-      unsigned long long xe = 0;
-      int be = 0;
-      if (s) { xe = W.x[e]; be = W.blk[e]; }
-      const uint32_t before = wave_incl_scan(s ? 1u : 0u) - (s ? 1u : 0u);
-      wave_lds_sync();
-      if (s) {
-        W.x[base + before] = xe;
-        W.blk[base + before] = be;
+    for (int e = tid; e < n; e += kMergeThreads) W.state[e] = 0;
+    __syncthreads();
+    merge_topk(W, n, k);
+    // keep the selected, in order: thread t owns entries [t E, t E + E),
+    // all read before the scan's barrier, written after it
+    const int E = (n + kMergeThreads - 1) / kMergeThreads;
+    unsigned long long xs[kMergeEpt];
+    int bs[kMergeEpt];
+    uint32_t sel = 0, ns = 0;
+#pragma unroll
+    for (int i = 0; i < kMergeEpt; ++i) {
+      const int e = tid * E + i;
+      xs[i] = 0;
+      bs[i] = 0;
+      if (i < E && e < n && W.state[e] == 1) {
+        xs[i] = W.x[e];
+        bs[i] = W.blk[e];
+        sel |= 1u << i;
+        ++ns;
       }
-      base += (int)wave_ballot_count(s);
-      wave_lds_sync();
     }
-    nkept = base;
+    uint32_t kept;
+    uint32_t dst = merge_excl_scan(ns, W.scn, &kept);
+#pragma unroll
+    for (int i = 0; i < kMergeEpt; ++i)
+      if ((sel >> i) & 1u) {
+        W.x[dst] = xs[i];
+        W.blk[dst] = bs[i];
+        ++dst;
+      }
+    __syncthreads();
+    nkept = (int)kept;
     consumed += take;
   } while (consumed < total);
   return nkept;
@@ -590,15 +629,15 @@ __device__ int wave_merge(WaveMergeLds& W, const unsigned long long* src, const 
 constexpr int kFastPerLane = 16;
 constexpr int kFastCap = 64 * kFastPerLane;  // candidates ranked in registers
 
-// One wave per (sequence, KV head). Fast path (every chunk list fits the
-// speculative slots, at most 1024 candidates): the counts and the first S
-// slots of every chunk list arrive in one round trip, and the candidates are
-// ranked in registers, 16 contiguous ones per lane, so lane order is page
-// order. Otherwise the LDS rounds of wave_merge.
-__global__ __launch_bounds__(64) void select_merge_kernel(SelectArgs a) {
+// One workgroup per (sequence, KV head). Fast path (every chunk list fits
+// the speculative slots, at most 1024 candidates), wave 0 alone: the counts
+// and the first S slots of every chunk list arrive in one round trip, and the
+// candidates are ranked in registers, 16 contiguous ones per lane, so lane
+// order is page order. Otherwise the workgroup's LDS rounds (merge_lists).
+__global__ __launch_bounds__(kMergeThreads) void select_merge_kernel(SelectArgs a) {
   const int kvh = blockIdx.x, b = blockIdx.y;
-  const int lane = threadIdx.x;
-  __shared__ WaveMergeLds W;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ MergeLds W;
   const size_t head = (size_t)b * a.Hkv + kvh;
   const int nc = a.n_chunks;
   const int32_t* counts = a.cand_count + head * nc;
@@ -616,16 +655,25 @@ __global__ __launch_bounds__(64) void select_merge_kernel(SelectArgs a) {
     const int c = lane + 64 * i;
     ccnt[i] = (c < nc) ? counts[c] : 0;
   }
+  // (wave 0 only: every wave reads the counts to take the same path)
   unsigned long long x[kFastPerLane];
   int bl[kFastPerLane], cof[kFastPerLane];
 #pragma unroll
   for (int i = 0; i < kFastPerLane; ++i) {
-    const int e = lane * kFastPerLane + i;
-    const int c = e >> lgS, sl = e & (S - 1);
-    const int idx = (c < nc) ? c * a.chunk + sl : 0;
-    x[i] = src[idx];
-    bl[i] = src_blk[idx];
-    cof[i] = (c < nc) ? counts[c] : 0;
+    x[i] = 0;
+    bl[i] = 0;
+    cof[i] = 0;
+  }
+  if (wave == 0) {
+#pragma unroll
+    for (int i = 0; i < kFastPerLane; ++i) {
+      const int e = lane * kFastPerLane + i;
+      const int c = e >> lgS, sl = e & (S - 1);
+      const int idx = (c < nc) ? c * a.chunk + sl : 0;
+      x[i] = src[idx];
+      bl[i] = src_blk[idx];
+      cof[i] = (c < nc) ? counts[c] : 0;
+    }
   }
   int total = 0;
   bool over = false;
@@ -635,15 +683,16 @@ __global__ __launch_bounds__(64) void select_merge_kernel(SelectArgs a) {
     over |= ccnt[i] > S;
   }
   total = (int)wave_sum_u32((uint32_t)total);
-  if (__ballot(over) != 0) {
-    const int nk = wave_merge(W, src, src_blk, counts, nc, a.chunk, a.k);
-    for (int i = lane; i < a.k; i += 64) {
+  if (__ballot(over) != 0) {  // the same in every wave
+    const int nk = merge_lists(W, src, src_blk, counts, nc, a.chunk, a.k);
+    for (int i = tid; i < a.k; i += kMergeThreads) {
       out[i] = (i < nk) ? (int32_t)(0xffffffffu - (uint32_t)(W.x[i] & 0xffffffffu)) : -1;
       outb[i] = (i < nk) ? W.blk[i] : -1;
     }
     return;
   }
   (void)total;
+  if (wave != 0) return;  // the fast path has no barrier
 
   uint32_t live = 0, sel = 0;
 #pragma unroll
@@ -779,7 +828,7 @@ hipError_t launch_select(const locks_dims& d, const WsLayout& L, const DevPtrs& 
     default: return hipErrorInvalidValue;
   }
 #undef LOCKS_CHUNK
-  hipLaunchKernelGGL(select_merge_kernel, dim3(d.n_kv_heads, d.batch), dim3(64), 0, s, a);
+  hipLaunchKernelGGL(select_merge_kernel, dim3(d.n_kv_heads, d.batch), dim3(kMergeThreads), 0, s, a);
   return hipGetLastError();
 }
 
