@@ -401,12 +401,12 @@ __global__ __launch_bounds__(kThreads) void select_chunk_kernel(SelectArgs a) {
 // whole workgroup ranks the chunk lists, in page order, in rounds: new
 // candidates are appended to the running top-k in LDS until the list's
 // kRoundCap entries are full, then ranked by bucket refinement over the live
-// key range with a 2048-bucket LDS histogram (4 buckets per thread):
+// key range with a 2048-bucket LDS histogram (2 buckets per thread):
 // elements above the bucket of the need-th key in, below it out, until the
 // count fits or the live keys are all equal (then the earliest, i.e. lowest
 // page ids, win).
 
-constexpr int kMergeThreads = 512;               // 8 waves: the fast path keeps its registers
+constexpr int kMergeThreads = 1024;              // 16 waves; the fast path fits 128 VGPRs
 constexpr int kMW = kMergeThreads / 64;
 constexpr int kRoundNew = 512;                   // candidates gathered per load batch
 constexpr int kRoundCap = kSelectMaxK + kRoundNew;
@@ -489,7 +489,7 @@ __device__ void merge_topk(MergeLds& W, int n, int need) {
     for (int e = tid; e < n; e += kMergeThreads)
       if (W.state[e] == 0) atomicAdd(&W.hist[hbucket((uint32_t)(W.x[e] >> 32), lo, scale)], 1u);
     __syncthreads();
-    // thread t owns buckets [4t, 4t+4): counts above them, then the bucket
+    // thread t owns buckets [2t, 2t+2): counts above them, then the bucket
     // holding the need-th key from the top
     uint32_t hb[kMergeBpt], mine = 0;
 #pragma unroll
@@ -548,13 +548,12 @@ __device__ void merge_topk(MergeLds& W, int n, int need) {
 __device__ int merge_lists(MergeLds& W, const unsigned long long* src, const int32_t* src_blk,
                            const int32_t* counts, int n_chunks, int chunk, int k) {
   const int tid = threadIdx.x;
-  // chunk offsets (at most 1024 chunks: two per thread)
-  const uint32_t c0 = (2 * tid < n_chunks) ? (uint32_t)counts[2 * tid] : 0u;
-  const uint32_t c1 = (2 * tid + 1 < n_chunks) ? (uint32_t)counts[2 * tid + 1] : 0u;
+  // chunk offsets (at most 1024 chunks: one per thread)
+  static_assert(kMergeThreads >= 1024, "one chunk count per thread");
+  const uint32_t c0 = (tid < n_chunks) ? (uint32_t)counts[tid] : 0u;
   uint32_t total_u;
-  const uint32_t o = merge_excl_scan(c0 + c1, W.scn, &total_u);
-  if (2 * tid < n_chunks) W.off[2 * tid] = (int)o;
-  if (2 * tid + 1 < n_chunks) W.off[2 * tid + 1] = (int)(o + c0);
+  const uint32_t o = merge_excl_scan(c0, W.scn, &total_u);
+  if (tid < n_chunks) W.off[tid] = (int)o;
   if (tid == 0) W.off[n_chunks] = (int)total_u;
   __syncthreads();
   const int total = (int)total_u;
