@@ -401,12 +401,12 @@ __global__ __launch_bounds__(kThreads) void select_chunk_kernel(SelectArgs a) {
 // whole workgroup ranks the chunk lists, in page order, in rounds: new
 // candidates are appended to the running top-k in LDS until the list's
 // kRoundCap entries are full, then ranked by bucket refinement over the live
-// key range with a 2048-bucket LDS histogram (2 buckets per thread):
+// key range with a 2048-bucket LDS histogram (4 buckets per thread):
 // elements above the bucket of the need-th key in, below it out, until the
 // count fits or the live keys are all equal (then the earliest, i.e. lowest
 // page ids, win).
 
-constexpr int kMergeThreads = 1024;              // 16 waves; the fast path fits 128 VGPRs
+constexpr int kMergeThreads = 512;               // 8 waves: up to 256 VGPRs, no spills
 constexpr int kMW = kMergeThreads / 64;
 constexpr int kRoundNew = 512;                   // candidates gathered per load batch
 constexpr int kRoundCap = kSelectMaxK + kRoundNew;
@@ -489,7 +489,7 @@ __device__ void merge_topk(MergeLds& W, int n, int need) {
     for (int e = tid; e < n; e += kMergeThreads)
       if (W.state[e] == 0) atomicAdd(&W.hist[hbucket((uint32_t)(W.x[e] >> 32), lo, scale)], 1u);
     __syncthreads();
-    // thread t owns buckets [2t, 2t+2): counts above them, then the bucket
+    // thread t owns buckets [4t, 4t+4): counts above them, then the bucket
     // holding the need-th key from the top
     uint32_t hb[kMergeBpt], mine = 0;
 #pragma unroll
@@ -542,21 +542,29 @@ __device__ void merge_topk(MergeLds& W, int n, int need) {
   }
 }
 
+// W.off[c] = first list entry of chunk c, W.off[n_chunks] = the total (at
+// most 1024 chunks: two per thread). Ends with a barrier.
+__device__ __forceinline__ void merge_chunk_offsets(MergeLds& W, const int32_t* counts, int n_chunks) {
+  static_assert(2 * kMergeThreads >= 1024, "two chunk counts per thread");
+  const int tid = threadIdx.x;
+  const uint32_t c0 = (2 * tid < n_chunks) ? (uint32_t)counts[2 * tid] : 0u;
+  const uint32_t c1 = (2 * tid + 1 < n_chunks) ? (uint32_t)counts[2 * tid + 1] : 0u;
+  uint32_t total;
+  const uint32_t o = merge_excl_scan(c0 + c1, W.scn, &total);
+  if (2 * tid < n_chunks) W.off[2 * tid] = (int)o;
+  if (2 * tid + 1 < n_chunks) W.off[2 * tid + 1] = (int)(o + c0);
+  if (tid == 0) W.off[n_chunks] = (int)total;
+  __syncthreads();
+}
+
 // The exact top-k of one (sequence, KV head)'s candidate lists, run by the
 // whole workgroup; leaves the kept sort keys and blocks, in page order, in
 // W.x / W.blk and returns their count.
 __device__ int merge_lists(MergeLds& W, const unsigned long long* src, const int32_t* src_blk,
                            const int32_t* counts, int n_chunks, int chunk, int k) {
   const int tid = threadIdx.x;
-  // chunk offsets (at most 1024 chunks: one per thread)
-  static_assert(kMergeThreads >= 1024, "one chunk count per thread");
-  const uint32_t c0 = (tid < n_chunks) ? (uint32_t)counts[tid] : 0u;
-  uint32_t total_u;
-  const uint32_t o = merge_excl_scan(c0, W.scn, &total_u);
-  if (tid < n_chunks) W.off[tid] = (int)o;
-  if (tid == 0) W.off[n_chunks] = (int)total_u;
-  __syncthreads();
-  const int total = (int)total_u;
+  merge_chunk_offsets(W, counts, n_chunks);
+  const int total = W.off[n_chunks];
   int nkept = 0, consumed = 0;
   do {
     // a round fills the LDS list: after the first, k kept plus what fits
@@ -625,6 +633,183 @@ __device__ int merge_lists(MergeLds& W, const unsigned long long* src, const int
   return nkept;
 }
 
+// Candidate sets larger than one LDS list: the k-th largest sort key is
+// found by a radix select over every candidate where it lies (the lists stay
+// in L2): after the high bits all candidates share, digits of up to 11 bits
+// of the key's 32 order bits, one histogram pass each; then one pass in page
+// order writes the selected ids.
+// A candidate whose fixed high bits (prefix) exceed the chosen ones is
+// "above" (kept), equal is "live", lower is out; live candidates left when
+// all 32 bits are fixed have equal keys, and the earliest (lowest page ids)
+// take the remaining places.
+constexpr int kGlobalEpt = 16;     // consecutive candidates per thread per batch
+
+// 2: above, 1: live, 0: out, for `plen` fixed high bits equal to `prefix`
+__device__ __forceinline__ int global_class(uint32_t u, int plen, uint32_t prefix) {
+  if (plen == 0) return 1;
+  const uint32_t h = u >> (32 - plen);
+  return h > prefix ? 2 : (h == prefix ? 1 : 0);
+}
+
+// Calls f(u) for the order bits of every candidate of this thread's
+// contiguous slice of the lists, 8 loads in flight at a time.
+template <class F>
+__device__ __forceinline__ void global_for_each(const MergeLds& W, const unsigned long long* src,
+                                                int n_chunks, int chunk, int total, F&& f) {
+  const int per = (total + kMergeThreads - 1) / kMergeThreads;
+  const int e_begin = min(total, (int)threadIdx.x * per), e_end = min(total, e_begin + per);
+  int c = 0;
+  if (e_begin < e_end)
+    for (int lo = 0, hi = n_chunks - 1; lo <= hi;) {
+      const int mid = (lo + hi) >> 1;
+      if (W.off[mid] <= e_begin) { c = mid; lo = mid + 1; } else hi = mid - 1;
+    }
+  for (int e = e_begin; e < e_end; e += 8) {
+    int idx[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      idx[i] = 0;
+      if (e + i < e_end) {
+        while (W.off[c + 1] <= e + i) ++c;
+        idx[i] = c * chunk + (e + i - W.off[c]);
+      }
+    }
+    uint32_t u[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) u[i] = (uint32_t)(src[idx[i]] >> 32);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (e + i < e_end) f(u[i]);
+  }
+}
+
+__device__ void merge_global(MergeLds& W, const unsigned long long* src, const int32_t* src_blk,
+                             const int32_t* counts, int n_chunks, int chunk, int k, int32_t* out,
+                             int32_t* outb) {
+  const int tid = threadIdx.x;
+  merge_chunk_offsets(W, counts, n_chunks);
+  const int total = W.off[n_chunks];
+
+  // the high bits every candidate shares are fixed at once (their keys lie
+  // in a narrow range: a first digit over them would put nearly all into one
+  // bucket, one LDS address)
+  uint32_t mn = 0xffffffffu, mx = 0u;
+  global_for_each(W, src, n_chunks, chunk, total, [&](uint32_t u) {
+    mn = min(mn, u);
+    mx = max(mx, u);
+  });
+  mn = wave_min_u32(mn);
+  mx = wave_max_u32(mx);
+  if ((tid & 63) == 0) { W.red3[1][tid >> 6] = mn; W.red3[2][tid >> 6] = mx; }
+  __syncthreads();
+  mn = 0xffffffffu;
+  mx = 0u;
+#pragma unroll
+  for (int w = 0; w < kMW; ++w) {
+    mn = min(mn, W.red3[1][w]);
+    mx = max(mx, W.red3[2][w]);
+  }
+  __syncthreads();  // W.red3 free again
+  int plen = (mn == mx) ? 32 : __builtin_clz(mn ^ mx);
+  uint32_t prefix = (plen == 0) ? 0u : (plen == 32 ? mn : mn >> (32 - plen));
+  int need = k;
+  bool all_live = false;  // the live set is exactly the `need` still to take
+  for (int level = 0; level < 3 && plen < 32; ++level) {
+    const int width = min(11, 32 - plen), shift = 32 - plen - width;
+#pragma unroll
+    for (int q = 0; q < kMergeBpt; ++q) W.hist[kMergeBpt * tid + q] = 0u;
+    __syncthreads();
+    global_for_each(W, src, n_chunks, chunk, total, [&](uint32_t u) {
+      if (global_class(u, plen, prefix) == 1) atomicAdd(&W.hist[(u >> shift) & ((1u << width) - 1u)], 1u);
+    });
+    __syncthreads();
+    // the digit holding the need-th live key, from the top
+    uint32_t hb[kMergeBpt], mine = 0;
+#pragma unroll
+    for (int q = 0; q < kMergeBpt; ++q) {
+      hb[q] = W.hist[kMergeBpt * tid + q];
+      mine += hb[q];
+    }
+    uint32_t tot;
+    const uint32_t pre = merge_excl_scan(mine, W.scn, &tot);
+    uint32_t acc = tot - pre - mine;
+#pragma unroll
+    for (int q = kMergeBpt - 1; q >= 0; --q) {
+      if (acc < (uint32_t)need && (uint32_t)need <= acc + hb[q]) {
+        W.bstar = kMergeBpt * tid + q;
+        W.babove = acc;
+        W.red3[0][0] = hb[q];
+      }
+      acc += hb[q];
+    }
+    __syncthreads();
+    prefix = (prefix << width) | (uint32_t)W.bstar;
+    plen += width;
+    need -= (int)W.babove;
+    const uint32_t in_digit = W.red3[0][0];
+    __syncthreads();  // hist, bstar, red3 free again
+    if ((int)in_digit == need) { all_live = true; break; }
+  }
+
+  // ---- output pass in page order: above, then live ones while `need` lasts
+  int nsel = 0, nlive = 0;
+  for (int base = 0; base < total; base += kMergeThreads * kGlobalEpt) {
+    const int e0 = base + tid * kGlobalEpt;
+    int c = 0;
+    if (e0 < total)
+      for (int lo = 0, hi = n_chunks - 1; lo <= hi;) {
+        const int mid = (lo + hi) >> 1;
+        if (W.off[mid] <= e0) { c = mid; lo = mid + 1; } else hi = mid - 1;
+      }
+    unsigned long long xv[kGlobalEpt];
+    int bv[kGlobalEpt], cls[kGlobalEpt];
+    uint32_t nl = 0;
+#pragma unroll
+    for (int i = 0; i < kGlobalEpt; ++i) {
+      const int e = e0 + i;
+      int sidx = 0;
+      if (e < total) {
+        while (W.off[c + 1] <= e) ++c;
+        sidx = c * chunk + (e - W.off[c]);
+      }
+      xv[i] = src[sidx];
+      bv[i] = src_blk[sidx];
+      cls[i] = (e < total) ? global_class((uint32_t)(xv[i] >> 32), plen, prefix) : 0;
+      nl += cls[i] == 1 ? 1u : 0u;
+    }
+    uint32_t live_tot;
+    uint32_t lrank = (uint32_t)nlive + merge_excl_scan(nl, W.scn, &live_tot);
+    uint32_t ns = 0;
+#pragma unroll
+    for (int i = 0; i < kGlobalEpt; ++i) {
+      if (cls[i] == 1) {
+        if (!all_live && lrank >= (uint32_t)need) cls[i] = 0;
+        ++lrank;
+      }
+      ns += cls[i] != 0 ? 1u : 0u;
+    }
+    __syncthreads();  // W.scn read by every thread before it is reused
+    uint32_t sel_tot;
+    uint32_t pos = (uint32_t)nsel + merge_excl_scan(ns, W.scn, &sel_tot);
+#pragma unroll
+    for (int i = 0; i < kGlobalEpt; ++i)
+      if (cls[i] != 0) {
+        if (pos < (uint32_t)k) {
+          out[pos] = (int32_t)(0xffffffffu - (uint32_t)(xv[i] & 0xffffffffu));
+          outb[pos] = bv[i];
+        }
+        ++pos;
+      }
+    nlive += (int)live_tot;
+    nsel += (int)sel_tot;
+    __syncthreads();
+  }
+  for (int i = nsel + tid; i < k; i += kMergeThreads) {
+    out[i] = -1;
+    outb[i] = -1;
+  }
+}
+
 constexpr int kFastPerLane = 16;
 constexpr int kFastCap = 64 * kFastPerLane;  // candidates ranked in registers
 
@@ -683,6 +868,10 @@ __global__ __launch_bounds__(kMergeThreads) void select_merge_kernel(SelectArgs 
   }
   total = (int)wave_sum_u32((uint32_t)total);
   if (__ballot(over) != 0) {  // the same in every wave
+    if (total > kRoundCap) {
+      merge_global(W, src, src_blk, counts, nc, a.chunk, a.k, out, outb);
+      return;
+    }
     const int nk = merge_lists(W, src, src_blk, counts, nc, a.chunk, a.k);
     for (int i = tid; i < a.k; i += kMergeThreads) {
       out[i] = (i < nk) ? (int32_t)(0xffffffffu - (uint32_t)(W.x[i] & 0xffffffffu)) : -1;

@@ -315,14 +315,15 @@ def test_graph_replay_matches_eager(locks):
 
 # ----------------------------------------------------------------- full size
 
-@pytest.mark.parametrize("config,budget", [(4, 2048), (4, 512), (5, 512), (5, 2048), (4, 16384)])
+@pytest.mark.parametrize("config,budget",
+                         [(4, 2048), (4, 512), (5, 512), (5, 2048), (4, 16384), (4, 65536), (5, 65536)])
 def test_full_size_decode_parity(locks, config, budget):
     """The full 1M-token workloads in the launch configuration the benchmark
     times: every score and selection compared, output against the oracle on
     the GPU's selected pages (only those K/V blocks are copied to the host).
-    The 16-head layer at budget 2048 (~4,000 candidates per KV head) and the
-    8-KV-head layer at budget 16384 (k = 1024) take the merge's multi-wave
-    LDS rounds."""
+    The 16-head layer at budget 2048 (~4,000 candidates per KV head) takes
+    the merge's workgroup-wide LDS ranking; budgets 16384 and 65536 (k = 1024
+    and the maximum 4096) take its refinement over every candidate."""
     say(f"full-size decode parity config {config} budget {budget}")
     w = workloads.make(config, device=DEV, budget=budget)
     summ = locks.build_summaries(w.k_cache, w.page_table, w.seq_lens)
