@@ -683,7 +683,9 @@ __device__ __forceinline__ void global_for_each(const MergeLds& W, const unsigne
   }
 }
 
-__device__ void merge_global(MergeLds& W, const unsigned long long* src, const int32_t* src_blk,
+// Not inlined: the register path of the merge kernel keeps its own allocation
+// (inlined, it made the usual workloads 0.5-1 us slower per step).
+__device__ __attribute__((noinline)) void merge_global(MergeLds& W, const unsigned long long* src, const int32_t* src_blk,
                              const int32_t* counts, int n_chunks, int chunk, int k, int32_t* out,
                              int32_t* outb) {
   const int tid = threadIdx.x;
