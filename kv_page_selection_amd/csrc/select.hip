@@ -27,13 +27,12 @@
 //        comparison applies "larger key, then lower id"); those with key >= T
 //        are written, with their physical blocks, in page order (typically a
 //        few hundred per (sequence, KV head) in all).
-//  2. merge: one wave per (sequence, KV head) ranks the chunk lists in page
-//     order, in rounds of up to 512 new candidates appended to the running
-//     top-k; kept candidates always precede the new ones in page order, so the
-//     result comes out sorted without a sort. It also writes the physical
-//     blocks of the kept pages for the attention pass. One wave needs no
-//     barriers; workgroup-wide ranking at this size is bound by barrier and
-//     LDS round trips, not work.
+//  2. merge: one workgroup per (sequence, KV head) ranks the chunk lists in
+//     page order and writes the kept ids, sorted without a sort because the
+//     lists are in page order, with their physical blocks for the attention
+//     pass. Up to 1024 candidates (the usual case) one wave ranks them in
+//     registers with no barrier; up to 4,608 the workgroup ranks an LDS copy;
+//     beyond that a radix select runs over the lists where they lie.
 // Ranking = exact selection by bucket refinement on the key bits: a 2048-bucket
 // histogram over the live [lo, hi] key range picks the bucket holding the
 // k-th key; everything above it is in, below it out; repeat inside that
