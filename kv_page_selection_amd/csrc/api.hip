@@ -60,7 +60,13 @@ bool ws_layout(const locks_dims& d, int k, WsLayout* L, const char** why) {
   L->sel_chunk = (int)M;
   L->n_sel_chunks = (int)((N + M - 1) / M);
   // list entries: k selected pages, then the tail (tokens of the partly filled page)
-  L->n_att_split = (k + 1 + kSparsePagesPerSplit - 1) / kSparsePagesPerSplit;
+  // sparse list: 4-page splits (one page per wave) while a (sequence, KV
+  // head) has at most 128 of them; longer lists (large budgets) double the
+  // split, up to 64 pages, so the partials the merge folds stay few
+  long long app = kSparsePagesPerSplit;
+  while (app < 64 && (k + 1 + app - 1) / app > 128) app *= 2;
+  L->att_pages_per_split = (int)app;
+  L->n_att_split = (int)((k + 1 + app - 1) / app);
   if (L->n_att_split > kMaxSplits) {
     *why = "budget/16 above the sparse-attention split capacity";
     return false;

@@ -445,7 +445,7 @@ hipError_t launch_g(const locks_dims& d, const WsLayout& L, const DevPtrs& P, co
   a.N = d.max_pages_per_seq;
   a.num_blocks = d.num_blocks;
   a.k = L.k;
-  a.pages_per_split = dense ? L.dense_pages_per_split : kSparsePagesPerSplit;
+  a.pages_per_split = dense ? L.dense_pages_per_split : L.att_pages_per_split;
   a.n_split = dense ? L.n_dense_split : L.n_att_split;
   // MFMA where a query group fills enough of the 16 rows: G >= 8 always, and
   // G = 4 for the long dense splits; a sparse split at G = 4 (one page per

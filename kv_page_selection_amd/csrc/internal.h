@@ -14,7 +14,7 @@ constexpr int kScorePagesPerWave = 64;  // 4 tiles x 16 pages per wave and KV he
 constexpr int kSelectMaxK = 4096;       // budget/16 limit (the merge keeps up to k between rounds)
 constexpr int kSelectChunk = 4096;      // pages per select workgroup at most (4 per thread)
 constexpr int kBoundSlots = 16384;      // (head, super-range) maxima the bound pass holds in LDS
-constexpr int kSparsePagesPerSplit = 4; // one page per wave
+constexpr int kSparsePagesPerSplit = 4; // one page per wave (longer for large budgets)
 constexpr int kDensePagesPerSplit = 256; // usual dense split; smaller for small grids, larger past kMaxSplits
 constexpr int kDenseMinWgs = 1024;       // dense splits shrink while the grid has fewer workgroups
 constexpr int kMaxSplits = 2048;        // split partials one merge workgroup combines
@@ -40,7 +40,7 @@ struct WsLayout {
   // pages), else 64-page ranges; units per super-range for each kind
   int sup_r = 1, sup_t = 1;
   int sel_chunk = 0, n_sel_chunks = 0;
-  int n_att_split = 0, n_dense_split = 0, dense_pages_per_split = 0;
+  int n_att_split = 0, n_dense_split = 0, dense_pages_per_split = 0, att_pages_per_split = 0;
 };
 
 // Returns false (and sets *why) when the dims/budget exceed the kernels' limits.
