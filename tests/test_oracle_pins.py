@@ -586,3 +586,96 @@ def test_theorem1_mass_retention_bound(orc, rank):
     mass = lambda idx: np.exp(exact[idx]).sum()
     assert mass(chosen) >= math.exp(-2 * eta) * mass(best) * (1 - 1e-12)
     assert mass(chosen) >= math.exp(-4 * eta) * mass(best)
+
+
+# ------------------------------------------ variant drivers over a paged cache
+
+def bf16_f64(bits):
+    """bf16 bit patterns -> float64 via torch (exact)."""
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16)
+    return t.double().numpy()
+
+
+def variant_cache(r):
+    """A tiny paged cache: 2 sequences, 2 KV heads (G = 2), a permuted page
+    table with one absent page (block id -1) and one block id past the cache,
+    a ragged tail in the second sequence, and unreferenced blocks."""
+    B, Hq, Hkv, N = 2, 4, 2, 7
+    nb = B * N + 3
+    keys = np.stack([np.stack([planted_page(r, 8, noise=0.05) for _ in range(Hkv)])
+                     for _ in range(nb)])
+    kb, _ = bf16_round(keys)
+    pt = r.permutation(nb)[: B * N].reshape(B, N).astype(np.int32)
+    pt[0, 2] = -1          # absent page inside n_b
+    pt[1, 4] = nb + 5      # block id outside [0, num_blocks): absent as well
+    lens = np.array([N * PAGE, 5 * PAGE + 9], dtype=np.int32)  # 7 and 5 full pages
+    q = r.standard_normal((B, Hq, DIM)).astype(np.float32)
+    return kb, pt, lens, q, Hkv
+
+
+@pytest.mark.parametrize("r", [4, 8, 16])
+@pytest.mark.parametrize("vb", [2, 4, 16])
+def test_variant_build_driver_places_records_through_the_page_table(orc, r, vb):
+    """(A "Caveats": the int4 / int2 / unquantised summaries compared; B
+    mechanism 1: one record per page, built from that page's keys.) Every full
+    present page (b, j) gets, at [page_table[b][j], kvh], the record of its own
+    key tile, decoded here by the independent numpy decoder; absent pages, the
+    tail page and unreferenced blocks leave the output untouched."""
+    rr = rng(400 + 10 * r + vb)
+    kb, pt, lens, _, Hkv = variant_cache(rr)
+    nb = kb.shape[0]
+    nbytes = orc.variant_record_bytes(r, vb)
+    fill = np.full((nb, Hkv, nbytes), 0xA5, dtype=np.uint8)
+    got = orc.build_summaries_variant(kb, pt, lens, r, vb, summaries=fill.copy())
+    written = set()
+    for b in range(pt.shape[0]):
+        for j in range(int(lens[b]) // PAGE):
+            blk = int(pt[b, j])
+            if 0 <= blk < nb:
+                written.add(blk)
+    for blk in range(nb):
+        for h in range(Hkv):
+            if blk not in written:
+                assert np.all(got[blk, h] == 0xA5), (blk, h)
+                continue
+            mu, V, C, _, _ = decode_variant_numpy(got[blk, h], r, vb)
+            ref = decode_variant_numpy(orc.build_record_variant(kb[blk, h], r, vb), r, vb)
+            assert np.array_equal(mu, ref[0]) and np.array_equal(V, ref[1]) and np.array_equal(C, ref[2])
+            if vb == 16:
+                # fp16 storage: the record holds this tile's rank-r summary, so
+                # its residual is the tile's SVD tail energy (Eckart-Young),
+                # up to fp16 rounding
+                keys = bf16_f64(kb[blk, h])
+                dev = keys - keys.mean(0)
+                sv = np.linalg.svd(dev, compute_uv=False)
+                tail = math.sqrt(float((sv[r:] ** 2).sum()))
+                res = np.linalg.norm(mu[None, :] + C @ V.T - keys)
+                assert abs(res - tail) <= 1e-3 * np.linalg.norm(keys), (blk, h, res, tail)
+
+
+@pytest.mark.parametrize("r", [4, 8, 16])
+@pytest.mark.parametrize("vb", [2, 4, 16])
+def test_variant_score_driver_is_the_lse_of_reconstructed_keys(orc, r, vb):
+    """(A "How LOCKS works": a page's score is the log-sum-exp of its
+    reconstructed in-page logits; B mechanism 2.) Every score the variant
+    driver writes equals scipy's log-sum-exp over the 16 keys mu + V c_i that
+    the record at [page_table[b][j], h / G] reconstructs (independent decoder);
+    absent pages, the tail page and pages past n_b score -inf."""
+    rr = rng(500 + 10 * r + vb)
+    kb, pt, lens, q, Hkv = variant_cache(rr)
+    summ = orc.build_summaries_variant(kb, pt, lens, r, vb)
+    sc = orc.scores_variant(q, summ, pt, lens, Hkv, r, vb)
+    B, Hq, N = sc.shape
+    G = Hq // Hkv
+    nb = kb.shape[0]
+    for b in range(B):
+        n = int(lens[b]) // PAGE
+        for h in range(Hq):
+            for j in range(N):
+                blk = int(pt[b, j])
+                if j >= n or not (0 <= blk < nb):
+                    assert sc[b, h, j] == -np.inf, (b, h, j)
+                    continue
+                mu, V, C, _, _ = decode_variant_numpy(summ[blk, h // G], r, vb)
+                want = exact_lse(q[b, h].astype(np.float64), mu[None, :] + C @ V.T)
+                assert abs(sc[b, h, j] - want) <= 1e-9, (b, h, j, sc[b, h, j], want)
