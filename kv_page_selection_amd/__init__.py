@@ -124,33 +124,74 @@ def new_workspace(dims: Dims, budget_tokens: int, device) -> torch.Tensor:
     return torch.zeros(workspace_bytes(dims, budget_tokens), dtype=torch.uint8, device=device)
 
 
-def _check_common(q, k_cache, page_table, seq_lens):
-    if q is not None and (q.dtype != torch.float32 or q.dim() != 3 or q.shape[2] != HEAD_DIM):
-        raise ValueError("q must be float32 [B, Hq, 128]")
-    if k_cache.dtype != torch.bfloat16 or k_cache.dim() != 4 or tuple(k_cache.shape[2:]) != (16, 128):
-        raise ValueError("caches must be bfloat16 [num_blocks, Hkv, 16, 128]")
-    if page_table.dtype != torch.int32 or page_table.dim() != 2:
-        raise ValueError("page_table must be int32 [B, max_pages]")
-    if seq_lens.dtype != torch.int32 or seq_lens.dim() != 1:
-        raise ValueError("seq_lens must be int32 [B]")
-    dev = k_cache.device
-    for t in (q, page_table, seq_lens):
-        if t is not None and t.device != dev:
-            raise ValueError("all LOCKS tensors must be on the same device")
+def _tensor(t, name: str, dtype: torch.dtype, shape) -> None:
+    """Raises ValueError unless t is a contiguous tensor of this dtype and shape
+    (None in `shape` accepts any extent there)."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != len(shape) or any(w is not None and int(g) != w for g, w in zip(t.shape, shape)):
+        want = "[" + ", ".join("*" if w is None else str(w) for w in shape) + "]"
+        raise ValueError(f"{name} must have shape {want}, got {list(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _devices(named: dict) -> torch.device:
+    """Every tensor on one cuda device (the C ABI takes device pointers only)."""
+    devs = {n: t.device for n, t in named.items() if t is not None}
+    dev = next(iter(devs.values()))
+    for n, d in devs.items():
+        if d != dev:
+            raise ValueError(f"all LOCKS tensors must be on one device: {n} is on {d}, not {dev}")
     if dev.type != "cuda":
         raise ValueError("LOCKS runs on the GPU only; tensors must be on a cuda device")
+    return dev
+
+
+def _check_common(q, k_cache, page_table, seq_lens):
+    """Shapes shared by every call: k_cache bf16 [num_blocks, Hkv, 16, 128],
+    page_table int32 [B, max_pages], seq_lens int32 [B] and (when given) q f32
+    [B, Hq, 128] with Hq a multiple of Hkv. Returns (B, Hq, Hkv, max_pages,
+    num_blocks); Hq is None without q."""
+    _tensor(k_cache, "k_cache", torch.bfloat16, (None, None, PAGE_SIZE, HEAD_DIM))
+    _tensor(page_table, "page_table", torch.int32, (None, None))
+    B, N = int(page_table.shape[0]), int(page_table.shape[1])
+    nb, hkv = int(k_cache.shape[0]), int(k_cache.shape[1])
+    _tensor(seq_lens, "seq_lens", torch.int32, (B,))
+    hq = None
+    if q is not None:
+        _tensor(q, "q", torch.float32, (B, None, HEAD_DIM))
+        hq = int(q.shape[1])
+        if hkv == 0 or hq % hkv != 0:
+            raise ValueError(f"q's {hq} heads must be a multiple of the caches' {hkv} KV heads")
+    return B, hq, hkv, N, nb
+
+
+def _pages(budget_tokens: int) -> int:
+    if int(budget_tokens) < PAGE_SIZE or int(budget_tokens) % PAGE_SIZE != 0:
+        raise ValueError("budget_tokens must be a positive multiple of 16")
+    return int(budget_tokens) // PAGE_SIZE
+
+
+def _workspace(workspace) -> None:
+    _tensor(workspace, "workspace", torch.uint8, (None,))
 
 
 def build_summaries(k_cache: torch.Tensor, page_table: torch.Tensor, seq_lens: torch.Tensor,
                     summaries: torch.Tensor | None = None, n_q_heads: int = 1) -> torch.Tensor:
     """Summary records [num_blocks, Hkv, 784] (uint8) of every full page."""
-    _check_common(None, k_cache, page_table, seq_lens)
-    dims = make_dims(page_table.shape[0], k_cache, page_table, n_q_heads=k_cache.shape[1])
+    B, _, hkv, N, nb = _check_common(None, k_cache, page_table, seq_lens)
+    if summaries is not None:
+        _tensor(summaries, "summaries", torch.uint8, (nb, hkv, summary_record_bytes()))
+    dev = _devices(dict(k_cache=k_cache, page_table=page_table, seq_lens=seq_lens,
+                        summaries=summaries))
+    dims = Dims(B, hkv, hkv, HEAD_DIM, PAGE_SIZE, RANK, N, nb)
     if summaries is None:
-        summaries = torch.zeros(k_cache.shape[0], k_cache.shape[1], summary_record_bytes(),
-                                dtype=torch.uint8, device=k_cache.device)
+        summaries = torch.zeros(nb, hkv, summary_record_bytes(), dtype=torch.uint8, device=dev)
     _check(lib().locks_build_summaries(ctypes.byref(dims), _ptr(k_cache), _ptr(page_table),
-                                       _ptr(seq_lens), _ptr(summaries), _stream(k_cache.device)))
+                                       _ptr(seq_lens), _ptr(summaries), _stream(dev)))
     return summaries
 
 
@@ -158,31 +199,40 @@ def build_blocks(k_cache: torch.Tensor, blocks: torch.Tensor, summaries: torch.T
     """Rebuilds, in place, the records of the listed physical blocks (every KV
     head): the pages that just filled. blocks: int32 [n] on the device;
     entries outside [0, num_blocks) are skipped."""
-    _check_common(None, k_cache, torch.zeros(1, 1, dtype=torch.int32, device=k_cache.device),
-                  torch.zeros(1, dtype=torch.int32, device=k_cache.device))
-    if blocks.dtype != torch.int32 or blocks.dim() != 1 or blocks.device != k_cache.device:
-        raise ValueError("blocks must be int32 [n] on the caches' device")
-    if summaries.dtype != torch.uint8 or tuple(summaries.shape) != (
-            k_cache.shape[0], k_cache.shape[1], summary_record_bytes()):
-        raise ValueError("summaries must be uint8 [num_blocks, Hkv, 784]")
-    blocks = blocks.contiguous()
-    dims = Dims(1, k_cache.shape[1], k_cache.shape[1], HEAD_DIM, 16, 8, 1, k_cache.shape[0])
+    _tensor(k_cache, "k_cache", torch.bfloat16, (None, None, PAGE_SIZE, HEAD_DIM))
+    nb, hkv = int(k_cache.shape[0]), int(k_cache.shape[1])
+    _tensor(blocks, "blocks", torch.int32, (None,))
+    _tensor(summaries, "summaries", torch.uint8, (nb, hkv, summary_record_bytes()))
+    dev = _devices(dict(k_cache=k_cache, blocks=blocks, summaries=summaries))
+    dims = Dims(1, hkv, hkv, HEAD_DIM, PAGE_SIZE, RANK, 1, nb)
     _check(lib().locks_build_blocks(ctypes.byref(dims), _ptr(k_cache), _ptr(blocks),
-                                    blocks.numel(), _ptr(summaries), _stream(k_cache.device)))
+                                    blocks.numel(), _ptr(summaries), _stream(dev)))
     return summaries
 
 
 def decode_step(q, summaries, k_cache, v_cache, page_table, seq_lens, budget_tokens: int,
                 out=None, selected=None, page_scores=None, workspace=None):
     """One LOCKS decode step. Returns (out [B,Hq,128] f32, selected [B,Hkv,k] i32)."""
-    _check_common(q, k_cache, page_table, seq_lens)
+    B, hq, hkv, N, nb = _check_common(q, k_cache, page_table, seq_lens)
+    k = _pages(budget_tokens)
+    _tensor(summaries, "summaries", torch.uint8, (nb, hkv, summary_record_bytes()))
+    _tensor(v_cache, "v_cache", torch.bfloat16, tuple(k_cache.shape))
+    if out is not None:
+        _tensor(out, "out", torch.float32, (B, hq, HEAD_DIM))
+    if selected is not None:
+        _tensor(selected, "selected", torch.int32, (B, hkv, k))
+    if page_scores is not None:
+        _tensor(page_scores, "page_scores", torch.float32, (B, hq, N))
+    if workspace is not None:
+        _workspace(workspace)
+    dev = _devices(dict(q=q, summaries=summaries, k_cache=k_cache, v_cache=v_cache,
+                        page_table=page_table, seq_lens=seq_lens, out=out, selected=selected,
+                        page_scores=page_scores, workspace=workspace))
     dims = make_dims(q, k_cache, page_table)
-    dev = q.device
-    k = budget_tokens // PAGE_SIZE
     if out is None:
         out = torch.empty_like(q)
     if selected is None:
-        selected = torch.empty(dims.batch, dims.n_kv_heads, k, dtype=torch.int32, device=dev)
+        selected = torch.empty(B, hkv, k, dtype=torch.int32, device=dev)
     if workspace is None:
         workspace = new_workspace(dims, budget_tokens, dev)
     _check(lib().locks_decode_step(
@@ -195,23 +245,36 @@ def decode_step(q, summaries, k_cache, v_cache, page_table, seq_lens, budget_tok
 def score_pages(q, summaries, k_cache, page_table, seq_lens, budget_tokens: int, workspace,
                 page_scores=None):
     """Phase 1 (k_cache only supplies the dims)."""
-    _check_common(q, k_cache, page_table, seq_lens)
+    B, hq, hkv, N, nb = _check_common(q, k_cache, page_table, seq_lens)
+    _pages(budget_tokens)
+    _tensor(summaries, "summaries", torch.uint8, (nb, hkv, summary_record_bytes()))
+    _workspace(workspace)
+    if page_scores is not None:
+        _tensor(page_scores, "page_scores", torch.float32, (B, hq, N))
+    dev = _devices(dict(q=q, summaries=summaries, k_cache=k_cache, page_table=page_table,
+                        seq_lens=seq_lens, workspace=workspace, page_scores=page_scores))
     dims = make_dims(q, k_cache, page_table)
     _check(lib().locks_score_pages(ctypes.byref(dims), _ptr(q), _ptr(summaries), _ptr(page_table),
                                    _ptr(seq_lens), int(budget_tokens), _ptr(page_scores),
-                                   _ptr(workspace), workspace.numel(), _stream(q.device)))
+                                   _ptr(workspace), workspace.numel(), _stream(dev)))
 
 
 def exact_score_pages(q, k_cache, page_table, seq_lens, budget_tokens: int, workspace,
                       page_scores=None):
     """Reference phase 1: exact page masses from the keys (then select_pages
     selects by exact mass)."""
-    _check_common(q, k_cache, page_table, seq_lens)
+    B, hq, hkv, N, nb = _check_common(q, k_cache, page_table, seq_lens)
+    _pages(budget_tokens)
+    _workspace(workspace)
+    if page_scores is not None:
+        _tensor(page_scores, "page_scores", torch.float32, (B, hq, N))
+    dev = _devices(dict(q=q, k_cache=k_cache, page_table=page_table, seq_lens=seq_lens,
+                        workspace=workspace, page_scores=page_scores))
     dims = make_dims(q, k_cache, page_table)
     _check(lib().locks_exact_score_pages(ctypes.byref(dims), _ptr(q), _ptr(k_cache),
                                          _ptr(page_table), _ptr(seq_lens), int(budget_tokens),
                                          _ptr(page_scores), _ptr(workspace), workspace.numel(),
-                                         _stream(q.device)))
+                                         _stream(dev)))
 
 
 def variant_record_bytes(rank: int, v_bits: int) -> int:
@@ -224,59 +287,90 @@ def variant_record_bytes(rank: int, v_bits: int) -> int:
 def build_summaries_variant(k_cache, page_table, seq_lens, rank: int, v_bits: int,
                             summaries=None):
     """Variant records [num_blocks, Hkv, variant_record_bytes] of every full page."""
-    _check_common(None, k_cache, page_table, seq_lens)
-    dims = make_dims(page_table.shape[0], k_cache, page_table, n_q_heads=k_cache.shape[1])
+    B, _, hkv, N, nb = _check_common(None, k_cache, page_table, seq_lens)
+    nbytes = variant_record_bytes(rank, v_bits)
+    if summaries is not None:
+        _tensor(summaries, "summaries", torch.uint8, (nb, hkv, nbytes))
+    dev = _devices(dict(k_cache=k_cache, page_table=page_table, seq_lens=seq_lens,
+                        summaries=summaries))
+    dims = Dims(B, hkv, hkv, HEAD_DIM, PAGE_SIZE, RANK, N, nb)
     if summaries is None:
-        summaries = torch.zeros(k_cache.shape[0], k_cache.shape[1],
-                                variant_record_bytes(rank, v_bits), dtype=torch.uint8,
-                                device=k_cache.device)
+        summaries = torch.zeros(nb, hkv, nbytes, dtype=torch.uint8, device=dev)
     _check(lib().locks_build_summaries_variant(ctypes.byref(dims), _ptr(k_cache), _ptr(page_table),
                                                _ptr(seq_lens), rank, v_bits, _ptr(summaries),
-                                               _stream(k_cache.device)))
+                                               _stream(dev)))
     return summaries
 
 
 def score_pages_variant(q, summaries, k_cache, page_table, seq_lens, budget_tokens: int, rank: int,
                         v_bits: int, workspace, page_scores=None):
     """Phase 1 from variant records (then select_pages / sparse_attention as usual)."""
-    _check_common(q, k_cache, page_table, seq_lens)
+    B, hq, hkv, N, nb = _check_common(q, k_cache, page_table, seq_lens)
+    _pages(budget_tokens)
+    _tensor(summaries, "summaries", torch.uint8, (nb, hkv, variant_record_bytes(rank, v_bits)))
+    _workspace(workspace)
+    if page_scores is not None:
+        _tensor(page_scores, "page_scores", torch.float32, (B, hq, N))
+    dev = _devices(dict(q=q, summaries=summaries, k_cache=k_cache, page_table=page_table,
+                        seq_lens=seq_lens, workspace=workspace, page_scores=page_scores))
     dims = make_dims(q, k_cache, page_table)
     _check(lib().locks_score_pages_variant(ctypes.byref(dims), _ptr(q), _ptr(summaries),
                                            _ptr(page_table), _ptr(seq_lens), int(budget_tokens),
                                            rank, v_bits, _ptr(page_scores), _ptr(workspace),
-                                           workspace.numel(), _stream(q.device)))
+                                           workspace.numel(), _stream(dev)))
 
 
 def select_pages(q, k_cache, page_table, seq_lens, budget_tokens: int, selected, workspace,
                  page_scores=None):
     """Phase 2 (q and k_cache only supply the dims)."""
-    _check_common(q, k_cache, page_table, seq_lens)
+    B, hq, hkv, N, nb = _check_common(q, k_cache, page_table, seq_lens)
+    k = _pages(budget_tokens)
+    _tensor(selected, "selected", torch.int32, (B, hkv, k))
+    _workspace(workspace)
+    if page_scores is not None:
+        _tensor(page_scores, "page_scores", torch.float32, (B, hq, N))
+    dev = _devices(dict(q=q, k_cache=k_cache, page_table=page_table, seq_lens=seq_lens,
+                        selected=selected, workspace=workspace, page_scores=page_scores))
     dims = make_dims(q, k_cache, page_table)
     _check(lib().locks_select_pages(ctypes.byref(dims), _ptr(page_table), _ptr(seq_lens),
                                     int(budget_tokens), _ptr(selected), _ptr(page_scores),
-                                    _ptr(workspace), workspace.numel(), _stream(q.device)))
+                                    _ptr(workspace), workspace.numel(), _stream(dev)))
 
 
 def sparse_attention(q, k_cache, v_cache, page_table, seq_lens, budget_tokens: int, selected,
                      out, workspace):
     """Phase 3: attention over the pages listed in `selected` [B, Hkv, budget/16]."""
-    _check_common(q, k_cache, page_table, seq_lens)
+    B, hq, hkv, N, nb = _check_common(q, k_cache, page_table, seq_lens)
+    k = _pages(budget_tokens)
+    _tensor(v_cache, "v_cache", torch.bfloat16, tuple(k_cache.shape))
+    _tensor(selected, "selected", torch.int32, (B, hkv, k))
+    _tensor(out, "out", torch.float32, (B, hq, HEAD_DIM))
+    _workspace(workspace)
+    dev = _devices(dict(q=q, k_cache=k_cache, v_cache=v_cache, page_table=page_table,
+                        seq_lens=seq_lens, selected=selected, out=out, workspace=workspace))
     dims = make_dims(q, k_cache, page_table)
     _check(lib().locks_sparse_attention(
         ctypes.byref(dims), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
         _ptr(seq_lens), int(budget_tokens), _ptr(selected), _ptr(out), _ptr(workspace),
-        workspace.numel(), _stream(q.device)))
+        workspace.numel(), _stream(dev)))
 
 
 def dense_attention(q, k_cache, v_cache, page_table, seq_lens, out=None, workspace=None):
     """Dense decode attention over every full page (the comparator)."""
-    _check_common(q, k_cache, page_table, seq_lens)
+    B, hq, hkv, N, nb = _check_common(q, k_cache, page_table, seq_lens)
+    _tensor(v_cache, "v_cache", torch.bfloat16, tuple(k_cache.shape))
+    if out is not None:
+        _tensor(out, "out", torch.float32, (B, hq, HEAD_DIM))
+    if workspace is not None:
+        _workspace(workspace)
+    dev = _devices(dict(q=q, k_cache=k_cache, v_cache=v_cache, page_table=page_table,
+                        seq_lens=seq_lens, out=out, workspace=workspace))
     dims = make_dims(q, k_cache, page_table)
     if out is None:
         out = torch.empty_like(q)
     if workspace is None:
-        workspace = new_workspace(dims, PAGE_SIZE, q.device)
+        workspace = new_workspace(dims, PAGE_SIZE, dev)
     _check(lib().locks_dense_attention(
         ctypes.byref(dims), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
-        _ptr(seq_lens), _ptr(out), _ptr(workspace), workspace.numel(), _stream(q.device)))
+        _ptr(seq_lens), _ptr(out), _ptr(workspace), workspace.numel(), _stream(dev)))
     return out

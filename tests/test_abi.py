@@ -124,3 +124,89 @@ def test_binding_refuses_cpu_tensors(L):
     sl = torch.zeros(1, dtype=torch.int32)
     with pytest.raises(ValueError):
         L.dense_attention(q, kc, kc, pt, sl)
+
+
+def _valid_cpu_args(torch, B=2, Hq=8, Hkv=2, N=6, nb=16, budget=32):
+    """Well-formed tensors for every binding call, on the CPU (so each call
+    fails only at its device check, after every shape and dtype check)."""
+    k = budget // 16
+    return dict(
+        q=torch.zeros(B, Hq, 128), kc=torch.zeros(nb, Hkv, 16, 128, dtype=torch.bfloat16),
+        vc=torch.zeros(nb, Hkv, 16, 128, dtype=torch.bfloat16),
+        pt=torch.zeros(B, N, dtype=torch.int32), sl=torch.zeros(B, dtype=torch.int32),
+        summ=torch.zeros(nb, Hkv, 784, dtype=torch.uint8),
+        out=torch.zeros(B, Hq, 128), sel=torch.zeros(B, Hkv, k, dtype=torch.int32),
+        ps=torch.zeros(B, Hq, N), ws=torch.zeros(4096, dtype=torch.uint8), budget=budget)
+
+
+def _calls(L, a):
+    """Every binding entry point over the argument dict a."""
+    return {
+        "decode_step": lambda: L.decode_step(a["q"], a["summ"], a["kc"], a["vc"], a["pt"], a["sl"],
+                                             a["budget"], out=a["out"], selected=a["sel"],
+                                             page_scores=a["ps"], workspace=a["ws"]),
+        "score_pages": lambda: L.score_pages(a["q"], a["summ"], a["kc"], a["pt"], a["sl"],
+                                             a["budget"], a["ws"], page_scores=a["ps"]),
+        "exact_score_pages": lambda: L.exact_score_pages(a["q"], a["kc"], a["pt"], a["sl"],
+                                                         a["budget"], a["ws"], page_scores=a["ps"]),
+        "select_pages": lambda: L.select_pages(a["q"], a["kc"], a["pt"], a["sl"], a["budget"],
+                                               a["sel"], a["ws"], page_scores=a["ps"]),
+        "sparse_attention": lambda: L.sparse_attention(a["q"], a["kc"], a["vc"], a["pt"], a["sl"],
+                                                       a["budget"], a["sel"], a["out"], a["ws"]),
+        "dense_attention": lambda: L.dense_attention(a["q"], a["kc"], a["vc"], a["pt"], a["sl"],
+                                                     out=a["out"], workspace=a["ws"]),
+        "build_summaries": lambda: L.build_summaries(a["kc"], a["pt"], a["sl"], summaries=a["summ"]),
+        "build_blocks": lambda: L.build_blocks(a["kc"], a["sl"], a["summ"]),
+    }
+
+
+def test_binding_validates_shapes_dtypes_and_devices_before_any_call(L):
+    """Every argument's dtype and shape is checked before the C call (the C ABI
+    cannot see the size behind a device pointer): an undersized or mistyped
+    tensor raises ValueError naming it; well-formed CPU tensors raise at the
+    device check."""
+    import torch
+    good = _valid_cpu_args(torch)
+    for name, call in _calls(L, good).items():
+        with pytest.raises(ValueError, match="cuda device"):
+            call()
+    bad = {  # argument -> wrong replacement, with the calls that take it
+        "q": [torch.zeros(2, 8, 64), torch.zeros(3, 8, 128), torch.zeros(2, 7, 128),
+              torch.zeros(2, 8, 128, dtype=torch.float64)],
+        "kc": [torch.zeros(16, 2, 16, 64, dtype=torch.bfloat16), torch.zeros(16, 2, 16, 128)],
+        "vc": [torch.zeros(16, 1, 16, 128, dtype=torch.bfloat16), torch.zeros(16, 2, 16, 128)],
+        "pt": [torch.zeros(2, 6, dtype=torch.int64), torch.zeros(12, dtype=torch.int32)],
+        "sl": [torch.zeros(1, dtype=torch.int32), torch.zeros(2, dtype=torch.int64)],
+        "summ": [torch.zeros(16, 2, 776, dtype=torch.uint8), torch.zeros(15, 2, 784, dtype=torch.uint8),
+                 torch.zeros(16, 2, 784, dtype=torch.int8)],
+        "out": [torch.zeros(2, 8, 127), torch.zeros(2, 8, 128, dtype=torch.float16)],
+        "sel": [torch.zeros(2, 2, 1, dtype=torch.int32), torch.zeros(2, 2, 2, dtype=torch.int64)],
+        "ps": [torch.zeros(2, 8, 5), torch.zeros(2, 8, 6, dtype=torch.float64)],
+        "ws": [torch.zeros(4096, dtype=torch.int32), torch.zeros(64, 64, dtype=torch.uint8)],
+        "budget": [24, 0],
+    }
+    uses = {"decode_step": "q summ kc vc pt sl out sel ps ws budget",
+            "score_pages": "q summ kc pt sl ps ws budget",
+            "exact_score_pages": "q kc pt sl ps ws budget",
+            "select_pages": "q kc pt sl sel ps ws budget",
+            "sparse_attention": "q kc vc pt sl sel out ws budget",
+            "dense_attention": "q kc vc pt sl out ws",
+            "build_summaries": "kc pt sl summ",
+            "build_blocks": "kc summ"}
+    for fn, args in uses.items():
+        for arg in args.split():
+            for wrong in bad[arg]:
+                a = dict(good)
+                a[arg] = wrong
+                with pytest.raises(ValueError) as e:
+                    _calls(L, a)[fn]()
+                assert "cuda device" not in str(e.value), (fn, arg, str(e.value))
+    # non-contiguous and mixed-device tensors
+    a = dict(good)
+    a["q"] = torch.zeros(2, 128, 8).transpose(1, 2)
+    with pytest.raises(ValueError, match="contiguous"):
+        _calls(L, a)["decode_step"]()
+    a = dict(good)
+    a["out"] = torch.zeros(2, 8, 128, device="meta")
+    with pytest.raises(ValueError, match="one device"):
+        _calls(L, a)["decode_step"]()
