@@ -126,3 +126,46 @@ def decode_and_check(w: workloads.Workload, summ: torch.Tensor, budget: int | No
         f"out max-abs {err:.2e}, cos {cos:.7f}")
     return dict(score_err=s_err, swaps=swaps, out_err=err, cos=cos, out=out, sel=sel,
                 scores=scores, o_keys=o_keys)
+
+
+def plant_cutoff_tie(w: workloads.Workload, summ_host: np.ndarray, dup: int, seed: int = 0):
+    """Maps `dup` low-scoring logical pages of sequence 0 onto the physical
+    block of one page near the k-th place of (sequence 0, KV head 0), so that
+    dup + 1 pages share one record and their group keys are bit-identical. The
+    records are indexed by block, so no rebuild is needed. The page is chosen
+    so that the tied pages straddle the k-th place after the remap (the extra
+    copies move every head's total mass, hence every key). Returns the new
+    host page table and the tied logical pages."""
+    q, pt0, sl = host(w)
+    k = w.k_pages
+    n = int(sl[0]) // 16
+    keys = oracle.group_keys(oracle.scores(q, summ_host, pt0, sl, w.n_kv_heads), w.n_kv_heads)
+    order = np.lexsort((np.arange(n), -keys[0, 0, :n]))
+    rng = np.random.default_rng(seed)
+    victims = np.sort(rng.choice(order[n // 2:], size=dup, replace=False))  # far below the cut-off
+    for r in sorted(range(max(0, k - 4 * dup), min(n // 2, k + dup)), key=lambda r: abs(r - k)):
+        j0 = int(order[r])
+        pt = pt0.copy()
+        pt[0, victims] = pt[0, j0]
+        kk = oracle.group_keys(oracle.scores(q, summ_host, pt, sl, w.n_kv_heads),
+                               w.n_kv_heads)[0, 0]
+        above = int((kk > kk[j0]).sum())
+        near = (np.abs(kk - kk[j0]) <= 2 * TIE_TOL) & (kk != kk[j0])
+        if above < k < above + dup + 1 and not near.any():
+            return pt, np.sort(np.append(victims, j0))
+    raise AssertionError("no page near the cut-off gives a straddling tie")
+
+
+def cutoff_tie_premise(o_keys: np.ndarray, tied: np.ndarray, k: int):
+    """The tied pages straddle the k-th place of (sequence 0, KV head 0) and
+    no other key there lies within the near-tie band of theirs, so both sides
+    must keep exactly the same ids there: those above, then the lowest tied
+    ids. Returns the count above the tie."""
+    kk = o_keys[0, 0]
+    tie = kk[tied[0]]
+    assert np.all(kk[tied] == tie), "tied pages must have bit-identical oracle keys"
+    above = int((kk > tie).sum())
+    assert above < k < above + len(tied), f"tie does not straddle the cut-off ({above}, {len(tied)})"
+    near = (np.abs(kk - tie) <= 2 * TIE_TOL) & (kk != tie)
+    assert not near.any(), "another key lies in the near-tie band of the planted tie"
+    return above

@@ -55,7 +55,12 @@ def test_exact_scores_and_selection(locks, case):
     ref = oracle.exact_scores(q, workloads.bf16_bits(w.k_cache), pt, sl)
     g = scores.cpu().numpy()
     valid = np.isfinite(ref)
-    assert np.all(g[~valid & ~np.isnan(g)] == -np.inf)   # absent pages: -inf
+    # pages j < n_b that are absent get exactly -inf; entries j >= n_b are
+    # never written (they keep the NaN fill)
+    n_b = np.minimum(sl // 16, w.max_pages)
+    inside = np.broadcast_to(np.arange(w.max_pages)[None, None, :] < n_b[:, None, None], g.shape)
+    assert np.all(g[~valid & inside] == -np.inf)
+    assert np.all(np.isnan(g[~inside]))
     err = float(np.abs(g[valid] - ref[valid]).max())
     keys = oracle.group_keys(ref, w.n_kv_heads)
     o_sel = oracle.select(keys, w.k_pages)

@@ -8,7 +8,8 @@ import torch
 
 import oracle
 import workloads
-from parity import COS_MIN, decode_and_check, host, out_ok, say
+from parity import (COS_MIN, cutoff_tie_premise, decode_and_check, host, out_ok,
+                    plant_cutoff_tie, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -72,6 +73,37 @@ def test_selection_paths(locks, case):
     decode_and_check(w, summ, full_oracle_attention=False)
     del w, summ
     torch.cuda.empty_cache()
+
+
+# (ctx, budget, tied pages): the merge's register path (k = 32, a few hundred
+# candidates), its workgroup-wide LDS ranking (k = 1024 of 3000 pages: fewer
+# 16-page tiles than k, so no bound and every page is a candidate) and its
+# radix select over the lists (k = 4096 of 8192 candidates)
+TIE_CASES = [(16 * 1000, 512, 24), (16 * 3000, 16384, 40), (16 * 8192, 65536, 40)]
+
+
+@pytest.mark.parametrize("ctx,budget,dup", TIE_CASES, ids=["k32-register", "k1024-lds", "k4096-radix"])
+def test_bit_exact_ties_at_the_cutoff_go_to_the_lower_ids(locks, ctx, budget, dup):
+    """Several logical pages mapped onto one physical block share its record,
+    so their scores and group keys are bit-identical on both sides. Planted at
+    the k-th place, the tie must be broken toward the lower page ids (larger
+    key first, then lower id; ids ascending), and the GPU's selection must
+    equal the oracle's exactly, with no near-tie allowance."""
+    say(f"cut-off tie ctx {ctx} budget {budget} dup {dup}")
+    w = workloads.make(2, device=DEV, ctx=ctx, budget=budget, seed=77)
+    summ = locks.build_summaries(w.k_cache, w.page_table, w.seq_lens)
+    pt, tied = plant_cutoff_tie(w, summ.cpu().numpy(), dup)
+    w.page_table = torch.from_numpy(pt).to(DEV)
+    r = decode_and_check(w, summ)
+    above = cutoff_tie_premise(r["o_keys"], tied, w.k_pages)
+    g = r["sel"].cpu().numpy()[0, 0]
+    o = oracle.select(r["o_keys"], w.k_pages)[0, 0]
+    assert np.array_equal(g, o), "selection of (0, 0) differs from the oracle's"
+    assert np.array_equal(np.intersect1d(g, tied), tied[: w.k_pages - above])
+    sc = r["scores"].cpu().numpy()
+    for h in range(w.group):  # the GPU's own scores of the tied pages are bit-identical
+        assert np.all(sc[0, h, tied] == sc[0, h, tied[0]])
+    say(f"  {above} above the tie, {w.k_pages - above} of {len(tied)} tied pages kept")
 
 
 def test_decode_parity_on_oracle_built_summaries(locks):
@@ -156,14 +188,18 @@ def plant_nan_after_seq_len(w):
             w.v_cache[blk, :, first:] = float("nan")
 
 
+@pytest.mark.parametrize("budget", [512, 16384], ids=["k32", "k1024"])
 @pytest.mark.parametrize("config,hkv,hq", [(1, 1, 1), (2, 16, 32), (2, 8, 32), (2, 4, 32), (5, 2, 32)],
                          ids=["G1", "G2", "G4", "G8", "G16"])
-def test_tail_tokens_are_attended_and_nothing_after_seq_len_is_read(locks, config, hkv, hq):
+def test_tail_tokens_are_attended_and_nothing_after_seq_len_is_read(locks, config, hkv, hq, budget):
     """The partly filled last page has no summary: it is never scored or
     selected, but its tokens are attended in the decode step, in sparse
     attention on a given selection and in dense attention. Rows past seq_len
-    hold NaN; none may reach the output."""
-    w = workloads.make(config, device=DEV, ctx=16 * 160, batch=4, budget=512, n_kv_heads=hkv,
+    hold NaN; none may reach the output. Budget 16384 (k = 1024: more than 128
+    four-page splits) runs the sparse list in 16-page splits, with the tail
+    entry inside the last one."""
+    say(f"tail G={hq // hkv} budget {budget}")
+    w = workloads.make(config, device=DEV, ctx=16 * 160, batch=4, budget=budget, n_kv_heads=hkv,
                        n_q_heads=hq, seq_lens=[16 * 90 + 5, 16 * 160, 7, 16 * 33 + 15], seed=17)
     plant_nan_after_seq_len(w)
     summ = locks.build_summaries(w.k_cache, w.page_table, w.seq_lens)
