@@ -238,6 +238,25 @@ locks_status locks_sparse_attention(const locks_dims* dims, const float* q,
                                     int32_t budget_tokens, const int32_t* selected, float* out,
                                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * locks_decode_step with its workspace in a library-owned device array of
+ * LOCKS_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU, which the library looks up on
+ * its first call on a device and holds until the process ends. The call
+ * allocates nothing. Arguments, layouts and results are those of
+ * locks_decode_step. Dims and budgets whose locks_workspace_bytes exceed the
+ * scratch return LOCKS_ERR_WORKSPACE before anything is enqueued. Every call
+ * on a GPU shares that GPU's scratch, so calls that may overlap on one GPU
+ * (different streams, threads or processes' graphs replayed concurrently)
+ * race and must be serialised by the caller; the scratch needs no
+ * initialisation between calls. */
+#define LOCKS_NOALLOC_SCRATCH_BYTES (64u << 20)
+locks_status locks_decode_step_noalloc(const locks_dims* dims, const float* q,
+                                       const void* summaries, const void* k_cache,
+                                       const void* v_cache, const int32_t* page_table,
+                                       const int32_t* seq_lens, int32_t budget_tokens, float* out,
+                                       int32_t* selected, float* page_scores, hipStream_t stream);
+
 /* Dense decode attention over all seq_lens[b] tokens: every full page and the
  * tail (A "Code": the full-KV comparison; A "Results": the dense baseline the
  * speed-ups are quoted against). Same layouts and workspace rules as locks_decode_step; size the

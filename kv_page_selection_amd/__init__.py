@@ -24,6 +24,7 @@ PAGE_SIZE = 16
 RANK = 8
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4
+NOALLOC_SCRATCH_BYTES = 64 << 20  # LOCKS_NOALLOC_SCRATCH_BYTES
 
 
 class Dims(ctypes.Structure):
@@ -60,6 +61,7 @@ def lib() -> ctypes.CDLL:
         L.locks_build_summaries.argtypes = [D, P, P, P, P, P]
         L.locks_build_blocks.argtypes = [D, P, P, I, P, P]
         L.locks_decode_step.argtypes = [D, P, P, P, P, P, P, I, P, P, P, P, S, P]
+        L.locks_decode_step_noalloc.argtypes = [D, P, P, P, P, P, P, I, P, P, P, P]
         L.locks_score_pages.argtypes = [D, P, P, P, P, I, P, P, S, P]
         L.locks_exact_score_pages.argtypes = [D, P, P, P, P, I, P, P, S, P]
         L.locks_variant_record_bytes.argtypes = [I, I, ctypes.POINTER(S)]
@@ -69,7 +71,7 @@ def lib() -> ctypes.CDLL:
         L.locks_sparse_attention.argtypes = [D, P, P, P, P, P, I, P, P, P, S, P]
         L.locks_dense_attention.argtypes = [D, P, P, P, P, P, P, P, S, P]
         for name in ("locks_workspace_bytes", "locks_build_summaries", "locks_build_blocks",
-                     "locks_decode_step",
+                     "locks_decode_step", "locks_decode_step_noalloc",
                      "locks_score_pages", "locks_exact_score_pages", "locks_select_pages",
                      "locks_variant_record_bytes", "locks_build_summaries_variant",
                      "locks_score_pages_variant",
@@ -239,6 +241,30 @@ def decode_step(q, summaries, k_cache, v_cache, page_table, seq_lens, budget_tok
         ctypes.byref(dims), _ptr(q), _ptr(summaries), _ptr(k_cache), _ptr(v_cache),
         _ptr(page_table), _ptr(seq_lens), int(budget_tokens), _ptr(out), _ptr(selected),
         _ptr(page_scores), _ptr(workspace), workspace.numel(), _stream(dev)))
+    return out, selected
+
+
+def decode_step_noalloc(q, summaries, k_cache, v_cache, page_table, seq_lens, budget_tokens: int,
+                        out, selected, page_scores=None):
+    """decode_step for callers that cannot allocate: the workspace is the
+    library's own per-GPU scratch (NOALLOC_SCRATCH_BYTES); out and selected are
+    the caller's. Calls that overlap on one GPU race on that scratch."""
+    B, hq, hkv, N, nb = _check_common(q, k_cache, page_table, seq_lens)
+    k = _pages(budget_tokens)
+    _tensor(summaries, "summaries", torch.uint8, (nb, hkv, summary_record_bytes()))
+    _tensor(v_cache, "v_cache", torch.bfloat16, tuple(k_cache.shape))
+    _tensor(out, "out", torch.float32, (B, hq, HEAD_DIM))
+    _tensor(selected, "selected", torch.int32, (B, hkv, k))
+    if page_scores is not None:
+        _tensor(page_scores, "page_scores", torch.float32, (B, hq, N))
+    dev = _devices(dict(q=q, summaries=summaries, k_cache=k_cache, v_cache=v_cache,
+                        page_table=page_table, seq_lens=seq_lens, out=out, selected=selected,
+                        page_scores=page_scores))
+    dims = make_dims(q, k_cache, page_table)
+    _check(lib().locks_decode_step_noalloc(
+        ctypes.byref(dims), _ptr(q), _ptr(summaries), _ptr(k_cache), _ptr(v_cache),
+        _ptr(page_table), _ptr(seq_lens), int(budget_tokens), _ptr(out), _ptr(selected),
+        _ptr(page_scores), _stream(dev)))
     return out, selected
 
 

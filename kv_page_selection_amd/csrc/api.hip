@@ -10,6 +10,8 @@
 #include "internal.h"
 
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 #include "locks.h"
 
 namespace locks {
@@ -182,6 +184,51 @@ locks_status need(const void* p, size_t align, const char* name) {
 locks_status hip_status(hipError_t e, const char* what) {
   if (e != hipSuccess)
     return fail(LOCKS_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+  return LOCKS_OK;
+}
+
+// Library-owned workspace of locks_decode_step_noalloc: one copy per GPU (the
+// runtime places a __device__ array on every device the library runs on),
+// held until the process ends. In host code `scratch` names a host-side
+// stand-in, never the device memory: its device address is looked up once per
+// device with hipGetSymbolAddress and kept in scratch_dev.
+__device__ __align__(256) uint8_t scratch[LOCKS_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 256;
+std::atomic<void*> scratch_dev[kMaxDevices];
+std::mutex scratch_mu;
+
+// Device address of `scratch` on the device `stream` runs on; the first call
+// for a device looks it up with that device current.
+locks_status scratch_for(hipStream_t stream, void** out) {
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return fail(LOCKS_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  int dev = cur;
+  if (stream) {
+    e = hipStreamGetDevice(stream, &dev);
+    if (e != hipSuccess)
+      return fail(LOCKS_ERR_HIP, std::string("hipStreamGetDevice: ") + hipGetErrorString(e));
+  }
+  if (dev < 0 || dev >= kMaxDevices) return fail(LOCKS_ERR_UNSUPPORTED, "device ordinal above 255");
+  void* p = scratch_dev[dev].load(std::memory_order_acquire);
+  if (p) {
+    *out = p;
+    return LOCKS_OK;
+  }
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  p = scratch_dev[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess)
+      return fail(LOCKS_ERR_HIP, std::string("hipSetDevice: ") + hipGetErrorString(e));
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) (void)hipSetDevice(cur);
+    if (e != hipSuccess || !p)
+      return fail(LOCKS_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") +
+                                     (e != hipSuccess ? hipGetErrorString(e) : "null address"));
+    scratch_dev[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
   return LOCKS_OK;
 }
 
@@ -423,6 +470,38 @@ locks_status locks_decode_step(const locks_dims* dims, const float* q, const voi
                                   static_cast<const uint16_t*>(v_cache), page_table, seq_lens,
                                   selected, P.sel_blk, out, false, stream),
                     "sparse attention launch");
+}
+
+locks_status locks_decode_step_noalloc(const locks_dims* dims, const float* q,
+                                       const void* summaries, const void* k_cache,
+                                       const void* v_cache, const int32_t* page_table,
+                                       const int32_t* seq_lens, int32_t budget_tokens, float* out,
+                                       int32_t* selected, float* page_scores, hipStream_t stream) {
+  g_err.clear();
+  LOCKS_TRY(check_dims(dims));
+  LOCKS_TRY(check_budget(budget_tokens));
+  WsLayout L;
+  LOCKS_TRY(layout(dims, budget_tokens, &L));
+  if (L.total > (size_t)LOCKS_NOALLOC_SCRATCH_BYTES)
+    return fail(LOCKS_ERR_WORKSPACE,
+                "these dims and budget need " + std::to_string(L.total) +
+                    " bytes of workspace, above the library's no-allocation scratch of " +
+                    std::to_string((size_t)LOCKS_NOALLOC_SCRATCH_BYTES) +
+                    " bytes: use locks_decode_step with a caller workspace");
+  LOCKS_TRY(need(q, 4, "q"));
+  LOCKS_TRY(need(summaries, 16, "summaries"));
+  LOCKS_TRY(need(k_cache, 16, "k_cache"));
+  LOCKS_TRY(need(v_cache, 16, "v_cache"));
+  LOCKS_TRY(need(page_table, 4, "page_table"));
+  LOCKS_TRY(need(seq_lens, 4, "seq_lens"));
+  LOCKS_TRY(need(out, 4, "out"));
+  LOCKS_TRY(need(selected, 4, "selected"));
+  if (page_scores) LOCKS_TRY(need(page_scores, 4, "page_scores"));
+  void* ws = nullptr;
+  LOCKS_TRY(scratch_for(stream, &ws));
+  return locks_decode_step(dims, q, summaries, k_cache, v_cache, page_table, seq_lens,
+                           budget_tokens, out, selected, page_scores, ws,
+                           (size_t)LOCKS_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 locks_status locks_dense_attention(const locks_dims* dims, const float* q, const void* k_cache,

@@ -210,3 +210,15 @@ def test_binding_validates_shapes_dtypes_and_devices_before_any_call(L):
     a["out"] = torch.zeros(2, 8, 128, device="meta")
     with pytest.raises(ValueError, match="one device"):
         _calls(L, a)["decode_step"]()
+
+
+def test_noalloc_step_refuses_workloads_beyond_its_scratch_on_host(L):
+    """locks_decode_step_noalloc checks the workspace its dims need against the
+    library's scratch before anything else touches the GPU."""
+    lib = L.lib()
+    d = dims(L, batch=64, num_blocks=64 * 65536)
+    assert L.workspace_bytes(d, 2048) > L.NOALLOC_SCRATCH_BYTES
+    fake = ctypes.c_void_p(1 << 20)
+    st = lib.locks_decode_step_noalloc(ctypes.byref(d), fake, fake, fake, fake, fake, fake, 2048,
+                                       fake, fake, None, None)
+    assert st == L.ERR_WORKSPACE and b"scratch" in lib.locks_last_error()
