@@ -330,6 +330,34 @@ def main():
     torch.cuda.synchronize()
     tail_step_us = ts.elapsed_time(te) * 1e3 / args.steps
     del tgraphs
+
+    # ---- the step in which every sequence's last page has just filled: the
+    # page is attended in full, and the step builds its records (every KV
+    # head) in workgroups of its own scoring launch
+    filled = (w.seq_lens % 16 == 0).to(torch.int32).contiguous()
+
+    def step_fill(r):
+        s_, kc_, vc_ = reps[r]
+        locks.decode_step(w.q, s_, kc_, vc_, w.page_table, w.seq_lens, w.budget,
+                          out=outs[r], selected=sels[r], workspace=ws[r], filled=filled)
+
+    fgraphs = []
+    for r in range(R):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step_fill(r)
+        fgraphs.append(g)
+    for i in range(args.warmup):
+        fgraphs[i % R].replay()
+    torch.cuda.synchronize()
+    ts.record()
+    for i in range(args.steps):
+        fgraphs[i % R].replay()
+    te.record()
+    torch.cuda.synchronize()
+    fill_step_us = ts.elapsed_time(te) * 1e3 / args.steps
+    n_filled = int(((filled != 0) & (w.seq_lens >= 16)).sum().item())
+    del fgraphs
     # restore the full-page selection for anything below that reads it
     for i in range(R):
         graphs[i].replay()
@@ -485,6 +513,11 @@ def main():
         "page_fill_build": {"us": round(fill_us, 2), "page_heads": B * Hkv,
                             "blocks": "one per sequence, every KV head"},
         "ragged_tail_step": {"us_per_step": round(tail_step_us, 2), "tail_tokens": "seq_len % 16 = 11"},
+        "step_with_page_fill": {"us_per_step": round(fill_step_us, 2),
+                                "plain_us_per_step": round(step_ms * 1e3, 2),
+                                "filled_pages": n_filled, "page_heads_built": n_filled * Hkv,
+                                "how": "last page of each sequence just filled: attended in full, "
+                                       "its records built by workgroups of the step's scoring launch"},
         "summary_build": {"us": round(build_us, 1), "page_heads": B * Hkv * N,
                           "page_heads_per_s": round(B * Hkv * N / (build_us * 1e-6), 1)},
         "dense": dense,

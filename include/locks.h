@@ -238,6 +238,32 @@ locks_status locks_sparse_attention(const locks_dims* dims, const float* q,
                                     int32_t budget_tokens, const int32_t* selected, float* out,
                                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* A decode step in which some sequences' last page has just filled (its 16th
+ * token landed in this step): the step also builds that page's summary, off
+ * its critical path (A "How LOCKS works": the summary is built once, when a
+ * page fills; B mechanism 4: summary building stays off the decode critical
+ * path, the whole step in one graph). Same arguments and results as
+ * locks_decode_step, plus:
+ *  filled     device i32[batch]; filled[b] != 0 marks that page n_b - 1 of
+ *             sequence b filled in this step (seq_lens[b] = 16 n_b, n_b >= 1;
+ *             marks on other sequences are ignored). A marked page has no
+ *             summary yet: it is not scored or selected, and all 16 of its
+ *             tokens are attended like a partly filled tail page.
+ *  summaries  also written: the records of every marked page (block
+ *             page_table[b][n_b - 1], every KV head), the bytes
+ *             locks_build_blocks writes for that block. They are built by
+ *             workgroups of the scoring launch itself, which run first and
+ *             alongside the scoring (no scoring workgroup reads them), so the
+ *             build costs the step little time; from the next step on the page
+ *             is scored as usual. A marked page's block must not also be a
+ *             scored page of another sequence in the same step. */
+locks_status locks_decode_step_fill(const locks_dims* dims, const float* q, void* summaries,
+                                    const void* k_cache, const void* v_cache,
+                                    const int32_t* page_table, const int32_t* seq_lens,
+                                    const int32_t* filled, int32_t budget_tokens, float* out,
+                                    int32_t* selected, float* page_scores, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream);
+
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc):
  * locks_decode_step with its workspace in a library-owned device array of

@@ -62,6 +62,7 @@ def lib() -> ctypes.CDLL:
         L.locks_build_blocks.argtypes = [D, P, P, I, P, P]
         L.locks_decode_step.argtypes = [D, P, P, P, P, P, P, I, P, P, P, P, S, P]
         L.locks_decode_step_noalloc.argtypes = [D, P, P, P, P, P, P, I, P, P, P, P]
+        L.locks_decode_step_fill.argtypes = [D, P, P, P, P, P, P, P, I, P, P, P, P, S, P]
         L.locks_score_pages.argtypes = [D, P, P, P, P, I, P, P, S, P]
         L.locks_exact_score_pages.argtypes = [D, P, P, P, P, I, P, P, S, P]
         L.locks_variant_record_bytes.argtypes = [I, I, ctypes.POINTER(S)]
@@ -71,7 +72,7 @@ def lib() -> ctypes.CDLL:
         L.locks_sparse_attention.argtypes = [D, P, P, P, P, P, I, P, P, P, S, P]
         L.locks_dense_attention.argtypes = [D, P, P, P, P, P, P, P, S, P]
         for name in ("locks_workspace_bytes", "locks_build_summaries", "locks_build_blocks",
-                     "locks_decode_step", "locks_decode_step_noalloc",
+                     "locks_decode_step", "locks_decode_step_noalloc", "locks_decode_step_fill",
                      "locks_score_pages", "locks_exact_score_pages", "locks_select_pages",
                      "locks_variant_record_bytes", "locks_build_summaries_variant",
                      "locks_score_pages_variant",
@@ -213,8 +214,11 @@ def build_blocks(k_cache: torch.Tensor, blocks: torch.Tensor, summaries: torch.T
 
 
 def decode_step(q, summaries, k_cache, v_cache, page_table, seq_lens, budget_tokens: int,
-                out=None, selected=None, page_scores=None, workspace=None):
-    """One LOCKS decode step. Returns (out [B,Hq,128] f32, selected [B,Hkv,k] i32)."""
+                out=None, selected=None, page_scores=None, workspace=None, filled=None):
+    """One LOCKS decode step. Returns (out [B,Hq,128] f32, selected [B,Hkv,k] i32).
+    filled (int32 [B], optional): nonzero where the sequence's last page filled
+    in this step; that page is attended in full and not scored, and the step
+    builds its summary records into `summaries` (locks_decode_step_fill)."""
     B, hq, hkv, N, nb = _check_common(q, k_cache, page_table, seq_lens)
     k = _pages(budget_tokens)
     _tensor(summaries, "summaries", torch.uint8, (nb, hkv, summary_record_bytes()))
@@ -227,9 +231,11 @@ def decode_step(q, summaries, k_cache, v_cache, page_table, seq_lens, budget_tok
         _tensor(page_scores, "page_scores", torch.float32, (B, hq, N))
     if workspace is not None:
         _workspace(workspace)
+    if filled is not None:
+        _tensor(filled, "filled", torch.int32, (B,))
     dev = _devices(dict(q=q, summaries=summaries, k_cache=k_cache, v_cache=v_cache,
                         page_table=page_table, seq_lens=seq_lens, out=out, selected=selected,
-                        page_scores=page_scores, workspace=workspace))
+                        page_scores=page_scores, workspace=workspace, filled=filled))
     dims = make_dims(q, k_cache, page_table)
     if out is None:
         out = torch.empty_like(q)
@@ -237,10 +243,16 @@ def decode_step(q, summaries, k_cache, v_cache, page_table, seq_lens, budget_tok
         selected = torch.empty(B, hkv, k, dtype=torch.int32, device=dev)
     if workspace is None:
         workspace = new_workspace(dims, budget_tokens, dev)
-    _check(lib().locks_decode_step(
-        ctypes.byref(dims), _ptr(q), _ptr(summaries), _ptr(k_cache), _ptr(v_cache),
-        _ptr(page_table), _ptr(seq_lens), int(budget_tokens), _ptr(out), _ptr(selected),
-        _ptr(page_scores), _ptr(workspace), workspace.numel(), _stream(dev)))
+    if filled is None:
+        _check(lib().locks_decode_step(
+            ctypes.byref(dims), _ptr(q), _ptr(summaries), _ptr(k_cache), _ptr(v_cache),
+            _ptr(page_table), _ptr(seq_lens), int(budget_tokens), _ptr(out), _ptr(selected),
+            _ptr(page_scores), _ptr(workspace), workspace.numel(), _stream(dev)))
+    else:
+        _check(lib().locks_decode_step_fill(
+            ctypes.byref(dims), _ptr(q), _ptr(summaries), _ptr(k_cache), _ptr(v_cache),
+            _ptr(page_table), _ptr(seq_lens), _ptr(filled), int(budget_tokens), _ptr(out),
+            _ptr(selected), _ptr(page_scores), _ptr(workspace), workspace.numel(), _stream(dev)))
     return out, selected
 
 

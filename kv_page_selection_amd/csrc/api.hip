@@ -240,6 +240,48 @@ locks_status scratch_for(hipStream_t stream, void** out) {
 
 }  // namespace
 
+namespace {
+
+// The three phases of a decode step on one workspace; fill (nullable) marks,
+// per sequence, a last full page that filled in this step (attended as the
+// tail, not scored).
+locks_status decode_step_impl(const locks_dims* dims, const float* q, const void* summaries,
+                              const void* k_cache, const void* v_cache,
+                              const int32_t* page_table, const int32_t* seq_lens,
+                              const int32_t* fill, int32_t budget_tokens, float* out,
+                              int32_t* selected, float* page_scores, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+  g_err.clear();
+  LOCKS_TRY(check_dims(dims));
+  LOCKS_TRY(check_budget(budget_tokens));
+  LOCKS_TRY(need(q, 4, "q"));
+  LOCKS_TRY(need(summaries, 16, "summaries"));
+  LOCKS_TRY(need(k_cache, 16, "k_cache"));
+  LOCKS_TRY(need(v_cache, 16, "v_cache"));
+  LOCKS_TRY(need(page_table, 4, "page_table"));
+  LOCKS_TRY(need(seq_lens, 4, "seq_lens"));
+  LOCKS_TRY(need(out, 4, "out"));
+  LOCKS_TRY(need(selected, 4, "selected"));
+  if (page_scores) LOCKS_TRY(need(page_scores, 4, "page_scores"));
+  WsLayout L;
+  LOCKS_TRY(layout(dims, budget_tokens, &L));
+  LOCKS_TRY(check_ws(L, workspace, workspace_bytes));
+  const DevPtrs P = ws_ptrs(*dims, L, workspace, page_scores);
+  (void)hipGetLastError();
+  LOCKS_TRY(hip_status(launch_score(*dims, L, P, q, static_cast<const uint8_t*>(summaries),
+                                    page_table, seq_lens, fill,
+                                    static_cast<const uint16_t*>(k_cache), stream),
+                       "score launch"));
+  LOCKS_TRY(hip_status(launch_select(*dims, L, P, page_table, seq_lens, fill, selected, stream),
+                       "select launch"));
+  return hip_status(launch_attend(*dims, L, P, q, static_cast<const uint16_t*>(k_cache),
+                                  static_cast<const uint16_t*>(v_cache), page_table, seq_lens,
+                                  fill, selected, P.sel_blk, out, false, stream),
+                    "sparse attention launch");
+}
+
+}  // namespace
+
 extern "C" {
 
 size_t locks_summary_record_bytes(void) { return kStride; }
@@ -309,7 +351,7 @@ locks_status locks_score_pages(const locks_dims* dims, const float* q, const voi
   const DevPtrs P = ws_ptrs(*dims, L, workspace, page_scores);
   (void)hipGetLastError();
   return hip_status(launch_score(*dims, L, P, q, static_cast<const uint8_t*>(summaries), page_table,
-                                 seq_lens, stream),
+                                 seq_lens, nullptr, nullptr, stream),
                     "score launch");
 }
 
@@ -408,7 +450,7 @@ locks_status locks_select_pages(const locks_dims* dims, const int32_t* page_tabl
   LOCKS_TRY(check_ws(L, workspace, workspace_bytes));
   const DevPtrs P = ws_ptrs(*dims, L, workspace, const_cast<float*>(page_scores));
   (void)hipGetLastError();
-  return hip_status(launch_select(*dims, L, P, page_table, seq_lens, selected, stream),
+  return hip_status(launch_select(*dims, L, P, page_table, seq_lens, nullptr, selected, stream),
                     "select launch");
 }
 
@@ -434,7 +476,7 @@ locks_status locks_sparse_attention(const locks_dims* dims, const float* q, cons
   (void)hipGetLastError();
   return hip_status(launch_attend(*dims, L, P, q, static_cast<const uint16_t*>(k_cache),
                                   static_cast<const uint16_t*>(v_cache), page_table, seq_lens,
-                                  selected, nullptr, out, false, stream),
+                                  nullptr, selected, nullptr, out, false, stream),
                     "sparse attention launch");
 }
 
@@ -444,32 +486,24 @@ locks_status locks_decode_step(const locks_dims* dims, const float* q, const voi
                                int32_t budget_tokens, float* out, int32_t* selected,
                                float* page_scores, void* workspace, size_t workspace_bytes,
                                hipStream_t stream) {
+  return decode_step_impl(dims, q, summaries, k_cache, v_cache, page_table, seq_lens, nullptr,
+                          budget_tokens, out, selected, page_scores, workspace, workspace_bytes,
+                          stream);
+}
+
+locks_status locks_decode_step_fill(const locks_dims* dims, const float* q, void* summaries,
+                                    const void* k_cache, const void* v_cache,
+                                    const int32_t* page_table, const int32_t* seq_lens,
+                                    const int32_t* filled, int32_t budget_tokens, float* out,
+                                    int32_t* selected, float* page_scores, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream) {
   g_err.clear();
-  LOCKS_TRY(check_dims(dims));
-  LOCKS_TRY(check_budget(budget_tokens));
-  LOCKS_TRY(need(q, 4, "q"));
-  LOCKS_TRY(need(summaries, 16, "summaries"));
-  LOCKS_TRY(need(k_cache, 16, "k_cache"));
-  LOCKS_TRY(need(v_cache, 16, "v_cache"));
-  LOCKS_TRY(need(page_table, 4, "page_table"));
-  LOCKS_TRY(need(seq_lens, 4, "seq_lens"));
-  LOCKS_TRY(need(out, 4, "out"));
-  LOCKS_TRY(need(selected, 4, "selected"));
-  if (page_scores) LOCKS_TRY(need(page_scores, 4, "page_scores"));
-  WsLayout L;
-  LOCKS_TRY(layout(dims, budget_tokens, &L));
-  LOCKS_TRY(check_ws(L, workspace, workspace_bytes));
-  const DevPtrs P = ws_ptrs(*dims, L, workspace, page_scores);
-  (void)hipGetLastError();
-  LOCKS_TRY(hip_status(launch_score(*dims, L, P, q, static_cast<const uint8_t*>(summaries),
-                                    page_table, seq_lens, stream),
-                       "score launch"));
-  LOCKS_TRY(hip_status(launch_select(*dims, L, P, page_table, seq_lens, selected, stream),
-                       "select launch"));
-  return hip_status(launch_attend(*dims, L, P, q, static_cast<const uint16_t*>(k_cache),
-                                  static_cast<const uint16_t*>(v_cache), page_table, seq_lens,
-                                  selected, P.sel_blk, out, false, stream),
-                    "sparse attention launch");
+  LOCKS_TRY(need(filled, 4, "filled"));
+  if (dims && (long long)dims->batch * dims->n_kv_heads > (1LL << 30))
+    return fail(LOCKS_ERR_UNSUPPORTED, "batch * n_kv_heads above 2^30");
+  return decode_step_impl(dims, q, summaries, k_cache, v_cache, page_table, seq_lens, filled,
+                          budget_tokens, out, selected, page_scores, workspace, workspace_bytes,
+                          stream);
 }
 
 locks_status locks_decode_step_noalloc(const locks_dims* dims, const float* q,
@@ -523,7 +557,7 @@ locks_status locks_dense_attention(const locks_dims* dims, const float* q, const
   (void)hipGetLastError();
   return hip_status(launch_attend(*dims, L, P, q, static_cast<const uint16_t*>(k_cache),
                                   static_cast<const uint16_t*>(v_cache), page_table, seq_lens,
-                                  nullptr, nullptr, out, true, stream),
+                                  nullptr, nullptr, nullptr, out, true, stream),
                     "dense attention launch");
 }
 

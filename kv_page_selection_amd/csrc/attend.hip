@@ -35,6 +35,7 @@ struct AttnArgs {
   const uint16_t* vc;
   const int32_t* page_table;
   const int32_t* seq_lens;
+  const int32_t* fill;  // nullable: pages that filled in this step (attended as the tail)
   const int32_t* sel;      // nullptr: dense (every full page)
   const int32_t* sel_blk;  // physical blocks of sel's pages (nullptr: look them up)
   float* partials;
@@ -48,8 +49,8 @@ __global__ __launch_bounds__(256) void attend_kernel(AttnArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int tok = lane & 15, c = lane >> 4;
   const int N = a.N;
-  const int n_b = full_pages(a.seq_lens, b, N);
-  const int tail = tail_tokens(a.seq_lens, b, N);
+  const int n_b = full_pages(a.seq_lens, a.fill, b, N);
+  const int tail = tail_tokens(a.seq_lens, a.fill, b, N);
   const int base_len = a.sel ? a.k : n_b;  // entry base_len is the tail, if any
   const int list_len = base_len + (tail > 0 ? 1 : 0);
   const int s0 = split * a.pages_per_split;
@@ -219,8 +220,8 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(AttnArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int li = lane & 15, lj = lane >> 4;
   const int N = a.N;
-  const int n_b = full_pages(a.seq_lens, b, N);
-  const int tail = tail_tokens(a.seq_lens, b, N);
+  const int n_b = full_pages(a.seq_lens, a.fill, b, N);
+  const int tail = tail_tokens(a.seq_lens, a.fill, b, N);
   const int base_len = a.sel ? a.k : n_b;  // entry base_len is the tail, if any
   const int list_len = base_len + (tail > 0 ? 1 : 0);
   const int s0 = split * a.pages_per_split;
@@ -428,14 +429,15 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(const float* partials
 template <int G>
 hipError_t launch_g(const locks_dims& d, const WsLayout& L, const DevPtrs& P, const float* q,
                     const uint16_t* kc, const uint16_t* vc, const int32_t* pt, const int32_t* sl,
-                    const int32_t* sel, const int32_t* sel_blk, float* out, bool dense,
-                    hipStream_t s) {
+                    const int32_t* fill, const int32_t* sel, const int32_t* sel_blk, float* out,
+                    bool dense, hipStream_t s) {
   AttnArgs a;
   a.q = q;
   a.kc = kc;
   a.vc = vc;
   a.page_table = pt;
   a.seq_lens = sl;
+  a.fill = fill;
   a.sel = dense ? nullptr : sel;
   a.sel_blk = dense ? nullptr : sel_blk;
   a.partials = dense ? P.dense_part : P.att_part;
@@ -470,14 +472,14 @@ hipError_t launch_g(const locks_dims& d, const WsLayout& L, const DevPtrs& P, co
 
 hipError_t launch_attend(const locks_dims& d, const WsLayout& L, const DevPtrs& P, const float* q,
                          const uint16_t* kc, const uint16_t* vc, const int32_t* pt,
-                         const int32_t* sl, const int32_t* sel, const int32_t* sel_blk,
-                         float* out, bool dense, hipStream_t s) {
+                         const int32_t* sl, const int32_t* fill, const int32_t* sel,
+                         const int32_t* sel_blk, float* out, bool dense, hipStream_t s) {
   switch (d.n_q_heads / d.n_kv_heads) {
-    case 1: return launch_g<1>(d, L, P, q, kc, vc, pt, sl, sel, sel_blk, out, dense, s);
-    case 2: return launch_g<2>(d, L, P, q, kc, vc, pt, sl, sel, sel_blk, out, dense, s);
-    case 4: return launch_g<4>(d, L, P, q, kc, vc, pt, sl, sel, sel_blk, out, dense, s);
-    case 8: return launch_g<8>(d, L, P, q, kc, vc, pt, sl, sel, sel_blk, out, dense, s);
-    case 16: return launch_g<16>(d, L, P, q, kc, vc, pt, sl, sel, sel_blk, out, dense, s);
+    case 1: return launch_g<1>(d, L, P, q, kc, vc, pt, sl, fill, sel, sel_blk, out, dense, s);
+    case 2: return launch_g<2>(d, L, P, q, kc, vc, pt, sl, fill, sel, sel_blk, out, dense, s);
+    case 4: return launch_g<4>(d, L, P, q, kc, vc, pt, sl, fill, sel, sel_blk, out, dense, s);
+    case 8: return launch_g<8>(d, L, P, q, kc, vc, pt, sl, fill, sel, sel_blk, out, dense, s);
+    case 16: return launch_g<16>(d, L, P, q, kc, vc, pt, sl, fill, sel, sel_blk, out, dense, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -31,19 +31,29 @@ __device__ __forceinline__ float f16bits_to_float(uint32_t h) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(h & 0xffffu));
 }
 
-// Number of full pages of sequence b, clamped to [0, max_pages].
-__device__ __forceinline__ int full_pages(const int32_t* seq_lens, int b, int max_pages) {
-  int n = seq_lens[b] / kPage;
+// Pages of sequence b that have a summary: its full pages, clamped to [0,
+// max_pages], less the last one when `fill` (nullable) marks it as having
+// filled in this step (fill[b] != 0 and seq_lens[b] a multiple of 16): that
+// page's summary is being built concurrently, so it is attended like a tail
+// instead of scored.
+__device__ __forceinline__ int full_pages(const int32_t* seq_lens, const int32_t* fill, int b,
+                                          int max_pages) {
+  const int len = seq_lens[b];
+  int n = len / kPage;
   n = n < 0 ? 0 : n;
-  return n > max_pages ? max_pages : n;
+  n = n > max_pages ? max_pages : n;
+  if (fill && n > 0 && len == n * kPage && fill[b] != 0) --n;
+  return n;
 }
 
-// Tokens of sequence b after its last full page: they sit in logical page
+// Tokens of sequence b after its scored pages: they sit in logical page
 // full_pages(), which has no summary yet (a page's summary is built when its
-// 16th token lands); 0 when the full pages already reach max_pages.
-__device__ __forceinline__ int tail_tokens(const int32_t* seq_lens, int b, int max_pages) {
+// 16th token lands): the partly filled last page, or all 16 tokens of a page
+// that filled in this step; 0 when the scored pages already reach max_pages.
+__device__ __forceinline__ int tail_tokens(const int32_t* seq_lens, const int32_t* fill, int b,
+                                           int max_pages) {
   const int len = seq_lens[b];
-  const int n = full_pages(seq_lens, b, max_pages);
+  const int n = full_pages(seq_lens, fill, b, max_pages);
   return (len <= 0 || n >= max_pages) ? 0 : len - n * kPage;
 }
 

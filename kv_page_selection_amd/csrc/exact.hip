@@ -42,7 +42,7 @@ __global__ __launch_bounds__(256) void exact_score_kernel(ExactArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int li = lane & 15, lj = lane >> 4;
   const int N = a.N;
-  const int n_b = full_pages(a.seq_lens, b, N);
+  const int n_b = full_pages(a.seq_lens, nullptr, b, N);
   const int p0 = range * 64 + wave * 16;  // this wave's first page
   __shared__ float out[64][G];            // base-2 page scores, [page][head]; -inf: absent
 

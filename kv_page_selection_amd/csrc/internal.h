@@ -61,9 +61,13 @@ struct DevPtrs {
 DevPtrs ws_ptrs(const locks_dims& d, const WsLayout& L, void* ws, float* page_scores);
 
 // Kernel launchers (enqueue only; return hipGetLastError()).
+// fill (nullable): per sequence, nonzero when its last full page filled in
+// this step; that page is attended as the tail instead of scored (see
+// full_pages()), and this launch also builds its records (every KV head) from
+// kc into summ, in workgroups of its own.
 hipError_t launch_score(const locks_dims& d, const WsLayout& L, const DevPtrs& P, const float* q,
                         const uint8_t* summ, const int32_t* page_table, const int32_t* seq_lens,
-                        hipStream_t s);
+                        const int32_t* fill, const uint16_t* kc, hipStream_t s);
 // Variant record formats (precision / rank ablation): bytes per record (0 if
 // unsupported), whole-cache build, and scores (same workspace outputs as
 // launch_score).
@@ -80,11 +84,11 @@ hipError_t launch_exact_score(const locks_dims& d, const WsLayout& L, const DevP
                               const float* q, const uint16_t* kc, const int32_t* page_table,
                               const int32_t* seq_lens, hipStream_t s);
 hipError_t launch_select(const locks_dims& d, const WsLayout& L, const DevPtrs& P,
-                         const int32_t* page_table, const int32_t* seq_lens, int32_t* selected,
-                         hipStream_t s);
+                         const int32_t* page_table, const int32_t* seq_lens, const int32_t* fill,
+                         int32_t* selected, hipStream_t s);
 hipError_t launch_attend(const locks_dims& d, const WsLayout& L, const DevPtrs& P, const float* q,
                          const uint16_t* kc, const uint16_t* vc, const int32_t* page_table,
-                         const int32_t* seq_lens, const int32_t* selected,
+                         const int32_t* seq_lens, const int32_t* fill, const int32_t* selected,
                          const int32_t* selected_blocks, float* out, bool dense, hipStream_t s);
 // Whole cache (blocks == nullptr: every full page through the page table) or
 // the n_blocks listed blocks, every KV head of each.

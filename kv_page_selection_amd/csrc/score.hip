@@ -41,8 +41,7 @@
 // LDS table); every tile then issues its 13 record loads back to back in a
 // fixed order (V rows first) and consumes them in that order, so the first
 // MFMAs run while the tail of the tile is still arriving.
-#include "device_common.h"
-#include "internal.h"
+#include "build_device.h"
 
 namespace locks {
 
@@ -60,11 +59,53 @@ struct ScoreArgs {
   const uint8_t* summ;
   const int32_t* page_table;
   const int32_t* seq_lens;
+  const int32_t* fill;  // nullable: pages that filled in this step (attended as the tail)
   float* scores;
   float* partials;
   float* tile_max;
   int Hq, Hkv, N, num_blocks, n_ranges, tile_pages;
+  // with a fill (1-D grid): the first fill_wgs workgroups build the records
+  // of the pages that filled in this step (fb); the rest score, as workgroup
+  // (x, y, z) of a gx x Hkv x B grid in x-fastest order
+  BuildArgs fb;
+  int fill_wgs, gx;
 };
+
+// A scoring kernel's LDS; with a fill, shared with the build waves' LDS.
+template <class SL, bool Fill>
+struct KernelLds {
+  SL s;
+};
+template <class SL>
+struct KernelLds<SL, true> {
+  union {
+    SL s;
+    WaveLds b[4];
+  };
+};
+
+// The workgroup's scoring coordinates (bx, by, bz); with a fill, false for a
+// workgroup that built records instead (one page-head per wave).
+template <bool Fill, class U>
+__device__ __forceinline__ bool score_workgroup(const ScoreArgs& a, U& lds, int wave, int lane, int& bx,
+                                                int& by, int& bz) {
+  bx = blockIdx.x;
+  by = blockIdx.y;
+  bz = blockIdx.z;
+  if constexpr (Fill) {
+    int lid = blockIdx.x;
+    if (lid < a.fill_wgs) {
+      build_wave<1>(a.fb, lds.b[wave], (long long)lid * 4 + wave, lane);
+      return false;
+    }
+    lid -= a.fill_wgs;
+    bx = lid % a.gx;
+    lid /= a.gx;
+    by = lid % a.Hkv;
+    bz = lid / a.Hkv;
+  }
+  return true;
+}
 
 __device__ __forceinline__ int nib_lo(uint32_t x) { return (int)((x << 4) & 0xF0F0F0F0u); }
 __device__ __forceinline__ int nib_hi(uint32_t x) { return (int)(x & 0xF0F0F0F0u); }
@@ -272,30 +313,33 @@ struct TileRec {
 // per wave, four per workgroup) or, for grids that would leave SIMDs idle,
 // 16 (a range over four waves). 8-head waves are held to 128 VGPRs (4 waves
 // per SIMD; left alone they take a few more and drop to 3).
-template <int G, int P>
+template <int G, int P, bool Fill>
 __global__ __launch_bounds__(256, G == 8 ? 4 : 1) void score_kernel(ScoreArgs a) {
   static_assert(G <= 8, "16-head groups use score16_kernel");
   constexpr int RB = G < 4 ? 1 : G / 4;   // stage-1 row blocks (4 heads each)
   constexpr int PG = 16 / G;              // pages per stage-2 pass
   constexpr int W = kScorePagesPerWave / P;  // waves per range
   constexpr int TPW = P / 16;                // tiles per wave
-  __shared__ ScoreLds<G, TileLds<G, P>> S;
+  __shared__ KernelLds<ScoreLds<G, TileLds<G, P>>, Fill> U;
+  auto& S = U.s;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = lane & 15, kg = lane >> 4;
-  const int b = blockIdx.z;
-  const int kvh = blockIdx.y;
-  const int range = blockIdx.x * (4 / W) + wave / W;
+  int bx, by, bz;
+  if (!score_workgroup<Fill>(a, U, wave, lane, bx, by, bz)) return;  // workgroup-uniform
+  const int b = bz;
+  const int kvh = by;
+  const int range = bx * (4 / W) + wave / W;
   const int part = wave % W;  // the wave's part of its range
   const int hbase = kvh * G;  // first query head of the group
   const int N = a.N;
-  const int n_b = full_pages(a.seq_lens, b, N);
+  const int n_b = full_pages(a.seq_lens, a.fill, b, N);
   TileLds<G, P>& T = S.w[wave];
   const int p0 = range * kScorePagesPerWave + part * P;
 
   // A range wholly past the sequence's full pages (shorter sequences of a
   // batch) has no work and writes nothing (its partials are never read);
   // the whole workgroup leaves at once when none of its ranges has a page.
-  if (blockIdx.x * (4 / W) * kScorePagesPerWave >= n_b) return;  // workgroup-uniform
+  if (bx * (4 / W) * kScorePagesPerWave >= n_b) return;  // workgroup-uniform
 
   // page table of this wave's P pages, one entry per lane; issued first, so
   // its latency overlaps the q prologue below
@@ -576,26 +620,29 @@ struct Score16Lds {
   float esc[16];                            // per head: 2^-e log2(e) / sqrt(128)
 };
 
-template <int PPW>
+template <int PPW, bool Fill>
 __global__ __launch_bounds__(256, 4) void score16_kernel(ScoreArgs a) {
   constexpr int G = 16;
   constexpr int k16PagesPerWave = PPW;
   constexpr int k16Tiles = PPW / 16;
   constexpr int k16WavesPerRange = kScorePagesPerWave / PPW;  // 2 or 4
   constexpr int k16RangesPerWg = 4 / k16WavesPerRange;
-  __shared__ Score16Lds<PPW> S;
+  __shared__ KernelLds<Score16Lds<PPW>, Fill> U;
+  auto& S = U.s;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = lane & 15, kg = lane >> 4;
-  const int b = blockIdx.z;
-  const int kvh = blockIdx.y;
-  const int range = blockIdx.x * k16RangesPerWg + wave / k16WavesPerRange;
+  int bx, by, bz;
+  if (!score_workgroup<Fill>(a, U, wave, lane, bx, by, bz)) return;  // workgroup-uniform
+  const int b = bz;
+  const int kvh = by;
+  const int range = bx * k16RangesPerWg + wave / k16WavesPerRange;
   const int half = wave % k16WavesPerRange;  // the wave's part of its range
   const int hbase = kvh * G;
   const int N = a.N;
-  const int n_b = full_pages(a.seq_lens, b, N);
+  const int n_b = full_pages(a.seq_lens, a.fill, b, N);
   const int p0 = range * kScorePagesPerWave + half * k16PagesPerWave;  // the wave's first page
 
-  if (blockIdx.x * k16RangesPerWg * kScorePagesPerWave >= n_b) return;  // workgroup-uniform
+  if (bx * k16RangesPerWg * kScorePagesPerWave >= n_b) return;  // workgroup-uniform
 
   // A wave past the ranges or the sequence's full pages has no work but still
   // reaches the workgroup barriers below (no wave returns after this point).
@@ -842,14 +889,30 @@ __global__ __launch_bounds__(256, 4) void score16_kernel(ScoreArgs a) {
   }
 }
 
+// Launches kernel K over grid (gx, Hkv, B); with a fill, as a 1-D grid whose
+// first workgroups build the records of the pages that filled in this step.
+template <class K>
+void launch_scorer(K kernel, K fill_kernel, ScoreArgs& a, const locks_dims& d, int gx, hipStream_t s) {
+  if (!a.fill) {
+    hipLaunchKernelGGL(kernel, dim3(gx, d.n_kv_heads, d.batch), dim3(256), 0, s, a);
+    return;
+  }
+  a.gx = gx;
+  a.fill_wgs = (int)((a.fb.items + 3) / 4);  // one page-head per wave
+  const long long wgs = (long long)a.fill_wgs + (long long)gx * d.n_kv_heads * d.batch;
+  hipLaunchKernelGGL(fill_kernel, dim3((unsigned)wgs), dim3(256), 0, s, a);
+}
+
 template <int G>
 hipError_t launch_g(const locks_dims& d, const WsLayout& L, const DevPtrs& P, const float* q,
-                    const uint8_t* summ, const int32_t* pt, const int32_t* sl, hipStream_t s) {
+                    const uint8_t* summ, const int32_t* pt, const int32_t* sl, const int32_t* fill,
+                    const uint16_t* kc, hipStream_t s) {
   ScoreArgs a;
   a.q = q;
   a.summ = summ;
   a.page_table = pt;
   a.seq_lens = sl;
+  a.fill = fill;
   a.scores = P.scores;
   a.partials = P.score_part;
   a.tile_max = P.tile_max;
@@ -859,29 +922,38 @@ hipError_t launch_g(const locks_dims& d, const WsLayout& L, const DevPtrs& P, co
   a.N = d.max_pages_per_seq;
   a.num_blocks = d.num_blocks;
   a.n_ranges = L.n_score_wg;
+  a.fill_wgs = 0;
+  a.gx = 0;
+  a.fb.kc = kc;
+  a.fb.page_table = pt;
+  a.fb.seq_lens = sl;
+  a.fb.blocks = nullptr;
+  a.fb.fill = fill;
+  // the records of the pages that filled are written by this launch and read
+  // by none of its scoring workgroups (those pages are not scored this step)
+  a.fb.summ = const_cast<uint8_t*>(summ);
+  a.fb.B = d.batch;
+  a.fb.Hkv = d.n_kv_heads;
+  a.fb.N = d.max_pages_per_seq;
+  a.fb.num_blocks = d.num_blocks;
+  a.fb.items = (long long)d.batch * d.n_kv_heads;
   if constexpr (G == 16) {
     // 32 pages per wave (two ranges per workgroup); 16 (one range per
     // workgroup) when that grid still fits one round of resident waves
-    if ((long long)d.batch * d.n_kv_heads * L.n_score_wg * 4 <= kScoreRoundWaves) {
-      const dim3 grid(L.n_score_wg, d.n_kv_heads, d.batch);
-      hipLaunchKernelGGL(score16_kernel<16>, grid, dim3(256), 0, s, a);
-    } else {
-      const dim3 grid((L.n_score_wg + 1) / 2, d.n_kv_heads, d.batch);
-      hipLaunchKernelGGL(score16_kernel<32>, grid, dim3(256), 0, s, a);
-    }
+    if ((long long)d.batch * d.n_kv_heads * L.n_score_wg * 4 <= kScoreRoundWaves)
+      launch_scorer(score16_kernel<16, false>, score16_kernel<16, true>, a, d, L.n_score_wg, s);
+    else
+      launch_scorer(score16_kernel<32, false>, score16_kernel<32, true>, a, d, (L.n_score_wg + 1) / 2, s);
   } else {
     // 64 pages per wave (four ranges per workgroup); 16 (a range over four
     // waves) when that grid still fits one round of resident waves: four
     // times the waves to hide latency with where the 64-page grid leaves a
     // SIMD one wave or none
     const long long units = (long long)d.batch * d.n_kv_heads * L.n_score_wg;  // (seq, KV head, range)
-    if (units * 4 <= kScoreRoundWaves) {
-      const dim3 grid(L.n_score_wg, d.n_kv_heads, d.batch);
-      hipLaunchKernelGGL((score_kernel<G, 16>), grid, dim3(256), 0, s, a);
-    } else {
-      const dim3 grid((L.n_score_wg + 3) / 4, d.n_kv_heads, d.batch);
-      hipLaunchKernelGGL((score_kernel<G, 64>), grid, dim3(256), 0, s, a);
-    }
+    if (units * 4 <= kScoreRoundWaves)
+      launch_scorer(score_kernel<G, 16, false>, score_kernel<G, 16, true>, a, d, L.n_score_wg, s);
+    else
+      launch_scorer(score_kernel<G, 64, false>, score_kernel<G, 64, true>, a, d, (L.n_score_wg + 3) / 4, s);
   }
   return hipGetLastError();
 }
@@ -889,13 +961,14 @@ hipError_t launch_g(const locks_dims& d, const WsLayout& L, const DevPtrs& P, co
 }  // namespace
 
 hipError_t launch_score(const locks_dims& d, const WsLayout& L, const DevPtrs& P, const float* q,
-                        const uint8_t* summ, const int32_t* pt, const int32_t* sl, hipStream_t s) {
+                        const uint8_t* summ, const int32_t* pt, const int32_t* sl,
+                        const int32_t* fill, const uint16_t* kc, hipStream_t s) {
   switch (d.n_q_heads / d.n_kv_heads) {
-    case 1: return launch_g<1>(d, L, P, q, summ, pt, sl, s);
-    case 2: return launch_g<2>(d, L, P, q, summ, pt, sl, s);
-    case 4: return launch_g<4>(d, L, P, q, summ, pt, sl, s);
-    case 8: return launch_g<8>(d, L, P, q, summ, pt, sl, s);
-    case 16: return launch_g<16>(d, L, P, q, summ, pt, sl, s);
+    case 1: return launch_g<1>(d, L, P, q, summ, pt, sl, fill, kc, s);
+    case 2: return launch_g<2>(d, L, P, q, summ, pt, sl, fill, kc, s);
+    case 4: return launch_g<4>(d, L, P, q, summ, pt, sl, fill, kc, s);
+    case 8: return launch_g<8>(d, L, P, q, summ, pt, sl, fill, kc, s);
+    case 16: return launch_g<16>(d, L, P, q, summ, pt, sl, fill, kc, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -56,6 +56,7 @@ struct SelectArgs {
   const float* tile_max;
   const int32_t* page_table;
   const int32_t* seq_lens;
+  const int32_t* fill;  // nullable: pages that filled in this step (attended as the tail)
   unsigned long long* cand;
   int32_t* cand_blk;
   int32_t* cand_count;
@@ -197,7 +198,7 @@ __global__ __launch_bounds__(kThreads) void select_chunk_kernel(SelectArgs a) {
   const int chunk = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int N = a.N, nt = a.n_tiles;
-  const int n_b = full_pages(a.seq_lens, b, N);
+  const int n_b = full_pages(a.seq_lens, a.fill, b, N);
   // bound units of this sequence: 16-page tiles when it has fewer than 2k
   // ranges (a bound over so few units prunes little; the scoring pass wrote
   // tile maxima exactly for such sequences), else 64-page ranges; only the
@@ -981,13 +982,15 @@ __global__ __launch_bounds__(kMergeThreads) void select_merge_kernel(SelectArgs 
 }  // namespace
 
 hipError_t launch_select(const locks_dims& d, const WsLayout& L, const DevPtrs& P,
-                         const int32_t* pt, const int32_t* sl, int32_t* selected, hipStream_t s) {
+                         const int32_t* pt, const int32_t* sl, const int32_t* fill,
+                         int32_t* selected, hipStream_t s) {
   SelectArgs a;
   a.scores = P.scores;
   a.score_part = P.score_part;
   a.tile_max = P.tile_max;
   a.page_table = pt;
   a.seq_lens = sl;
+  a.fill = fill;
   a.cand = P.cand;
   a.cand_blk = P.cand_blk;
   a.cand_count = P.cand_count;

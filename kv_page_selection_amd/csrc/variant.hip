@@ -80,7 +80,7 @@ __global__ __launch_bounds__(64) void score_variant_kernel(VarArgs a) {
   const int range = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x;
   const int N = a.N;
-  const int n_b = full_pages(a.seq_lens, b, N);
+  const int n_b = full_pages(a.seq_lens, nullptr, b, N);
   if (range * 64 >= n_b) return;  // nothing of the sequence here (partials not read)
   __shared__ float qs[G][kDim];
   {

@@ -375,3 +375,34 @@ def decode_step(q, summaries, k_cache_bits, v_cache_bits, page_table, seq_lens,
                              _ptr(pt), _ptr(_as(seq_lens, np.int32)), budget_tokens, _ptr(out),
                              _ptr(sel), _ptr(sc), _ptr(ky))
     return out, sel, sc, ky
+
+
+def decode_step_fill(q, summaries, k_cache_bits, v_cache_bits, page_table, seq_lens,
+                     budget_tokens: int, filled):
+    """Decode step in which the sequences marked by filled[b] != 0 (with a
+    length that is a positive multiple of 16) have just filled their last
+    page, page n_b - 1, whose summary is not built yet (A "How LOCKS works": a
+    summary is built once, when its page fills; B mechanism 4: building stays
+    off the decode critical path). Reading: that page is treated as the
+    newest, summary-less page, like a partly filled tail: never scored or
+    selected, all 16 of its tokens attended. Composed from the pinned steps:
+    scores over the first n_b - 1 pages, group keys, top-k, then attention
+    over the kept pages plus page n_b - 1. Returns (out, selected, scores,
+    keys) as decode_step does."""
+    q = _as(q, np.float32)
+    pt = _as(page_table, np.int32)
+    sl = _as(seq_lens, np.int32)
+    filled = np.asarray(filled).ravel()
+    B, N = pt.shape
+    hkv = np.asarray(k_cache_bits).shape[1]
+    n_full = np.minimum(np.maximum(sl // PAGE, 0), N)
+    held = (filled != 0) & (n_full > 0) & (sl == PAGE * n_full)
+    sl_scored = np.where(held, sl - PAGE, sl).astype(np.int32)
+    sc = scores(q, summaries, pt, sl_scored, hkv)
+    ky = group_keys(sc, hkv)
+    k = budget_tokens // PAGE
+    sel = select(ky, k)
+    extra = np.where(held, n_full - 1, -1).astype(np.int32)
+    listed = np.concatenate([sel, np.repeat(extra[:, None, None], hkv, axis=1)], axis=2)
+    out = attention(q, k_cache_bits, v_cache_bits, pt, sl, listed)
+    return out, sel, sc, ky

@@ -122,15 +122,24 @@ def test_full_size_build_glm_layer(locks):
     torch.cuda.empty_cache()
 
 
-def test_build_blocks_matches_whole_cache_build(locks):
+@pytest.mark.parametrize("case", [dict(ctx=16 * 200, batch=2, seed=9),
+                                  dict(ctx=16 * 601, batch=4, seed=61,
+                                       seq_lens=[16 * 600, 16 * 411 + 7, 16 * 350, 16 * 200])],
+                         ids=["b2", "b4-ragged"])
+def test_build_blocks_matches_whole_cache_build(locks, case):
     """Rebuilding a block list (pages that just filled) writes exactly the
     records the whole-cache build writes for those blocks and nothing else;
-    a build made only from block lists meets the oracle bars."""
-    w = workloads.make(2, device=DEV, ctx=16 * 200, batch=2, seed=9)
+    a build made only from block lists meets the oracle bars. Short lists run
+    one page per wave, the whole cache four: a page that converges before the
+    others of its wave stops rotating there, so both give the same bytes (the
+    second case holds a page that converges sweeps before its wave-mates)."""
+    w = workloads.make(2, device=DEV, **case)
     full = locks.build_summaries(w.k_cache, w.page_table, w.seq_lens)
     pt = w.page_table.cpu().numpy()
     stale = torch.full_like(full, 0xAB)
     listed = [int(pt[1, 7]), -1, int(pt[0, 0]), w.num_blocks, int(pt[1, 7]), int(pt[0, 199])]
+    if w.batch > 2:
+        listed += [int(pt[0, 599]), int(pt[2, 349])]
     locks.build_blocks(w.k_cache, torch.tensor(listed, dtype=torch.int32, device=DEV), stale)
     torch.cuda.synchronize()
     f, g = full.cpu().numpy(), stale.cpu().numpy()
@@ -141,7 +150,9 @@ def test_build_blocks_matches_whole_cache_build(locks):
             assert np.all(g[blk] == 0xAB), blk
     # every page built through block lists of 64, one list per page fill
     fresh = torch.zeros_like(full)
-    order = torch.from_numpy(pt.T.reshape(-1).copy()).to(DEV)
+    sl = w.seq_lens.cpu().numpy()
+    full_pages = [pt[b, j] for j in range(w.max_pages) for b in range(w.batch) if j < sl[b] // 16]
+    order = torch.tensor(full_pages, dtype=torch.int32, device=DEV)
     for i in range(0, order.numel(), 64):
         locks.build_blocks(w.k_cache, order[i:i + 64].contiguous(), fresh)
     torch.cuda.synchronize()

@@ -679,3 +679,39 @@ def test_variant_score_driver_is_the_lse_of_reconstructed_keys(orc, r, vb):
                 mu, V, C, _, _ = decode_variant_numpy(summ[blk, h // G], r, vb)
                 want = exact_lse(q[b, h].astype(np.float64), mu[None, :] + C @ V.T)
                 assert abs(sc[b, h, j] - want) <= 1e-9, (b, h, j, sc[b, h, j], want)
+
+
+# ------------------------------------------ step with a page that just filled
+
+def test_fill_step_attends_the_new_page_in_full_and_never_scores_it(orc):
+    """(A "How LOCKS works": a page's summary is built once, when it fills; B
+    mechanism 4: off the decode critical path.) Reading: in the step where a
+    sequence's last page fills, that page has no summary yet and is attended
+    like a tail. Pins: its score is -inf and it is never selected; an unmarked
+    sequence gets exactly the plain step; at a full budget the output is
+    torch's SDPA over every token of the sequence; and at a small budget it is
+    SDPA over the kept pages plus all 16 tokens of the new page."""
+    r = rng(81)
+    B, Hq, Hkv, N, k = 3, 4, 2, 12, 3
+    kb, kd, vb, vd, pt, q = oracle_inputs(r, B, Hq, Hkv, N)
+    lens = np.array([N * PAGE, 9 * PAGE, 7 * PAGE + 5], dtype=np.int32)
+    fill = np.array([1, 0, 1], dtype=np.int32)  # the third: length not a multiple of 16
+    summ = orc.build_summaries(kb, pt, lens)
+    out, sel, sc, ky = orc.decode_step_fill(q, summ, kb, vb, pt, lens, k * PAGE, fill)
+    ref = orc.decode_step(q, summ, kb, vb, pt, lens, k * PAGE)
+    for b in (1, 2):  # unmarked, and marked but mid-page: the plain step
+        assert np.array_equal(sel[b], ref[1][b]) and np.array_equal(out[b], ref[0][b])
+    assert np.all(np.isneginf(sc[0, :, N - 1])) and np.all(np.isfinite(sc[0, :, : N - 1]))
+    assert not np.any(sel[0] == N - 1)
+    G = Hq // Hkv
+    for h in range(Hq):  # kept pages plus the whole new page, through SDPA
+        pages = sorted(sel[0, h // G].tolist()) + [N - 1]
+        want = sdpa_ref(q[0, h].astype(np.float64), kd[pt[0, pages], h // G].reshape(-1, DIM),
+                        vd[pt[0, pages], h // G].reshape(-1, DIM))
+        assert np.allclose(out[0, h], want, atol=1e-12)
+    full, fsel, _, _ = orc.decode_step_fill(q, summ, kb, vb, pt, lens, N * PAGE, fill)
+    assert list(fsel[0, 0, : N - 1]) == list(range(N - 1)) and np.all(fsel[0, :, N - 1:] == -1)
+    for h in range(Hq):
+        keys = kd[pt[0], h // G].reshape(-1, DIM)
+        vals = vd[pt[0], h // G].reshape(-1, DIM)
+        assert np.allclose(full[0, h], sdpa_ref(q[0, h].astype(np.float64), keys, vals), atol=1e-12)
