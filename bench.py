@@ -729,8 +729,91 @@ def ablation(args):
         torch.cuda.empty_cache()
 
 
+def prop1(args):
+    """Shared-basis comparison (not the default line; Proposition 1 of the
+    pages: a fixed shared projection is blind to page content in its null
+    space). On the blind-direction workload (every page varies in one common
+    8-dim basis S, one planted carrier per sequence varies along the group's
+    mean query outside S), per budget and selector: carrier retention,
+    coverage of the exact selection's group mass, recall, and the scoring
+    time. Selectors: LOCKS as shipped (int4/int8 rank 8), LOCKS rank 8 with
+    fp16 values, the shared-basis selector (W = S, the sequence's top-8
+    deviation subspace, fp16 records, same score form), and the exact-mass
+    selector. One JSON line each."""
+    import numpy as np
+    import torch
+
+    import kv_page_selection_amd as locks
+    import workloads
+
+    dev = torch.device("cuda:0")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, n=5):
+        fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n
+
+    budgets = [int(x) for x in args.prop1.split(",")]
+    w = workloads.make(2, device=dev, ctx=args.ctx, batch=args.batch, budget=max(budgets),
+                       keys="shared")
+    print(f"[prop1] {w.recipe}", file=sys.stderr, flush=True)
+    B, Hq, Hkv, N = w.batch, w.n_q_heads, w.n_kv_heads, w.max_pages
+    records = {
+        "locks_int4": locks.build_summaries(w.k_cache, w.page_table, w.seq_lens),
+        "locks_fp16": locks.build_summaries_variant(w.k_cache, w.page_table, w.seq_lens, 8, 16),
+        "shared_fp16": locks.build_summaries_shared(w.k_cache, w.page_table, w.seq_lens,
+                                                    w.shared_basis.contiguous()),
+    }
+    for budget in budgets:
+        k = budget // 16
+        ws = locks.new_workspace(locks.make_dims(w.q, w.k_cache, w.page_table), budget, dev)
+        ex_scores = torch.empty(B, Hq, N, device=dev)
+        ex_sel = torch.empty(B, Hkv, k, dtype=torch.int32, device=dev)
+        ex_score = lambda: locks.exact_score_pages(w.q, w.k_cache, w.page_table, w.seq_lens,
+                                                   budget, ws, page_scores=ex_scores)
+        ex_us = timed(ex_score)
+        ex_score()
+        locks.select_pages(w.q, w.k_cache, w.page_table, w.seq_lens, budget, ex_sel, ws,
+                           page_scores=ex_scores)
+        sel = torch.empty_like(ex_sel)
+        for name, summ in list(records.items()) + [("exact", None)]:
+            if name == "locks_int4":
+                score = lambda: locks.score_pages(w.q, summ, w.k_cache, w.page_table, w.seq_lens,
+                                                  budget, ws)
+            elif name == "exact":
+                score = lambda: locks.exact_score_pages(w.q, w.k_cache, w.page_table, w.seq_lens,
+                                                        budget, ws)
+            else:
+                score = lambda: locks.score_pages_variant(w.q, summ, w.k_cache, w.page_table,
+                                                          w.seq_lens, budget, 8, 16, ws)
+            us = ex_us if name == "exact" else timed(score)
+            score()
+            locks.select_pages(w.q, w.k_cache, w.page_table, w.seq_lens, budget, sel, ws)
+            torch.cuda.synchronize()
+            line = {"mode": "prop1", "workload": w.recipe, "budget_tokens": budget,
+                    "selector": name, "score_us": round(us, 1),
+                    "record_bytes": (None if summ is None else int(summ.shape[2]))}
+            line.update(selection_quality(locks, w, sel, ex_sel, ex_scores))
+            print(json.dumps(line), flush=True)
+        del ws, ex_scores, ex_sel, sel
+        torch.cuda.empty_cache()
+
+
 if __name__ == "__main__":
-    if "--ablation" in sys.argv:
+    if "--prop1" in sys.argv:
+        ap = argparse.ArgumentParser()
+        ap.add_argument("--prop1", default="512,2048",
+                        help="comma-separated token budgets (shared-basis comparison)")
+        ap.add_argument("--ctx", type=int, default=131072)
+        ap.add_argument("--batch", type=int, default=8)
+        prop1(ap.parse_args())
+    elif "--ablation" in sys.argv:
         ap = argparse.ArgumentParser()
         ap.add_argument("--ablation", default="3:2048,3:512,4:512",
                         help="comma-separated config:budget workloads (precision / rank ablation)")

@@ -218,6 +218,23 @@ locks_status locks_score_pages_variant(const locks_dims* dims, const float* q, c
                                        float* page_scores, void* workspace,
                                        size_t workspace_bytes, hipStream_t stream);
 
+/* Shared-basis comparison (A "Why shared-basis sparse attention is
+ * structurally broken"; B section 3, Proposition 1: a fixed projection shared
+ * by all pages is blind to page content in its null space). Writes, for every
+ * full page, the record a shared-basis selector scores with, in the LOCKS
+ * page-score form: centroid mu = mean of the page's 16 keys, coefficients
+ * C = (K - 1 mu^T) W, V = W, where W = basis[b][kvh] is the one 128 x 8
+ * projection of sequence b and KV head kvh (row-major [d][k], f32, 16-byte
+ * aligned; the caller builds it, e.g. from the sequence's keys). Records use
+ * the variant layout at rank 8 with fp16 values (locks_variant_record_bytes(8,
+ * 16) bytes each), so locks_score_pages_variant(rank 8, v_bits 16) scores them
+ * and locks_select_pages / locks_sparse_attention follow unchanged. A
+ * measurement path, not a decode path. */
+locks_status locks_build_summaries_shared(const locks_dims* dims, const void* k_cache,
+                                          const int32_t* page_table, const int32_t* seq_lens,
+                                          const float* basis, void* summaries,
+                                          hipStream_t stream);
+
 /* Phase 2: group combine (B mechanism 3: every head's mass share averaged over
  * the GQA group) and top-k (A "Code": top-k by score, ids sorted ascending).
  * Ties between equal keys go to the lower page id. Must follow

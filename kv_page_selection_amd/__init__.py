@@ -68,6 +68,7 @@ def lib() -> ctypes.CDLL:
         L.locks_variant_record_bytes.argtypes = [I, I, ctypes.POINTER(S)]
         L.locks_build_summaries_variant.argtypes = [D, P, P, P, I, I, P, P]
         L.locks_score_pages_variant.argtypes = [D, P, P, P, P, I, I, I, P, P, S, P]
+        L.locks_build_summaries_shared.argtypes = [D, P, P, P, P, P, P]
         L.locks_select_pages.argtypes = [D, P, P, I, P, P, P, S, P]
         L.locks_sparse_attention.argtypes = [D, P, P, P, P, P, I, P, P, P, S, P]
         L.locks_dense_attention.argtypes = [D, P, P, P, P, P, P, P, S, P]
@@ -75,7 +76,7 @@ def lib() -> ctypes.CDLL:
                      "locks_decode_step", "locks_decode_step_noalloc", "locks_decode_step_fill",
                      "locks_score_pages", "locks_exact_score_pages", "locks_select_pages",
                      "locks_variant_record_bytes", "locks_build_summaries_variant",
-                     "locks_score_pages_variant",
+                     "locks_score_pages_variant", "locks_build_summaries_shared",
                      "locks_sparse_attention",
                      "locks_dense_attention"):
             getattr(L, name).restype = ctypes.c_int
@@ -337,6 +338,26 @@ def build_summaries_variant(k_cache, page_table, seq_lens, rank: int, v_bits: in
     _check(lib().locks_build_summaries_variant(ctypes.byref(dims), _ptr(k_cache), _ptr(page_table),
                                                _ptr(seq_lens), rank, v_bits, _ptr(summaries),
                                                _stream(dev)))
+    return summaries
+
+
+def build_summaries_shared(k_cache, page_table, seq_lens, basis, summaries=None):
+    """Shared-basis comparison records [num_blocks, Hkv, variant_record_bytes(8, 16)]
+    of every full page under basis [B, Hkv, 128, 8] (f32): mu, C = (K - mu) W,
+    V = W as fp16 values; score them with score_pages_variant(rank=8, v_bits=16)."""
+    B, _, hkv, N, nb = _check_common(None, k_cache, page_table, seq_lens)
+    _tensor(basis, "basis", torch.float32, (B, hkv, HEAD_DIM, RANK))
+    nbytes = variant_record_bytes(RANK, 16)
+    if summaries is not None:
+        _tensor(summaries, "summaries", torch.uint8, (nb, hkv, nbytes))
+    dev = _devices(dict(k_cache=k_cache, page_table=page_table, seq_lens=seq_lens, basis=basis,
+                        summaries=summaries))
+    dims = Dims(B, hkv, hkv, HEAD_DIM, PAGE_SIZE, RANK, N, nb)
+    if summaries is None:
+        summaries = torch.zeros(nb, hkv, nbytes, dtype=torch.uint8, device=dev)
+    _check(lib().locks_build_summaries_shared(ctypes.byref(dims), _ptr(k_cache), _ptr(page_table),
+                                              _ptr(seq_lens), _ptr(basis), _ptr(summaries),
+                                              _stream(dev)))
     return summaries
 
 

@@ -17,7 +17,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "liblocks.so")
-SOURCES = ["api.hip", "score.hip", "select.hip", "attend.hip", "build.hip", "exact.hip", "variant.hip"]
+SOURCES = ["api.hip", "score.hip", "select.hip", "attend.hip", "build.hip", "exact.hip", "variant.hip",
+           "shared.hip"]
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall",

@@ -407,6 +407,27 @@ locks_status locks_build_summaries_variant(const locks_dims* dims, const void* k
                     "variant build launch");
 }
 
+locks_status locks_build_summaries_shared(const locks_dims* dims, const void* k_cache,
+                                          const int32_t* page_table, const int32_t* seq_lens,
+                                          const float* basis, void* summaries,
+                                          hipStream_t stream) {
+  g_err.clear();
+  LOCKS_TRY(check_dims(dims));
+  LOCKS_TRY(need(k_cache, 16, "k_cache"));
+  LOCKS_TRY(need(page_table, 4, "page_table"));
+  LOCKS_TRY(need(seq_lens, 4, "seq_lens"));
+  LOCKS_TRY(need(basis, 16, "basis"));
+  LOCKS_TRY(need(summaries, 16, "summaries"));
+  if ((long long)dims->batch * dims->max_pages_per_seq * dims->n_kv_heads > (1LL << 35))
+    return fail(LOCKS_ERR_UNSUPPORTED, "batch * max_pages_per_seq * n_kv_heads above 2^35");
+  if ((unsigned long long)dims->num_blocks * dims->n_kv_heads * shared_record_bytes() > (1ULL << 40))
+    return fail(LOCKS_ERR_UNSUPPORTED, "shared-basis records above 1 TiB");
+  (void)hipGetLastError();
+  return hip_status(launch_build_shared(*dims, static_cast<const uint16_t*>(k_cache), page_table,
+                                        seq_lens, basis, static_cast<uint8_t*>(summaries), stream),
+                    "shared-basis build launch");
+}
+
 locks_status locks_score_pages_variant(const locks_dims* dims, const float* q, const void* summaries,
                                        const int32_t* page_table, const int32_t* seq_lens,
                                        int32_t budget_tokens, int32_t rank, int32_t v_bits,

@@ -90,6 +90,12 @@ hipError_t launch_attend(const locks_dims& d, const WsLayout& L, const DevPtrs& 
                          const uint16_t* kc, const uint16_t* vc, const int32_t* page_table,
                          const int32_t* seq_lens, const int32_t* fill, const int32_t* selected,
                          const int32_t* selected_blocks, float* out, bool dense, hipStream_t s);
+// Shared-basis comparison records (variant layout, rank 8, fp16 values) of
+// every full page, under basis [B][Hkv][128][8].
+size_t shared_record_bytes();
+hipError_t launch_build_shared(const locks_dims& d, const uint16_t* kc, const int32_t* page_table,
+                               const int32_t* seq_lens, const float* basis, uint8_t* summ,
+                               hipStream_t s);
 // Whole cache (blocks == nullptr: every full page through the page table) or
 // the n_blocks listed blocks, every KV head of each.
 hipError_t launch_build(const locks_dims& d, const uint16_t* kc, const int32_t* page_table,

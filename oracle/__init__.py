@@ -102,6 +102,12 @@ def lib() -> ctypes.CDLL:
         L.oracle_build_summaries_variant.restype = None
         L.oracle_scores_variant.argtypes = [I, I, I, I, I, P, P, I, I, P, P, P]
         L.oracle_scores_variant.restype = None
+        L.oracle_build_record_shared.argtypes = [P, P, I, P]
+        L.oracle_build_record_shared.restype = None
+        L.oracle_build_summaries_shared.argtypes = [I, I, I, I, P, P, P, P, I, P]
+        L.oracle_build_summaries_shared.restype = None
+        L.oracle_shared_basis.argtypes = [I, I, I, I, P, P, P, I, P]
+        L.oracle_shared_basis.restype = None
         L.oracle_num_threads.argtypes = []
         L.oracle_num_threads.restype = I
         _lib = L
@@ -275,6 +281,52 @@ def scores_variant(q, summaries, page_table, seq_lens, num_kv_heads: int, rank: 
     out = np.zeros((B, Hq, pt.shape[1]))
     lib().oracle_scores_variant(B, Hq, num_kv_heads, pt.shape[1], sm.shape[0], _ptr(q), _ptr(sm),
                                 rank, vbits, _ptr(pt), _ptr(_as(seq_lens, np.int32)), _ptr(out))
+    return out
+
+
+# ------------------ shared-basis comparison (Proposition 1: blind directions)
+
+def build_record_shared(keys_bf16: np.ndarray, W: np.ndarray) -> np.ndarray:
+    """Record of one page under a fixed shared basis W [128, r]: mu = the keys'
+    mean, C = (K - mu) W, V = W, in the variant layout with fp16 values
+    (rank r, v_bits 16), so that scores_variant scores it (A "Why shared-basis
+    sparse attention is structurally broken"; B section 3, Proposition 1)."""
+    kb = _as(keys_bf16, np.uint16)
+    W = _as(W, np.float64)
+    r = W.shape[1]
+    assert kb.shape == (PAGE, DIM) and W.shape == (DIM, r)
+    rec = np.zeros(variant_record_bytes(r, 16), dtype=np.uint8)
+    lib().oracle_build_record_shared(_ptr(kb), _ptr(W), r, _ptr(rec))
+    return rec
+
+
+def build_summaries_shared(k_cache_bits, page_table, seq_lens, basis,
+                           summaries: np.ndarray | None = None) -> np.ndarray:
+    """Shared-basis records of every full page; basis [B, Hkv, 128, r] holds
+    each (sequence, KV head)'s fixed projection."""
+    kc = _as(k_cache_bits, np.uint16)
+    nb, hkv = kc.shape[0], kc.shape[1]
+    pt = _as(page_table, np.int32)
+    basis = _as(basis, np.float64)
+    r = basis.shape[-1]
+    if summaries is None:
+        summaries = np.zeros((nb, hkv, variant_record_bytes(r, 16)), dtype=np.uint8)
+    lib().oracle_build_summaries_shared(pt.shape[0], hkv, pt.shape[1], nb, _ptr(kc), _ptr(pt),
+                                        _ptr(_as(seq_lens, np.int32)), _ptr(basis), r,
+                                        _ptr(summaries))
+    return summaries
+
+
+def shared_basis(k_cache_bits, page_table, seq_lens, rank: int = RANK) -> np.ndarray:
+    """[B, Hkv, 128, rank]: per (sequence, KV head), the top eigenvectors of the
+    pooled within-page deviation scatter over the sequence's full pages (the
+    one projection a sequence-level selector shares across pages)."""
+    kc = _as(k_cache_bits, np.uint16)
+    nb, hkv = kc.shape[0], kc.shape[1]
+    pt = _as(page_table, np.int32)
+    out = np.zeros((pt.shape[0], hkv, DIM, rank))
+    lib().oracle_shared_basis(pt.shape[0], hkv, pt.shape[1], nb, _ptr(kc), _ptr(pt),
+                              _ptr(_as(seq_lens, np.int32)), rank, _ptr(out))
     return out
 
 

@@ -415,6 +415,128 @@ void oracle_build_summaries_variant(int B, int Hkv, int max_pages, int num_block
   }
 }
 
+/* ------------------------------------------------------------------ */
+/* The shared-basis comparison of Proposition 1 (A "Why shared-basis    */
+/* sparse attention is structurally broken"; B section 3 theory): a     */
+/* selector that scores pages through one fixed projection W shared by */
+/* all pages of a sequence, in the same page-score form as LOCKS.       */
+/* ------------------------------------------------------------------ */
+
+/* Record of one page under a fixed shared basis W (128 x r, row-major
+ * [d][k]): centroid mu = mean of the 16 keys, coefficients C = (K - 1 mu^T) W
+ * (the deviations projected onto W), V = W. Stored in the variant layout with
+ * fp16 values (v_bits 16, scales 1.0), so the variant score reads it. */
+void oracle_build_record_shared(const uint16_t* keys_bf16, const double* W, int r, uint8_t* rec) {
+  double keys[OP * OD], mu[OD], C[OP * 16];
+  for (int i = 0; i < OP * OD; i++) keys[i] = oracle_bf16_to_double(keys_bf16[i]);
+  for (int d = 0; d < OD; d++) {
+    double m = 0;
+    for (int i = 0; i < OP; i++) m += keys[i * OD + d];
+    mu[d] = m / OP;
+  }
+  for (int i = 0; i < OP; i++)
+    for (int k = 0; k < r; k++) {
+      double c = 0;
+      for (int d = 0; d < OD; d++) c += (keys[i * OD + d] - mu[d]) * W[d * r + k];
+      C[i * r + k] = c;
+    }
+  size_t om = (size_t)OD * r * 2, oc = om + (size_t)OD * 2, os = oc + (size_t)OP * r * 2;
+  memset(rec, 0, oracle_variant_record_bytes(r, 16));
+  store_tensor(W, OD * r, 16, rec);
+  store_tensor(mu, OD, 16, rec + om);
+  store_tensor(C, OP * r, 16, rec + oc);
+  for (int t = 0; t < 3; t++) {
+    rec[os + 2 * t] = 0x00;
+    rec[os + 2 * t + 1] = 0x3C; /* fp16 1.0 */
+  }
+}
+
+/* Shared-basis records of every full page: the page's sequence b and KV head
+ * select its basis, basis[b][kvh] (128 x r, row-major). */
+void oracle_build_summaries_shared(int B, int Hkv, int max_pages, int num_blocks,
+                                   const uint16_t* k_cache, const int32_t* page_table,
+                                   const int32_t* seq_lens, const double* basis, int r,
+                                   uint8_t* summaries) {
+  size_t stride = oracle_variant_record_bytes(r, 16);
+  for (int b = 0; b < B; b++) {
+    int n = seq_lens[b] / OP;
+    if (n > max_pages) n = max_pages;
+    if (n < 0) n = 0;
+#pragma omp parallel for schedule(dynamic, 64)
+    for (int u = 0; u < n * Hkv; u++) {
+      int j = u / Hkv, kvh = u % Hkv;
+      int blk = page_table[(size_t)b * max_pages + j];
+      if (blk < 0 || blk >= num_blocks) continue;
+      const uint16_t* tile = k_cache + ((size_t)blk * Hkv + kvh) * OP * OD;
+      oracle_build_record_shared(tile, basis + ((size_t)b * Hkv + kvh) * OD * r, r,
+                                 summaries + ((size_t)blk * Hkv + kvh) * stride);
+    }
+  }
+}
+
+/* The basis a sequence-level shared projection would use: for each
+ * (sequence, KV head), the top-r eigenvectors (eigenvalues descending, ties
+ * by index) of the pooled within-page deviation scatter sum_j D_j^T D_j over
+ * the sequence's full, present pages, D_j = K_j - 1 mu_j^T. Written as
+ * basis[b][kvh] (128 x r, row-major [d][k]), each column's largest-|.|
+ * entry made positive (lowest d on ties). */
+void oracle_shared_basis(int B, int Hkv, int max_pages, int num_blocks, const uint16_t* k_cache,
+                         const int32_t* page_table, const int32_t* seq_lens, int r,
+                         double* basis) {
+  double* S = (double*)malloc(sizeof(double) * OD * OD);
+  double* U = (double*)malloc(sizeof(double) * OD * OD);
+  double w[OD];
+  for (int b = 0; b < B; b++) {
+    int n = seq_lens[b] / OP;
+    if (n > max_pages) n = max_pages;
+    if (n < 0) n = 0;
+    for (int kvh = 0; kvh < Hkv; kvh++) {
+      memset(S, 0, sizeof(double) * OD * OD);
+      for (int j = 0; j < n; j++) {
+        int blk = page_table[(size_t)b * max_pages + j];
+        if (blk < 0 || blk >= num_blocks) continue;
+        const uint16_t* tile = k_cache + ((size_t)blk * Hkv + kvh) * OP * OD;
+        double keys[OP * OD], mu[OD];
+        for (int i = 0; i < OP * OD; i++) keys[i] = oracle_bf16_to_double(tile[i]);
+        for (int d = 0; d < OD; d++) {
+          double m = 0;
+          for (int i = 0; i < OP; i++) m += keys[i * OD + d];
+          mu[d] = m / OP;
+        }
+        for (int i = 0; i < OP; i++)
+          for (int d = 0; d < OD; d++) keys[i * OD + d] -= mu[d];
+        for (int x = 0; x < OD; x++)
+          for (int y = 0; y < OD; y++) {
+            double acc = 0;
+            for (int i = 0; i < OP; i++) acc += keys[i * OD + x] * keys[i * OD + y];
+            S[x * OD + y] += acc;
+          }
+      }
+      oracle_jacobi_eigh(OD, S, w, U);
+      int order[OD];
+      for (int i = 0; i < OD; i++) order[i] = i;
+      for (int i = 1; i < OD; i++) { /* stable insertion sort, descending */
+        int v = order[i], j = i - 1;
+        while (j >= 0 && w[order[j]] < w[v]) {
+          order[j + 1] = order[j];
+          j--;
+        }
+        order[j + 1] = v;
+      }
+      double* dst = basis + ((size_t)b * Hkv + kvh) * OD * r;
+      for (int k = 0; k < r; k++) {
+        int c = order[k], arg = 0;
+        for (int d = 1; d < OD; d++)
+          if (fabs(U[d * OD + c]) > fabs(U[arg * OD + c])) arg = d;
+        double sg = U[arg * OD + c] < 0 ? -1.0 : 1.0;
+        for (int d = 0; d < OD; d++) dst[d * r + k] = sg * U[d * OD + c];
+      }
+    }
+  }
+  free(S);
+  free(U);
+}
+
 /* Summaries of every full page of every sequence; records of unreferenced
  * blocks are left untouched. */
 void oracle_build_summaries(int B, int Hkv, int max_pages, int num_blocks,

@@ -715,3 +715,96 @@ def test_fill_step_attends_the_new_page_in_full_and_never_scores_it(orc):
         keys = kd[pt[0], h // G].reshape(-1, DIM)
         vals = vd[pt[0], h // G].reshape(-1, DIM)
         assert np.allclose(full[0, h], sdpa_ref(q[0, h].astype(np.float64), keys, vals), atol=1e-12)
+
+
+# ------------------ shared-basis comparison (Proposition 1: blind directions)
+
+def test_shared_basis_is_the_top_eigenspace_of_pooled_page_deviations(orc):
+    """(B section 3: a shared basis built from the sequence.) The oracle's
+    shared basis equals numpy's eigh of the pooled within-page deviation
+    scatter, column by column (sign rule: largest-|.| entry positive)."""
+    r = rng(91)
+    B, Hkv, N = 2, 2, 12
+    kb, kd, vb, vd, pt, q = oracle_inputs(r, B, 2 * Hkv, Hkv, N, structured=False)
+    lens = np.array([N * PAGE, 9 * PAGE + 3], dtype=np.int32)
+    pt[1, 4] = -1  # an absent page is left out
+    W = orc.shared_basis(kb, pt, lens, rank=8)
+    for b in range(B):
+        for h in range(Hkv):
+            n = int(lens[b]) // PAGE
+            tiles = [kd[pt[b, j], h] for j in range(n) if pt[b, j] >= 0]
+            S = sum((t - t.mean(0)).T @ (t - t.mean(0)) for t in tiles)
+            lam, U = np.linalg.eigh(S)
+            top = U[:, ::-1][:, :8]
+            top = top * np.sign(top[np.abs(top).argmax(0), np.arange(8)])
+            assert np.allclose(W[b, h], top, atol=1e-8), (b, h)
+
+
+def test_shared_record_holds_mean_and_projected_deviations(orc):
+    """A shared-basis record (variant layout, fp16 values) decodes, by the
+    independent numpy decoder, to fp16(W), fp16(mean of the keys) and
+    fp16((K - mu) W)."""
+    r = rng(92)
+    kb, kd = bf16_round(planted_page(r, 8, noise=0.05))
+    W, _ = np.linalg.qr(r.standard_normal((DIM, 8)))
+    rec = orc.build_record_shared(kb, W)
+    mu, V, C, _, sc = decode_variant_numpy(rec, 8, 16)
+    f16 = lambda x: x.astype(np.float16).astype(np.float64)
+    assert np.array_equal(V, f16(W)) and np.array_equal(mu, f16(kd.mean(0)))
+    assert np.array_equal(C, f16((kd - kd.mean(0)) @ W)) and np.all(sc[:3] == 1.0)
+
+
+def test_shared_basis_is_blind_to_deviations_in_its_null_space(orc):
+    """Proposition 1 (A "Why shared-basis sparse attention is structurally
+    broken"; B section 3): a fixed shared projection cannot see page content
+    in its null space. A page whose deviations lie there scores exactly
+    q.mu/sqrt(d) + ln 16 from its shared record (the coefficients vanish),
+    whatever those deviations are, while its exact LSE and its page-local
+    LOCKS score (unquantised rank 8) see them; deviations inside span(W)
+    are scored exactly by the shared record too."""
+    r = rng(93)
+    W, _ = np.linalg.qr(r.standard_normal((DIM, 8)))
+    q = r.standard_normal(DIM)
+    u = q - W @ (W.T @ q)
+    u /= np.linalg.norm(u)
+    mu = np.round(r.standard_normal(DIM) * 64) / 64  # exact in bf16 and fp16
+    alpha = np.full(PAGE, -1.0)
+    alpha[3] = 15.0
+    keys = mu[None, :] + alpha[:, None] * u[None, :]
+    kb, kd = bf16_round(keys)
+    m, V, C = orc.unpack_record_variant(orc.build_record_shared(kb, W), 8, 16)
+    blind = orc.page_score_f64(q, m, V, C)
+    closed = float(q @ m) / math.sqrt(DIM) + math.log(PAGE)
+    assert abs(blind - closed) < 1e-2, (blind, closed)  # C is fp16 of a ~0 projection
+    exact = exact_lse(q, kd)
+    mu_l, V_l, C_l, _ = orc.page_summary_f64(kd, rank=8)
+    local = orc.page_score_f64(q, mu_l, V_l, C_l)
+    assert abs(local - exact) < 1e-9 and exact - blind > 1.0
+    # deviations inside span(W): the shared record reconstructs them
+    keys_in = mu[None, :] + (r.standard_normal((PAGE, 8)) / np.arange(1, 9)) @ W.T
+    kb2, kd2 = bf16_round(keys_in)
+    m2, V2, C2 = orc.unpack_record_variant(orc.build_record_shared(kb2, W), 8, 16)
+    assert abs(orc.page_score_f64(q, m2, V2, C2) - exact_lse(q, kd2)) < 2e-2
+
+
+def test_shared_driver_places_records_with_each_sequence_basis(orc):
+    """Every full present page (b, j) gets, at [page_table[b][j], kvh], the
+    shared record of its own tile under basis[b][kvh]; other blocks untouched."""
+    rr = rng(94)
+    kb, pt, lens, q, Hkv = variant_cache(rr)
+    B = pt.shape[0]
+    basis = np.stack([np.stack([np.linalg.qr(rr.standard_normal((DIM, 8)))[0] for _ in range(Hkv)])
+                      for _ in range(B)])
+    nb = kb.shape[0]
+    fill = np.full((nb, Hkv, orc.variant_record_bytes(8, 16)), 0x5A, dtype=np.uint8)
+    got = orc.build_summaries_shared(kb, pt, lens, basis, summaries=fill.copy())
+    seen = set()
+    for b in range(B):
+        for j in range(int(lens[b]) // PAGE):
+            blk = int(pt[b, j])
+            if 0 <= blk < nb:
+                seen.add(blk)
+                for h in range(Hkv):
+                    assert np.array_equal(got[blk, h], orc.build_record_shared(kb[blk, h], basis[b, h]))
+    for blk in set(range(nb)) - seen:
+        assert np.all(got[blk] == 0x5A)

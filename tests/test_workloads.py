@@ -70,3 +70,27 @@ def test_sketch_constants_golden():
     payload = g["d_head"] * g["rank"] // 2 + g["d_head"] + g["page_size"] * g["rank"] + 6
     page_kv = g["page_size"] * g["d_head"] * 2 * 2
     assert math.isclose(payload / page_kv, g["summary_fraction_of_page_kv_approx"], rel_tol=0.1)
+
+
+def test_shared_keys_workload_premise():
+    """The blind-direction workload: the planted common basis S is what a
+    sequence-level PCA of the page deviations finds (the oracle's shared
+    basis spans it, once the sequence has enough pages that S's weakest
+    direction outweighs the one carrier's), and every carrier's deviations lie
+    in S's null space."""
+    import numpy as np
+    import oracle
+    w = workloads.make(2, ctx=16 * 2000, batch=2, budget=512, keys="shared", seed=5,
+                       n_kv_heads=2, n_q_heads=8)
+    q, pt, sl = w.q.numpy(), w.page_table.numpy(), w.seq_lens.numpy()
+    kb = workloads.bf16_bits(w.k_cache)
+    S = w.shared_basis.double().numpy()
+    W = oracle.shared_basis(kb, pt, sl)
+    for b in range(w.batch):
+        for h in range(w.n_kv_heads):
+            cosines = np.linalg.svd(S[b, h].T @ W[b, h], compute_uv=False)
+            assert cosines.min() > 0.99, (b, h, cosines.min())
+            keys = w.k_cache[pt[b, w.carrier[b]], h].double().numpy()
+            dev = keys - keys.mean(0)
+            inside = np.linalg.norm(dev @ S[b, h]) / np.linalg.norm(dev)
+            assert inside < 0.05, (b, h, inside)  # only the 0.05-std noise and bf16 rounding

@@ -16,6 +16,13 @@ Workloads (ctx = tokens per sequence, 16 tokens per page, head dim 128):
 Structured keys of one page: k_i = mu + sum_k c_ik b_k + e_i with mu ~ N(0, I),
 {b_k} a random orthonormal 8x128 basis drawn per page, c_ik ~ N(0, (1/k)^2) and
 e_i ~ N(0, 0.05^2 I).
+keys="shared" (the blind-direction workload of the shared-basis comparison):
+every page of a (sequence, KV head) varies in one common orthonormal 8x128
+basis S (returned as shared_basis, S^T per (sequence, KV head)); one planted
+carrier page per sequence instead holds a centroid ~ N(0, I) plus, along the
+unit vector u of the group's mean query with its component in span(S)
+removed, one token at +spike and the other 15 at -spike/15 (so its deviations
+lie in the null space of S).
 """
 from __future__ import annotations
 
@@ -44,6 +51,7 @@ class Workload:
     page_table: torch.Tensor  # i32 [B, max_pages]
     seq_lens: torch.Tensor   # i32 [B]
     carrier: torch.Tensor | None = None  # i32 [B] logical page of the planted carrier
+    shared_basis: torch.Tensor | None = None  # f32 [B, Hkv, 128, 8] (keys="shared")
     seed: int = 0
     recipe: str = ""
 
@@ -91,11 +99,23 @@ def structured_keys(gen: torch.Generator, n_pages: int, device, noise_std: float
     return mu[:, None, :] + torch.bmm(coef, basis) + noise
 
 
+def shared_subspace_keys(gen: torch.Generator, n_pages: int, S: torch.Tensor, device,
+                         noise_std: float = 0.05) -> torch.Tensor:
+    """Keys [n_pages, 16, 128] f32 whose in-page variation lies in the rows of S
+    (8 x 128, orthonormal), common to all pages: centroid + coefficients in S +
+    noise."""
+    mu = torch.randn(n_pages, DIM, generator=gen, device=device)
+    sig = 1.0 / torch.arange(1, RANK + 1, device=device, dtype=torch.float32)
+    coef = torch.randn(n_pages, PAGE, RANK, generator=gen, device=device) * sig
+    noise = torch.randn(n_pages, PAGE, DIM, generator=gen, device=device) * noise_std
+    return mu[:, None, :] + coef @ S + noise
+
+
 def make(config: int, device="cpu", ctx: int | None = None, batch: int | None = None,
          budget: int | None = None, seed: int | None = None, n_kv_heads: int | None = None,
          n_q_heads: int | None = None, keys: str | None = None,
          seq_lens: list[int] | None = None, extra_blocks: int = 0,
-         chunk_pages: int = 8192) -> Workload:
+         chunk_pages: int = 8192, spike: float = 16.0) -> Workload:
     """Workload `config` (1..5) with optional overrides (smaller ctx for tests,
     ragged seq_lens, spare physical blocks). seq_lens entries may be shorter
     than ctx; ctx sets max_pages = ctx // 16."""
@@ -122,7 +142,9 @@ def make(config: int, device="cpu", ctx: int | None = None, batch: int | None = 
     k_cache = torch.zeros(num_blocks, Hkv, PAGE, DIM, dtype=torch.bfloat16, device=device)
     v_cache = torch.zeros(num_blocks, Hkv, PAGE, DIM, dtype=torch.bfloat16, device=device)
     q = torch.empty(B, Hq, DIM, dtype=torch.float32, device=device)
-    carrier = torch.full((B,), -1, dtype=torch.int32) if p.get("carrier") else None
+    shared = p["keys"] == "shared"
+    carrier = torch.full((B,), -1, dtype=torch.int32) if (p.get("carrier") or shared) else None
+    shared_basis = torch.empty(B, Hkv, DIM, RANK, device=device) if shared else None
     G = Hq // Hkv
     pt_dev = page_table.to(device=device, dtype=torch.long)
 
@@ -134,13 +156,30 @@ def make(config: int, device="cpu", ctx: int | None = None, batch: int | None = 
             cpage = int(torch.randint(0, N, (1,), generator=gen, device=device).item())
             carrier[b] = cpage
         for kvh in range(Hkv):
+            if shared:
+                S = _orthonormal_rows(gen, 1, device)[0]  # 8 x 128
+                shared_basis[b, kvh] = S.t()
             for j0 in range(0, N, chunk_pages):
                 n = min(chunk_pages, N - j0)
                 if p["keys"] == "iid":
                     kk = torch.randn(n, PAGE, DIM, generator=gen, device=device)
+                elif shared:
+                    kk = shared_subspace_keys(gen, n, S, device)
                 else:
                     kk = structured_keys(gen, n, device)
-                if cpage is not None and j0 <= cpage < j0 + n:
+                if shared and j0 <= cpage < j0 + n:
+                    # planted carrier: deviations along u, the group's mean
+                    # query with its span(S) component removed
+                    u = q[b, kvh * G:(kvh + 1) * G].mean(0)
+                    u = u - S.t() @ (S @ u)
+                    u = u / u.norm()
+                    alpha = torch.full((PAGE,), -spike / (PAGE - 1), device=device)
+                    i0 = int(torch.randint(0, PAGE, (1,), generator=gen, device=device).item())
+                    alpha[i0] = spike
+                    mu_c = torch.randn(DIM, generator=gen, device=device)
+                    noise = torch.randn(PAGE, DIM, generator=gen, device=device) * 0.05
+                    kk[cpage - j0] = mu_c[None, :] + alpha[:, None] * u[None, :] + noise
+                elif cpage is not None and j0 <= cpage < j0 + n:
                     # planted carrier: centroid along the group's mean-q direction
                     u = q[b, kvh * G:(kvh + 1) * G].mean(0)
                     u = u / u.norm()
@@ -160,7 +199,8 @@ def make(config: int, device="cpu", ctx: int | None = None, batch: int | None = 
     return Workload(name=f"config{config}", batch=B, n_q_heads=Hq, n_kv_heads=Hkv,
                     max_pages=N, num_blocks=num_blocks, budget=p["budget"], q=q,
                     k_cache=k_cache, v_cache=v_cache, page_table=page_table.to(device),
-                    seq_lens=lens.to(device), carrier=carrier, seed=seed, recipe=recipe)
+                    seq_lens=lens.to(device), carrier=carrier, seed=seed, recipe=recipe,
+                    shared_basis=shared_basis)
 
 
 def bf16_bits(t: torch.Tensor):
