@@ -82,7 +82,9 @@ def traffic_from(fetch_csv, write_csv, bench_log):
         score, copy = [], []
         for r in csv.DictReader(open(path)):
             name, v = r["Kernel_Name"], float(r["Counter_Value"])
-            if re.search(r"(^|::)score_kernel<", name):  # not exact_/variant scorers
+            # the plain scorer only: not exact_/variant scorers, nor the
+            # instantiation that also builds just-filled pages
+            if re.search(r"(^|::)score_kernel<\d+, \d+, false>", name):
                 score.append(v)
             elif "copyBuffer" in name:
                 copy.append((int(r["Dispatch_Id"]), v))

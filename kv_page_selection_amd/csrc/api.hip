@@ -49,11 +49,12 @@ bool ws_layout(const locks_dims& d, int k, WsLayout* L, const char** why) {
   while (M < kSelectChunk && M < N) M *= 2;
   {
     // each chunk workgroup folds G heads per page: while the chunk grid has
-    // fewer than 8G workgroups (few sequences and KV heads), smaller chunks
+    // fewer than 64G workgroups (few sequences and KV heads), smaller chunks
     // spread that work over more CUs; below it, the merge's extra lists cost
-    // more than they save
+    // more than they save (measured: the 1M-token layer of 8 KV heads takes
+    // 2048-page chunks, -1.2 us per step against 4096; 1024 costs +4.7 us)
     const long long G = d.n_q_heads / d.n_kv_heads;
-    while (M > 1024 && B * Hkv * ((N + M - 1) / M) < 8 * G) M /= 2;
+    while (M > 1024 && B * Hkv * ((N + M - 1) / M) < 64 * G) M /= 2;
   }
   if ((N + M - 1) / M > 1024) {
     *why = "more than 1024 select chunks (max_pages_per_seq above 2^22)";
