@@ -397,19 +397,17 @@ __global__ __launch_bounds__(kThreads) void select_chunk_kernel(SelectArgs a) {
 //
 // One workgroup of kMergeThreads per (sequence, KV head). Fast path (every
 // chunk list fits the speculative slots, at most 1024 candidates): wave 0
-// alone ranks them in registers and the other waves leave. Otherwise the
-// whole workgroup ranks the chunk lists, in page order, in rounds: new
-// candidates are appended to the running top-k in LDS until the list's
-// kRoundCap entries are full, then ranked by bucket refinement over the live
-// key range with a 2048-bucket LDS histogram (4 buckets per thread):
-// elements above the bucket of the need-th key in, below it out, until the
-// count fits or the live keys are all equal (then the earliest, i.e. lowest
-// page ids, win).
+// alone ranks them in registers and the other waves leave. Up to kRoundCap
+// candidates the whole workgroup copies the chunk lists, in page order, into
+// one LDS list and ranks it by bucket refinement over the live key range with
+// a 2048-bucket LDS histogram (4 buckets per thread): elements above the
+// bucket of the need-th key in, below it out, until the count fits or the
+// live keys are all equal (then the earliest, i.e. lowest page ids, win).
+// Larger sets: merge_global, a radix select over the lists in L2.
 
 constexpr int kMergeThreads = 512;               // 8 waves: up to 256 VGPRs, no spills
 constexpr int kMW = kMergeThreads / 64;
-constexpr int kRoundNew = 512;                   // candidates gathered per load batch
-constexpr int kRoundCap = kSelectMaxK + kRoundNew;
+constexpr int kRoundCap = kSelectMaxK + 512;     // candidates the LDS list holds
 constexpr int kMergeBpt = kHistBuckets / kMergeThreads;           // histogram buckets per thread
 constexpr int kMergeEpt = (kRoundCap + kMergeThreads - 1) / kMergeThreads;  // list entries per thread
 
@@ -557,80 +555,73 @@ __device__ __forceinline__ void merge_chunk_offsets(MergeLds& W, const int32_t* 
   __syncthreads();
 }
 
-// The exact top-k of one (sequence, KV head)'s candidate lists, run by the
-// whole workgroup; leaves the kept sort keys and blocks, in page order, in
+// The exact top-k of one (sequence, KV head)'s candidate lists (at most
+// kRoundCap of them: larger sets take merge_global), run by the whole
+// workgroup in one pass: the lists are copied into the LDS list in page order
+// and ranked there; leaves the kept sort keys and blocks, in page order, in
 // W.x / W.blk and returns their count.
 __device__ int merge_lists(MergeLds& W, const unsigned long long* src, const int32_t* src_blk,
                            const int32_t* counts, int n_chunks, int chunk, int k) {
   const int tid = threadIdx.x;
   merge_chunk_offsets(W, counts, n_chunks);
-  const int total = W.off[n_chunks];
-  int nkept = 0, consumed = 0;
-  do {
-    // a round fills the LDS list: after the first, k kept plus what fits
-    const int take = min(total - consumed, kRoundCap - nkept);
-    unsigned long long xv[kMergeEpt];
-    int bv[kMergeEpt];
+  const int n = W.off[n_chunks];  // <= kRoundCap (the caller's condition)
+  unsigned long long xv[kMergeEpt];
+  int bv[kMergeEpt];
 #pragma unroll
-    for (int i = 0; i < kMergeEpt; ++i) {
-      const int e = tid + kMergeThreads * i;
-      int sidx = 0;
-      if (e < take) {
-        const int gidx = consumed + e;
-        int c = 0;
-        for (int lo = 0, hi = n_chunks - 1; lo <= hi;) {
-          const int mid = (lo + hi) >> 1;
-          if (W.off[mid] <= gidx) { c = mid; lo = mid + 1; } else hi = mid - 1;
-        }
-        sidx = c * chunk + (gidx - W.off[c]);
+  for (int i = 0; i < kMergeEpt; ++i) {
+    const int e = tid + kMergeThreads * i;
+    int sidx = 0;
+    if (e < n) {
+      int c = 0;
+      for (int lo = 0, hi = n_chunks - 1; lo <= hi;) {
+        const int mid = (lo + hi) >> 1;
+        if (W.off[mid] <= e) { c = mid; lo = mid + 1; } else hi = mid - 1;
       }
-      xv[i] = src[sidx];
-      bv[i] = src_blk[sidx];
+      sidx = c * chunk + (e - W.off[c]);
     }
+    xv[i] = src[sidx];
+    bv[i] = src_blk[sidx];
+  }
 #pragma unroll
-    for (int i = 0; i < kMergeEpt; ++i) {
-      const int e = tid + kMergeThreads * i;
-      if (e < take) {
-        W.x[nkept + e] = xv[i];
-        W.blk[nkept + e] = bv[i];
-      }
+  for (int i = 0; i < kMergeEpt; ++i) {
+    const int e = tid + kMergeThreads * i;
+    if (e < n) {
+      W.x[e] = xv[i];
+      W.blk[e] = bv[i];
     }
-    const int n = nkept + take;
-    for (int e = tid; e < n; e += kMergeThreads) W.state[e] = 0;
-    __syncthreads();
-    merge_topk(W, n, k);
-    // keep the selected, in order: thread t owns entries [t E, t E + E),
-    // all read before the scan's barrier, written after it
-    const int E = (n + kMergeThreads - 1) / kMergeThreads;
-    unsigned long long xs[kMergeEpt];
-    int bs[kMergeEpt];
-    uint32_t sel = 0, ns = 0;
+  }
+  for (int e = tid; e < n; e += kMergeThreads) W.state[e] = 0;
+  __syncthreads();
+  merge_topk(W, n, k);
+  // keep the selected, in order: thread t owns entries [t E, t E + E), all
+  // read before the scan's barrier, written after it
+  const int E = (n + kMergeThreads - 1) / kMergeThreads;
+  unsigned long long xs[kMergeEpt];
+  int bs[kMergeEpt];
+  uint32_t sel = 0, ns = 0;
 #pragma unroll
-    for (int i = 0; i < kMergeEpt; ++i) {
-      const int e = tid * E + i;
-      xs[i] = 0;
-      bs[i] = 0;
-      if (i < E && e < n && W.state[e] == 1) {
-        xs[i] = W.x[e];
-        bs[i] = W.blk[e];
-        sel |= 1u << i;
-        ++ns;
-      }
+  for (int i = 0; i < kMergeEpt; ++i) {
+    const int e = tid * E + i;
+    xs[i] = 0;
+    bs[i] = 0;
+    if (i < E && e < n && W.state[e] == 1) {
+      xs[i] = W.x[e];
+      bs[i] = W.blk[e];
+      sel |= 1u << i;
+      ++ns;
     }
-    uint32_t kept;
-    uint32_t dst = merge_excl_scan(ns, W.scn, &kept);
+  }
+  uint32_t kept;
+  uint32_t dst = merge_excl_scan(ns, W.scn, &kept);
 #pragma unroll
-    for (int i = 0; i < kMergeEpt; ++i)
-      if ((sel >> i) & 1u) {
-        W.x[dst] = xs[i];
-        W.blk[dst] = bs[i];
-        ++dst;
-      }
-    __syncthreads();
-    nkept = (int)kept;
-    consumed += take;
-  } while (consumed < total);
-  return nkept;
+  for (int i = 0; i < kMergeEpt; ++i)
+    if ((sel >> i) & 1u) {
+      W.x[dst] = xs[i];
+      W.blk[dst] = bs[i];
+      ++dst;
+    }
+  __syncthreads();
+  return (int)kept;
 }
 
 // Candidate sets larger than one LDS list: the k-th largest sort key is

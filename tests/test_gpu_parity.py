@@ -52,16 +52,25 @@ def test_decode_parity_on_gpu_built_summaries(locks, case):
         say(f"  carrier retention {np.mean(kept):.3f}")
 
 
-# selection paths the reduced cases do not reach
+# selection paths the reduced cases do not reach (candidate counts per KV
+# head estimated on the host from the oracle's records)
 SELECT_PATHS = [
-    # 512 ranges of 64 pages but 1024 pages to keep: no pruning bound exists, so
-    # every one of the 32768 pages is a candidate and the merge runs several rounds
+    # k = 1024 of 32768 pages: 2048 tiles >= k, so the tile bound exists, but
+    # it leaves ~4,400-5,500 candidates per KV head: the merge's workgroup-wide
+    # LDS ranking (<= 4,608) for some heads, its radix select over the lists
+    # in L2 for the others
     dict(config=4, ctx=16 * 32768, budget=16 * 1024),
     # G = 16 with 2048 ranges: the 32768 (head, range) maxima exceed what the
-    # bound pass holds, so it pools ranges in pairs
+    # bound pass holds, so it pools ranges in pairs (~300 candidates: the
+    # register path)
     dict(config=5, ctx=16 * 131072, budget=512, n_kv_heads=1, n_q_heads=16),
-    # G = 16 with 2048-page select chunks (two pages per chunk-pass thread)
+    # G = 16, 4 sequences: 1024-page select chunks, 400-1,400 candidates per
+    # KV head: the register path for some heads, the LDS ranking for others
     dict(config=5, ctx=16 * 32768, batch=4, budget=512),
+    # G = 16 with 2048-page select chunks (two pages per chunk-pass thread):
+    # chunks are halved only while the chunk grid has fewer than 64 G = 1024
+    # workgroups, so this takes 512 (sequence, KV head) pairs of 2049 pages
+    dict(config=5, ctx=16 * 2049, batch=64, n_kv_heads=8, n_q_heads=128, budget=512),
 ]
 
 
