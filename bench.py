@@ -38,7 +38,7 @@ METRIC = "decode-step us + achieved HBM GB/s (score+top-k+sparse attn) at 256K/1
 REC_PAYLOAD = 776
 PROFILE_TRAFFIC = os.path.join(ROOT, "profiles", "score_kernel_traffic.json")
 SCORE_SOURCES = [os.path.join(ROOT, "kv_page_selection_amd", "csrc", f)
-                 for f in ("score.hip", "device_common.h")]
+                 for f in ("score.hip", "device_common.h", "build_device.h")]
 
 
 def algorithmic_bytes(B, Hq, Hkv, N, k, n_sel):
