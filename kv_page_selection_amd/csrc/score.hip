@@ -149,12 +149,26 @@ struct ScoreLds {
 
 // q of the G heads at qg -> per-head exponent e (max |q| * 2^e in [2^21,
 // 2^22)) -> three signed int8 digit planes, q * 2^e = d0 + 256 d1 + 65536 d2;
-// wave w converts heads w, w+4, ...
+// wave w converts heads w, w+4, ... All of the wave's q loads are issued
+// before any is used: one memory round trip at launch, before the grid's
+// record loads queue up (a trip per head, the later ones behind those loads,
+// cost 16-head launches ~1 us).
 template <int G>
 __device__ __forceinline__ void q_digit_planes(const float* qg, int8_t (&dig)[3][G][kDim],
                                                float* esc, int wave, int lane) {
-  for (int h = wave; h < G; h += 4) {
-    const float q0 = qg[h * kDim + lane], q1 = qg[h * kDim + 64 + lane];
+  constexpr int HPW = (G + 3) / 4;  // heads per wave
+  float qv[HPW][2];
+#pragma unroll
+  for (int i = 0; i < HPW; ++i) {
+    const int h = wave + 4 * i;
+    qv[i][0] = h < G ? qg[h * kDim + lane] : 0.f;
+    qv[i][1] = h < G ? qg[h * kDim + 64 + lane] : 0.f;
+  }
+#pragma unroll
+  for (int i = 0; i < HPW; ++i) {
+    const int h = wave + 4 * i;
+    if (h >= G) break;
+    const float q0 = qv[i][0], q1 = qv[i][1];
     const float qm = wave_max(fmaxf(fabsf(q0), fabsf(q1)));
     int e = 0;
     if (qm > 0.f) {
