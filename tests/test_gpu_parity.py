@@ -358,6 +358,48 @@ def test_graph_replay_matches_eager(locks):
         _ = (w.q * 2).sum().item()  # eager work between replays
 
 
+def test_multi_step_graph_matches_eager(locks):
+    """Several steps captured back to back in one graph (different queries,
+    two workspaces reused in turn, as a decode graph of several layers and the
+    benchmark run them), replayed with eager work in between: every replay
+    gives each step's eager result."""
+    w = workloads.make(4, device=DEV, ctx=16 * 3000, seed=8)
+    summ = locks.build_summaries(w.k_cache, w.page_table, w.seq_lens)
+    dims = locks.make_dims(w.q, w.k_cache, w.page_table)
+    g_ = torch.Generator(device="cpu").manual_seed(99)
+    qs = [w.q] + [torch.randn(w.q.shape, generator=g_).to(DEV) for _ in range(2)]
+    refs = [locks.decode_step(q, summ, w.k_cache, w.v_cache, w.page_table, w.seq_lens, w.budget)
+            for q in qs]
+    torch.cuda.synchronize()
+    wss = [locks.new_workspace(dims, w.budget, DEV) for _ in range(2)]
+    outs = [torch.empty_like(w.q) for _ in qs]
+    sels = [torch.empty(1, 8, w.k_pages, dtype=torch.int32, device=DEV) for _ in qs]
+
+    def steps():
+        for i, q in enumerate(qs):
+            locks.decode_step(q, summ, w.k_cache, w.v_cache, w.page_table, w.seq_lens, w.budget,
+                              out=outs[i], selected=sels[i], workspace=wss[i % 2])
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):  # warm-up on the capture stream
+        steps()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        steps()
+    for rep in range(3):
+        for o, sl in zip(outs, sels):
+            o.zero_()
+            sl.fill_(-7)
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (ro, rs) in enumerate(refs):
+            assert torch.equal(outs[i], ro) and torch.equal(sels[i], rs), f"replay {rep}, step {i}"
+        _ = (w.q * 3).sum().item()  # eager work between replays
+
+
 # ----------------------------------------------------------------- full size
 
 @pytest.mark.parametrize("config,budget",
