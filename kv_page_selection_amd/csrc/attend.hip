@@ -87,6 +87,25 @@ __global__ __launch_bounds__(256) void attend_kernel(AttnArgs a) {
   int blk_next = blk_first;
   if (!(a.sel_blk && s0 + wave < a.k)) blk_next = (s0 + wave < s1) ? page_block(s0 + wave) : -1;
 
+  // a page's K and V rows for this lane (rows >= ntok: not read, zero)
+  uint4 kr[4];
+  uint32_t vr[kPage];
+  auto load_page = [&](int s, int blk) {
+    const int ntok = (s == base_len) ? tail : kPage;
+    const size_t tile = ((size_t)blk * a.Hkv + kvh) * (kPage * kDim);
+    const uint4* krow = reinterpret_cast<const uint4*>(a.kc + tile + tok * kDim + c * 32);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) kr[u] = (tok < ntok) ? krow[u] : make_uint4(0u, 0u, 0u, 0u);
+    const uint32_t* vbase = reinterpret_cast<const uint32_t*>(a.vc + tile) + lane;
+#pragma unroll
+    for (int i = 0; i < kPage; ++i) vr[i] = (i < ntok) ? vbase[i * (kDim / 2)] : 0u;
+  };
+  // the wave's first page goes out before q is staged: its rows need only the
+  // block id, and travel during the q load and the barrier
+  int blk = blk_next;
+  if (s0 + wave < s1 && blk >= 0) load_page(s0 + wave, blk);
+  blk_next = (s0 + wave + 4 < s1) ? page_block(s0 + wave + 4) : -1;
+
   const float qscale = kLog2e * kInvSqrtD;  // logits in base-2 units
   for (int i = tid; i < G * kDim; i += 256)
     q_s[i / kDim][i % kDim] = a.q[((size_t)b * a.Hq + (size_t)kvh * G) * kDim + i] * qscale;
@@ -97,19 +116,13 @@ __global__ __launch_bounds__(256) void attend_kernel(AttnArgs a) {
   for (int h = 0; h < G; ++h) { m[h] = -INFINITY; l[h] = 0.f; o0[h] = 0.f; o1[h] = 0.f; }
 
   for (int s = s0 + wave; s < s1; s += 4) {
-    const int blk = blk_next;
-    blk_next = (s + 4 < s1) ? page_block(s + 4) : -1;
+    if (s > s0 + wave) {  // later pages of a long split: loaded in turn
+      blk = blk_next;
+      blk_next = (s + 4 < s1) ? page_block(s + 4) : -1;
+      if (blk >= 0) load_page(s, blk);
+    }
     if (blk < 0) continue;
     const int ntok = (s == base_len) ? tail : kPage;  // rows >= ntok: not read, not weighted
-    const size_t tile = ((size_t)blk * a.Hkv + kvh) * (kPage * kDim);
-    const uint4* krow = reinterpret_cast<const uint4*>(a.kc + tile + tok * kDim + c * 32);
-    uint4 kr[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) kr[u] = (tok < ntok) ? krow[u] : make_uint4(0u, 0u, 0u, 0u);
-    uint32_t vr[kPage];
-    const uint32_t* vbase = reinterpret_cast<const uint32_t*>(a.vc + tile) + lane;
-#pragma unroll
-    for (int i = 0; i < kPage; ++i) vr[i] = (i < ntok) ? vbase[i * (kDim / 2)] : 0u;
 
     // ---- logits of token `tok`, partial over d in [32c, 32c+32)
     float lg[G];
