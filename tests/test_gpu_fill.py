@@ -16,7 +16,7 @@ import torch
 
 import oracle
 import workloads
-from parity import SCORE_TOL, decode_and_check, host, out_ok, say, selection_ok
+from parity import SCORE_TOL, compact_cache, decode_and_check, host, out_ok, say, selection_ok
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -114,3 +114,43 @@ def test_fill_step_builds_the_new_pages_inside_the_step(locks, config, hkv):
     # records the step built
     w.seq_lens = w.seq_lens + 1
     decode_and_check(w, summ)
+
+
+@pytest.mark.parametrize("config,budget", [(4, 2048), (5, 512)], ids=["1M-G4", "1M-G16"])
+def test_full_size_fill_step(locks, config, budget):
+    """The step with a page fill at the full 1M-token layers, in the launch
+    configuration the benchmark times for its step with page fills: the
+    records the scoring launch builds for the just-filled page are the
+    whole-cache build's bytes; the other pages' scores, the selection and the
+    output (over the selected pages plus the new one, only those K/V blocks
+    copied to the host) match the oracle's reading of a just-filled page."""
+    say(f"full-size step with a page fill, config {config}, budget {budget}")
+    w = workloads.make(config, device=DEV, budget=budget)
+    q, pt, sl = host(w)
+    n = int(sl[0]) // 16
+    assert sl[0] == 16 * n and n == w.max_pages, "premise: the last page is full"
+    summ = locks.build_summaries(w.k_cache, w.page_table, w.seq_lens)
+    fresh = summ.clone()
+    summ[int(pt[0, n - 1])] = 0xA5  # not built yet: garbage in its place
+    filled = torch.ones(1, dtype=torch.int32, device=DEV)
+    scores = torch.full((1, w.n_q_heads, w.max_pages), float("nan"), device=DEV)
+    out, sel = locks.decode_step(w.q, summ, w.k_cache, w.v_cache, w.page_table, w.seq_lens, budget,
+                                 page_scores=scores, filled=filled)
+    torch.cuda.synchronize()
+    assert torch.equal(summ, fresh), "the step's records differ from the whole-cache build's"
+    del fresh
+    sm = summ.cpu().numpy()
+    o_sc = oracle.scores(q, sm, pt, sl - 16, w.n_kv_heads)  # the new page is not scored
+    g_sc = scores.cpu().numpy()
+    assert np.all(np.isnan(g_sc[0, :, n - 1])), "the new page was scored"
+    valid = np.isfinite(o_sc)
+    s_err = float(np.abs(g_sc[valid] - o_sc[valid]).max())
+    assert s_err <= SCORE_TOL, f"page score error {s_err}"
+    o_keys = oracle.group_keys(o_sc, w.n_kv_heads)
+    k = budget // 16
+    g_sel = sel.cpu().numpy()
+    swaps = selection_ok(g_sel, oracle.select(o_keys, k), o_keys, k, np.isfinite(o_keys).sum(-1))
+    listed = np.concatenate([g_sel, np.full((1, w.n_kv_heads, 1), n - 1, dtype=np.int32)], axis=2)
+    kb, vb, cpt = compact_cache(w, listed)
+    err, cos = out_ok(out.cpu().numpy(), oracle.attention(q, kb, vb, cpt, sl, listed))
+    say(f"  score err {s_err:.2e}, near-tie swaps {swaps}, out max-abs {err:.2e}, cos {cos:.7f}")
