@@ -513,7 +513,11 @@ def main():
                    "copy_gbs": round(copy_gbs, 1)},
         "page_heads_scored_per_s": round(B * Hkv * N / (step_ms * 1e-3), 1),
         "phases_us": {"score": round(score_us, 2), "select": round(select_us, 2),
-                      "attend": round(attend_us, 2)},
+                      "attend": round(attend_us, 2),
+                      "note": "the three phase entry points alone (select with its merge launch, "
+                              "attention on a given selection); the step itself ranks inside its "
+                              "attention launch at budgets up to 4096 tokens on grids up to 1024 "
+                              "attention workgroups, with no merge launch"},
         "page_fill_build": {"us": round(fill_us, 2), "page_heads": B * Hkv,
                             "blocks": "one per sequence, every KV head"},
         "ragged_tail_step": {"us_per_step": round(tail_step_us, 2), "tail_tokens": "seq_len % 16 = 11"},

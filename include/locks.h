@@ -148,7 +148,9 @@ locks_status locks_build_blocks(const locks_dims* dims, const void* k_cache,
                                 hipStream_t stream);
 
 /* One LOCKS decode step = locks_score_pages + locks_select_pages +
- * locks_sparse_attention on the same workspace.
+ * locks_sparse_attention on the same workspace, with the same results (for
+ * budgets up to 4096 tokens on small grids the selection's final ranking runs
+ * inside the attention launch instead of a launch of its own).
  *  q            f32 queries, one token per sequence.
  *  summaries    records written by locks_build_summaries (or any records in
  *               the documented format).

@@ -273,11 +273,18 @@ locks_status decode_step_impl(const locks_dims* dims, const float* q, const void
                                     page_table, seq_lens, fill,
                                     static_cast<const uint16_t*>(k_cache), stream),
                        "score launch"));
-  LOCKS_TRY(hip_status(launch_select(*dims, L, P, page_table, seq_lens, fill, selected, stream),
+  // small budgets on small grids: no merge launch, the attention workgroups
+  // rank the lists (each (sequence, KV head)'s ranking repeats in all its
+  // splits, which pays only while the grid fits the GPU about once)
+  const bool rank_in_attend =
+      L.k <= kRankInAttendMaxK &&
+      (long long)dims->batch * dims->n_kv_heads * L.n_att_split <= kRankInAttendMaxWgs;
+  LOCKS_TRY(hip_status(launch_select(*dims, L, P, page_table, seq_lens, fill, selected,
+                                     !rank_in_attend, stream),
                        "select launch"));
   return hip_status(launch_attend(*dims, L, P, q, static_cast<const uint16_t*>(k_cache),
                                   static_cast<const uint16_t*>(v_cache), page_table, seq_lens,
-                                  fill, selected, P.sel_blk, out, false, stream),
+                                  fill, selected, P.sel_blk, out, false, rank_in_attend, stream),
                     "sparse attention launch");
 }
 
@@ -472,7 +479,7 @@ locks_status locks_select_pages(const locks_dims* dims, const int32_t* page_tabl
   LOCKS_TRY(check_ws(L, workspace, workspace_bytes));
   const DevPtrs P = ws_ptrs(*dims, L, workspace, const_cast<float*>(page_scores));
   (void)hipGetLastError();
-  return hip_status(launch_select(*dims, L, P, page_table, seq_lens, nullptr, selected, stream),
+  return hip_status(launch_select(*dims, L, P, page_table, seq_lens, nullptr, selected, true, stream),
                     "select launch");
 }
 
@@ -498,7 +505,7 @@ locks_status locks_sparse_attention(const locks_dims* dims, const float* q, cons
   (void)hipGetLastError();
   return hip_status(launch_attend(*dims, L, P, q, static_cast<const uint16_t*>(k_cache),
                                   static_cast<const uint16_t*>(v_cache), page_table, seq_lens,
-                                  nullptr, selected, nullptr, out, false, stream),
+                                  nullptr, selected, nullptr, out, false, false, stream),
                     "sparse attention launch");
 }
 
@@ -579,7 +586,7 @@ locks_status locks_dense_attention(const locks_dims* dims, const float* q, const
   (void)hipGetLastError();
   return hip_status(launch_attend(*dims, L, P, q, static_cast<const uint16_t*>(k_cache),
                                   static_cast<const uint16_t*>(v_cache), page_table, seq_lens,
-                                  nullptr, nullptr, nullptr, out, true, stream),
+                                  nullptr, nullptr, nullptr, out, true, false, stream),
                     "dense attention launch");
 }
 

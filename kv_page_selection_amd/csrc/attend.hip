@@ -24,6 +24,7 @@
 // (attend_mfma_kernel below).
 #include "device_common.h"
 #include "internal.h"
+#include "rank_device.h"
 
 namespace locks {
 
@@ -41,9 +42,65 @@ struct AttnArgs {
   float* partials;
   float* out;
   int Hq, Hkv, N, num_blocks, k, pages_per_split, n_split;
+  // ranking launches only: the chunk pass's candidate lists, and where split 0
+  // writes the kept ids
+  const unsigned long long* cand;
+  const int32_t* cand_blk;
+  const int32_t* cand_count;
+  int32_t* sel_out;
+  int n_chunks, chunk;
 };
 
-template <int G>
+// LDS of a launch that ranks its own list: the workgroup path's space and
+// the blocks of this split's entries (at most 64 pages per split).
+template <bool RANK>
+struct RankSpace {
+  RankLds<256> r;
+  int sblk[64];
+};
+template <>
+struct RankSpace<false> {
+  int sblk[1];
+};
+
+// The kept list of this workgroup's (sequence, KV head), ranked here from the
+// chunk lists exactly as the select merge launch does: the blocks of list
+// entries [s0, s0 + pages_per_split) go to sblk (-1 past the kept pages), and
+// split 0 writes the kept ids, the step's selection output. Every thread
+// calls it; the caller's next barrier publishes sblk.
+__device__ __forceinline__ void rank_split(const AttnArgs& a, RankSpace<true>& RS, size_t head, int split) {
+  const int wave = threadIdx.x >> 6;
+  const size_t lists = head * a.n_chunks;
+  const CandLists L{a.cand + lists * a.chunk, a.cand_blk + lists * a.chunk, a.cand_count + lists,
+                    a.n_chunks, a.chunk};
+  const int s0 = split * a.pages_per_split, pps = a.pages_per_split;
+  int32_t* ids = (split == 0) ? a.sel_out + head * a.k : nullptr;
+  int* sblk = RS.sblk;
+  auto emit = [ids, sblk, s0, pps](int pos, int id, int blk) {
+    if (ids) ids[pos] = id;
+    const unsigned r = (unsigned)(pos - s0);
+    if (r < (unsigned)pps) sblk[r] = blk;
+  };
+  // every wave reads the counts while wave 0 gathers speculatively
+  const int lgS = fast_lg_slots(L.nc);
+  int cc[16];
+  fast_count_load(L, cc);
+  unsigned long long x[kFastPerLane];
+  int bl[kFastPerLane], cof[kFastPerLane];
+  if (wave == 0) fast_slots_load(L, lgS, x, bl, cof);
+  int total;
+  const bool over = fast_count_check(L, lgS, cc, &total);  // the same in every wave
+  if (over && total > kFastCap) {
+    rank_global<256>(RS.r, L, a.k, emit);
+    return;
+  }
+  if (wave != 0) return;
+  const uint32_t live = over ? fast_gather_exact(L, RS.r.off, total, x, bl) : fast_slots_live(L, lgS, cof);
+  fast_emit(x, bl, fast_rank(x, live, a.k, RS.r.hist), a.k, emit);
+}
+
+// RANK: the list is ranked here (rank_split) instead of read from sel_blk.
+template <int G, bool RANK>
 __global__ __launch_bounds__(256) void attend_kernel(AttnArgs a) {
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -54,10 +111,12 @@ __global__ __launch_bounds__(256) void attend_kernel(AttnArgs a) {
   const int base_len = a.sel ? a.k : n_b;  // entry base_len is the tail, if any
   const int list_len = base_len + (tail > 0 ? 1 : 0);
   const int s0 = split * a.pages_per_split;
+  __shared__ RankSpace<RANK> RS;
+  if constexpr (RANK) rank_split(a, RS, (size_t)b * a.Hkv + kvh, split);
   // the first entry's block id: a selected page (entry < k) needs no sequence
   // length, so its load goes out together with the length's
   int blk_first = -1;
-  if (a.sel_blk && s0 + wave < a.k) {
+  if (!RANK && a.sel_blk && s0 + wave < a.k) {
     const int blk = a.sel_blk[((size_t)b * a.Hkv + kvh) * a.k + s0 + wave];
     blk_first = (blk >= 0 && blk < a.num_blocks) ? blk : -1;
   }
@@ -67,12 +126,14 @@ __global__ __launch_bounds__(256) void attend_kernel(AttnArgs a) {
   __shared__ float wm_s[4][G], wl_s[4][G];
   __shared__ float wo_s[4][G][kDim];
 
-  // physical block of list entry s (-1: skip): from the selection's block
-  // list, through the page table, or (dense) page s itself
+  // physical block of list entry s (-1: skip): from this launch's ranking, the
+  // selection's block list, through the page table, or (dense) page s itself
   auto page_block = [&](int s) -> int {
     int blk;
     if (s == base_len) {
       blk = a.page_table[(size_t)b * N + n_b];  // the tail page (n_b < N here)
+    } else if constexpr (RANK) {
+      blk = RS.sblk[s - s0];
     } else if (a.sel_blk) {
       blk = a.sel_blk[((size_t)b * a.Hkv + kvh) * a.k + s];
     } else {
@@ -85,7 +146,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttnArgs a) {
   // a selected entry's block id was loaded above; others (the tail, dense
   // lists, caller-given ids) are looked up here
   int blk_next = blk_first;
-  if (!(a.sel_blk && s0 + wave < a.k)) blk_next = (s0 + wave < s1) ? page_block(s0 + wave) : -1;
+  if (!RANK && !(a.sel_blk && s0 + wave < a.k)) blk_next = (s0 + wave < s1) ? page_block(s0 + wave) : -1;
 
   // a page's K and V rows for this lane (rows >= ntok: not read, zero)
   uint4 kr[4];
@@ -101,15 +162,24 @@ __global__ __launch_bounds__(256) void attend_kernel(AttnArgs a) {
     for (int i = 0; i < kPage; ++i) vr[i] = (i < ntok) ? vbase[i * (kDim / 2)] : 0u;
   };
   // the wave's first page goes out before q is staged: its rows need only the
-  // block id, and travel during the q load and the barrier
-  int blk = blk_next;
-  if (s0 + wave < s1 && blk >= 0) load_page(s0 + wave, blk);
-  blk_next = (s0 + wave + 4 < s1) ? page_block(s0 + wave + 4) : -1;
+  // block id, and travel during the q load and the barrier (a ranking launch
+  // knows its blocks only after that barrier)
+  int blk = -1;
+  if constexpr (!RANK) {
+    blk = blk_next;
+    if (s0 + wave < s1 && blk >= 0) load_page(s0 + wave, blk);
+    blk_next = (s0 + wave + 4 < s1) ? page_block(s0 + wave + 4) : -1;
+  }
 
   const float qscale = kLog2e * kInvSqrtD;  // logits in base-2 units
   for (int i = tid; i < G * kDim; i += 256)
     q_s[i / kDim][i % kDim] = a.q[((size_t)b * a.Hq + (size_t)kvh * G) * kDim + i] * qscale;
   __syncthreads();
+  if constexpr (RANK) {
+    blk = (s0 + wave < s1) ? page_block(s0 + wave) : -1;
+    if (blk >= 0) load_page(s0 + wave, blk);
+    blk_next = (s0 + wave + 4 < s1) ? page_block(s0 + wave + 4) : -1;
+  }
 
   float m[G], l[G], o0[G], o1[G];
 #pragma unroll
@@ -225,7 +295,7 @@ __device__ __forceinline__ short bf16_bits(float x) {
 //     per-wave LDS copy of the tile whose 272-byte rows make the 4-token
 //     column reads bank-conflict free; a lane accumulates O[head 4(l/16)+r]
 //     [dim 16 blk + l%16].
-template <int G>
+template <int G, bool RANK>
 __global__ __launch_bounds__(256) void attend_mfma_kernel(AttnArgs a) {
   static_assert(G >= 4 && G <= 16, "MFMA rows are the query heads of a group");
   constexpr int kVRow = kDim + 8;  // staged V row in bf16 (272 bytes)
@@ -241,7 +311,7 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(AttnArgs a) {
   // the first entry's block id: a selected page (entry < k) needs no sequence
   // length, so its load goes out together with the length's
   int blk_first = -1;
-  if (a.sel_blk && s0 + wave < a.k) {
+  if (!RANK && a.sel_blk && s0 + wave < a.k) {
     const int blk = a.sel_blk[((size_t)b * a.Hkv + kvh) * a.k + s0 + wave];
     blk_first = (blk >= 0 && blk < a.num_blocks) ? blk : -1;
   }
@@ -254,11 +324,14 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(AttnArgs a) {
   };
   __shared__ __align__(16) AttnLds U;
   __shared__ float wm_s[4][G], wl_s[4][G];
+  __shared__ RankSpace<RANK> RS;
 
   auto page_block = [&](int s) -> int {
     int blk;
     if (s == base_len) {
       blk = a.page_table[(size_t)b * N + n_b];  // the tail page (n_b < N here)
+    } else if constexpr (RANK) {
+      blk = RS.sblk[s - s0];
     } else if (a.sel_blk) {
       blk = a.sel_blk[((size_t)b * a.Hkv + kvh) * a.k + s];
     } else {
@@ -269,7 +342,7 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(AttnArgs a) {
     return (blk >= 0 && blk < a.num_blocks) ? blk : -1;
   };
   int blk_next = blk_first;
-  if (!(a.sel_blk && s0 + wave < a.k)) blk_next = (s0 + wave < s1) ? page_block(s0 + wave) : -1;
+  if (!RANK && !(a.sel_blk && s0 + wave < a.k)) blk_next = (s0 + wave < s1) ? page_block(s0 + wave) : -1;
 
   // q of head li (zero for li >= G), base-2 logit scale, bf16 hi + lo
   bf8_t qh[4], ql[4];
@@ -289,6 +362,12 @@ __global__ __launch_bounds__(256) void attend_mfma_kernel(AttnArgs a) {
         ql[c][e] = (__bf16)(x - (float)h);
       }
     }
+  }
+
+  if constexpr (RANK) {  // the list, ranked here, after q's loads went out
+    rank_split(a, RS, (size_t)b * a.Hkv + kvh, split);
+    __syncthreads();
+    blk_next = (s0 + wave < s1) ? page_block(s0 + wave) : -1;
   }
 
   float m_run = -INFINITY, l_run = 0.f;  // head li
@@ -443,7 +522,7 @@ template <int G>
 hipError_t launch_g(const locks_dims& d, const WsLayout& L, const DevPtrs& P, const float* q,
                     const uint16_t* kc, const uint16_t* vc, const int32_t* pt, const int32_t* sl,
                     const int32_t* fill, const int32_t* sel, const int32_t* sel_blk, float* out,
-                    bool dense, hipStream_t s) {
+                    bool dense, bool rank, hipStream_t s) {
   AttnArgs a;
   a.q = q;
   a.kc = kc;
@@ -452,7 +531,7 @@ hipError_t launch_g(const locks_dims& d, const WsLayout& L, const DevPtrs& P, co
   a.seq_lens = sl;
   a.fill = fill;
   a.sel = dense ? nullptr : sel;
-  a.sel_blk = dense ? nullptr : sel_blk;
+  a.sel_blk = (dense || rank) ? nullptr : sel_blk;
   a.partials = dense ? P.dense_part : P.att_part;
   a.out = out;
   a.Hq = d.n_q_heads;
@@ -462,6 +541,13 @@ hipError_t launch_g(const locks_dims& d, const WsLayout& L, const DevPtrs& P, co
   a.k = L.k;
   a.pages_per_split = dense ? L.dense_pages_per_split : L.att_pages_per_split;
   a.n_split = dense ? L.n_dense_split : L.n_att_split;
+  a.cand = P.cand;
+  a.cand_blk = P.cand_blk;
+  a.cand_count = P.cand_count;
+  a.sel_out = rank ? const_cast<int32_t*>(sel) : nullptr;
+  a.n_chunks = L.n_sel_chunks;
+  a.chunk = L.sel_chunk;
+  if (rank && (dense || a.pages_per_split > 64)) return hipErrorInvalidValue;
   // MFMA where a query group fills enough of the 16 rows: G >= 8 always, and
   // G = 4 for the long dense splits; a sparse split at G = 4 (one page per
   // wave, 3/4 of the rows padding) stays on VALU: MFMA there showed no clear
@@ -469,12 +555,15 @@ hipError_t launch_g(const locks_dims& d, const WsLayout& L, const DevPtrs& P, co
   // eight of 256K tokens)
   const dim3 grid(a.n_split, d.n_kv_heads, d.batch);
   if constexpr (G >= 8) {
-    hipLaunchKernelGGL(attend_mfma_kernel<G>, grid, dim3(256), 0, s, a);
+    if (rank) hipLaunchKernelGGL((attend_mfma_kernel<G, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((attend_mfma_kernel<G, false>), grid, dim3(256), 0, s, a);
   } else if constexpr (G == 4) {
-    if (dense) hipLaunchKernelGGL(attend_mfma_kernel<G>, grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL(attend_kernel<G>, grid, dim3(256), 0, s, a);
+    if (dense) hipLaunchKernelGGL((attend_mfma_kernel<G, false>), grid, dim3(256), 0, s, a);
+    else if (rank) hipLaunchKernelGGL((attend_kernel<G, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((attend_kernel<G, false>), grid, dim3(256), 0, s, a);
   } else {
-    hipLaunchKernelGGL(attend_kernel<G>, grid, dim3(256), 0, s, a);
+    if (rank) hipLaunchKernelGGL((attend_kernel<G, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((attend_kernel<G, false>), grid, dim3(256), 0, s, a);
   }
   hipLaunchKernelGGL(attend_merge_kernel, dim3(d.n_q_heads, d.batch), dim3(256), 0, s, a.partials,
                      out, d.n_q_heads, a.n_split);
@@ -486,13 +575,13 @@ hipError_t launch_g(const locks_dims& d, const WsLayout& L, const DevPtrs& P, co
 hipError_t launch_attend(const locks_dims& d, const WsLayout& L, const DevPtrs& P, const float* q,
                          const uint16_t* kc, const uint16_t* vc, const int32_t* pt,
                          const int32_t* sl, const int32_t* fill, const int32_t* sel,
-                         const int32_t* sel_blk, float* out, bool dense, hipStream_t s) {
+                         const int32_t* sel_blk, float* out, bool dense, bool rank, hipStream_t s) {
   switch (d.n_q_heads / d.n_kv_heads) {
-    case 1: return launch_g<1>(d, L, P, q, kc, vc, pt, sl, fill, sel, sel_blk, out, dense, s);
-    case 2: return launch_g<2>(d, L, P, q, kc, vc, pt, sl, fill, sel, sel_blk, out, dense, s);
-    case 4: return launch_g<4>(d, L, P, q, kc, vc, pt, sl, fill, sel, sel_blk, out, dense, s);
-    case 8: return launch_g<8>(d, L, P, q, kc, vc, pt, sl, fill, sel, sel_blk, out, dense, s);
-    case 16: return launch_g<16>(d, L, P, q, kc, vc, pt, sl, fill, sel, sel_blk, out, dense, s);
+    case 1: return launch_g<1>(d, L, P, q, kc, vc, pt, sl, fill, sel, sel_blk, out, dense, rank, s);
+    case 2: return launch_g<2>(d, L, P, q, kc, vc, pt, sl, fill, sel, sel_blk, out, dense, rank, s);
+    case 4: return launch_g<4>(d, L, P, q, kc, vc, pt, sl, fill, sel, sel_blk, out, dense, rank, s);
+    case 8: return launch_g<8>(d, L, P, q, kc, vc, pt, sl, fill, sel, sel_blk, out, dense, rank, s);
+    case 16: return launch_g<16>(d, L, P, q, kc, vc, pt, sl, fill, sel, sel_blk, out, dense, rank, s);
     default: return hipErrorInvalidValue;
   }
 }

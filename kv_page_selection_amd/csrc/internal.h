@@ -20,6 +20,10 @@ constexpr int kDenseMinWgs = 1024;       // dense splits shrink while the grid h
 constexpr int kMaxSplits = 2048;        // split partials one merge workgroup combines
 constexpr int kPartialFloats = 130;     // (m, l, o[128]) per head and split
 constexpr int kTileBoundPages = 128;    // per selected page: sequences with fewer pages bound by tiles
+// decode steps with budget/16 up to this rank their lists inside the sparse
+// attention launch instead of a merge launch of their own
+constexpr int kRankInAttendMaxK = 256;
+constexpr int kRankInAttendMaxWgs = 1024;  // and with at most this many attention workgroups
 
 // Byte offsets of the regions of the caller's workspace (each 256-aligned).
 struct WsLayout {
@@ -83,13 +87,19 @@ hipError_t launch_score_variant(const locks_dims& d, const WsLayout& L, const De
 hipError_t launch_exact_score(const locks_dims& d, const WsLayout& L, const DevPtrs& P,
                               const float* q, const uint16_t* kc, const int32_t* page_table,
                               const int32_t* seq_lens, hipStream_t s);
+// merge == false: the chunk pass only (the attention launch then ranks the
+// candidate lists itself: launch_attend with rank == true).
 hipError_t launch_select(const locks_dims& d, const WsLayout& L, const DevPtrs& P,
                          const int32_t* page_table, const int32_t* seq_lens, const int32_t* fill,
-                         int32_t* selected, hipStream_t s);
+                         int32_t* selected, bool merge, hipStream_t s);
+// rank == true (sparse only): every workgroup ranks its (sequence, KV head)'s
+// candidate lists left by launch_select(merge = false) and split 0 writes the
+// kept ids to `selected`; selected_blocks is unused.
 hipError_t launch_attend(const locks_dims& d, const WsLayout& L, const DevPtrs& P, const float* q,
                          const uint16_t* kc, const uint16_t* vc, const int32_t* page_table,
                          const int32_t* seq_lens, const int32_t* fill, const int32_t* selected,
-                         const int32_t* selected_blocks, float* out, bool dense, hipStream_t s);
+                         const int32_t* selected_blocks, float* out, bool dense, bool rank,
+                         hipStream_t s);
 // Shared-basis comparison records (variant layout, rank 8, fp16 values) of
 // every full page, under basis [B][Hkv][128][8].
 size_t shared_record_bytes();

@@ -32,7 +32,9 @@
 //     lists are in page order, with their physical blocks for the attention
 //     pass. Up to 1024 candidates (the usual case) one wave ranks them in
 //     registers with no barrier; up to 4,608 the workgroup ranks an LDS copy;
-//     beyond that a radix select runs over the lists where they lie.
+//     beyond that a radix select runs over the lists where they lie. (For
+//     small budgets the decode step skips this launch: each sparse attention
+//     workgroup ranks its own (sequence, KV head)'s lists the same way.)
 // Ranking = exact selection by bucket refinement on the key bits: a histogram
 // over the live [lo, hi] key range (2048 buckets; 512 on the one-wave
 // register path) picks the bucket holding the k-th key; everything above it
@@ -41,6 +43,7 @@
 // lowest ids win.
 #include "device_common.h"
 #include "internal.h"
+#include "rank_device.h"
 
 namespace locks {
 
@@ -396,51 +399,27 @@ __global__ __launch_bounds__(kThreads) void select_chunk_kernel(SelectArgs a) {
 
 // ============================================================ merge
 //
-// One workgroup of kMergeThreads per (sequence, KV head). Fast path (every
-// chunk list fits the speculative slots, at most 1024 candidates): wave 0
-// alone ranks them in registers and the other waves leave. Up to kRoundCap
-// candidates the whole workgroup copies the chunk lists, in page order, into
-// one LDS list and ranks it by bucket refinement over the live key range with
-// a 2048-bucket LDS histogram (4 buckets per thread): elements above the
-// bucket of the need-th key in, below it out, until the count fits or the
-// live keys are all equal (then the earliest, i.e. lowest page ids, win).
-// Larger sets: merge_global, a radix select over the lists in L2.
+// One workgroup of kMergeThreads per (sequence, KV head). Up to kFastCap
+// candidates (the usual case) wave 0 alone ranks them in registers and the
+// other waves leave. Up to kRoundCap the whole workgroup copies the chunk
+// lists, in page order, into one LDS list and ranks it by bucket refinement
+// over the live key range with a 2048-bucket LDS histogram (4 buckets per
+// thread): elements above the bucket of the need-th key in, below it out,
+// until the count fits or the live keys are all equal (then the earliest,
+// i.e. lowest page ids, win). Larger sets: rank_global, a radix select over
+// the lists where they lie.
 
 constexpr int kMergeThreads = 512;               // 8 waves: up to 256 VGPRs, no spills
-constexpr int kMW = kMergeThreads / 64;
 constexpr int kRoundCap = kSelectMaxK + 512;     // candidates the LDS list holds
-constexpr int kMergeBpt = kHistBuckets / kMergeThreads;           // histogram buckets per thread
+constexpr int kMergeBpt = kRankBuckets / kMergeThreads;           // histogram buckets per thread
 constexpr int kMergeEpt = (kRoundCap + kMergeThreads - 1) / kMergeThreads;  // list entries per thread
 
 struct MergeLds {
   unsigned long long x[kRoundCap];  // sort keys; 0 = rejected
   int blk[kRoundCap];
   uint8_t state[kRoundCap];         // 0 live, 1 selected, 2 rejected
-  uint32_t hist[kHistBuckets];
-  int off[1025];
-  uint32_t red3[3][kMW];
-  uint32_t scn[kMW];
-  int bstar;
-  uint32_t babove;
+  RankLds<kMergeThreads> r;         // histogram, list offsets, reduction slots
 };
-
-// Exclusive prefix sum over the workgroup (thread order) of one u32; *total
-// gets the workgroup total. One barrier; scn is free again after the next.
-__device__ __forceinline__ uint32_t merge_excl_scan(uint32_t v, uint32_t* scn, uint32_t* total) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint32_t inc = wave_incl_scan(v);
-  if (lane == 63) scn[wave] = inc;
-  __syncthreads();
-  uint32_t pre = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < kMW; ++w) {
-    const uint32_t c = scn[w];
-    pre += (w < wave) ? c : 0u;
-    tot += c;
-  }
-  *total = tot;
-  return pre + inc - v;
-}
 
 // Ranks x[0..n) (state all live on entry) and marks the `need` largest
 // selected; every thread of the workgroup takes part.
@@ -458,16 +437,16 @@ __device__ void merge_topk(MergeLds& W, int n, int need) {
     cnt = wave_sum_u32(cnt);
     lo = wave_min_u32(lo);
     hi = wave_max_u32(hi);
-    if (lane == 0) { W.red3[0][wave] = cnt; W.red3[1][wave] = lo; W.red3[2][wave] = hi; }
+    if (lane == 0) { W.r.red3[0][wave] = cnt; W.r.red3[1][wave] = lo; W.r.red3[2][wave] = hi; }
     __syncthreads();
     cnt = 0;
     lo = 0xffffffffu;
     hi = 0u;
 #pragma unroll
-    for (int w = 0; w < kMW; ++w) {
-      cnt += W.red3[0][w];
-      lo = min(lo, W.red3[1][w]);
-      hi = max(hi, W.red3[2][w]);
+    for (int w = 0; w < kMergeThreads / 64; ++w) {
+      cnt += W.r.red3[0][w];
+      lo = min(lo, W.r.red3[1][w]);
+      hi = max(hi, W.r.red3[2][w]);
     }
     if ((int)cnt <= need) {  // every live element is in
       for (int e = tid; e < n; e += kMergeThreads)
@@ -476,35 +455,35 @@ __device__ void merge_topk(MergeLds& W, int n, int need) {
       return;
     }
     if (lo == hi) break;
-    const float scale = (float)kHistBuckets / ((float)(hi - lo) + 1.0f);
+    const float scale = (float)kRankBuckets / ((float)(hi - lo) + 1.0f);
 #pragma unroll
-    for (int q = 0; q < kMergeBpt; ++q) W.hist[kMergeBpt * tid + q] = 0u;
+    for (int q = 0; q < kMergeBpt; ++q) W.r.hist[kMergeBpt * tid + q] = 0u;
     __syncthreads();
     for (int e = tid; e < n; e += kMergeThreads)
-      if (W.state[e] == 0) atomicAdd(&W.hist[hbucket((uint32_t)(W.x[e] >> 32), lo, scale)], 1u);
+      if (W.state[e] == 0) atomicAdd(&W.r.hist[hbucket((uint32_t)(W.x[e] >> 32), lo, scale)], 1u);
     __syncthreads();
     // thread t owns buckets [4t, 4t+4): counts above them, then the bucket
     // holding the need-th key from the top
     uint32_t hb[kMergeBpt], mine = 0;
 #pragma unroll
     for (int q = 0; q < kMergeBpt; ++q) {
-      hb[q] = W.hist[kMergeBpt * tid + q];
+      hb[q] = W.r.hist[kMergeBpt * tid + q];
       mine += hb[q];
     }
     uint32_t tot;
-    const uint32_t pre = merge_excl_scan(mine, W.scn, &tot);
+    const uint32_t pre = rank_excl_scan<kMergeThreads>(mine, W.r.scn, &tot);
     uint32_t acc = tot - pre - mine;
 #pragma unroll
     for (int q = kMergeBpt - 1; q >= 0; --q) {
       if (acc < (uint32_t)need && (uint32_t)need <= acc + hb[q]) {
-        W.bstar = kMergeBpt * tid + q;  // exactly one thread finds it
-        W.babove = acc;
+        W.r.bstar = kMergeBpt * tid + q;  // exactly one thread finds it
+        W.r.babove = acc;
       }
       acc += hb[q];
     }
     __syncthreads();
-    const int bstar = W.bstar;
-    const uint32_t above = W.babove;
+    const int bstar = W.r.bstar;
+    const uint32_t above = W.r.babove;
     for (int e = tid; e < n; e += kMergeThreads)
       if (W.state[e] == 0) {
         const int bk = hbucket((uint32_t)(W.x[e] >> 32), lo, scale);
@@ -524,7 +503,7 @@ __device__ void merge_topk(MergeLds& W, int n, int need) {
       if (e < n && W.state[e] == 0) ++nl;
     }
     uint32_t tot;
-    uint32_t before = merge_excl_scan(nl, W.scn, &tot);
+    uint32_t before = rank_excl_scan<kMergeThreads>(nl, W.r.scn, &tot);
     for (int i = 0; i < E; ++i) {
       const int e = tid * E + i;
       if (e < n && W.state[e] == 0) {
@@ -536,31 +515,15 @@ __device__ void merge_topk(MergeLds& W, int n, int need) {
   }
 }
 
-// W.off[c] = first list entry of chunk c, W.off[n_chunks] = the total (at
-// most 1024 chunks: two per thread). Ends with a barrier.
-__device__ __forceinline__ void merge_chunk_offsets(MergeLds& W, const int32_t* counts, int n_chunks) {
-  static_assert(2 * kMergeThreads >= 1024, "two chunk counts per thread");
-  const int tid = threadIdx.x;
-  const uint32_t c0 = (2 * tid < n_chunks) ? (uint32_t)counts[2 * tid] : 0u;
-  const uint32_t c1 = (2 * tid + 1 < n_chunks) ? (uint32_t)counts[2 * tid + 1] : 0u;
-  uint32_t total;
-  const uint32_t o = merge_excl_scan(c0 + c1, W.scn, &total);
-  if (2 * tid < n_chunks) W.off[2 * tid] = (int)o;
-  if (2 * tid + 1 < n_chunks) W.off[2 * tid + 1] = (int)(o + c0);
-  if (tid == 0) W.off[n_chunks] = (int)total;
-  __syncthreads();
-}
-
 // The exact top-k of one (sequence, KV head)'s candidate lists (at most
-// kRoundCap of them: larger sets take merge_global), run by the whole
+// kRoundCap of them: larger sets take rank_global), run by the whole
 // workgroup in one pass: the lists are copied into the LDS list in page order
 // and ranked there; leaves the kept sort keys and blocks, in page order, in
 // W.x / W.blk and returns their count.
-__device__ int merge_lists(MergeLds& W, const unsigned long long* src, const int32_t* src_blk,
-                           const int32_t* counts, int n_chunks, int chunk, int k) {
+__device__ int merge_lists(MergeLds& W, const CandLists& L, int k) {
   const int tid = threadIdx.x;
-  merge_chunk_offsets(W, counts, n_chunks);
-  const int n = W.off[n_chunks];  // <= kRoundCap (the caller's condition)
+  rank_list_offsets<kMergeThreads>(W.r, L);
+  const int n = W.r.off[L.nc];  // <= kRoundCap (the caller's condition)
   unsigned long long xv[kMergeEpt];
   int bv[kMergeEpt];
 #pragma unroll
@@ -569,14 +532,14 @@ __device__ int merge_lists(MergeLds& W, const unsigned long long* src, const int
     int sidx = 0;
     if (e < n) {
       int c = 0;
-      for (int lo = 0, hi = n_chunks - 1; lo <= hi;) {
+      for (int lo = 0, hi = L.nc - 1; lo <= hi;) {
         const int mid = (lo + hi) >> 1;
-        if (W.off[mid] <= e) { c = mid; lo = mid + 1; } else hi = mid - 1;
+        if (W.r.off[mid] <= e) { c = mid; lo = mid + 1; } else hi = mid - 1;
       }
-      sidx = c * chunk + (e - W.off[c]);
+      sidx = c * L.chunk + (e - W.r.off[c]);
     }
-    xv[i] = src[sidx];
-    bv[i] = src_blk[sidx];
+    xv[i] = L.x[sidx];
+    bv[i] = L.blk[sidx];
   }
 #pragma unroll
   for (int i = 0; i < kMergeEpt; ++i) {
@@ -608,7 +571,7 @@ __device__ int merge_lists(MergeLds& W, const unsigned long long* src, const int
     }
   }
   uint32_t kept;
-  uint32_t dst = merge_excl_scan(ns, W.scn, &kept);
+  uint32_t dst = rank_excl_scan<kMergeThreads>(ns, W.r.scn, &kept);
 #pragma unroll
   for (int i = 0; i < kMergeEpt; ++i)
     if ((sel >> i) & 1u) {
@@ -620,366 +583,54 @@ __device__ int merge_lists(MergeLds& W, const unsigned long long* src, const int
   return (int)kept;
 }
 
-// Candidate sets larger than one LDS list: the k-th largest sort key is
-// found by a radix select over every candidate where it lies (the lists stay
-// in L2): after the high bits all candidates share, digits of up to 11 bits
-// of the key's 32 order bits, one histogram pass each; then one pass in page
-// order writes the selected ids.
-// A candidate whose fixed high bits (prefix) exceed the chosen ones is
-// "above" (kept), equal is "live", lower is out; live candidates left when
-// all 32 bits are fixed have equal keys, and the earliest (lowest page ids)
-// take the remaining places.
-constexpr int kGlobalEpt = 16;     // consecutive candidates per thread per batch
-
-// 2: above, 1: live, 0: out, for `plen` fixed high bits equal to `prefix`
-__device__ __forceinline__ int global_class(uint32_t u, int plen, uint32_t prefix) {
-  if (plen == 0) return 1;
-  const uint32_t h = u >> (32 - plen);
-  return h > prefix ? 2 : (h == prefix ? 1 : 0);
-}
-
-// Calls f(u) for the order bits of every candidate of this thread's
-// contiguous slice of the lists, 8 loads in flight at a time.
-template <class F>
-__device__ __forceinline__ void global_for_each(const MergeLds& W, const unsigned long long* src,
-                                                int n_chunks, int chunk, int total, F&& f) {
-  const int per = (total + kMergeThreads - 1) / kMergeThreads;
-  const int e_begin = min(total, (int)threadIdx.x * per), e_end = min(total, e_begin + per);
-  int c = 0;
-  if (e_begin < e_end)
-    for (int lo = 0, hi = n_chunks - 1; lo <= hi;) {
-      const int mid = (lo + hi) >> 1;
-      if (W.off[mid] <= e_begin) { c = mid; lo = mid + 1; } else hi = mid - 1;
-    }
-  for (int e = e_begin; e < e_end; e += 8) {
-    int idx[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      idx[i] = 0;
-      if (e + i < e_end) {
-        while (W.off[c + 1] <= e + i) ++c;
-        idx[i] = c * chunk + (e + i - W.off[c]);
-      }
-    }
-    uint32_t u[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) u[i] = (uint32_t)(src[idx[i]] >> 32);
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (e + i < e_end) f(u[i]);
-  }
-}
-
-// Not inlined: the register path of the merge kernel keeps its own allocation
-// (inlined, it made the usual workloads 0.5-1 us slower per step).
-__device__ __attribute__((noinline)) void merge_global(MergeLds& W, const unsigned long long* src, const int32_t* src_blk,
-                             const int32_t* counts, int n_chunks, int chunk, int k, int32_t* out,
-                             int32_t* outb) {
-  const int tid = threadIdx.x;
-  merge_chunk_offsets(W, counts, n_chunks);
-  const int total = W.off[n_chunks];
-
-  // the high bits every candidate shares are fixed at once (their keys lie
-  // in a narrow range: a first digit over them would put nearly all into one
-  // bucket, one LDS address)
-  uint32_t mn = 0xffffffffu, mx = 0u;
-  global_for_each(W, src, n_chunks, chunk, total, [&](uint32_t u) {
-    mn = min(mn, u);
-    mx = max(mx, u);
-  });
-  mn = wave_min_u32(mn);
-  mx = wave_max_u32(mx);
-  if ((tid & 63) == 0) { W.red3[1][tid >> 6] = mn; W.red3[2][tid >> 6] = mx; }
-  __syncthreads();
-  mn = 0xffffffffu;
-  mx = 0u;
-#pragma unroll
-  for (int w = 0; w < kMW; ++w) {
-    mn = min(mn, W.red3[1][w]);
-    mx = max(mx, W.red3[2][w]);
-  }
-  __syncthreads();  // W.red3 free again
-  int plen = (mn == mx) ? 32 : __builtin_clz(mn ^ mx);
-  uint32_t prefix = (plen == 0) ? 0u : (plen == 32 ? mn : mn >> (32 - plen));
-  int need = k;
-  bool all_live = false;  // the live set is exactly the `need` still to take
-  for (int level = 0; level < 3 && plen < 32; ++level) {
-    const int width = min(11, 32 - plen), shift = 32 - plen - width;
-#pragma unroll
-    for (int q = 0; q < kMergeBpt; ++q) W.hist[kMergeBpt * tid + q] = 0u;
-    __syncthreads();
-    global_for_each(W, src, n_chunks, chunk, total, [&](uint32_t u) {
-      if (global_class(u, plen, prefix) == 1) atomicAdd(&W.hist[(u >> shift) & ((1u << width) - 1u)], 1u);
-    });
-    __syncthreads();
-    // the digit holding the need-th live key, from the top
-    uint32_t hb[kMergeBpt], mine = 0;
-#pragma unroll
-    for (int q = 0; q < kMergeBpt; ++q) {
-      hb[q] = W.hist[kMergeBpt * tid + q];
-      mine += hb[q];
-    }
-    uint32_t tot;
-    const uint32_t pre = merge_excl_scan(mine, W.scn, &tot);
-    uint32_t acc = tot - pre - mine;
-#pragma unroll
-    for (int q = kMergeBpt - 1; q >= 0; --q) {
-      if (acc < (uint32_t)need && (uint32_t)need <= acc + hb[q]) {
-        W.bstar = kMergeBpt * tid + q;
-        W.babove = acc;
-        W.red3[0][0] = hb[q];
-      }
-      acc += hb[q];
-    }
-    __syncthreads();
-    prefix = (prefix << width) | (uint32_t)W.bstar;
-    plen += width;
-    need -= (int)W.babove;
-    const uint32_t in_digit = W.red3[0][0];
-    __syncthreads();  // hist, bstar, red3 free again
-    if ((int)in_digit == need) { all_live = true; break; }
-  }
-
-  // ---- output pass in page order: above, then live ones while `need` lasts
-  int nsel = 0, nlive = 0;
-  for (int base = 0; base < total; base += kMergeThreads * kGlobalEpt) {
-    const int e0 = base + tid * kGlobalEpt;
-    int c = 0;
-    if (e0 < total)
-      for (int lo = 0, hi = n_chunks - 1; lo <= hi;) {
-        const int mid = (lo + hi) >> 1;
-        if (W.off[mid] <= e0) { c = mid; lo = mid + 1; } else hi = mid - 1;
-      }
-    unsigned long long xv[kGlobalEpt];
-    int bv[kGlobalEpt], cls[kGlobalEpt];
-    uint32_t nl = 0;
-#pragma unroll
-    for (int i = 0; i < kGlobalEpt; ++i) {
-      const int e = e0 + i;
-      int sidx = 0;
-      if (e < total) {
-        while (W.off[c + 1] <= e) ++c;
-        sidx = c * chunk + (e - W.off[c]);
-      }
-      xv[i] = src[sidx];
-      bv[i] = src_blk[sidx];
-      cls[i] = (e < total) ? global_class((uint32_t)(xv[i] >> 32), plen, prefix) : 0;
-      nl += cls[i] == 1 ? 1u : 0u;
-    }
-    uint32_t live_tot;
-    uint32_t lrank = (uint32_t)nlive + merge_excl_scan(nl, W.scn, &live_tot);
-    uint32_t ns = 0;
-#pragma unroll
-    for (int i = 0; i < kGlobalEpt; ++i) {
-      if (cls[i] == 1) {
-        if (!all_live && lrank >= (uint32_t)need) cls[i] = 0;
-        ++lrank;
-      }
-      ns += cls[i] != 0 ? 1u : 0u;
-    }
-    __syncthreads();  // W.scn read by every thread before it is reused
-    uint32_t sel_tot;
-    uint32_t pos = (uint32_t)nsel + merge_excl_scan(ns, W.scn, &sel_tot);
-#pragma unroll
-    for (int i = 0; i < kGlobalEpt; ++i)
-      if (cls[i] != 0) {
-        if (pos < (uint32_t)k) {
-          out[pos] = (int32_t)(0xffffffffu - (uint32_t)(xv[i] & 0xffffffffu));
-          outb[pos] = bv[i];
-        }
-        ++pos;
-      }
-    nlive += (int)live_tot;
-    nsel += (int)sel_tot;
-    __syncthreads();
-  }
-  for (int i = nsel + tid; i < k; i += kMergeThreads) {
-    out[i] = -1;
-    outb[i] = -1;
-  }
-}
-
-constexpr int kFastPerLane = 16;
-constexpr int kFastCap = 64 * kFastPerLane;  // candidates ranked in registers
-// the register path's histogram: kFastBpl buckets per lane (512 in all; at
-// most 1024 candidates, 2^9 of range per pass resolves the k-th key in about
-// as many passes as 2048 buckets, with a quarter of the LDS clears and reads:
-// -0.2 to -0.9 us per step)
-constexpr int kFastBpl = 8;
-constexpr int kFastBuckets = 64 * kFastBpl;
-// LDS slot of fast-path bucket bk, lane l owning buckets [kFastBpl l, +kFastBpl):
-// lane-major, so the lanes reading their q-th bucket hit different banks
-__device__ __forceinline__ int fast_slot(int bk) { return ((bk % kFastBpl) << 6) | (bk / kFastBpl); }
-
-// One workgroup per (sequence, KV head). Fast path (every chunk list fits
-// the speculative slots, at most 1024 candidates), wave 0 alone: the counts
-// and the first S slots of every chunk list arrive in one round trip, and the
-// candidates are ranked in registers, 16 contiguous ones per lane, so lane
-// order is page order. Otherwise the workgroup's LDS rounds (merge_lists).
+// One workgroup per (sequence, KV head); writes the kept ids and their
+// blocks in page order, -1 past them.
 __global__ __launch_bounds__(kMergeThreads) void select_merge_kernel(SelectArgs a) {
   const int kvh = blockIdx.x, b = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, wave = tid >> 6;
   __shared__ MergeLds W;
   const size_t head = (size_t)b * a.Hkv + kvh;
   const int nc = a.n_chunks;
-  const int32_t* counts = a.cand_count + head * nc;
-  const unsigned long long* src = a.cand + head * nc * a.chunk;
-  const int32_t* src_blk = a.cand_blk + head * nc * a.chunk;
+  const CandLists L{a.cand + head * nc * a.chunk, a.cand_blk + head * nc * a.chunk,
+                    a.cand_count + head * nc, nc, a.chunk};
   int32_t* out = a.selected + head * a.k;
   int32_t* outb = a.sel_blk + head * a.k;
+  auto emit = [out, outb](int pos, int id, int blk) {
+    out[pos] = id;
+    outb[pos] = blk;
+  };
 
-  // slots per chunk loaded speculatively: a power of two with nc * S <= 1024
-  const int lgS = 31 - __builtin_clz(max(1, kFastCap / nc));
-  const int S = 1 << lgS;
-  int ccnt[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int c = lane + 64 * i;
-    ccnt[i] = (c < nc) ? counts[c] : 0;
-  }
-  // (wave 0 only: every wave reads the counts to take the same path)
+  // every wave reads the counts while wave 0 gathers speculatively
+  const int lgS = fast_lg_slots(nc);
+  int cc[16];
+  fast_count_load(L, cc);
   unsigned long long x[kFastPerLane];
   int bl[kFastPerLane], cof[kFastPerLane];
-#pragma unroll
-  for (int i = 0; i < kFastPerLane; ++i) {
-    x[i] = 0;
-    bl[i] = 0;
-    cof[i] = 0;
-  }
-  if (wave == 0) {
-#pragma unroll
-    for (int i = 0; i < kFastPerLane; ++i) {
-      const int e = lane * kFastPerLane + i;
-      const int c = e >> lgS, sl = e & (S - 1);
-      const int idx = (c < nc) ? c * a.chunk + sl : 0;
-      x[i] = src[idx];
-      bl[i] = src_blk[idx];
-      cof[i] = (c < nc) ? counts[c] : 0;
-    }
-  }
-  int total = 0;
-  bool over = false;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    total += ccnt[i];
-    over |= ccnt[i] > S;
-  }
-  total = (int)wave_sum_u32((uint32_t)total);
-  if (__ballot(over) != 0) {  // the same in every wave
+  if (wave == 0) fast_slots_load(L, lgS, x, bl, cof);
+  int total;
+  const bool over = fast_count_check(L, lgS, cc, &total);  // the same in every wave
+  if (over && total > kFastCap) {
     if (total > kRoundCap) {
-      merge_global(W, src, src_blk, counts, nc, a.chunk, a.k, out, outb);
+      rank_global<kMergeThreads>(W.r, L, a.k, emit);
       return;
     }
-    const int nk = merge_lists(W, src, src_blk, counts, nc, a.chunk, a.k);
+    const int nk = merge_lists(W, L, a.k);
     for (int i = tid; i < a.k; i += kMergeThreads) {
       out[i] = (i < nk) ? (int32_t)(0xffffffffu - (uint32_t)(W.x[i] & 0xffffffffu)) : -1;
       outb[i] = (i < nk) ? W.blk[i] : -1;
     }
     return;
   }
-  (void)total;
-  if (wave != 0) return;  // the fast path has no barrier
-
-  uint32_t live = 0, sel = 0;
-#pragma unroll
-  for (int i = 0; i < kFastPerLane; ++i) {
-    const int e = lane * kFastPerLane + i;
-    if ((e >> lgS) < nc && (e & (S - 1)) < cof[i]) live |= 1u << i;
-  }
-  int need = a.k;
-  for (int iter = 0; iter < 8; ++iter) {
-    uint32_t cnt = __popc(live), lo = 0xffffffffu, hi = 0u;
-#pragma unroll
-    for (int i = 0; i < kFastPerLane; ++i)
-      if ((live >> i) & 1u) {
-        const uint32_t v = (uint32_t)(x[i] >> 32);
-        lo = min(lo, v);
-        hi = max(hi, v);
-      }
-    cnt = wave_sum_u32(cnt);
-    lo = wave_min_u32(lo);
-    hi = wave_max_u32(hi);
-    if ((int)cnt <= need) { sel |= live; live = 0; break; }
-    if (lo == hi) break;
-    const float scale = (float)kFastBuckets / ((float)(hi - lo) + 1.0f);
-#pragma unroll
-    for (int q = 0; q < kFastBpl; ++q) W.hist[(q << 6) | lane] = 0u;
-    wave_lds_sync();
-    int bk[kFastPerLane];
-#pragma unroll
-    for (int i = 0; i < kFastPerLane; ++i) {
-      bk[i] = -1;
-      if ((live >> i) & 1u) {
-        bk[i] = min(kFastBuckets - 1, (int)((float)((uint32_t)(x[i] >> 32) - lo) * scale));
-        atomicAdd(&W.hist[fast_slot(bk[i])], 1u);
-      }
-    }
-    wave_lds_sync();
-    uint32_t hb[kFastBpl];
-    uint32_t mine = 0;
-#pragma unroll
-    for (int q = 0; q < kFastBpl; ++q) {
-      hb[q] = W.hist[(q << 6) | lane];
-      mine += hb[q];
-    }
-    const uint32_t pre = wave_incl_scan(mine);
-    const uint32_t tot = __builtin_amdgcn_readlane(pre, 63);
-    uint32_t acc = tot - pre;
-    int bstar = -1;
-    uint32_t above = 0;
-#pragma unroll
-    for (int q = kFastBpl - 1; q >= 0; --q) {
-      if (acc < (uint32_t)need && (uint32_t)need <= acc + hb[q]) { bstar = kFastBpl * lane + q; above = acc; }
-      acc += hb[q];
-    }
-    const uint64_t owner = __ballot(bstar >= 0);
-    if (owner == 0) break;  // unreachable: some bucket holds the need-th key
-    const int srcl = __builtin_ctzll(owner);
-    bstar = __builtin_amdgcn_readlane(bstar, srcl);
-    above = __builtin_amdgcn_readlane(above, srcl);
-#pragma unroll
-    for (int i = 0; i < kFastPerLane; ++i)
-      if ((live >> i) & 1u) {
-        if (bk[i] > bstar) sel |= 1u << i;
-        if (bk[i] != bstar) live &= ~(1u << i);
-      }
-    need -= (int)above;
-    wave_lds_sync();
-  }
-  if (__ballot(live != 0) != 0) {
-    // live keys all equal: the earliest (lowest page ids) win
-    const uint32_t nl = __popc(live);
-    int before = (int)(wave_incl_scan(nl) - nl);
-#pragma unroll
-    for (int i = 0; i < kFastPerLane; ++i)
-      if ((live >> i) & 1u) {
-        if (before < need) sel |= 1u << i;
-        ++before;
-      }
-  }
-  // ---- write the kept pages in page order, then the -1 tail
-  const uint32_t ns = __popc(sel);
-  const uint32_t pre = wave_incl_scan(ns);
-  const int nk = (int)__builtin_amdgcn_readlane(pre, 63);
-  int o = (int)(pre - ns);
-#pragma unroll
-  for (int i = 0; i < kFastPerLane; ++i)
-    if ((sel >> i) & 1u) {
-      out[o] = (int32_t)(0xffffffffu - (uint32_t)(x[i] & 0xffffffffu));
-      outb[o] = bl[i];
-      ++o;
-    }
-  for (int i = nk + lane; i < a.k; i += 64) {
-    out[i] = -1;
-    outb[i] = -1;
-  }
+  if (wave != 0) return;  // the register path has no barrier
+  const uint32_t live = over ? fast_gather_exact(L, W.r.off, total, x, bl) : fast_slots_live(L, lgS, cof);
+  fast_emit(x, bl, fast_rank(x, live, a.k, W.r.hist), a.k, emit);
 }
 
 }  // namespace
 
 hipError_t launch_select(const locks_dims& d, const WsLayout& L, const DevPtrs& P,
                          const int32_t* pt, const int32_t* sl, const int32_t* fill,
-                         int32_t* selected, hipStream_t s) {
+                         int32_t* selected, bool merge, hipStream_t s) {
   SelectArgs a;
   a.scores = P.scores;
   a.score_part = P.score_part;
@@ -1016,7 +667,8 @@ hipError_t launch_select(const locks_dims& d, const WsLayout& L, const DevPtrs& 
     default: return hipErrorInvalidValue;
   }
 #undef LOCKS_CHUNK
-  hipLaunchKernelGGL(select_merge_kernel, dim3(d.n_kv_heads, d.batch), dim3(kMergeThreads), 0, s, a);
+  if (merge)
+    hipLaunchKernelGGL(select_merge_kernel, dim3(d.n_kv_heads, d.batch), dim3(kMergeThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -115,6 +115,38 @@ def test_bit_exact_ties_at_the_cutoff_go_to_the_lower_ids(locks, ctx, budget, du
     say(f"  {above} above the tie, {w.k_pages - above} of {len(tied)} tied pages kept")
 
 
+@pytest.mark.parametrize("config,hkv,hq", [(2, 32, 32), (2, 16, 32), (4, 8, 32), (2, 4, 32), (5, 2, 32)],
+                         ids=["G1", "G2", "G4", "G8", "G16"])
+def test_ranking_inside_attention_matches_the_merge_launch(locks, config, hkv, hq):
+    """At budgets of at most 256 pages the decode step has no merge launch:
+    every sparse attention workgroup ranks its (sequence, KV head)'s candidate
+    lists itself. Three 1024-page select chunks (256 speculative slots each)
+    and three sequences reach its three ways in: 1000 pages, fewer 16-page
+    tiles than k (no bound: every page a candidate, all in the first chunk, at
+    most 1024 in all: the exact register gather); 2000 pages (2000 candidates:
+    the workgroup radix select); 3000 pages (bounded: a few hundred
+    candidates). The selection and output must equal, bit for bit, the
+    separate select launch (with its merge) followed by attention on that
+    selection, and the oracle within its bars."""
+    budget = 2048
+    say(f"ranking inside attention G={hq // hkv}")
+    w = workloads.make(config, device=DEV, ctx=16 * 3000, batch=3, budget=budget, n_kv_heads=hkv,
+                       n_q_heads=hq, seq_lens=[16 * 1000 + 5, 16 * 2000 + 9, 16 * 3000], seed=31)
+    summ = locks.build_summaries(w.k_cache, w.page_table, w.seq_lens)
+    r = decode_and_check(w, summ)
+    ws = locks.new_workspace(locks.make_dims(w.q, w.k_cache, w.page_table), budget, DEV)
+    sel = torch.full_like(r["sel"], -7)
+    out = torch.full_like(w.q, float("nan"))
+    locks.score_pages(w.q, summ, w.k_cache, w.page_table, w.seq_lens, budget, ws)
+    locks.select_pages(w.q, w.k_cache, w.page_table, w.seq_lens, budget, sel, ws)
+    locks.sparse_attention(w.q, w.k_cache, w.v_cache, w.page_table, w.seq_lens, budget, sel, out, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(sel, r["sel"]), "selection differs from the merge launch's"
+    assert torch.equal(out, r["out"]), "output differs from attention on the merge launch's selection"
+    g = r["sel"].cpu().numpy()
+    assert np.all(g[0, :, :] >= 0) and np.all(g[1, :, :] >= 0)  # k = 128 of 1000 and of 2000
+
+
 def test_decode_parity_on_oracle_built_summaries(locks):
     """Summaries packed by the oracle, decoded by the GPU: the record format is
     read the same way on both sides."""
