@@ -64,22 +64,25 @@ struct RankSpace<false> {
 };
 
 // The kept list of this workgroup's (sequence, KV head), ranked here from the
-// chunk lists exactly as the select merge launch does: the blocks of list
-// entries [s0, s0 + pages_per_split) go to sblk (-1 past the kept pages), and
-// split 0 writes the kept ids, the step's selection output. Every thread
-// calls it; the caller's next barrier publishes sblk.
+// chunk lists exactly as the select merge launch does; of it, this split's
+// entries [s0, s0 + pages_per_split): their blocks go to sblk and their ids
+// to the step's selection output (-1 past the kept pages), so the splits
+// together write the whole list. Every thread calls it; the caller's next
+// barrier publishes sblk.
 __device__ __forceinline__ void rank_split(const AttnArgs& a, RankSpace<true>& RS, size_t head, int split) {
   const int wave = threadIdx.x >> 6;
   const size_t lists = head * a.n_chunks;
   const CandLists L{a.cand + lists * a.chunk, a.cand_blk + lists * a.chunk, a.cand_count + lists,
                     a.n_chunks, a.chunk};
   const int s0 = split * a.pages_per_split, pps = a.pages_per_split;
-  int32_t* ids = (split == 0) ? a.sel_out + head * a.k : nullptr;
+  int32_t* ids = a.sel_out + head * a.k;
   int* sblk = RS.sblk;
   auto emit = [ids, sblk, s0, pps](int pos, int id, int blk) {
-    if (ids) ids[pos] = id;
     const unsigned r = (unsigned)(pos - s0);
-    if (r < (unsigned)pps) sblk[r] = blk;
+    if (r < (unsigned)pps) {
+      ids[pos] = id;
+      sblk[r] = blk;
+    }
   };
   // every wave reads the counts while wave 0 gathers speculatively
   const int lgS = fast_lg_slots(L.nc);
@@ -96,7 +99,7 @@ __device__ __forceinline__ void rank_split(const AttnArgs& a, RankSpace<true>& R
   }
   if (wave != 0) return;
   const uint32_t live = over ? fast_gather_exact(L, RS.r.off, total, x, bl) : fast_slots_live(L, lgS, cof);
-  fast_emit(x, bl, fast_rank(x, live, a.k, RS.r.hist), a.k, emit);
+  fast_emit(x, bl, fast_rank(x, live, a.k, !over, RS.r.hist), a.k, !over, s0, s0 + pps, emit);
 }
 
 // RANK: the list is ranked here (rank_split) instead of read from sel_blk.
@@ -112,6 +115,16 @@ __global__ __launch_bounds__(256) void attend_kernel(AttnArgs a) {
   const int list_len = base_len + (tail > 0 ? 1 : 0);
   const int s0 = split * a.pages_per_split;
   __shared__ RankSpace<RANK> RS;
+  // q of the group, base-2 logit scale: loaded first, so that a ranking
+  // launch's wave 0 finds it arrived when it stages its share after ranking
+  constexpr int QPT = (G * kDim + 255) / 256;  // q values per thread
+  const float qscale = kLog2e * kInvSqrtD;
+  float qv[QPT];
+#pragma unroll
+  for (int j = 0; j < QPT; ++j) {
+    const int i = tid + 256 * j;
+    qv[j] = (i < G * kDim) ? a.q[((size_t)b * a.Hq + (size_t)kvh * G) * kDim + i] * qscale : 0.f;
+  }
   if constexpr (RANK) rank_split(a, RS, (size_t)b * a.Hkv + kvh, split);
   // the first entry's block id: a selected page (entry < k) needs no sequence
   // length, so its load goes out together with the length's
@@ -171,9 +184,11 @@ __global__ __launch_bounds__(256) void attend_kernel(AttnArgs a) {
     blk_next = (s0 + wave + 4 < s1) ? page_block(s0 + wave + 4) : -1;
   }
 
-  const float qscale = kLog2e * kInvSqrtD;  // logits in base-2 units
-  for (int i = tid; i < G * kDim; i += 256)
-    q_s[i / kDim][i % kDim] = a.q[((size_t)b * a.Hq + (size_t)kvh * G) * kDim + i] * qscale;
+#pragma unroll
+  for (int j = 0; j < QPT; ++j) {  // logits in base-2 units
+    const int i = tid + 256 * j;
+    if (i < G * kDim) q_s[i / kDim][i % kDim] = qv[j];
+  }
   __syncthreads();
   if constexpr (RANK) {
     blk = (s0 + wave < s1) ? page_block(s0 + wave) : -1;

@@ -10,10 +10,12 @@
 // order, and the ranking keeps that order, so the kept ids come out ascending
 // without a sort.
 //
-// Register path (one wave, no barrier): at most kFastCap candidates, 16
-// consecutive ones per lane, so lane order is page order. Gathered in one
-// round trip with the list counts when every list fits kFastCap/n_lists
-// speculative slots, else (still at most kFastCap in all) after the counts.
+// Register path (one wave, no barrier): at most kFastCap candidates, 16 per
+// lane. Gathered in one round trip with the list counts when every list fits
+// kFastCap/n_lists speculative slots, entry 64 i + lane in slot i of each lane
+// (so each load instruction reads 64 consecutive slots and page order is
+// (slot, lane) order); else (still at most kFastCap in all) after the counts,
+// entry 16 lane + i (lane order is page order).
 // Ranked by bucket refinement: a 512-bucket histogram over the live key range
 // picks the bucket holding the k-th key; candidates above it are in, below it
 // out; repeat inside it until the count fits or every live key is equal, where
@@ -94,8 +96,8 @@ __device__ __forceinline__ bool fast_count_check(const CandLists& L, int lgS, co
   return __ballot(over) != 0;
 }
 
-// Speculative gather (one wave): lane l's entries e = 16 l + i are slot e % S
-// of list e / S, S = 2^lgS, with that list's count in cof.
+// Speculative gather (one wave): entry e = 64 i + lane (slot i of the lane)
+// is slot e % S of list e / S, S = 2^lgS, with that list's count in cof.
 __device__ __forceinline__ void fast_slots_load(const CandLists& L, int lgS,
                                                 unsigned long long (&x)[kFastPerLane],
                                                 int (&bl)[kFastPerLane], int (&cof)[kFastPerLane]) {
@@ -103,7 +105,7 @@ __device__ __forceinline__ void fast_slots_load(const CandLists& L, int lgS,
   const int S = 1 << lgS;
 #pragma unroll
   for (int i = 0; i < kFastPerLane; ++i) {
-    const int e = lane * kFastPerLane + i;
+    const int e = 64 * i + lane;
     const int c = e >> lgS, sl = e & (S - 1);
     const int idx = (c < L.nc) ? c * L.chunk + sl : 0;
     x[i] = L.x[idx];
@@ -119,7 +121,7 @@ __device__ __forceinline__ uint32_t fast_slots_live(const CandLists& L, int lgS,
   uint32_t live = 0;
 #pragma unroll
   for (int i = 0; i < kFastPerLane; ++i) {
-    const int e = lane * kFastPerLane + i;
+    const int e = 64 * i + lane;
     live |= ((e >> lgS) < L.nc && (e & ((1 << lgS) - 1)) < cof[i]) ? 1u << i : 0u;
   }
   return live;
@@ -127,8 +129,9 @@ __device__ __forceinline__ uint32_t fast_slots_live(const CandLists& L, int lgS,
 
 // Exact gather (one wave) of total <= kFastCap candidates when some list
 // overflowed its speculative slots: list offsets by a wave scan into off
-// (LDS, nc + 1 words), then entry e = 16 l + i < total from the list holding
-// it. Returns the lane's live bits (entries below total).
+// (LDS, nc + 1 words), then entry e = 16 lane + i < total (lane-major: one
+// search per lane, then consecutive entries) from the list holding it.
+// Returns the lane's live bits (entries below total).
 __device__ __forceinline__ uint32_t fast_gather_exact(const CandLists& L, int* off, int total,
                                                       unsigned long long (&x)[kFastPerLane],
                                                       int (&bl)[kFastPerLane]) {
@@ -174,11 +177,18 @@ __device__ __forceinline__ uint32_t fast_gather_exact(const CandLists& L, int* o
   return live;
 }
 
-// Ranks the live candidates (one wave; lane order is page order) and returns
-// the lane's kept bits: the k largest sort keys, or every live one if fewer.
-// hist: kFastBuckets words of LDS that only this wave uses.
+// Lanes below this one whose bit is set in the wave mask m.
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Ranks the live candidates (one wave) and returns the lane's kept bits: the
+// k largest sort keys, or every live one if fewer. imajor: page order is
+// (slot, lane) order (the speculative gather), else lane order (the exact
+// gather); it decides only which of several equal keys are kept. hist:
+// kFastBuckets words of LDS that only this wave uses.
 __device__ __forceinline__ uint32_t fast_rank(const unsigned long long (&x)[kFastPerLane], uint32_t live,
-                                              int k, uint32_t* hist) {
+                                              int k, bool imajor, uint32_t* hist) {
   const int lane = threadIdx.x & 63;
   uint32_t sel = 0;
   int need = k;
@@ -243,36 +253,68 @@ __device__ __forceinline__ uint32_t fast_rank(const unsigned long long (&x)[kFas
   }
   if (__ballot(live != 0) != 0) {
     // live keys all equal: the earliest (lowest page ids) win
-    const uint32_t nl = __popc(live);
-    int before = (int)(wave_incl_scan(nl) - nl);
+    if (imajor) {
+      int base = 0;
 #pragma unroll
-    for (int i = 0; i < kFastPerLane; ++i)
-      if ((live >> i) & 1u) {
-        if (before < need) sel |= 1u << i;
-        ++before;
+      for (int i = 0; i < kFastPerLane; ++i) {
+        const uint64_t m = __ballot((live >> i) & 1u);
+        if (((live >> i) & 1u) && base + lanes_below(m) < need) sel |= 1u << i;
+        base += __popcll(m);
       }
+    } else {
+      const uint32_t nl = __popc(live);
+      int before = (int)(wave_incl_scan(nl) - nl);
+#pragma unroll
+      for (int i = 0; i < kFastPerLane; ++i)
+        if ((live >> i) & 1u) {
+          if (before < need) sel |= 1u << i;
+          ++before;
+        }
+    }
   }
   return sel;
 }
 
-// Hands out the kept candidates (one wave): emit(pos, page id, block) at
-// positions 0, 1, ... in page order, then emit(pos, -1, -1) up to k.
+// Hands out the kept candidates (one wave) whose positions in the kept list
+// (page order; imajor as for fast_rank) fall in [w0, w1): emit(pos, page id,
+// block), and emit(pos, -1, -1) for the positions of [w0, w1) from the kept
+// count up to k.
 template <class Emit>
 __device__ __forceinline__ void fast_emit(const unsigned long long (&x)[kFastPerLane],
-                                          const int (&bl)[kFastPerLane], uint32_t sel, int k,
-                                          Emit&& emit) {
+                                          const int (&bl)[kFastPerLane], uint32_t sel, int k, bool imajor,
+                                          int w0, int w1, Emit&& emit) {
   const int lane = threadIdx.x & 63;
-  const uint32_t ns = __popc(sel);
-  const uint32_t pre = wave_incl_scan(ns);
-  const int nk = (int)__builtin_amdgcn_readlane(pre, 63);
-  int o = (int)(pre - ns);
+  auto id_of = [](unsigned long long v) { return (int)(0xffffffffu - (uint32_t)(v & 0xffffffffu)); };
+  int nk;
+  if (imajor) {
+    // slot i of every lane is one run of the list: a ballot places it
+    int base = 0;
 #pragma unroll
-  for (int i = 0; i < kFastPerLane; ++i)
-    if ((sel >> i) & 1u) {
-      emit(o, (int)(0xffffffffu - (uint32_t)(x[i] & 0xffffffffu)), bl[i]);
-      ++o;
+    for (int i = 0; i < kFastPerLane; ++i) {
+      const uint64_t m = __ballot((sel >> i) & 1u);
+      const int n = __popcll(m);
+      if (base < w1 && base + n > w0 && ((sel >> i) & 1u)) {
+        const int pos = base + lanes_below(m);
+        if (pos >= w0 && pos < w1) emit(pos, id_of(x[i]), bl[i]);
+      }
+      base += n;
     }
-  for (int i = nk + lane; i < k; i += 64) emit(i, -1, -1);
+    nk = base;
+  } else {
+    const uint32_t ns = __popc(sel);
+    const uint32_t pre = wave_incl_scan(ns);
+    nk = (int)__builtin_amdgcn_readlane(pre, 63);
+    int o = (int)(pre - ns);
+    if (o < w1 && o + (int)ns > w0) {
+#pragma unroll
+      for (int i = 0; i < kFastPerLane; ++i)
+        if ((sel >> i) & 1u) {
+          if (o >= w0 && o < w1) emit(o, id_of(x[i]), bl[i]);
+          ++o;
+        }
+    }
+  }
+  for (int i = max(nk, w0) + lane; i < min(k, w1); i += 64) emit(i, -1, -1);
 }
 
 // ----------------------------------------------------------- workgroup path

@@ -623,7 +623,7 @@ __global__ __launch_bounds__(kMergeThreads) void select_merge_kernel(SelectArgs 
   }
   if (wave != 0) return;  // the register path has no barrier
   const uint32_t live = over ? fast_gather_exact(L, W.r.off, total, x, bl) : fast_slots_live(L, lgS, cof);
-  fast_emit(x, bl, fast_rank(x, live, a.k, W.r.hist), a.k, emit);
+  fast_emit(x, bl, fast_rank(x, live, a.k, !over, W.r.hist), a.k, !over, 0, a.k, emit);
 }
 
 }  // namespace
