@@ -39,7 +39,7 @@ constexpr int kFastBuckets = 64 * kFastBpl;
 
 // LDS slot of register-path bucket bk, lane l owning buckets [kFastBpl l, +kFastBpl):
 // lane-major, so the lanes reading their q-th bucket hit different banks
-__device__ __forceinline__ int fast_slot(int bk) { return ((bk % kFastBpl) << 6) | (bk / kFastBpl); }
+__device__ __forceinline__ uint32_t fast_slot(uint32_t bk) { return ((bk % kFastBpl) << 6) | (bk / kFastBpl); }
 
 // One (sequence, KV head)'s candidate lists: list c holds count[c] sort keys
 // (and their physical blocks) at x[c * chunk ...], in page order.
@@ -186,38 +186,41 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
 // k largest sort keys, or every live one if fewer. imajor: page order is
 // (slot, lane) order (the speculative gather), else lane order (the exact
 // gather); it decides only which of several equal keys are kept. hist:
-// kFastBuckets words of LDS that only this wave uses.
+// kFastBuckets + 64 words of LDS that only this wave uses (the last 64 take
+// the increments of dead slots, one per lane, so that no branch skips them).
 __device__ __forceinline__ uint32_t fast_rank(const unsigned long long (&x)[kFastPerLane], uint32_t live,
                                               int k, bool imajor, uint32_t* hist) {
   const int lane = threadIdx.x & 63;
   uint32_t sel = 0;
   int need = k;
+  // every step is branch-free over the 16 slots: dead slots take neutral
+  // values and a private histogram word
   for (int iter = 0; iter < 8; ++iter) {
     uint32_t cnt = __popc(live), lo = 0xffffffffu, hi = 0u;
 #pragma unroll
-    for (int i = 0; i < kFastPerLane; ++i)
-      if ((live >> i) & 1u) {
-        const uint32_t v = (uint32_t)(x[i] >> 32);
-        lo = min(lo, v);
-        hi = max(hi, v);
-      }
+    for (int i = 0; i < kFastPerLane; ++i) {
+      const uint32_t v = (uint32_t)(x[i] >> 32);
+      const bool on = (live >> i) & 1u;
+      lo = min(lo, on ? v : 0xffffffffu);
+      hi = max(hi, on ? v : 0u);
+    }
     cnt = wave_sum_u32(cnt);
     lo = wave_min_u32(lo);
     hi = wave_max_u32(hi);
     if ((int)cnt <= need) { sel |= live; live = 0; break; }
     if (lo == hi) break;
-    const float scale = (float)kFastBuckets / ((float)(hi - lo) + 1.0f);
+    // any positive scale near kFastBuckets / range keeps the bucket map
+    // monotone, which is all the selection needs (out-of-range results clamp)
+    const float scale = (float)kFastBuckets * __builtin_amdgcn_rcpf((float)(hi - lo) + 1.0f);
 #pragma unroll
     for (int q = 0; q < kFastBpl; ++q) hist[(q << 6) | lane] = 0u;
     wave_lds_sync();
-    int bk[kFastPerLane];
+    uint32_t bk[kFastPerLane];
 #pragma unroll
     for (int i = 0; i < kFastPerLane; ++i) {
-      bk[i] = -1;
-      if ((live >> i) & 1u) {
-        bk[i] = min(kFastBuckets - 1, (int)((float)((uint32_t)(x[i] >> 32) - lo) * scale));
-        atomicAdd(&hist[fast_slot(bk[i])], 1u);
-      }
+      const bool on = (live >> i) & 1u;
+      bk[i] = min((uint32_t)(kFastBuckets - 1), (uint32_t)((float)((uint32_t)(x[i] >> 32) - lo) * scale));
+      atomicAdd(&hist[on ? fast_slot(bk[i]) : (uint32_t)(kFastBuckets + lane)], 1u);
     }
     wave_lds_sync();
     uint32_t hb[kFastBpl];
@@ -240,14 +243,16 @@ __device__ __forceinline__ uint32_t fast_rank(const unsigned long long (&x)[kFas
     const uint64_t owner = __ballot(bstar >= 0);
     if (owner == 0) break;  // unreachable: some bucket holds the need-th key
     const int srcl = __builtin_ctzll(owner);
-    bstar = __builtin_amdgcn_readlane(bstar, srcl);
+    const uint32_t bs = (uint32_t)__builtin_amdgcn_readlane(bstar, srcl);
     above = __builtin_amdgcn_readlane(above, srcl);
+    uint32_t gt = 0, eq = 0;
 #pragma unroll
-    for (int i = 0; i < kFastPerLane; ++i)
-      if ((live >> i) & 1u) {
-        if (bk[i] > bstar) sel |= 1u << i;
-        if (bk[i] != bstar) live &= ~(1u << i);
-      }
+    for (int i = 0; i < kFastPerLane; ++i) {
+      gt |= bk[i] > bs ? 1u << i : 0u;
+      eq |= bk[i] == bs ? 1u << i : 0u;
+    }
+    sel |= live & gt;
+    live &= eq;
     need -= (int)above;
     wave_lds_sync();
   }
