@@ -17,9 +17,12 @@
 //        max_g(unit max of s_hat_g - L_g) - log2 G, so the k-th largest of
 //        these per-unit bounds (over distinct units) cannot exceed the k-th
 //        largest key. One 2048-bucket histogram that keeps each bucket's
-//        smallest member gives that k-th largest bound. Units are pooled into
-//        super-ranges when the (head, unit) maxima exceed what LDS holds (the
-//        maximum over a super-range still bounds one of its pages).
+//        smallest member gives that k-th largest bound; it spans 128 (base-2
+//        log) below the largest bound, which the fold already knows (the max
+//        over heads of max s_hat_g - L_g), so no reduction finds its range.
+//        Units are pooled into super-ranges when the (head, unit) maxima
+//        exceed what LDS holds (the maximum over a super-range still bounds
+//        one of its pages).
 //        Computing this in every workgroup costs less than a launch of its
 //        own.
 //     b. the keys of the workgroup's <= 4096 pages as 64-bit sort keys
@@ -53,6 +56,9 @@ constexpr int kThreads = 1024;
 constexpr int kNW = kThreads / 64;
 constexpr int kHistBuckets = 2 * kThreads;                // 2 buckets per thread
 constexpr int kChunkEpt = kSelectChunk / kThreads;        // <= 4 pages per thread
+// log2 range of the bound histogram below the largest unit bound; bounds
+// further down share its lowest bucket (a looser but still valid threshold)
+constexpr float kBoundSpan = 128.0f;
 
 struct SelectArgs {
   const float* scores;
@@ -76,7 +82,6 @@ struct BoundLds {
 struct ChunkShared {
   BoundLds bound;
   uint32_t hcnt[kHistBuckets];
-  uint32_t red3[3][kNW];
   uint32_t scn[2][kNW];
   float redf[kNW][2];
   uint32_t wsum[kNW];
@@ -119,31 +124,6 @@ __device__ __forceinline__ void wave_lse2(float& m, float& s) {
     m = __uint_as_float(rm[0]);
     s = __uint_as_float(rs[0]);
     lse2_acc(m, s, __uint_as_float(rm[1]), __uint_as_float(rs[1]));
-  }
-}
-
-// Block-wide (count, min, max) of u32 triples for 1024 threads, one barrier
-// (red must not be reused before another barrier has passed).
-__device__ __forceinline__ void big_reduce3(uint32_t& c, uint32_t& mn, uint32_t& mx,
-                                            uint32_t (&red)[3][kNW]) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  c = wave_sum_u32(c);
-  mn = wave_min_u32(mn);
-  mx = wave_max_u32(mx);
-  if (lane == 0) {
-    red[0][wave] = c;
-    red[1][wave] = mn;
-    red[2][wave] = mx;
-  }
-  __syncthreads();
-  c = 0;
-  mn = 0xffffffffu;
-  mx = 0u;
-#pragma unroll
-  for (int w = 0; w < kNW; ++w) {
-    c += red[0][w];
-    mn = min(mn, red[1][w]);
-    mx = max(mx, red[2][w]);
   }
 }
 
@@ -289,18 +269,25 @@ __global__ __launch_bounds__(kThreads) void select_chunk_kernel(SelectArgs a) {
   }
   wave_lse2(lm, ls);
   if (lane == 0) { sh.redf[wave][0] = lm; sh.redf[wave][1] = ls; }
+  if (tid == 0) sh.tlb = -INFINITY;  // kept when fewer than k units have pages: no pruning
   __syncthreads();
   float L[G];  // base 2; every thread folds every head's wave partials itself
+  float top = -INFINITY;  // the largest unit bound plus log2 G: max over heads of (max s_hat_g - L_g)
 #pragma unroll
   for (int gg = 0; gg < G; ++gg) {
     float m = sh.redf[gg * WPG][0], sv = sh.redf[gg * WPG][1];
 #pragma unroll
     for (int w = 1; w < WPG; ++w) lse2_acc(m, sv, sh.redf[gg * WPG + w][0], sh.redf[gg * WPG + w][1]);
     L[gg] = (sv > 0.f) ? m + fast_log2(sv) : -INFINITY;
+    if (sv > 0.f) top = fmaxf(top, m - L[gg]);
   }
   const float log2G = (float)__builtin_ctz(G);
+  // bucket range of the bounds: [top - kBoundSpan, top] in order bits, known
+  // without a reduction (lower bounds share the lowest bucket)
+  const float topb = top - log2G;
+  const uint32_t hi = key_order_bits(topb), lo = key_order_bits(topb - kBoundSpan);
+  const float scale = (float)kHistBuckets / ((float)(hi - lo) + 1.0f);
   uint32_t lb[kLbPt];
-  uint32_t cnt = 0, lo = 0xffffffffu, hi = 0u;
 #pragma unroll
   for (int i = 0; i < kLbPt; ++i) {
     lb[i] = 0u;
@@ -313,27 +300,16 @@ __global__ __launch_bounds__(kThreads) void select_chunk_kernel(SelectArgs a) {
 #pragma unroll
       for (int gg = 0; gg < G; ++gg)
         if (mu[gg]) v = fmaxf(v, key_from_order_bits(mu[gg]) - L[gg]);
-      if (v > -INFINITY) {
-        lb[i] = key_order_bits(v - log2G);
-        ++cnt;
-        lo = min(lo, lb[i]);
-        hi = max(hi, lb[i]);
-      }
+      if (v > -INFINITY) lb[i] = key_order_bits(v - log2G);
     }
   }
-  big_reduce3(cnt, lo, hi, sh.red3);
-  float tlb;
-  if ((int)cnt < a.k) {
-    tlb = -INFINITY;  // fewer bound units than k: no pruning
-  } else if (lo == hi) {
-    tlb = key_from_order_bits(lo) - 1e-3f;
-  } else {
+  float tlb = -INFINITY;  // fewer than k units (some may hold no page): no pruning
+  if (nR >= a.k) {        // workgroup-uniform
     // the minimum of the bucket holding the k-th largest bound is at most it
-    const float scale = (float)kHistBuckets / ((float)(hi - lo) + 1.0f);
 #pragma unroll
     for (int i = 0; i < kLbPt; ++i)
       if (lb[i]) {
-        const int bk = hbucket(lb[i], lo, scale);
+        const int bk = hbucket(max(lb[i], lo), lo, scale);
         atomicAdd(&sh.hcnt[bk], 1u);
         atomicMin(&sh.bound.hmin[bk], lb[i]);
       }
@@ -347,7 +323,7 @@ __global__ __launch_bounds__(kThreads) void select_chunk_kernel(SelectArgs a) {
     // margin for fp32 rounding between these bounds and the keys formed below
     if (t) sh.tlb = key_from_order_bits(t) - 1e-3f;
     __syncthreads();
-    tlb = sh.tlb;
+    tlb = sh.tlb;  // -inf if fewer than k units held a page
   }
 
   // ================================================================ 2. chunk
