@@ -84,6 +84,7 @@ struct ChunkShared {
   uint32_t hcnt[kHistBuckets];
   uint32_t scn[2][kNW];
   float redf[kNW][2];
+  float reds[kNW];  // each wave's sum rescaled to its head's max
   uint32_t wsum[kNW];
   int scan[kNW];
   float tlb;
@@ -106,25 +107,12 @@ __device__ __forceinline__ void lse2_acc(float& m, float& s, float m2, float s2)
 }
 
 // (max, sum) pairs merged over the 64 lanes; every lane gets the same result.
+// Max first, then one rescale per lane and a plain sum: one exp2 per lane
+// instead of two per butterfly step (an empty pair is (-1e30, 0)).
 __device__ __forceinline__ void wave_lse2(float& m, float& s) {
-  lse2_acc(m, s, dpp_mov<kDppXor1>(m), dpp_mov<kDppXor1>(s));
-  lse2_acc(m, s, dpp_mov<kDppXor2>(m), dpp_mov<kDppXor2>(s));
-  lse2_acc(m, s, dpp_mov<kDppHalfMirror>(m), dpp_mov<kDppHalfMirror>(s));
-  lse2_acc(m, s, dpp_mov<kDppMirror>(m), dpp_mov<kDppMirror>(s));
-  {
-    const auto rm = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
-    const auto rs = __builtin_amdgcn_permlane16_swap(__float_as_uint(s), __float_as_uint(s), false, false);
-    m = __uint_as_float(rm[0]);
-    s = __uint_as_float(rs[0]);
-    lse2_acc(m, s, __uint_as_float(rm[1]), __uint_as_float(rs[1]));
-  }
-  {
-    const auto rm = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
-    const auto rs = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
-    m = __uint_as_float(rm[0]);
-    s = __uint_as_float(rs[0]);
-    lse2_acc(m, s, __uint_as_float(rm[1]), __uint_as_float(rs[1]));
-  }
+  const float M = wave_max(m);
+  s = wave_sum(s * fast_exp2(m - M));
+  m = M;
 }
 
 // Bucket of order bits u among kHistBuckets linear buckets over [lo, hi]
@@ -271,13 +259,29 @@ __global__ __launch_bounds__(kThreads) void select_chunk_kernel(SelectArgs a) {
   if (lane == 0) { sh.redf[wave][0] = lm; sh.redf[wave][1] = ls; }
   if (tid == 0) sh.tlb = -INFINITY;  // kept when fewer than k units have pages: no pruning
   __syncthreads();
-  float L[G];  // base 2; every thread folds every head's wave partials itself
+  // L_g: with several waves per head, each wave first rescales its sum to the
+  // head's max (one exp2, a second barrier), so every thread then only adds
+  float L[G];  // base 2
   float top = -INFINITY;  // the largest unit bound plus log2 G: max over heads of (max s_hat_g - L_g)
+  if constexpr (WPG > 1) {
+    float Mg = sh.redf[g * WPG][0];
+#pragma unroll
+    for (int w = 1; w < WPG; ++w) Mg = fmaxf(Mg, sh.redf[g * WPG + w][0]);
+    if (lane == 0) sh.reds[wave] = ls * fast_exp2(lm - Mg);
+    __syncthreads();
+  }
 #pragma unroll
   for (int gg = 0; gg < G; ++gg) {
-    float m = sh.redf[gg * WPG][0], sv = sh.redf[gg * WPG][1];
+    float m = sh.redf[gg * WPG][0], sv;
+    if constexpr (WPG > 1) {
 #pragma unroll
-    for (int w = 1; w < WPG; ++w) lse2_acc(m, sv, sh.redf[gg * WPG + w][0], sh.redf[gg * WPG + w][1]);
+      for (int w = 1; w < WPG; ++w) m = fmaxf(m, sh.redf[gg * WPG + w][0]);
+      sv = 0.f;
+#pragma unroll
+      for (int w = 0; w < WPG; ++w) sv += sh.reds[gg * WPG + w];
+    } else {
+      sv = sh.redf[gg][1];
+    }
     L[gg] = (sv > 0.f) ? m + fast_log2(sv) : -INFINITY;
     if (sv > 0.f) top = fmaxf(top, m - L[gg]);
   }
