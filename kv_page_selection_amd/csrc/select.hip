@@ -220,11 +220,22 @@ __global__ __launch_bounds__(kThreads) void select_chunk_kernel(SelectArgs a) {
       const int r = r0 + j + i * P;
       v[i] = (r < nr) ? part[r] : make_float2(-INFINITY, 0.f);
     }
+    if (r0 + 8 * P <= nr) {  // workgroup-uniform: a full batch, max first, one exp2 per partial
+      float bm = -1e30f, bs = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) bm = fmaxf(bm, v[i].y > 0.f ? v[i].x : -1e30f);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) bs += v[i].y * fast_exp2(v[i].x - bm);  // empty: (-inf, 0) adds 0
+      lse2_acc(lm, ls, bm, bs);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (v[i].y > 0.f) lse2_acc(lm, ls, v[i].x, v[i].y);
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int r = r0 + j + i * P;
       const bool ne = v[i].y > 0.f;  // range holds a present page
-      if (ne) lse2_acc(lm, ls, v[i].x, v[i].y);
       if (tiles) continue;
       if (S == 1) {
         if (r < nr) sh.bound.msup[g * nR + r] = ne ? key_order_bits(v[i].x) : 0u;
