@@ -213,27 +213,31 @@ __global__ __launch_bounds__(kThreads) void select_chunk_kernel(SelectArgs a) {
   const float2* part =
       reinterpret_cast<const float2*>(a.score_part) + ((size_t)b * a.Hq + (size_t)kvh * G + g) * a.n_ranges;
   float lm = -1e30f, ls = 0.f;
-  for (int r0 = 0; r0 < nr; r0 += 8 * P) {
-    float2 v[8];
+  // partials per thread in flight at once: 16 for 16-head groups at one page
+  // per thread (P = 64 threads per head: one round trip for 1024 ranges),
+  // else 8 (P >= 128: one batch covers 1024 ranges already)
+  constexpr int PB = (G == 16 && EPT == 1) ? 16 : 8;
+  for (int r0 = 0; r0 < nr; r0 += PB * P) {
+    float2 v[PB];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < PB; ++i) {
       const int r = r0 + j + i * P;
       v[i] = (r < nr) ? part[r] : make_float2(-INFINITY, 0.f);
     }
-    if (r0 + 8 * P <= nr) {  // workgroup-uniform: a full batch, max first, one exp2 per partial
+    if (r0 + PB * P <= nr) {  // workgroup-uniform: a full batch, max first, one exp2 per partial
       float bm = -1e30f, bs = 0.f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) bm = fmaxf(bm, v[i].y > 0.f ? v[i].x : -1e30f);
+      for (int i = 0; i < PB; ++i) bm = fmaxf(bm, v[i].y > 0.f ? v[i].x : -1e30f);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) bs += v[i].y * fast_exp2(v[i].x - bm);  // empty: (-inf, 0) adds 0
+      for (int i = 0; i < PB; ++i) bs += v[i].y * fast_exp2(v[i].x - bm);  // empty: (-inf, 0) adds 0
       lse2_acc(lm, ls, bm, bs);
     } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+      for (int i = 0; i < PB; ++i)
         if (v[i].y > 0.f) lse2_acc(lm, ls, v[i].x, v[i].y);
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < PB; ++i) {
       const int r = r0 + j + i * P;
       const bool ne = v[i].y > 0.f;  // range holds a present page
       if (tiles) continue;
@@ -267,7 +271,16 @@ __global__ __launch_bounds__(kThreads) void select_chunk_kernel(SelectArgs a) {
     }
   }
   wave_lse2(lm, ls);
-  if (lane == 0) { sh.redf[wave][0] = lm; sh.redf[wave][1] = ls; }
+  if (lane == 0) {
+    if constexpr (WPG > 1) {
+      sh.redf[wave][0] = lm;
+      sh.redf[wave][1] = ls;
+    } else {  // one wave per head: its L and max - L, so readers need no log2
+      const float Lw = (ls > 0.f) ? lm + fast_log2(ls) : -INFINITY;
+      sh.redf[wave][0] = Lw;
+      sh.redf[wave][1] = (ls > 0.f) ? lm - Lw : -INFINITY;
+    }
+  }
   if (tid == 0) sh.tlb = -INFINITY;  // kept when fewer than k units have pages: no pruning
   __syncthreads();
   // L_g: with several waves per head, each wave first rescales its sum to the
@@ -283,19 +296,22 @@ __global__ __launch_bounds__(kThreads) void select_chunk_kernel(SelectArgs a) {
   }
 #pragma unroll
   for (int gg = 0; gg < G; ++gg) {
-    float m = sh.redf[gg * WPG][0], sv;
     if constexpr (WPG > 1) {
+      float m = sh.redf[gg * WPG][0], sv = 0.f;
 #pragma unroll
       for (int w = 1; w < WPG; ++w) m = fmaxf(m, sh.redf[gg * WPG + w][0]);
-      sv = 0.f;
 #pragma unroll
       for (int w = 0; w < WPG; ++w) sv += sh.reds[gg * WPG + w];
+      L[gg] = (sv > 0.f) ? m + fast_log2(sv) : -INFINITY;
+      if (sv > 0.f) top = fmaxf(top, m - L[gg]);
     } else {
-      sv = sh.redf[gg][1];
+      L[gg] = sh.redf[gg][0];
+      top = fmaxf(top, sh.redf[gg][1]);
     }
-    L[gg] = (sv > 0.f) ? m + fast_log2(sv) : -INFINITY;
-    if (sv > 0.f) top = fmaxf(top, m - L[gg]);
+    // the same in every lane: held in a scalar register
+    L[gg] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(L[gg])));
   }
+  top = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(top)));
   const float log2G = (float)__builtin_ctz(G);
   // bucket range of the bounds: [top - kBoundSpan, top] in order bits, known
   // without a reduction (lower bounds share the lowest bucket)
