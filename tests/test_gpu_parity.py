@@ -62,14 +62,17 @@ SELECT_PATHS = [
     dict(config=4, ctx=16 * 32768, budget=16 * 1024),
     # G = 16 with 2048 ranges: the 32768 (head, range) maxima exceed what the
     # bound pass holds, so it pools ranges in pairs (~300 candidates: the
-    # register path)
+    # register path, inside the attention launch, whose 9 workgroups rank)
     dict(config=5, ctx=16 * 131072, budget=512, n_kv_heads=1, n_q_heads=16),
     # G = 16, 4 sequences: 1024-page select chunks, 400-1,400 candidates per
-    # KV head: the register path for some heads, the LDS ranking for others
+    # KV head, ranked inside the attention launch (72 workgroups): its
+    # register path for some heads, its radix select over the lists (more
+    # than 1024 candidates) for others
     dict(config=5, ctx=16 * 32768, batch=4, budget=512),
     # G = 16 with 2048-page select chunks (two pages per chunk-pass thread):
     # chunks are halved only while the chunk grid has fewer than 64 G = 1024
-    # workgroups, so this takes 512 (sequence, KV head) pairs of 2049 pages
+    # workgroups, so this takes 512 (sequence, KV head) pairs of 2049 pages;
+    # 4608 attention workgroups, above 1024, so the merge launch ranks
     dict(config=5, ctx=16 * 2049, batch=64, n_kv_heads=8, n_q_heads=128, budget=512),
 ]
 
@@ -84,10 +87,11 @@ def test_selection_paths(locks, case):
     torch.cuda.empty_cache()
 
 
-# (ctx, budget, tied pages): the merge's register path (k = 32, a few hundred
-# candidates), its workgroup-wide LDS ranking (k = 1024 of 3000 pages: fewer
-# 16-page tiles than k, so no bound and every page is a candidate) and its
-# radix select over the lists (k = 4096 of 8192 candidates)
+# (ctx, budget, tied pages): the register path (k = 32, a few hundred
+# candidates, ranked inside the attention launch), the merge launch's
+# workgroup-wide LDS ranking (k = 1024 of 3000 pages: fewer 16-page tiles than
+# k, so no bound and every page is a candidate) and its radix select over the
+# lists (k = 4096 of 8192 candidates)
 TIE_CASES = [(16 * 1000, 512, 24), (16 * 3000, 16384, 40), (16 * 8192, 65536, 40)]
 
 
