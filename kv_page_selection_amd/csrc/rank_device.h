@@ -234,10 +234,14 @@ __device__ __forceinline__ uint32_t fast_rank(const unsigned long long (&x)[kFas
     const uint32_t tot = __builtin_amdgcn_readlane(pre, 63);
     uint32_t acc = tot - pre;
     int bstar = -1;
-    uint32_t above = 0;
+    uint32_t above = 0, inb = 0;
 #pragma unroll
     for (int q = kFastBpl - 1; q >= 0; --q) {
-      if (acc < (uint32_t)need && (uint32_t)need <= acc + hb[q]) { bstar = kFastBpl * lane + q; above = acc; }
+      if (acc < (uint32_t)need && (uint32_t)need <= acc + hb[q]) {
+        bstar = kFastBpl * lane + q;
+        above = acc;
+        inb = hb[q];
+      }
       acc += hb[q];
     }
     const uint64_t owner = __ballot(bstar >= 0);
@@ -245,15 +249,21 @@ __device__ __forceinline__ uint32_t fast_rank(const unsigned long long (&x)[kFas
     const int srcl = __builtin_ctzll(owner);
     const uint32_t bs = (uint32_t)__builtin_amdgcn_readlane(bstar, srcl);
     above = __builtin_amdgcn_readlane(above, srcl);
+    inb = __builtin_amdgcn_readlane(inb, srcl);
     uint32_t gt = 0, eq = 0;
 #pragma unroll
     for (int i = 0; i < kFastPerLane; ++i) {
       gt |= bk[i] > bs ? 1u << i : 0u;
       eq |= bk[i] == bs ? 1u << i : 0u;
     }
+    need -= (int)above;
+    if ((int)inb == need) {  // the bucket is exactly the rest: all of it is in, no further pass
+      sel |= live & (gt | eq);
+      live = 0;
+      break;
+    }
     sel |= live & gt;
     live &= eq;
-    need -= (int)above;
     wave_lds_sync();
   }
   if (__ballot(live != 0) != 0) {
