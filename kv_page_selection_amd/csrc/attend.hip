@@ -70,7 +70,6 @@ struct RankSpace<false> {
 // together write the whole list. Every thread calls it; the caller's next
 // barrier publishes sblk.
 __device__ __forceinline__ void rank_split(const AttnArgs& a, RankSpace<true>& RS, size_t head, int split) {
-  const int wave = threadIdx.x >> 6;
   const size_t lists = head * a.n_chunks;
   const CandLists L{a.cand + lists * a.chunk, a.cand_blk + lists * a.chunk, a.cand_count + lists,
                     a.n_chunks, a.chunk};
@@ -84,22 +83,22 @@ __device__ __forceinline__ void rank_split(const AttnArgs& a, RankSpace<true>& R
       sblk[r] = blk;
     }
   };
-  // every wave reads the counts while wave 0 gathers speculatively
+  // the counts and the speculative slots, in one round trip
   const int lgS = fast_lg_slots(L.nc);
   int cc[16];
   fast_count_load(L, cc);
-  unsigned long long x[kFastPerLane];
-  int bl[kFastPerLane], cof[kFastPerLane];
-  if (wave == 0) fast_slots_load(L, lgS, x, bl, cof);
+  constexpr int KPL = kFastCap / 256;
+  unsigned long long x[KPL];
+  int bl[KPL], cof[KPL];
+  fast_slots_load<256>(L, lgS, x, bl, cof);
   int total;
   const bool over = fast_count_check(L, lgS, cc, &total);  // the same in every wave
   if (over && total > kFastCap) {
     rank_global<256>(RS.r, L, a.k, emit);
     return;
   }
-  if (wave != 0) return;
-  const uint32_t live = over ? fast_gather_exact(L, RS.r.off, total, x, bl) : fast_slots_live(L, lgS, cof);
-  fast_emit(x, bl, fast_rank(x, live, a.k, !over, RS.r.hist), a.k, !over, s0, s0 + pps, emit);
+  const uint32_t live = over ? fast_gather_exact<256>(L, RS.r.off, total, x, bl) : fast_slots_live<256>(L, lgS, cof);
+  fast_emit<256>(x, bl, fast_rank<256>(x, live, a.k, !over, RS.r), a.k, !over, s0, s0 + pps, RS.r, emit);
 }
 
 // RANK: the list is ranked here (rank_split) instead of read from sel_blk.
@@ -116,7 +115,7 @@ __global__ __launch_bounds__(256) void attend_kernel(AttnArgs a) {
   const int s0 = split * a.pages_per_split;
   __shared__ RankSpace<RANK> RS;
   // q of the group, base-2 logit scale: loaded first, so that a ranking
-  // launch's wave 0 finds it arrived when it stages its share after ranking
+  // launch finds it arrived when its waves stage their shares after ranking
   constexpr int QPT = (G * kDim + 255) / 256;  // q values per thread
   const float qscale = kLog2e * kInvSqrtD;
   float qv[QPT];

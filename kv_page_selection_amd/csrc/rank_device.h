@@ -10,12 +10,12 @@
 // order, and the ranking keeps that order, so the kept ids come out ascending
 // without a sort.
 //
-// Register path (one wave, no barrier): at most kFastCap candidates, 16 per
-// lane. Gathered in one round trip with the list counts when every list fits
-// kFastCap/n_lists speculative slots, entry 64 i + lane in slot i of each lane
-// (so each load instruction reads 64 consecutive slots and page order is
-// (slot, lane) order); else (still at most kFastCap in all) after the counts,
-// entry 16 lane + i (lane order is page order).
+// Register path: at most kFastCap candidates, spread over every wave of the
+// workgroup. Gathered in one round trip with the list counts when every list
+// fits kFastCap/n_lists speculative slots, entry 64 j + lane in lane `lane`
+// (so each load instruction reads 64 consecutive slots; page order is (j,
+// lane) order, j running over a wave's slots, then the next wave's); else (still at most kFastCap in all) after the counts,
+// consecutive entries per lane (lane order is page order).
 // Ranked by bucket refinement: a 512-bucket histogram over the live key range
 // picks the bucket holding the k-th key; candidates above it are in, below it
 // out; repeat inside it until the count fits or every live key is equal, where
@@ -58,21 +58,27 @@ struct RankLds {
   int off[1025];  // off[c]: first entry of list c in the concatenation; off[nc]: total
   uint32_t red3[3][NT / 64];
   uint32_t scn[NT / 64];
+  uint32_t kept[NT / 64];  // register path: kept candidates per wave
   int bstar;
   uint32_t babove;
 };
 
 // ------------------------------------------------------------ register path
+//
+// Every wave of the NT-thread workgroup takes part: wave w holds kFastCap / NT
+// candidates per lane (KPL), and page order is wave order, then the order
+// within the wave given below. A pass is two workgroup barriers; the
+// per-candidate work, most of a pass's instructions, is split over the waves.
 
 // log2 of the speculative slots per list: the largest power of two S with nc S <= kFastCap
 __device__ __forceinline__ int fast_lg_slots(int nc) { return 31 - __builtin_clz(max(1, kFastCap / nc)); }
 
 // Register-path loads are split from their use so that a caller issues all
-// of them (the counts in every wave, the speculative slots in wave 0) before
-// it consumes any: one round trip. Every load is unconditional (indices
-// clamped in range), so no branch holds one back.
+// of them (the counts and the speculative slots) before it consumes any: one
+// round trip. Every load is unconditional (indices clamped in range), so no
+// branch holds one back.
 
-// Counts of lists lane + 64 i (clamped: read but ignored past nc).
+// Counts of lists lane + 64 i (clamped: read but ignored past nc), in every wave.
 __device__ __forceinline__ void fast_count_load(const CandLists& L, int (&cc)[16]) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
@@ -96,16 +102,19 @@ __device__ __forceinline__ bool fast_count_check(const CandLists& L, int lgS, co
   return __ballot(over) != 0;
 }
 
-// Speculative gather (one wave): entry e = 64 i + lane (slot i of the lane)
-// is slot e % S of list e / S, S = 2^lgS, with that list's count in cof.
+// Speculative gather: entry e = 64 (KPL w + i) + lane (slot i of the lane in
+// wave w) is slot e % S of list e / S, S = 2^lgS, with that list's count in
+// cof; within a wave page order is (slot, lane) order.
+template <int NT>
 __device__ __forceinline__ void fast_slots_load(const CandLists& L, int lgS,
-                                                unsigned long long (&x)[kFastPerLane],
-                                                int (&bl)[kFastPerLane], int (&cof)[kFastPerLane]) {
-  const int lane = threadIdx.x & 63;
+                                                unsigned long long (&x)[kFastCap / NT],
+                                                int (&bl)[kFastCap / NT], int (&cof)[kFastCap / NT]) {
+  constexpr int KPL = kFastCap / NT;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int S = 1 << lgS;
 #pragma unroll
-  for (int i = 0; i < kFastPerLane; ++i) {
-    const int e = 64 * i + lane;
+  for (int i = 0; i < KPL; ++i) {
+    const int e = 64 * (KPL * wave + i) + lane;
     const int c = e >> lgS, sl = e & (S - 1);
     const int idx = (c < L.nc) ? c * L.chunk + sl : 0;
     x[i] = L.x[idx];
@@ -115,46 +124,53 @@ __device__ __forceinline__ void fast_slots_load(const CandLists& L, int lgS,
 }
 
 // The lane's live bits of a speculative gather: slots below their list's count.
+template <int NT>
 __device__ __forceinline__ uint32_t fast_slots_live(const CandLists& L, int lgS,
-                                                    const int (&cof)[kFastPerLane]) {
-  const int lane = threadIdx.x & 63;
+                                                    const int (&cof)[kFastCap / NT]) {
+  constexpr int KPL = kFastCap / NT;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   uint32_t live = 0;
 #pragma unroll
-  for (int i = 0; i < kFastPerLane; ++i) {
-    const int e = 64 * i + lane;
+  for (int i = 0; i < KPL; ++i) {
+    const int e = 64 * (KPL * wave + i) + lane;
     live |= ((e >> lgS) < L.nc && (e & ((1 << lgS) - 1)) < cof[i]) ? 1u << i : 0u;
   }
   return live;
 }
 
-// Exact gather (one wave) of total <= kFastCap candidates when some list
-// overflowed its speculative slots: list offsets by a wave scan into off
-// (LDS, nc + 1 words), then entry e = 16 lane + i < total (lane-major: one
-// search per lane, then consecutive entries) from the list holding it.
-// Returns the lane's live bits (entries below total).
+// Exact gather of total <= kFastCap candidates when some list overflowed its
+// speculative slots: wave 0 writes the list offsets (a wave scan) to off (LDS,
+// nc + 1 words), a barrier, then entry e = KPL (64 w + lane) + i < total (lane
+// order within a wave is page order: one search per lane, then consecutive
+// entries) comes from the list holding it. Every wave calls it; returns the
+// lane's live bits (entries below total).
+template <int NT>
 __device__ __forceinline__ uint32_t fast_gather_exact(const CandLists& L, int* off, int total,
-                                                      unsigned long long (&x)[kFastPerLane],
-                                                      int (&bl)[kFastPerLane]) {
-  const int lane = threadIdx.x & 63;
-  int cc[16];  // lane l: lists [16 l, 16 l + 16)
+                                                      unsigned long long (&x)[kFastCap / NT],
+                                                      int (&bl)[kFastCap / NT]) {
+  constexpr int KPL = kFastCap / NT;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (wave == 0) {
+    int cc[16];  // lane l: lists [16 l, 16 l + 16)
 #pragma unroll
-  for (int i = 0; i < 16; ++i) cc[i] = L.count[min(16 * lane + i, L.nc - 1)];  // unconditional
-  uint32_t s = 0;
+    for (int i = 0; i < 16; ++i) cc[i] = L.count[min(16 * lane + i, L.nc - 1)];  // unconditional
+    uint32_t s = 0;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    if (16 * lane + i >= L.nc) cc[i] = 0;
-    s += (uint32_t)cc[i];
+    for (int i = 0; i < 16; ++i) {
+      if (16 * lane + i >= L.nc) cc[i] = 0;
+      s += (uint32_t)cc[i];
+    }
+    uint32_t o = wave_incl_scan(s) - s;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int c = 16 * lane + i;
+      if (c < L.nc) off[c] = (int)o;
+      o += (uint32_t)cc[i];
+    }
+    if (lane == 0) off[L.nc] = total;
   }
-  uint32_t o = wave_incl_scan(s) - s;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int c = 16 * lane + i;
-    if (c < L.nc) off[c] = (int)o;
-    o += (uint32_t)cc[i];
-  }
-  if (lane == 0) off[L.nc] = total;
-  wave_lds_sync();
-  const int e0 = lane * kFastPerLane;
+  __syncthreads();
+  const int e0 = KPL * (64 * wave + lane);
   int c = 0;
   if (e0 < total)
     for (int lo = 0, hi = L.nc - 1; lo <= hi;) {  // last list starting at or before e0
@@ -163,7 +179,7 @@ __device__ __forceinline__ uint32_t fast_gather_exact(const CandLists& L, int* o
     }
   uint32_t live = 0;
 #pragma unroll
-  for (int i = 0; i < kFastPerLane; ++i) {
+  for (int i = 0; i < KPL; ++i) {
     const int e = e0 + i;
     int idx = 0;
     if (e < total) {
@@ -182,23 +198,55 @@ __device__ __forceinline__ int lanes_below(uint64_t m) {
   return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-// Ranks the live candidates (one wave) and returns the lane's kept bits: the
-// k largest sort keys, or every live one if fewer. imajor: page order is
+// The sum over the waves before this one (*before) and over all of them
+// (return) of a wave-uniform count, through the NT / 64 words w. One barrier;
+// w must not be written again before every wave has passed it.
+template <int NT>
+__device__ __forceinline__ int waves_prefix(uint32_t v, uint32_t* w, int* before) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) w[wave] = v;
+  __syncthreads();
+  uint32_t pre = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < NT / 64; ++i) {
+    const uint32_t c = w[i];
+    pre += (i < wave) ? c : 0u;
+    tot += c;
+  }
+  *before = (int)pre;
+  return (int)tot;
+}
+
+// Ranks the live candidates and returns the lane's kept bits: the k largest
+// sort keys, or every live one if fewer. imajor: page order within a wave is
 // (slot, lane) order (the speculative gather), else lane order (the exact
-// gather); it decides only which of several equal keys are kept. hist:
-// kFastBuckets + 64 words of LDS that only this wave uses (the last 64 take
-// the increments of dead slots, one per lane, so that no branch skips them).
-__device__ __forceinline__ uint32_t fast_rank(const unsigned long long (&x)[kFastPerLane], uint32_t live,
-                                              int k, bool imajor, uint32_t* hist) {
-  const int lane = threadIdx.x & 63;
+// gather); it decides only which of several equal keys are kept. Every wave
+// calls it with the same k; the decisions are workgroup-uniform.
+// Each pass: the live count and key range (a barrier), a 512-bucket
+// histogram of the live keys over that range (a barrier), read whole by every
+// wave, which finds the bucket of the need-th key from the top. The histogram
+// is double-buffered in R.hist (kFastBuckets + 64 words each; the last 64 take
+// the increments of dead slots, one per lane, so that no branch skips them),
+// each pass clearing the next one's buffer.
+template <int NT>
+__device__ __forceinline__ uint32_t fast_rank(const unsigned long long (&x)[kFastCap / NT], uint32_t live,
+                                              int k, bool imajor, RankLds<NT>& R) {
+  constexpr int KPL = kFastCap / NT, NW = NT / 64;
+  constexpr int kWords = kFastBuckets + 64;
+  static_assert(2 * kWords <= kRankBuckets, "two histograms fit R.hist");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int q = tid; q < kFastBuckets; q += NT) R.hist[q] = 0u;  // the first pass's buffer
   uint32_t sel = 0;
   int need = k;
-  // every step is branch-free over the 16 slots: dead slots take neutral
-  // values and a private histogram word
+  bool tie = false;  // live keys left all equal
   for (int iter = 0; iter < 8; ++iter) {
+    uint32_t* const hc = R.hist + (iter & 1) * kWords;
+    uint32_t* const hn = R.hist + (~iter & 1) * kWords;
+    // every step is branch-free over the slots: dead slots take neutral
+    // values and a private histogram word
     uint32_t cnt = __popc(live), lo = 0xffffffffu, hi = 0u;
 #pragma unroll
-    for (int i = 0; i < kFastPerLane; ++i) {
+    for (int i = 0; i < KPL; ++i) {
       const uint32_t v = (uint32_t)(x[i] >> 32);
       const bool on = (live >> i) & 1u;
       lo = min(lo, on ? v : 0xffffffffu);
@@ -207,27 +255,34 @@ __device__ __forceinline__ uint32_t fast_rank(const unsigned long long (&x)[kFas
     cnt = wave_sum_u32(cnt);
     lo = wave_min_u32(lo);
     hi = wave_max_u32(hi);
+    if (lane == 0) { R.red3[0][wave] = cnt; R.red3[1][wave] = lo; R.red3[2][wave] = hi; }
+    __syncthreads();
+    cnt = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      cnt += R.red3[0][w];
+      lo = min(lo, R.red3[1][w]);
+      hi = max(hi, R.red3[2][w]);
+    }
     if ((int)cnt <= need) { sel |= live; live = 0; break; }
-    if (lo == hi) break;
+    if (lo == hi) { tie = true; break; }
     // any positive scale near kFastBuckets / range keeps the bucket map
     // monotone, which is all the selection needs (out-of-range results clamp)
     const float scale = (float)kFastBuckets * __builtin_amdgcn_rcpf((float)(hi - lo) + 1.0f);
+    for (int q = tid; q < kFastBuckets; q += NT) hn[q] = 0u;  // read last in the previous pass
+    uint32_t bk[KPL];
 #pragma unroll
-    for (int q = 0; q < kFastBpl; ++q) hist[(q << 6) | lane] = 0u;
-    wave_lds_sync();
-    uint32_t bk[kFastPerLane];
-#pragma unroll
-    for (int i = 0; i < kFastPerLane; ++i) {
+    for (int i = 0; i < KPL; ++i) {
       const bool on = (live >> i) & 1u;
       bk[i] = min((uint32_t)(kFastBuckets - 1), (uint32_t)((float)((uint32_t)(x[i] >> 32) - lo) * scale));
-      atomicAdd(&hist[on ? fast_slot(bk[i]) : (uint32_t)(kFastBuckets + lane)], 1u);
+      atomicAdd(&hc[on ? fast_slot(bk[i]) : (uint32_t)(kFastBuckets + lane)], 1u);
     }
-    wave_lds_sync();
+    __syncthreads();
     uint32_t hb[kFastBpl];
     uint32_t mine = 0;
 #pragma unroll
     for (int q = 0; q < kFastBpl; ++q) {
-      hb[q] = hist[(q << 6) | lane];
+      hb[q] = hc[(q << 6) | lane];
       mine += hb[q];
     }
     const uint32_t pre = wave_incl_scan(mine);
@@ -252,7 +307,7 @@ __device__ __forceinline__ uint32_t fast_rank(const unsigned long long (&x)[kFas
     inb = __builtin_amdgcn_readlane(inb, srcl);
     uint32_t gt = 0, eq = 0;
 #pragma unroll
-    for (int i = 0; i < kFastPerLane; ++i) {
+    for (int i = 0; i < KPL; ++i) {
       gt |= bk[i] > bs ? 1u << i : 0u;
       eq |= bk[i] == bs ? 1u << i : 0u;
     }
@@ -264,23 +319,23 @@ __device__ __forceinline__ uint32_t fast_rank(const unsigned long long (&x)[kFas
     }
     sel |= live & gt;
     live &= eq;
-    wave_lds_sync();
   }
-  if (__ballot(live != 0) != 0) {
+  if (tie) {
     // live keys all equal: the earliest (lowest page ids) win
+    int before;
+    waves_prefix<NT>(wave_sum_u32(__popc(live)), R.scn, &before);
     if (imajor) {
-      int base = 0;
 #pragma unroll
-      for (int i = 0; i < kFastPerLane; ++i) {
+      for (int i = 0; i < KPL; ++i) {
         const uint64_t m = __ballot((live >> i) & 1u);
-        if (((live >> i) & 1u) && base + lanes_below(m) < need) sel |= 1u << i;
-        base += __popcll(m);
+        if (((live >> i) & 1u) && before + lanes_below(m) < need) sel |= 1u << i;
+        before += __popcll(m);
       }
     } else {
       const uint32_t nl = __popc(live);
-      int before = (int)(wave_incl_scan(nl) - nl);
+      before += (int)(wave_incl_scan(nl) - nl);
 #pragma unroll
-      for (int i = 0; i < kFastPerLane; ++i)
+      for (int i = 0; i < KPL; ++i)
         if ((live >> i) & 1u) {
           if (before < need) sel |= 1u << i;
           ++before;
@@ -290,22 +345,22 @@ __device__ __forceinline__ uint32_t fast_rank(const unsigned long long (&x)[kFas
   return sel;
 }
 
-// Hands out the kept candidates (one wave) whose positions in the kept list
-// (page order; imajor as for fast_rank) fall in [w0, w1): emit(pos, page id,
+// Hands out the kept candidates whose positions in the kept list (page
+// order; imajor as for fast_rank) fall in [w0, w1): emit(pos, page id,
 // block), and emit(pos, -1, -1) for the positions of [w0, w1) from the kept
-// count up to k.
-template <class Emit>
-__device__ __forceinline__ void fast_emit(const unsigned long long (&x)[kFastPerLane],
-                                          const int (&bl)[kFastPerLane], uint32_t sel, int k, bool imajor,
-                                          int w0, int w1, Emit&& emit) {
-  const int lane = threadIdx.x & 63;
+// count up to k. Every wave calls it (one barrier).
+template <int NT, class Emit>
+__device__ __forceinline__ void fast_emit(const unsigned long long (&x)[kFastCap / NT],
+                                          const int (&bl)[kFastCap / NT], uint32_t sel, int k, bool imajor,
+                                          int w0, int w1, RankLds<NT>& R, Emit&& emit) {
+  constexpr int KPL = kFastCap / NT;
   auto id_of = [](unsigned long long v) { return (int)(0xffffffffu - (uint32_t)(v & 0xffffffffu)); };
-  int nk;
+  int base;
+  const int nk = waves_prefix<NT>(wave_sum_u32(__popc(sel)), R.kept, &base);
   if (imajor) {
     // slot i of every lane is one run of the list: a ballot places it
-    int base = 0;
 #pragma unroll
-    for (int i = 0; i < kFastPerLane; ++i) {
+    for (int i = 0; i < KPL; ++i) {
       const uint64_t m = __ballot((sel >> i) & 1u);
       const int n = __popcll(m);
       if (base < w1 && base + n > w0 && ((sel >> i) & 1u)) {
@@ -314,22 +369,19 @@ __device__ __forceinline__ void fast_emit(const unsigned long long (&x)[kFastPer
       }
       base += n;
     }
-    nk = base;
   } else {
     const uint32_t ns = __popc(sel);
-    const uint32_t pre = wave_incl_scan(ns);
-    nk = (int)__builtin_amdgcn_readlane(pre, 63);
-    int o = (int)(pre - ns);
+    int o = base + (int)(wave_incl_scan(ns) - ns);
     if (o < w1 && o + (int)ns > w0) {
 #pragma unroll
-      for (int i = 0; i < kFastPerLane; ++i)
+      for (int i = 0; i < KPL; ++i)
         if ((sel >> i) & 1u) {
           if (o >= w0 && o < w1) emit(o, id_of(x[i]), bl[i]);
           ++o;
         }
     }
   }
-  for (int i = max(nk, w0) + lane; i < min(k, w1); i += 64) emit(i, -1, -1);
+  for (int i = max(nk, w0) + (int)threadIdx.x; i < min(k, w1); i += NT) emit(i, -1, -1);
 }
 
 // ----------------------------------------------------------- workgroup path

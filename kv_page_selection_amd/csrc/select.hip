@@ -33,14 +33,14 @@
 //  2. merge: one workgroup per (sequence, KV head) ranks the chunk lists in
 //     page order and writes the kept ids, sorted without a sort because the
 //     lists are in page order, with their physical blocks for the attention
-//     pass. Up to 1024 candidates (the usual case) one wave ranks them in
-//     registers with no barrier; up to 4,608 the workgroup ranks an LDS copy;
+//     pass. Up to 1024 candidates (the usual case) the waves rank them in
+//     registers, two candidates per lane; up to 4,608 the workgroup ranks an LDS copy;
 //     beyond that a radix select runs over the lists where they lie. (For
 //     small budgets the decode step skips this launch: each sparse attention
 //     workgroup ranks its own (sequence, KV head)'s lists the same way.)
 // Ranking = exact selection by bucket refinement on the key bits: a histogram
-// over the live [lo, hi] key range (2048 buckets; 512 on the one-wave
-// register path) picks the bucket holding the k-th key; everything above it
+// over the live [lo, hi] key range (2048 buckets; 512 on the register
+// path) picks the bucket holding the k-th key; everything above it
 // is in, below it out; repeat inside that bucket (range shrinks ~2^11, or
 // ~2^9, per pass) until the count fits or all live keys are equal, where the
 // lowest ids win.
@@ -407,8 +407,7 @@ __global__ __launch_bounds__(kThreads) void select_chunk_kernel(SelectArgs a) {
 // ============================================================ merge
 //
 // One workgroup of kMergeThreads per (sequence, KV head). Up to kFastCap
-// candidates (the usual case) wave 0 alone ranks them in registers and the
-// other waves leave. Up to kRoundCap the whole workgroup copies the chunk
+// candidates (the usual case) its waves rank them in registers. Up to kRoundCap the whole workgroup copies the chunk
 // lists, in page order, into one LDS list and ranks it by bucket refinement
 // over the live key range with a 2048-bucket LDS histogram (4 buckets per
 // thread): elements above the bucket of the need-th key in, below it out,
@@ -594,7 +593,7 @@ __device__ int merge_lists(MergeLds& W, const CandLists& L, int k) {
 // blocks in page order, -1 past them.
 __global__ __launch_bounds__(kMergeThreads) void select_merge_kernel(SelectArgs a) {
   const int kvh = blockIdx.x, b = blockIdx.y;
-  const int tid = threadIdx.x, wave = tid >> 6;
+  const int tid = threadIdx.x;
   __shared__ MergeLds W;
   const size_t head = (size_t)b * a.Hkv + kvh;
   const int nc = a.n_chunks;
@@ -607,13 +606,14 @@ __global__ __launch_bounds__(kMergeThreads) void select_merge_kernel(SelectArgs 
     outb[pos] = blk;
   };
 
-  // every wave reads the counts while wave 0 gathers speculatively
+  // the counts and the speculative slots, in one round trip
   const int lgS = fast_lg_slots(nc);
   int cc[16];
   fast_count_load(L, cc);
-  unsigned long long x[kFastPerLane];
-  int bl[kFastPerLane], cof[kFastPerLane];
-  if (wave == 0) fast_slots_load(L, lgS, x, bl, cof);
+  constexpr int KPL = kFastCap / kMergeThreads;
+  unsigned long long x[KPL];
+  int bl[KPL], cof[KPL];
+  fast_slots_load<kMergeThreads>(L, lgS, x, bl, cof);
   int total;
   const bool over = fast_count_check(L, lgS, cc, &total);  // the same in every wave
   if (over && total > kFastCap) {
@@ -628,9 +628,10 @@ __global__ __launch_bounds__(kMergeThreads) void select_merge_kernel(SelectArgs 
     }
     return;
   }
-  if (wave != 0) return;  // the register path has no barrier
-  const uint32_t live = over ? fast_gather_exact(L, W.r.off, total, x, bl) : fast_slots_live(L, lgS, cof);
-  fast_emit(x, bl, fast_rank(x, live, a.k, !over, W.r.hist), a.k, !over, 0, a.k, emit);
+  const uint32_t live = over ? fast_gather_exact<kMergeThreads>(L, W.r.off, total, x, bl)
+                             : fast_slots_live<kMergeThreads>(L, lgS, cof);
+  fast_emit<kMergeThreads>(x, bl, fast_rank<kMergeThreads>(x, live, a.k, !over, W.r), a.k, !over, 0, a.k, W.r,
+                           emit);
 }
 
 }  // namespace
