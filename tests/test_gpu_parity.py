@@ -87,23 +87,30 @@ def test_selection_paths(locks, case):
     torch.cuda.empty_cache()
 
 
-# (ctx, budget, tied pages): the register path (k = 32, a few hundred
-# candidates, ranked inside the attention launch), the merge launch's
-# workgroup-wide LDS ranking (k = 1024 of 3000 pages: fewer 16-page tiles than
-# k, so no bound and every page is a candidate) and its radix select over the
-# lists (k = 4096 of 8192 candidates)
-TIE_CASES = [(16 * 1000, 512, 24), (16 * 3000, 16384, 40), (16 * 8192, 65536, 40)]
+# (ctx, budget, tied pages, sequence length): the register path's speculative
+# gather (k = 32, a few hundred candidates, ranked inside the attention
+# launch); its exact gather (k = 128 of a 1000-page sequence in a 3000-page
+# table: fewer 16-page tiles than k, so no bound, and the 1000 candidates of
+# the first 1024-page chunk overflow its 256 speculative slots); the merge
+# launch's workgroup-wide LDS ranking (k = 1024 of 3000 pages: no bound, every
+# page a candidate) and its radix select over the lists (k = 4096 of 8192
+# candidates)
+TIE_CASES = [(16 * 1000, 512, 24, None), (16 * 3000, 2048, 24, 16 * 1000), (16 * 3000, 16384, 40, None),
+             (16 * 8192, 65536, 40, None)]
 
 
-@pytest.mark.parametrize("ctx,budget,dup", TIE_CASES, ids=["k32-register", "k1024-lds", "k4096-radix"])
-def test_bit_exact_ties_at_the_cutoff_go_to_the_lower_ids(locks, ctx, budget, dup):
+@pytest.mark.parametrize("ctx,budget,dup,seq_len", TIE_CASES,
+                         ids=["k32-register", "k128-exact-gather", "k1024-lds", "k4096-radix"])
+def test_bit_exact_ties_at_the_cutoff_go_to_the_lower_ids(locks, ctx, budget, dup, seq_len):
     """Several logical pages mapped onto one physical block share its record,
     so their scores and group keys are bit-identical on both sides. Planted at
     the k-th place, the tie must be broken toward the lower page ids (larger
     key first, then lower id; ids ascending), and the GPU's selection must
-    equal the oracle's exactly, with no near-tie allowance."""
-    say(f"cut-off tie ctx {ctx} budget {budget} dup {dup}")
-    w = workloads.make(2, device=DEV, ctx=ctx, budget=budget, seed=77)
+    equal the oracle's exactly, with no near-tie allowance. The separate
+    select launch (with its merge) must pick the same pages as the step."""
+    say(f"cut-off tie ctx {ctx} budget {budget} dup {dup} seq_len {seq_len}")
+    w = workloads.make(2, device=DEV, ctx=ctx, budget=budget, seed=77,
+                       **({} if seq_len is None else dict(seq_lens=[seq_len])))
     summ = locks.build_summaries(w.k_cache, w.page_table, w.seq_lens)
     pt, tied = plant_cutoff_tie(w, summ.cpu().numpy(), dup)
     w.page_table = torch.from_numpy(pt).to(DEV)
@@ -116,6 +123,12 @@ def test_bit_exact_ties_at_the_cutoff_go_to_the_lower_ids(locks, ctx, budget, du
     sc = r["scores"].cpu().numpy()
     for h in range(w.group):  # the GPU's own scores of the tied pages are bit-identical
         assert np.all(sc[0, h, tied] == sc[0, h, tied[0]])
+    ws = locks.new_workspace(locks.make_dims(w.q, w.k_cache, w.page_table), budget, DEV)
+    sel = torch.full_like(r["sel"], -7)
+    locks.score_pages(w.q, summ, w.k_cache, w.page_table, w.seq_lens, budget, ws)
+    locks.select_pages(w.q, w.k_cache, w.page_table, w.seq_lens, budget, sel, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(sel, r["sel"]), "the select launch's selection differs from the step's"
     say(f"  {above} above the tie, {w.k_pages - above} of {len(tied)} tied pages kept")
 
 
