@@ -238,7 +238,7 @@ __device__ __forceinline__ uint32_t fast_rank(const unsigned long long (&x)[kFas
   for (int q = tid; q < kFastBuckets; q += NT) R.hist[q] = 0u;  // the first pass's buffer
   uint32_t sel = 0;
   int need = k;
-  bool tie = false;  // live keys left all equal
+  bool settled = false;  // every kept key found (else the live keys left are all equal)
   for (int iter = 0; iter < 8; ++iter) {
     uint32_t* const hc = R.hist + (iter & 1) * kWords;
     uint32_t* const hn = R.hist + (~iter & 1) * kWords;
@@ -264,8 +264,8 @@ __device__ __forceinline__ uint32_t fast_rank(const unsigned long long (&x)[kFas
       lo = min(lo, R.red3[1][w]);
       hi = max(hi, R.red3[2][w]);
     }
-    if ((int)cnt <= need) { sel |= live; live = 0; break; }
-    if (lo == hi) { tie = true; break; }
+    if ((int)cnt <= need) { sel |= live; live = 0; settled = true; break; }
+    if (lo == hi) break;
     // any positive scale near kFastBuckets / range keeps the bucket map
     // monotone, which is all the selection needs (out-of-range results clamp)
     const float scale = (float)kFastBuckets * __builtin_amdgcn_rcpf((float)(hi - lo) + 1.0f);
@@ -315,13 +315,15 @@ __device__ __forceinline__ uint32_t fast_rank(const unsigned long long (&x)[kFas
     if ((int)inb == need) {  // the bucket is exactly the rest: all of it is in, no further pass
       sel |= live & (gt | eq);
       live = 0;
+      settled = true;
       break;
     }
     sel |= live & gt;
     live &= eq;
   }
-  if (tie) {
-    // live keys all equal: the earliest (lowest page ids) win
+  if (!settled) {  // workgroup-uniform
+    // live keys all equal (or, unreachably, out of passes): the earliest
+    // (lowest page ids) win
     int before;
     waves_prefix<NT>(wave_sum_u32(__popc(live)), R.scn, &before);
     if (imajor) {
