@@ -1,0 +1,92 @@
+"""GPU parity on seeded random shapes: the whole decode step through the C ABI
+against the fp64 oracle, with the bars of every other parity test (page scores
+<= 1e-3 abs; selected sets identical except keys within 1e-4 of the k-th;
+output <= 2e-2 max-abs, cosine >= 0.999).
+
+Each case draws a batch, a KV head count, a GQA group size, the page-table
+width, every sequence's length (empty sequences, sequences holding only a
+partly filled page and ragged lengths included), a few absent page-table
+entries (-1 or past the cache) in some draws, and a budget from 1 to 512
+pages, so it meets combinations the fixed cases leave out: grids on either
+side of the launch-shape switches (one or two waves' worth of scoring
+workgroups, ranking inside or outside the attention launch, 1024- to
+4096-page select chunks, tile or range bounds). Sizes keep the oracle within
+seconds per case."""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from parity import decode_and_check, say
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+SEEDS = list(range(7001, 7041))
+
+
+@pytest.fixture(scope="module")
+def locks():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import kv_page_selection_amd as m
+    m.lib()
+    return m
+
+
+def draw(seed: int) -> dict:
+    """One seeded shape: at most 64 query heads and 4 x 2500 pages."""
+    rng = np.random.default_rng(seed)
+    group = int(rng.choice([1, 2, 4, 8, 16]))
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    while group * hkv > 64:
+        hkv //= 2
+    batch = int(rng.integers(1, 5))
+    pages = int(rng.integers(1, 2501))  # page-table width
+    lens = []
+    for _ in range(batch):
+        u = rng.random()
+        if u < 0.1:
+            lens.append(0)                                    # empty
+        elif u < 0.2:
+            lens.append(int(rng.integers(1, 16)))             # a partly filled page only
+        elif u < 0.5:
+            lens.append(16 * pages)                           # every page full
+        else:
+            lens.append(int(rng.integers(1, 16 * pages + 1)))  # ragged
+    k = int(rng.choice([1, 2, 7, 32, 128, 129, 256, 300, 512]))
+    absent = []  # (sequence, page, entry): entry -1 or past the cache's blocks
+    if rng.random() < 0.4:
+        for _ in range(int(rng.integers(1, 6))):
+            b = int(rng.integers(0, batch))
+            if lens[b] >= 16:
+                absent.append((b, int(rng.integers(0, lens[b] // 16)), int(rng.choice([-1, 1 << 20]))))
+    return dict(batch=batch, n_kv_heads=hkv, n_q_heads=group * hkv, ctx=16 * pages, seq_lens=lens,
+                budget=16 * k, seed=seed), absent
+
+
+@pytest.mark.parametrize("seed", SEEDS)
+def test_random_shape_matches_the_oracle(locks, seed):
+    case, absent = draw(seed)
+    say(f"random shape {case} absent {absent}")
+    w = workloads.make(2, device=DEV, **case)
+    if absent:
+        pt = w.page_table.clone()
+        for b, j, e in absent:
+            pt[b, j] = e
+        w.page_table = pt
+    summ = locks.build_summaries(w.k_cache, w.page_table, w.seq_lens)
+    r = decode_and_check(w, summ, full_oracle_attention=False)
+    sel = r["sel"].cpu().numpy()
+    k = case["budget"] // 16
+    for b, n in enumerate(case["seq_lens"]):
+        full = n // 16
+        gone = {j for bb, j, _ in absent if bb == b}
+        n_keep = min(k, full - len(gone))
+        kept = sel[b][:, :n_keep]
+        assert np.all(kept >= 0) and np.all(kept < full), f"sequence {b}: a kept id outside its full pages"
+        assert not gone & set(kept.ravel().tolist()), f"sequence {b}: an absent page was kept"
+        assert np.all(sel[b][:, n_keep:] == -1), f"sequence {b}: entries past the kept pages are not -1"
+        assert np.all(np.diff(kept, axis=-1) > 0), f"sequence {b}: kept ids not ascending"
+    del w, summ
+    torch.cuda.empty_cache()
