@@ -11,13 +11,15 @@ pages, so it meets combinations the fixed cases leave out: grids on either
 side of the launch-shape switches (one or two waves' worth of scoring
 workgroups, ranking inside or outside the attention launch, 1024- to
 4096-page select chunks, tile or range bounds). Sizes keep the oracle within
-seconds per case."""
+seconds per case. The first 20 draws also run as steps in which some
+sequences' last page has just filled (built inside the scoring launch)."""
 import numpy as np
 import pytest
 import torch
 
 import workloads
 from parity import decode_and_check, say
+from test_gpu_fill import check_fill_step
 
 pytestmark = pytest.mark.gpu
 
@@ -89,4 +91,33 @@ def test_random_shape_matches_the_oracle(locks, seed):
         assert np.all(sel[b][:, n_keep:] == -1), f"sequence {b}: entries past the kept pages are not -1"
         assert np.all(np.diff(kept, axis=-1) > 0), f"sequence {b}: kept ids not ascending"
     del w, summ
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("seed", SEEDS[:20])
+def test_random_shape_fill_step_matches_the_oracle(locks, seed):
+    """The same shapes (no absent entries) as steps with page fills: each
+    sequence is marked filled with probability 0.6; a marked sequence whose
+    length is a whole number of pages has just filled its last page, whose
+    record holds garbage before the step and the whole-cache build's bytes
+    after it."""
+    case, _ = draw(seed)
+    rng = np.random.default_rng(seed + 1)
+    marks = [int(rng.random() < 0.6) for _ in range(case["batch"])]
+    say(f"random shape fill step {case} filled {marks}")
+    w = workloads.make(2, device=DEV, **case)
+    pt = w.page_table.cpu().numpy()
+    summ = locks.build_summaries(w.k_cache, w.page_table, w.seq_lens)
+    fresh = summ.clone()
+    for b, n in enumerate(case["seq_lens"]):
+        if marks[b] and n > 0 and n % 16 == 0:
+            summ[int(pt[b, n // 16 - 1])] = 0xA5  # not built yet
+    filled = torch.tensor(marks, dtype=torch.int32, device=DEV)
+    ps = torch.full((w.batch, w.n_q_heads, w.max_pages), float("nan"), device=DEV)
+    out, sel = locks.decode_step(w.q, summ, w.k_cache, w.v_cache, w.page_table, w.seq_lens, w.budget,
+                                 page_scores=ps, filled=filled)
+    torch.cuda.synchronize()
+    assert torch.equal(summ, fresh), "the step's records differ from the whole-cache build's"
+    check_fill_step(w, summ, filled, out, sel, ps)
+    del w, summ, fresh
     torch.cuda.empty_cache()
