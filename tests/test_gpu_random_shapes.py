@@ -12,13 +12,15 @@ side of the launch-shape switches (one or two waves' worth of scoring
 workgroups, ranking inside or outside the attention launch, 1024- to
 4096-page select chunks, tile or range bounds). Sizes keep the oracle within
 seconds per case. The first 20 draws also run as steps in which some
-sequences' last page has just filled (built inside the scoring launch)."""
+sequences' last page has just filled (built inside the scoring launch), and
+through the attention entry points on caller-given lists and dense."""
 import numpy as np
 import pytest
 import torch
 
+import oracle
 import workloads
-from parity import decode_and_check, say
+from parity import decode_and_check, host, out_ok, say
 from test_gpu_fill import check_fill_step
 
 pytestmark = pytest.mark.gpu
@@ -120,4 +122,44 @@ def test_random_shape_fill_step_matches_the_oracle(locks, seed):
     assert torch.equal(summ, fresh), "the step's records differ from the whole-cache build's"
     check_fill_step(w, summ, filled, out, sel, ps)
     del w, summ, fresh
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("seed", SEEDS[:20])
+def test_random_shape_attention_on_caller_lists_and_dense(locks, seed):
+    """The attention entry points on the same shapes (absent entries
+    included): sparse attention over a caller-given list per (sequence, KV
+    head) of distinct ids in shuffled order with -1 and out-of-range entries
+    mixed in (both skipped), and dense attention over every page; both against
+    the oracle's attention over the same lists, plus each sequence's tail."""
+    case, absent = draw(seed)
+    rng = np.random.default_rng(seed + 2)
+    say(f"random shape attention {case} absent {absent}")
+    w = workloads.make(2, device=DEV, **case)
+    if absent:
+        pt = w.page_table.clone()
+        for b, j, e in absent:
+            pt[b, j] = e
+        w.page_table = pt
+    B, hkv, k = w.batch, w.n_kv_heads, w.k_pages
+    sel = np.full((B, hkv, k), -1, dtype=np.int32)
+    for b, n in enumerate(case["seq_lens"]):
+        full = n // 16
+        for h in range(hkv):
+            ids = rng.permutation(full)[: max(0, k - 2)] if full else np.zeros(0, dtype=np.int64)
+            junk = [-1, full + int(rng.integers(0, 4)), -5][: k - len(ids)]
+            row = np.concatenate([ids, np.array(junk, dtype=np.int64)])
+            sel[b, h, : len(row)] = rng.permutation(row)
+    q, pt, sl = host(w)
+    kb, vb = workloads.bf16_bits(w.k_cache), workloads.bf16_bits(w.v_cache)
+    ws = locks.new_workspace(locks.make_dims(w.q, w.k_cache, w.page_table), case["budget"], DEV)
+    out = torch.full_like(w.q, float("nan"))
+    locks.sparse_attention(w.q, w.k_cache, w.v_cache, w.page_table, w.seq_lens, case["budget"],
+                           torch.from_numpy(sel).to(DEV), out, ws)
+    dense = locks.dense_attention(w.q, w.k_cache, w.v_cache, w.page_table, w.seq_lens)
+    torch.cuda.synchronize()
+    e_s, c_s = out_ok(out.cpu().numpy(), oracle.attention(q, kb, vb, pt, sl, sel))
+    e_d, c_d = out_ok(dense.cpu().numpy(), oracle.attention(q, kb, vb, pt, sl))
+    say(f"  sparse max-abs {e_s:.2e} cos {c_s:.7f}; dense max-abs {e_d:.2e} cos {c_d:.7f}")
+    del w
     torch.cuda.empty_cache()
