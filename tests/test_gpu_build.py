@@ -36,7 +36,7 @@ def compare_builds(w, summ_gpu, n_sample=1500, seed=0):
     pt = w.page_table.cpu().numpy()
     sl = w.seq_lens.cpu().numpy()
     items = [(b, j, h) for b in range(w.batch) for j in range(min(sl[b] // 16, w.max_pages))
-             for h in range(w.n_kv_heads)]
+             for h in range(w.n_kv_heads) if 0 <= pt[b, j] < w.num_blocks]  # absent pages: no record
     pick = rng.choice(len(items), size=min(n_sample, len(items)), replace=False)
     blocks = sorted({int(pt[items[i][0], items[i][1]]) for i in pick})
     idx = torch.tensor(blocks, dtype=torch.long, device=w.k_cache.device)

@@ -12,8 +12,9 @@ side of the launch-shape switches (one or two waves' worth of scoring
 workgroups, ranking inside or outside the attention launch, 1024- to
 4096-page select chunks, tile or range bounds). Sizes keep the oracle within
 seconds per case. The first 20 draws also run as steps in which some
-sequences' last page has just filled (built inside the scoring launch), and
-through the attention entry points on caller-given lists and dense."""
+sequences' last page has just filled (built inside the scoring launch),
+through the attention entry points on caller-given lists and dense, and
+through the summary build."""
 import numpy as np
 import pytest
 import torch
@@ -21,6 +22,7 @@ import torch
 import oracle
 import workloads
 from parity import decode_and_check, host, out_ok, say
+from test_gpu_build import compare_builds
 from test_gpu_fill import check_fill_step
 
 pytestmark = pytest.mark.gpu
@@ -162,4 +164,35 @@ def test_random_shape_attention_on_caller_lists_and_dense(locks, seed):
     e_d, c_d = out_ok(dense.cpu().numpy(), oracle.attention(q, kb, vb, pt, sl))
     say(f"  sparse max-abs {e_s:.2e} cos {c_s:.7f}; dense max-abs {e_d:.2e} cos {c_d:.7f}")
     del w
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("seed", SEEDS[:20])
+def test_random_shape_build_writes_exactly_the_full_pages(locks, seed):
+    """The summary build on the same shapes (absent entries included) writes
+    the record of every block that a full page of some sequence maps to, and
+    no other (tail pages, pages past a sequence's length, absent entries and
+    unreferenced blocks keep their bytes); sampled records meet the oracle
+    bars of the build tests."""
+    case, absent = draw(seed)
+    say(f"random shape build {case} absent {absent}")
+    w = workloads.make(2, device=DEV, **case)
+    if absent:
+        pt = w.page_table.clone()
+        for b, j, e in absent:
+            pt[b, j] = e
+        w.page_table = pt
+    summ = torch.full((w.num_blocks, w.n_kv_heads, locks.summary_record_bytes()), 0xAB, dtype=torch.uint8,
+                      device=DEV)
+    locks.build_summaries(w.k_cache, w.page_table, w.seq_lens, summaries=summ)
+    torch.cuda.synchronize()
+    pt = w.page_table.cpu().numpy()
+    built = {int(pt[b, j]) for b, n in enumerate(case["seq_lens"]) for j in range(n // 16)
+             if 0 <= pt[b, j] < w.num_blocks}
+    untouched = np.all(summ.cpu().numpy().reshape(w.num_blocks, -1) == 0xAB, axis=1)
+    for blk in range(w.num_blocks):
+        assert untouched[blk] != (blk in built), f"block {blk}: built {blk in built}, untouched {untouched[blk]}"
+    if built:
+        compare_builds(w, summ, n_sample=300, seed=seed)
+    del w, summ
     torch.cuda.empty_cache()
