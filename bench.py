@@ -816,19 +816,19 @@ def prop1(args):
 if __name__ == "__main__":
     if "--prop1" in sys.argv:
         ap = argparse.ArgumentParser()
-        ap.add_argument("--prop1", default="512,2048",
+        ap.add_argument("--prop1", nargs="?", const="512,2048", default="512,2048",
                         help="comma-separated token budgets (shared-basis comparison)")
         ap.add_argument("--ctx", type=int, default=131072)
         ap.add_argument("--batch", type=int, default=8)
         prop1(ap.parse_args())
     elif "--ablation" in sys.argv:
         ap = argparse.ArgumentParser()
-        ap.add_argument("--ablation", default="3:2048,3:512,4:512",
+        ap.add_argument("--ablation", nargs="?", const="3:2048,3:512,4:512", default="3:2048,3:512,4:512",
                         help="comma-separated config:budget workloads (precision / rank ablation)")
         ablation(ap.parse_args())
     elif "--sweep" in sys.argv:
         ap = argparse.ArgumentParser()
-        ap.add_argument("--sweep", default="1,2,4,8,16,32",
+        ap.add_argument("--sweep", nargs="?", const="1,2,4,8,16,32", default="1,2,4,8,16,32",
                         help="comma-separated batch sizes (variable-length batch-scaling mode)")
         ap.add_argument("--layers", type=int, default=2)
         ap.add_argument("--steps", type=int, default=200)
